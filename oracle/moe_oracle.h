@@ -1,0 +1,102 @@
+/*
+ * CPU oracle of the W8A8 MoE expert block -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, single-threaded C model of what the block computes, used to
+ * check the GPU library. Only the tests, the smoke entry and the benchmark's
+ * CPU-baseline leg may load it; the library never calls it and shares no code
+ * with it.
+ *
+ * Sources (pages, by title):
+ *  - "FusedDeepMoE Kernel 深度分析报告" (FusedDeepMoE):
+ *      sec. 1.2 operator signature; sec. 4.1 dispatch (table + prefix-sum
+ *      grouping, quantisation in dispatch); sec. 4.2 combine weighted top-k
+ *      sum (LocalWindowCopy); sec. 6.1 dequant + SwiGLU epilogue; sec. 6.2
+ *      dequant + bf16 cast epilogue; sec. 7.2 BlockQuant dynamic quantisation;
+ *      sec. 9.1-9.3 math correspondence and the five-op SmallOps chain.
+ *  - "DeepSeek V4 Decode Optimization": sec. 0 W8A8 contract (amax floored by
+ *      an eps, scaled to the int8 maximum; scales stay fp32) and the rule
+ *      that the golden uses the kernel's operation order and dtypes.
+ *
+ * Every floating-point step is one IEEE fp32 operation, round-to-nearest-even,
+ * in the order written (build with -O2 -ffp-contract=off, no fast-math).
+ * Integer accumulation is exact (int64).
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int32_t T;        /* tokens                                   */
+    int32_t H;        /* hidden                                   */
+    int32_t I;        /* routed intermediate (GEMM1 outputs 2*I)  */
+    int32_t I_s;      /* shared intermediate, 0 = none            */
+    int32_t K;        /* top-k                                    */
+    int32_t E_g;      /* global routed experts                    */
+    int32_t ep_size;  /* E_loc = E_g / ep_size                    */
+    int32_t ep_rank;  /* local experts [ep_rank*E_loc, +E_loc)    */
+    float eps;        /* amax floor                               */
+} moe_oracle_dims;
+
+/* Optional intermediates, indexed by grouped row: routed rows [0, P) in
+ * (local expert, token, k) order, then shared-expert rows [P, P + T_act) in
+ * token order. Row strides: q_x/acc2/z: H; acc1: 2*max(I, I_s);
+ * h/q_h: max(I, I_s). Any pointer may be NULL. Only rows of the tokens that
+ * forward() computes are written. */
+typedef struct {
+    int32_t *sorted_pair;   /* [T*K] pair id t*K+k per routed row          */
+    int32_t *row_of_pair;   /* [T*K] routed row of a pair, -1 if dropped    */
+    int32_t *offsets;       /* [E_loc+1] exclusive prefix of the counts     */
+    int32_t *shared_token;  /* [T] token of shared row P+i                 */
+    int32_t *num_rows;      /* [3] P, T_act, ids out of range              */
+    int8_t  *q_x;           /* quantised GEMM1 input                        */
+    float   *xs;            /* its per-row scale                            */
+    int32_t *acc1;          /* GEMM1 int32 accumulators                     */
+    float   *h;             /* SwiGLU output                                */
+    int8_t  *q_h;           /* requantised GEMM2 input                      */
+    float   *hs;            /* its per-row scale                            */
+    int32_t *acc2;          /* GEMM2 int32 accumulators                     */
+    uint16_t *z;            /* bf16 GEMM2 output rows                       */
+} moe_oracle_trace;
+
+/* bf16 <-> fp32 (bit patterns in uint16). */
+float    moe_oracle_bf16_to_f32(uint16_t b);
+uint16_t moe_oracle_f32_to_bf16(float f);
+
+/* Dispatch grouping. Returns P (kept pairs). */
+int32_t moe_oracle_route(const moe_oracle_dims *d, const int32_t *expert_ids,
+                         const uint8_t *mask, int32_t *counts, int32_t *offsets,
+                         int32_t *sorted_pair, int32_t *row_of_pair, int32_t *n_bad);
+
+/* Per-row dynamic int8 quantisation of v[0..n). */
+void moe_oracle_quant_row(const float *v, int32_t n, float eps, int8_t *q, float *scale);
+
+/* C[m][n] = sum_k A[m][k] * B[n][k], exact. Returns 0, or -1 if a sum leaves int32. */
+int32_t moe_oracle_gemm_i8(const int8_t *A, const int8_t *B, int32_t M, int32_t N,
+                           int32_t Kd, int32_t *C);
+
+/* SwiGLU of one dequantised GEMM1 row: h[j] = silu(y[j]) * y[n_half + j]. */
+void moe_oracle_swiglu(const float *y, int32_t n_half, float *h);
+
+/* Whole block. token_subset (n_subset entries, NULL = every token) selects
+ * which output rows are computed; others are left untouched. Returns 0 or a
+ * negative value on bad arguments. All pointers are host pointers. */
+int32_t moe_oracle_forward(const moe_oracle_dims *d, const uint16_t *x,
+                           const int32_t *expert_ids, const float *expert_scales,
+                           const int8_t *w1, const float *w1s,
+                           const int8_t *w2, const float *w2s,
+                           const int8_t *sw1, const float *sw1s,
+                           const int8_t *sw2, const float *sw2s,
+                           const float *smooth, const float *share_smooth,
+                           const uint8_t *mask,
+                           const int32_t *token_subset, int32_t n_subset,
+                           uint16_t *output, uint16_t *share_output,
+                           int32_t *expert_token_nums, moe_oracle_trace *tr);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

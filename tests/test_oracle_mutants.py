@@ -1,0 +1,64 @@
+"""Plant plausible mistakes in a copy of the CPU oracle and check that the pins
+catch every one of them. Each mutant is a textual edit of oracle/moe_oracle.c,
+compiled with gcc into a temporary library; the real oracle is untouched."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from test_oracle_pins import PINS
+
+MUTANTS = {
+    "gate_up_swapped": [("float g = y[j];", "float g = y[n_half + j];"),
+                        ("h[j] = s * y[n_half + j];", "h[j] = s * y[j];")],
+    "sigmoid_sign": [("float ng = -g;", "float ng = g;")],
+    "dequant_drops_row_scale": [("y[i] = f * row_scale;", "y[i] = f;")],
+    "dequant_drops_weight_scale": [("f = f * wscale[i];", "f = f;")],
+    "quant_scale_not_div127": [("*scale = a * inv127;", "*scale = a;")],
+    "quant_truncates": [("float r = rintf(t);", "float r = truncf(t);")],
+    "quant_round_half_away": [("float r = rintf(t);", "float r = roundf(t);")],
+    "eps_added_not_floored": [("if (a < eps) a = eps;", "a = a + eps;")],
+    "gemm_weight_transposed": [("s += (int64_t)a[k] * (int64_t)b[k];",
+                                "s += (int64_t)a[k] * (int64_t)B[(size_t)k * N + n];")],
+    "bf16_truncates": [("u += 0x7FFFu + lsb;", "u += 0u * lsb;")],
+    "combine_ignores_weight": [("float m = moe_oracle_bf16_to_f32(zr[n]) * s;",
+                                "float m = moe_oracle_bf16_to_f32(zr[n]);")],
+    "combine_skips_first_k": [("if (row_of_pair[t * K + k] < 0) continue;\n            const float s",
+                               "if (k == 0 || row_of_pair[t * K + k] < 0) continue;\n            const float s")],
+    "route_unstable_order": [("int32_t row = cursor[e]++;", "int32_t row = offsets[e + 1] - 1 - (cursor[e]++ - offsets[e]);")],
+    "mask_ignored_in_route": [("    for (int32_t t = 0; t < T; ++t) {\n        if (mask && !mask[t]) continue;\n        for (int32_t k = 0; k < K; ++k) {\n            int32_t g = expert_ids[t * K + k];\n            if (g < 0 || g >= d->E_g) { ++bad; continue; }",
+                               "    for (int32_t t = 0; t < T; ++t) {\n        for (int32_t k = 0; k < K; ++k) {\n            int32_t g = expert_ids[t * K + k];\n            if (g < 0 || g >= d->E_g) { ++bad; continue; }"),
+                              ("    for (int32_t t = 0; t < T; ++t) {\n        if (mask && !mask[t]) continue;\n        for (int32_t k = 0; k < K; ++k) {\n            int32_t g = expert_ids[t * K + k];\n            if (g < 0 || g >= d->E_g) continue;",
+                               "    for (int32_t t = 0; t < T; ++t) {\n        for (int32_t k = 0; k < K; ++k) {\n            int32_t g = expert_ids[t * K + k];\n            if (g < 0 || g >= d->E_g) continue;")],
+    "smooth_after_quant": [("if (ev->smooth) v = v * ev->smooth[i];", "")],
+    "shared_uses_routed_smooth": [("expert_view ev = {sw1, sw1s, sw2, sw2s, share_smooth, Is};",
+                                   "expert_view ev = {sw1, sw1s, sw2, sw2s, smooth, Is};")],
+    "ep_rank_offset_ignored": [("const int32_t base = d->ep_rank * E;", "const int32_t base = 0;")],
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, source, tmp_path):
+    src = source
+    for old, new in MUTANTS[name]:
+        assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+        src = src.replace(old, new)
+    path = tmp_path / "mutant.c"
+    path.write_text(src)
+    so = str(tmp_path / "libmutant.so")
+    subprocess.check_call(["gcc", *oracle.CFLAGS, "-I", os.path.dirname(oracle.SRC), str(path), "-o", so, "-lm"])
+    caught = []
+    with oracle.using(so):
+        for pin in PINS:
+            try:
+                pin()
+            except (AssertionError, OverflowError, RuntimeError):
+                caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
