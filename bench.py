@@ -1,0 +1,187 @@
+"""Benchmark of the fused W8A8 MoE expert block on one MI355X.
+
+One step = one call of moe_w8a8_forward (routing, quantisation, GEMM1 with
+SwiGLU, requantisation, GEMM2, combine, shared expert) over one batch of the
+DeepSeek-V4-Flash-shaped decode workload: T = 8 token rows, hidden 4096,
+expert intermediate 2048, 256 routed experts resident, top-8, one shared
+expert of intermediate 2048, int8 weights with fp32 per-channel scales.
+
+Inputs are resident in HBM before timing. The routed and shared weights are
+held in `--layers` copies at distinct addresses and step i uses copy
+i % layers, as consecutive MoE layers of a model would, so every step streams
+its experts' weights from HBM rather than from the 256 MB last-level cache.
+
+Prints one JSON line: the metric (µs per MoE layer), the achieved HBM GB/s of
+the layer, the roofline of the dominant kernel (GEMM1) from HIP events
+recorded on the launch stream around that kernel in every timed step, and the
+CPU oracle's time on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_expert_ffn_route_amd as moe  # noqa: E402
+from moe_expert_ffn_route_amd import binding, synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(case, counts):
+    """Bytes the layer must move at least once: every touched expert's weights
+    and scales, the shared expert's, the activations in and out."""
+    s = case.spec
+    H, I, Is, T, K = s.H, s.I, s.I_s, s.T, s.K
+    touched = int((counts > 0).sum())
+    per_expert = 3 * H * I + 4 * (2 * I + H)
+    shared = (3 * H * Is + 4 * (2 * Is + H)) if Is else 0
+    act = 2 * T * H + 8 * T * K + 2 * T * H * (2 if Is else 1)
+    if case.smooth is not None:
+        act += 4 * s.E_loc * H
+    gemm1 = touched * (2 * I * H + 8 * I) + ((2 * Is * H + 8 * Is) if Is else 0)
+    rows = int(counts.sum()) + (T if Is else 0)
+    gemm1 += rows * (H + 4 + 4 * max(I, Is))  # q_x and xs read, h written
+    return touched * per_expert + shared + act, gemm1, touched, rows
+
+
+def cpu_baseline(case, budget_s=12.0, max_reps=8):
+    """The CPU oracle as it stands, single-threaded, on the same batch."""
+    import oracle  # test infrastructure: only this leg of the benchmark uses it
+    oracle.lib()
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while len(times) < max_reps and (not times or time.perf_counter() < t_end):
+        t0 = time.perf_counter()
+        oracle.forward(case)
+        times.append(time.perf_counter() - t0)
+    return float(np.mean(times)) * 1e6, len(times)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1, help="workload index (0-4); 1 is the headline decode step")
+    ap.add_argument("--layers", type=int, default=4, help="weight copies cycled through to keep the cache cold")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stage-events", action="store_true",
+                    help="time the steps without per-stage events (stage times then come from a second pass)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(expert parallelism across GPUs is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    moe.library()  # fail loudly if the HIP library is missing
+
+    spec = synth.CONFIGS[args.config]
+    log(f"[bench] workload {spec.name}: generating inputs")
+    t0 = time.perf_counter()
+    case = synth.config_case(args.config)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s; uploading")
+    dev = moe.upload(case)
+    wkeys = [k for k in ("gmm1_weight", "gmm1_weight_scale", "gmm2_weight", "gmm2_weight_scale",
+                         "share_gmm1_weight", "share_gmm1_weight_scale", "share_gmm2_weight",
+                         "share_gmm2_weight_scale") if dev.get(k) is not None]
+    layers = [dev] + [dict(dev, **{k: dev[k].clone() for k in wkeys}) for _ in range(max(0, args.layers - 1))]
+    dims = moe.dims_of_case(case)
+    runner = moe.Runner(dims)
+    stream = torch.cuda.Stream()
+    n_ev = len(binding.STAGES) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    ev_ptrs = []
+    for evs in events:
+        for e in evs:
+            e.record(stream)  # materialise the HIP event handles
+        ev_ptrs.append((ctypes.c_void_p * n_ev)(*[e.cuda_event for e in evs]))
+    torch.cuda.synchronize()
+
+    log(f"[bench] warmup {args.warmup} steps")
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            runner(layers[i % len(layers)], stream=stream)
+    torch.cuda.synchronize()
+    counts = runner.expert_token_nums.cpu().numpy()
+
+    log(f"[bench] timing {args.steps} steps")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    dbgs = [binding.Debug(stage_events=ctypes.cast(p, ctypes.c_void_p).value) for p in ev_ptrs]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        t_start.record(stream)
+        for i in range(args.steps):
+            runner(layers[i % len(layers)], dbg=None if args.no_stage_events else dbgs[i], stream=stream)
+        t_stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_stop)
+    if args.no_stage_events:
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                runner(layers[i % len(layers)], dbg=dbgs[i], stream=stream)
+        torch.cuda.synchronize()
+    ms_per_step = total_ms / args.steps
+    stage_us = {name: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]) * 1e3)
+                for j, name in enumerate(binding.STAGES)}
+
+    out = runner.output.float()
+    if not torch.isfinite(out).all():
+        raise RuntimeError("non-finite output")
+
+    layer_bytes, gemm1_bytes, touched, rows = algorithmic_bytes(case, counts)
+    us = ms_per_step * 1e3
+    g1_us = stage_us["gemm1"]
+    g1_gbs = gemm1_bytes / (g1_us * 1e-6) / 1e9
+    rec = {
+        "metric": "µs per MoE layer (T=8 decode); achieved HBM GB/s in hbm_gbps",
+        "value": round(us, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "tokens": spec.T, "hidden": spec.H, "inter": spec.I,
+                   "experts": spec.E_g, "topk": spec.K, "share_inter": spec.I_s,
+                   "touched_experts": touched, "grouped_rows": rows, "weight_copies": len(layers)},
+        "hbm_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
+        "tokens_per_s": round(spec.T / (us * 1e-6), 1),
+        "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "roofline": {"kernel": "gemm1_swiglu", "bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": gemm1_bytes, "avg_us": round(g1_us, 2)},
+    }
+    if args.no_cpu_baseline:
+        rec["cpu_baseline"] = None
+    else:
+        log("[bench] CPU oracle baseline")
+        cpu_us, reps = cpu_baseline(case)
+        rec["cpu_baseline"] = {"value": round(cpu_us, 1), "unit": "us", "cores": 1, "kind": "oracle",
+                               "sample": f"the full batch of this workload, {reps} runs, single-threaded C oracle"}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

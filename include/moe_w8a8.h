@@ -1,0 +1,174 @@
+/*
+ * moe_w8a8 -- fused W8A8 MoE expert block for AMD MI355X (gfx950).
+ *
+ * One call runs the expert block of a DeepSeek-style decode step on one GPU:
+ *   1. dispatch grouping: per-local-expert token counts (expert_token_nums),
+ *      their exclusive prefix sum and the stable (expert, token, k) row order;
+ *   2. per-row dynamic INT8 quantisation of x (optionally times smooth scales);
+ *   3. grouped INT8 GEMM1 (gate and up halves) with exact int32 accumulation;
+ *   4. dequantisation by per-output-channel weight scale x per-row scale,
+ *      SwiGLU, and per-row INT8 requantisation;
+ *   5. grouped INT8 GEMM2 (down) and dequantisation to bf16;
+ *   6. routing-weighted top-k combine into `output`, and the optional shared
+ *      expert on every active token into `share_output`.
+ *
+ * Passages that define the operation (pages, by title):
+ *   "FusedDeepMoE Kernel 深度分析报告": sec. 1.2 (inputs, outputs, attributes),
+ *     sec. 2.1 (tiling info: ep size/rank, experts per rank, bs, k, h, 2*inter),
+ *     sec. 4.1 (dispatch: counts, prefix sum, quantisation fused in dispatch),
+ *     sec. 4.2 (combine: fp32 sum over k of row x routing weight, one bf16 cast),
+ *     sec. 6.1 (int32 -> fp32, x weight scale per column, x per-token scale,
+ *               left half x/(1+exp(-x))), sec. 6.2 (same dequant, cast to bf16),
+ *     sec. 7.2 (BlockQuant: scale = max|h|/127, q = rint(h*127/max)),
+ *     sec. 9.4 (supported ranges).
+ *   "DeepSeek V4 Decode Optimization" sec. 0: INT8 weights with FP32
+ *     per-output-channel scales; activations quantised per token, amax
+ *     floored by an eps and rescaled to 127; scales stay FP32.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers, row-major, owned by the caller; the
+ *     library never frees or retains them. 16-byte alignment is required for
+ *     x, output, share_output and every weight; the workspace must be 256-byte
+ *     aligned.
+ *   - Calls are stream-ordered and asynchronous: no host synchronisation, no
+ *     allocation. The library keeps no state between calls, so calls are
+ *     reentrant when each uses its own workspace; two calls in flight that
+ *     share one workspace race.
+ *   - Host-detectable errors (bad sizes, NULL required pointers, misaligned
+ *     pointers, short workspace) return a negative status and launch nothing.
+ *     A pair whose expert id lies outside [0, moe_expert_num) is dropped and
+ *     counted in a diagnostics word (readable through moe_w8a8_debug_t).
+ *     HIP launch failures return MOE_ERR_HIP; faults inside kernels surface at
+ *     the caller's next synchronisation.
+ */
+#ifndef MOE_W8A8_H
+#define MOE_W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_W8A8_API __attribute__((visibility("default")))
+#else
+#define MOE_W8A8_API
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* NULL / misaligned pointer, inconsistent sizes */
+    MOE_ERR_UNSUPPORTED = -2, /* legal for the operator, outside what this build runs */
+    MOE_ERR_WORKSPACE = -3,   /* workspace pointer NULL or workspace_bytes too small */
+    MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} moe_status_t;
+
+/* Sizes and attributes of one call (FusedDeepMoE sec. 1.2 attributes and the
+ * sec. 2.1 tiling struct, minus the communication-only group_ep / global_bs). */
+typedef struct {
+    int32_t num_tokens;     /* T >= 0 rows of x; T == 0 is legal (all counts 0)     */
+    int32_t hidden;         /* H > 0, multiple of 256                                */
+    int32_t inter;          /* I > 0, multiple of 256; GEMM1 has 2*I outputs:        */
+                            /*   gate = rows [0, I), up = rows [I, 2I) of gmm1_weight */
+    int32_t share_inter;    /* I_s: shared-expert intermediate, multiple of 256;     */
+                            /*   0 = no shared expert                                */
+    int32_t topk;           /* K in [1, 16]                                          */
+    int32_t moe_expert_num; /* E_g >= 1 global routed experts                        */
+    int32_t ep_rank_size;   /* >= 1, divides E_g; E_loc = E_g / ep_rank_size <= 512  */
+    int32_t ep_rank_id;     /* in [0, ep_rank_size): local experts are global ids    */
+                            /*   [ep_rank_id*E_loc, (ep_rank_id+1)*E_loc)            */
+    int32_t quant_mode;     /* 1 = per-token dynamic INT8 (the only mode)            */
+    float amax_eps;         /* > 0: row amax floor (e.g. 1e-6)                       */
+} moe_w8a8_dims_t;
+
+/* Optional intermediates for testing (every field may be NULL; all are device
+ * buffers written in stream order). Rows are "grouped rows": rows [0, P) are
+ * the kept routed pairs in (local expert, token, k) order, rows [P, P+T_act)
+ * the shared expert's rows, one per active token in token order. With
+ * R = T*K + T rows of capacity and Imax = max(I, I_s):                       */
+typedef struct {
+    int32_t *sorted_pair;   /* [T*K]   pair id t*K+k of routed row r           */
+    int32_t *row_of_pair;   /* [T*K]   routed row of pair t*K+k, -1 if dropped */
+    int32_t *group_offset;  /* [E_loc+1] exclusive prefix sum of the counts    */
+    int32_t *shared_token;  /* [T]     token of shared row P+i                 */
+    int32_t *num_rows;      /* [4]     P, T_act, #ids out of range, #chunks    */
+    int8_t  *q_x;           /* [R, H]  GEMM1 input codes                       */
+    float   *xs;            /* [R]     their per-row dequant scale             */
+    int32_t *acc1;          /* [R, 2*Imax] GEMM1 int32 accumulators            */
+    float   *h;             /* [R, Imax] SwiGLU output (fp32)                  */
+    int8_t  *q_h;           /* [R, Imax] GEMM2 input codes                     */
+    float   *hs;            /* [R]     their per-row dequant scale             */
+    int32_t *acc2;          /* [R, H]  GEMM2 int32 accumulators                */
+    uint16_t *z;            /* [R, H]  bf16 GEMM2 output rows                  */
+    void   **stage_events;  /* [7] caller-created hipEvent_t, recorded on the
+                               stream before routing and after each stage:
+                               route, quant, GEMM1, requant, GEMM2, combine   */
+} moe_w8a8_debug_t;
+
+/* Workspace bytes that moe_w8a8_forward needs for these dims. The size depends
+ * only on T, H, I, I_s, K and E_loc. Returns MOE_ERR_INVALID_ARG for NULL
+ * arguments and the same size errors as moe_w8a8_forward. */
+MOE_W8A8_API moe_status_t moe_w8a8_workspace_size(const moe_w8a8_dims_t *dims, size_t *bytes);
+
+/*
+ * The fused expert block (FusedDeepMoE sec. 1.2 signature; EP communication
+ * left out: non-local pairs are dropped, so `output` holds this rank's
+ * partial sum, exactly as one expert-parallel rank computes before combine).
+ *
+ *  x                  bf16 [T, H]   (x, expert_ids, expert_scales and output
+ *                     may be NULL when T == 0)
+ *  expert_ids         int32 [T, K] global expert ids
+ *  expert_scales      fp32 [T, K] routing weights
+ *  gmm1_weight        int8 [E_loc, 2I, H]  (output channel major, H contiguous)
+ *  gmm1_weight_scale  fp32 [E_loc, 2I]
+ *  gmm2_weight        int8 [E_loc, H, I]   (I contiguous)
+ *  gmm2_weight_scale  fp32 [E_loc, H]
+ *  share_gmm1_weight  int8 [2I_s, H], share_gmm1_weight_scale fp32 [2I_s]  } all four NULL
+ *  share_gmm2_weight  int8 [H, I_s],  share_gmm2_weight_scale fp32 [H]     } iff I_s == 0
+ *  expert_smooth_scales fp32 [E_loc, H] or NULL: x is multiplied by the row of
+ *                     the pair's expert before quantisation
+ *  share_smooth_scales  fp32 [H] or NULL (requires I_s > 0)
+ *  x_active_mask      uint8 [T] (0 / non-0) or NULL = every token active
+ *  output             bf16 [T, H]  sum over kept pairs (k ascending, fp32) of
+ *                     expert row x routing weight, one bf16 rounding; rows of
+ *                     inactive tokens or tokens with no kept pair are 0
+ *  share_output       bf16 [T, H]  shared-expert output (unweighted), 0 on
+ *                     inactive tokens; required iff I_s > 0, else ignored
+ *  expert_token_nums  int32 [E_loc] kept pairs per local expert
+ *  workspace          device scratch of >= moe_w8a8_workspace_size() bytes;
+ *                     need not be zeroed; contents are undefined afterwards
+ *  dbg                NULL in production; else intermediates (above)
+ *  stream             hipStream_t to launch on (NULL = the default stream)
+ */
+MOE_W8A8_API moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *dims,
+                              const void *x,
+                              const int32_t *expert_ids,
+                              const float *expert_scales,
+                              const int8_t *gmm1_weight,
+                              const float *gmm1_weight_scale,
+                              const int8_t *gmm2_weight,
+                              const float *gmm2_weight_scale,
+                              const int8_t *share_gmm1_weight,
+                              const float *share_gmm1_weight_scale,
+                              const int8_t *share_gmm2_weight,
+                              const float *share_gmm2_weight_scale,
+                              const float *expert_smooth_scales,
+                              const float *share_smooth_scales,
+                              const uint8_t *x_active_mask,
+                              void *output,
+                              void *share_output,
+                              int32_t *expert_token_nums,
+                              void *workspace,
+                              size_t workspace_bytes,
+                              const moe_w8a8_debug_t *dbg,
+                              void *stream);
+
+/* Static description of a status code. Never NULL. */
+MOE_W8A8_API const char *moe_w8a8_status_string(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_W8A8_H */

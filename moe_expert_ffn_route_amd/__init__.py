@@ -1,0 +1,8 @@
+"""MI355X (gfx950) fused W8A8 MoE expert block.
+
+The compute lives in libmoe_w8a8.so (hand-written HIP kernels behind the C ABI
+of include/moe_w8a8.h); `binding` is its ctypes front end and `synth` draws
+seeded synthetic inputs.
+"""
+from .binding import (Debug, Dims, MoeError, Runner, debug_buffers, dims_of_case, library, make_dims,  # noqa: F401
+                      moe_w8a8_forward, moe_w8a8_status_string, moe_w8a8_workspace_size, upload)

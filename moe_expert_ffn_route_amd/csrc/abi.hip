@@ -1,0 +1,270 @@
+// C ABI of libmoe_w8a8: argument validation, workspace carve-up and the
+// stream-ordered launch sequence of the expert block
+//   route -> quant_gather -> GEMM1 (+dequant, SwiGLU) -> requant
+//         -> GEMM2 (+dequant to bf16) -> combine
+// which is the unfused five-op chain of "FusedDeepMoE Kernel 深度分析报告"
+// sec. 9.3 with the dequant/SwiGLU/quant fused into the GEMMs' epilogues
+// (sec. 6.1, 6.2, 7.2). Nothing here allocates or synchronises.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/moe_w8a8.h"
+#include "internal.h"
+
+using namespace moe;
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t up256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+moe_status_t check_dims(const moe_w8a8_dims_t *d) {
+    if (!d) return MOE_ERR_INVALID_ARG;
+    if (d->num_tokens < 0 || d->hidden <= 0 || d->inter <= 0 || d->share_inter < 0 || d->topk <= 0 ||
+        d->moe_expert_num <= 0 || d->ep_rank_size <= 0 || d->ep_rank_id < 0 ||
+        d->ep_rank_id >= d->ep_rank_size || d->moe_expert_num % d->ep_rank_size != 0)
+        return MOE_ERR_INVALID_ARG;
+    if (!(d->amax_eps > 0.0f) || !isfinite(d->amax_eps)) return MOE_ERR_INVALID_ARG;
+    if (d->quant_mode != 1) return MOE_ERR_UNSUPPORTED;
+    if (d->topk > kMaxTopK || d->num_tokens > kMaxTokens) return MOE_ERR_UNSUPPORTED;
+    if (d->moe_expert_num / d->ep_rank_size > kMaxLocalExperts) return MOE_ERR_UNSUPPORTED;
+    if (d->hidden % 256 || d->inter % 256 || d->share_inter % 256) return MOE_ERR_UNSUPPORTED;
+    if (d->hidden > 16384 || d->inter > 16384 || d->share_inter > 16384) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+Layout make_layout(const moe_w8a8_dims_t *d) {
+    Layout L;
+    const size_t T = d->num_tokens, K = d->topk, H = d->hidden;
+    const size_t TK = T * K;
+    const size_t E = d->moe_expert_num / d->ep_rank_size;
+    const bool shared = d->share_inter > 0;
+    L.imax = d->inter > d->share_inter ? d->inter : d->share_inter;
+    L.rows_max = static_cast<int>(TK + T);
+    const size_t nonempty = E < TK ? E : TK;
+    L.max_chunks = static_cast<int>(nonempty + TK / kChunkRows + (shared ? (T + kChunkRows - 1) / kChunkRows : 0));
+    const size_t R = L.rows_max;
+    size_t o = 0;
+    L.meta = o;        o = up256(o + sizeof(int32_t) * kMetaWords);
+    L.offsets = o;     o = up256(o + sizeof(int32_t) * (E + 2));
+    L.sorted_pair = o; o = up256(o + sizeof(int32_t) * TK);
+    L.row_of_pair = o; o = up256(o + sizeof(int32_t) * TK);
+    L.row_token = o;   o = up256(o + sizeof(int32_t) * R);
+    L.row_group = o;   o = up256(o + sizeof(int32_t) * R);
+    L.chunks = o;      o = up256(o + sizeof(int4) * L.max_chunks);
+    L.q_x = o;         o = up256(o + R * H);
+    L.xs = o;          o = up256(o + sizeof(float) * R);
+    L.h = o;           o = up256(o + sizeof(float) * R * L.imax);
+    L.q_h = o;         o = up256(o + R * L.imax);
+    L.hs = o;          o = up256(o + sizeof(float) * R);
+    L.z = o;           o = up256(o + sizeof(uint16_t) * TK * H);
+    L.total = o;
+    return L;
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_w8a8_workspace_size(const moe_w8a8_dims_t *dims, size_t *bytes) {
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    const moe_status_t st = check_dims(dims);
+    if (st != MOE_OK) return st;
+    *bytes = make_layout(dims).total;
+    return MOE_OK;
+}
+
+extern "C" const char *moe_w8a8_status_string(moe_status_t s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument (NULL or misaligned pointer, or inconsistent sizes)";
+        case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x, const int32_t *expert_ids,
+                                         const float *expert_scales, const int8_t *gmm1_weight,
+                                         const float *gmm1_weight_scale, const int8_t *gmm2_weight,
+                                         const float *gmm2_weight_scale, const int8_t *share_gmm1_weight,
+                                         const float *share_gmm1_weight_scale, const int8_t *share_gmm2_weight,
+                                         const float *share_gmm2_weight_scale, const float *expert_smooth_scales,
+                                         const float *share_smooth_scales, const uint8_t *x_active_mask,
+                                         void *output, void *share_output, int32_t *expert_token_nums,
+                                         void *workspace, size_t workspace_bytes, const moe_w8a8_debug_t *dbg,
+                                         void *stream) {
+    moe_status_t st = check_dims(d);
+    if (st != MOE_OK) return st;
+    const bool shared = d->share_inter > 0;
+    const int n_share_ptrs = (share_gmm1_weight != nullptr) + (share_gmm1_weight_scale != nullptr) +
+                             (share_gmm2_weight != nullptr) + (share_gmm2_weight_scale != nullptr);
+    const bool need_tok = d->num_tokens > 0;
+    if ((need_tok && (!x || !expert_ids || !expert_scales || !output)) || !gmm1_weight || !gmm1_weight_scale ||
+        !gmm2_weight || !gmm2_weight_scale || !expert_token_nums)
+        return MOE_ERR_INVALID_ARG;
+    if (shared ? (n_share_ptrs != 4 || (need_tok && !share_output)) : (n_share_ptrs != 0 || share_smooth_scales))
+        return MOE_ERR_INVALID_ARG;
+    const void *a16[] = {x, output, gmm1_weight, gmm2_weight, share_gmm1_weight, share_gmm2_weight,
+                         expert_smooth_scales, share_smooth_scales, shared ? share_output : nullptr};
+    for (const void *p : a16)
+        if (p && !aligned(p, 16)) return MOE_ERR_INVALID_ARG;
+    const void *a4[] = {expert_ids, expert_scales, gmm1_weight_scale, gmm2_weight_scale,
+                        share_gmm1_weight_scale, share_gmm2_weight_scale, expert_token_nums};
+    for (const void *p : a4)
+        if (p && !aligned(p, 4)) return MOE_ERR_INVALID_ARG;
+
+    const Layout L = make_layout(d);
+    if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARG;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    auto I32 = [&](size_t off) { return reinterpret_cast<int32_t *>(ws + off); };
+    int32_t *meta = I32(L.meta);
+    const int T = d->num_tokens, K = d->topk, H = d->hidden;
+    const int E = d->moe_expert_num / d->ep_rank_size;
+    const moe_w8a8_debug_t nodbg = {};
+    const moe_w8a8_debug_t &D = dbg ? *dbg : nodbg;
+    auto mark = [&](int i) {
+        return !D.stage_events || hipEventRecord(static_cast<hipEvent_t>(D.stage_events[i]), s) == hipSuccess;
+    };
+    if (!mark(0)) return MOE_ERR_HIP;
+
+    RouteArgs ra;
+    ra.ids = expert_ids;
+    ra.mask = x_active_mask;
+    ra.T = T;
+    ra.K = K;
+    ra.E_g = d->moe_expert_num;
+    ra.E_loc = E;
+    ra.base = d->ep_rank_id * E;
+    ra.has_shared = shared;
+    ra.counts_out = expert_token_nums;
+    ra.offsets = I32(L.offsets);
+    ra.sorted_pair = I32(L.sorted_pair);
+    ra.row_of_pair = I32(L.row_of_pair);
+    ra.row_token = I32(L.row_token);
+    ra.row_group = I32(L.row_group);
+    ra.chunks = reinterpret_cast<int4 *>(ws + L.chunks);
+    ra.meta = meta;
+    ra.dbg_shared_token = D.shared_token;
+    if (launch_route(ra, s) != hipSuccess || !mark(1)) return MOE_ERR_HIP;
+
+    if (T > 0) {
+        QuantArgs qa;
+        qa.x = static_cast<const uint16_t *>(x);
+        qa.row_token = ra.row_token;
+        qa.row_group = ra.row_group;
+        qa.meta = meta;
+        qa.smooth = expert_smooth_scales;
+        qa.share_smooth = share_smooth_scales;
+        qa.E_loc = E;
+        qa.H = H;
+        qa.has_shared = shared;
+        qa.rows_max = L.rows_max;
+        qa.eps = d->amax_eps;
+        qa.q = reinterpret_cast<int8_t *>(ws + L.q_x);
+        qa.scale = reinterpret_cast<float *>(ws + L.xs);
+        if (launch_quant(qa, s) != hipSuccess || !mark(2)) return MOE_ERR_HIP;
+
+        GemmArgs g1 = {};
+        g1.A = qa.q;
+        g1.a_stride = H;
+        g1.a_scale = qa.scale;
+        g1.W = gmm1_weight;
+        g1.Ws = gmm1_weight_scale;
+        g1.W_sh = share_gmm1_weight;
+        g1.Ws_sh = share_gmm1_weight_scale;
+        g1.I = d->inter;
+        g1.I_s = d->share_inter;
+        g1.H = H;
+        g1.E_loc = E;
+        g1.imax = L.imax;
+        g1.g_lo = 0;
+        g1.g_hi = E + 1;
+        g1.n_tiles = L.imax / kTileN;
+        g1.chunks = ra.chunks;
+        g1.meta = meta;
+        g1.row_token = ra.row_token;
+        g1.h = reinterpret_cast<float *>(ws + L.h);
+        g1.dbg_acc = D.acc1;
+        if (launch_gemm1(g1, L.max_chunks, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
+
+        RequantArgs rq;
+        rq.h = g1.h;
+        rq.row_group = ra.row_group;
+        rq.meta = meta;
+        rq.E_loc = E;
+        rq.I = d->inter;
+        rq.I_s = d->share_inter;
+        rq.imax = L.imax;
+        rq.has_shared = shared;
+        rq.rows_max = L.rows_max;
+        rq.eps = d->amax_eps;
+        rq.q = reinterpret_cast<int8_t *>(ws + L.q_h);
+        rq.scale = reinterpret_cast<float *>(ws + L.hs);
+        if (launch_requant(rq, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;
+
+        GemmArgs g2 = g1;
+        g2.A = rq.q;
+        g2.a_stride = L.imax;
+        g2.a_scale = rq.scale;
+        g2.W = gmm2_weight;
+        g2.Ws = gmm2_weight_scale;
+        g2.W_sh = share_gmm2_weight;
+        g2.Ws_sh = share_gmm2_weight_scale;
+        g2.n_tiles = H / (2 * kTileN);
+        g2.h = nullptr;
+        g2.z = reinterpret_cast<uint16_t *>(ws + L.z);
+        g2.share_out = static_cast<uint16_t *>(share_output);
+        g2.dbg_acc = D.acc2;
+        g2.dbg_z = D.z;
+        // the contraction length of GEMM2 is the group's intermediate size
+        if (!shared || d->share_inter == d->inter) {
+            if (launch_gemm2(g2, L.max_chunks, d->inter, s) != hipSuccess) return MOE_ERR_HIP;
+        } else {
+            g2.g_hi = E;
+            if (launch_gemm2(g2, L.max_chunks, d->inter, s) != hipSuccess) return MOE_ERR_HIP;
+            g2.g_lo = E;
+            g2.g_hi = E + 1;
+            if (launch_gemm2(g2, L.max_chunks, d->share_inter, s) != hipSuccess) return MOE_ERR_HIP;
+        }
+        if (!mark(5)) return MOE_ERR_HIP;
+
+        CombineArgs ca;
+        ca.z = g2.z;
+        ca.row_of_pair = ra.row_of_pair;
+        ca.scales = expert_scales;
+        ca.mask = x_active_mask;
+        ca.T = T;
+        ca.K = K;
+        ca.H = H;
+        ca.has_shared = shared;
+        ca.out = static_cast<uint16_t *>(output);
+        ca.share_out = static_cast<uint16_t *>(share_output);
+        if (launch_combine(ca, s) != hipSuccess || !mark(6)) return MOE_ERR_HIP;
+    } else {
+        for (int i = 2; i < 7; ++i)
+            if (!mark(i)) return MOE_ERR_HIP;
+    }
+
+    // optional intermediates that live in the workspace
+    struct Copy { void *dst; size_t off, bytes; };
+    const size_t R = L.rows_max, TK = static_cast<size_t>(T) * K;
+    const Copy copies[] = {
+        {D.sorted_pair, L.sorted_pair, sizeof(int32_t) * TK},
+        {D.row_of_pair, L.row_of_pair, sizeof(int32_t) * TK},
+        {D.group_offset, L.offsets, sizeof(int32_t) * (E + 1)},
+        {D.num_rows, L.meta, sizeof(int32_t) * kMetaWords},
+        {D.q_x, L.q_x, R * H},
+        {D.xs, L.xs, sizeof(float) * R},
+        {D.h, L.h, sizeof(float) * R * L.imax},
+        {D.q_h, L.q_h, R * L.imax},
+        {D.hs, L.hs, sizeof(float) * R},
+    };
+    for (const Copy &c : copies)
+        if (c.dst && c.bytes && hipMemcpyAsync(c.dst, ws + c.off, c.bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+            return MOE_ERR_HIP;
+    return MOE_OK;
+}

@@ -1,0 +1,61 @@
+// Weighted top-k combine ("FusedDeepMoE Kernel 深度分析报告" sec. 4.2,
+// LocalWindowCopy): for each token, an fp32 sum that starts at zero and adds,
+// for k = 0..K-1 in order, the expert's bf16 row (cast to fp32) times the
+// routing weight; one round-to-nearest-even cast to bf16 at the end. Pairs
+// that were dropped (inactive token, non-local expert, bad id) contribute
+// nothing, so such tokens get zero rows. The sum order is fixed per element,
+// so the result is deterministic.
+//
+// One workgroup per token; each thread owns 8 consecutive channels (16-byte
+// loads of each expert row, 16-byte stores). It also clears the shared-expert
+// rows of inactive tokens, which GEMM2 never writes.
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+    const int t = blockIdx.x;
+    const bool act = !a.mask || a.mask[t];
+    const int32_t *rop = a.row_of_pair + static_cast<size_t>(t) * a.K;
+    const float *wt = a.scales + static_cast<size_t>(t) * a.K;
+    for (int c = threadIdx.x * 8; c < a.H; c += kThreads * 8) {
+        float sum[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sum[i] = 0.0f;
+        for (int k = 0; k < a.K; ++k) {
+            const int row = rop[k];
+            if (row < 0) continue;
+            const float wk = wt[k];
+            const uint4 raw = *reinterpret_cast<const uint4 *>(a.z + static_cast<size_t>(row) * a.H + c);
+            const uint32_t v[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float m0 = bf16_to_f32(static_cast<uint16_t>(v[i] & 0xFFFFu)) * wk;
+                const float m1 = bf16_to_f32(static_cast<uint16_t>(v[i] >> 16)) * wk;
+                sum[2 * i] = sum[2 * i] + m0;
+                sum[2 * i + 1] = sum[2 * i + 1] + m1;
+            }
+        }
+        uint4 o;
+        o.x = f32_to_bf16(sum[0]) | (static_cast<uint32_t>(f32_to_bf16(sum[1])) << 16);
+        o.y = f32_to_bf16(sum[2]) | (static_cast<uint32_t>(f32_to_bf16(sum[3])) << 16);
+        o.z = f32_to_bf16(sum[4]) | (static_cast<uint32_t>(f32_to_bf16(sum[5])) << 16);
+        o.w = f32_to_bf16(sum[6]) | (static_cast<uint32_t>(f32_to_bf16(sum[7])) << 16);
+        *reinterpret_cast<uint4 *>(a.out + static_cast<size_t>(t) * a.H + c) = o;
+        if (a.has_shared && !act)
+            *reinterpret_cast<uint4 *>(a.share_out + static_cast<size_t>(t) * a.H + c) = make_uint4(0, 0, 0, 0);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
+    if (a.T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

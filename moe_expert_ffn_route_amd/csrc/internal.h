@@ -1,0 +1,121 @@
+// Internal definitions shared by the HIP sources of libmoe_w8a8 (not part of
+// the public C ABI in include/moe_w8a8.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;            // CDNA wavefront width
+constexpr int kMaxLocalExperts = 512;
+constexpr int kRouteThreads = 1024;  // the routing kernel runs as one workgroup
+constexpr int kRouteWaves = kRouteThreads / kWave;
+constexpr int kChunkRows = 64;       // grouped rows per GEMM work item (4 MFMA row tiles)
+constexpr int kTileN = 16;           // MFMA 16x16x64 output tile edge
+constexpr int kMaxTopK = 16;
+constexpr int kMaxTokens = 1 << 16;
+
+// meta words written by the routing kernel
+enum { kMetaP = 0, kMetaTAct = 1, kMetaBad = 2, kMetaChunks = 3, kMetaWords = 4 };
+
+// Carve-up of the caller's workspace (byte offsets, 256-aligned).
+struct Layout {
+    int rows_max;    // T*K + T grouped-row capacity
+    int max_chunks;  // upper bound of GEMM work items
+    int imax;        // max(I, I_s)
+    size_t meta, offsets, sorted_pair, row_of_pair, row_token, row_group, chunks;
+    size_t q_x, xs, h, q_h, hs, z, total;
+};
+
+struct RouteArgs {
+    const int32_t *ids;
+    const uint8_t *mask;
+    int T, K, E_g, E_loc, base, has_shared;
+    int32_t *counts_out;   // expert_token_nums [E_loc]
+    int32_t *offsets;      // [E_loc + 2]
+    int32_t *sorted_pair;  // [T*K]
+    int32_t *row_of_pair;  // [T*K]
+    int32_t *row_token;    // [rows_max]
+    int32_t *row_group;    // [rows_max]
+    int4 *chunks;          // [max_chunks] (group, first row, rows, 0)
+    int32_t *meta;         // [kMetaWords]
+    int32_t *dbg_shared_token;  // [T] or null
+};
+
+struct QuantArgs {
+    const uint16_t *x;       // bf16 [T, H]
+    const int32_t *row_token;
+    const int32_t *row_group;
+    const int32_t *meta;
+    const float *smooth;        // [E_loc, H] or null
+    const float *share_smooth;  // [H] or null
+    int E_loc, H, has_shared, rows_max;
+    float eps;
+    int8_t *q;    // [rows_max, H]
+    float *scale; // [rows_max]
+};
+
+struct RequantArgs {
+    const float *h;           // [rows_max, imax]
+    const int32_t *row_group;
+    const int32_t *meta;
+    int E_loc, I, I_s, imax, has_shared, rows_max;
+    float eps;
+    int8_t *q;     // [rows_max, imax]
+    float *scale;  // [rows_max]
+};
+
+struct GemmArgs {
+    // activations: grouped int8 rows and their per-row scale
+    const int8_t *A;
+    int a_stride;
+    const float *a_scale;
+    // weights [E_loc, N, K] routed, [N, K] shared, and per-output-channel scales
+    const int8_t *W;
+    const float *Ws;
+    const int8_t *W_sh;
+    const float *Ws_sh;
+    int I, I_s, H, E_loc, imax;
+    int g_lo, g_hi;   // only chunks of groups in [g_lo, g_hi)
+    int n_tiles;      // work items per chunk along N
+    const int4 *chunks;
+    const int32_t *meta;
+    const int32_t *row_token;
+    // outputs
+    float *h;              // GEMM1: [rows_max, imax]
+    uint16_t *z;           // GEMM2 routed rows: [rows_max, H] bf16
+    uint16_t *share_out;   // GEMM2 shared rows: [T, H] bf16 indexed by token
+    int32_t *dbg_acc;      // optional [rows_max, 2*imax] (GEMM1) / [rows_max, H] (GEMM2)
+    uint16_t *dbg_z;       // optional [rows_max, H]
+};
+
+struct CombineArgs {
+    const uint16_t *z;
+    const int32_t *row_of_pair;
+    const float *scales;
+    const uint8_t *mask;
+    int T, K, H, has_shared;
+    uint16_t *out;
+    uint16_t *share_out;
+};
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
+hipError_t launch_requant(const RequantArgs &a, hipStream_t s);
+hipError_t launch_gemm1(const GemmArgs &a, int max_chunks, hipStream_t s);
+hipError_t launch_gemm2(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+
+// bf16 helpers (round to nearest even)
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+}  // namespace moe

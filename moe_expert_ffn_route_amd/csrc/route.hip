@@ -1,0 +1,202 @@
+// Dispatch grouping ("FusedDeepMoE Kernel 深度分析报告" sec. 4.1: per-expert
+// token counts, their prefix sum and the expand index; sec. 5.2.1: only active
+// tokens are counted; "DeepSeek V4 Decode Optimization" sec. 3.5: counters
+// reused across calls must be reset per call, which this kernel does by
+// rebuilding every index it owns from scratch).
+//
+// One workgroup of 1024 threads (16 waves) does the whole job: the problem is
+// at most a few thousand (token, k) pairs, so the cost is a handful of LDS
+// passes. The order of rows is a stable counting sort keyed by
+// (local expert, token, k): within each round of 1024 pairs, a wave finds the
+// lanes that share its expert with ballots on the expert id's bits, ranks
+// itself with a popcount of the lower lanes, and adds the counts of the lower
+// waves and of earlier rounds. No step depends on the order of atomics, so the
+// result is deterministic.
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ unsigned long long lanes_below(int lane) {
+    return (1ull << lane) - 1ull;
+}
+
+// Exclusive scan of v over the 1024 threads of the block; returns the prefix,
+// and the block total through *total. s_tmp holds kRouteWaves ints.
+__device__ int block_exclusive_scan(int v, int *s_tmp, int *total) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int o = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += o;
+    }
+    if (lane == kWave - 1) s_tmp[wave] = inc;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int w = 0; w < kRouteWaves; ++w) {
+        int c = s_tmp[w];
+        if (w < wave) before += c;
+        all += c;
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - v;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
+    __shared__ int s_count[kMaxLocalExperts + 1];
+    __shared__ int s_off[kMaxLocalExperts + 2];
+    __shared__ int s_run[kMaxLocalExperts];
+    __shared__ int s_tbl[kRouteWaves][kMaxLocalExperts];
+    __shared__ int s_tmp[kRouteWaves];
+    __shared__ int s_bad;
+    __shared__ int s_nch;  // chunks emitted so far
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const int E = a.E_loc, TK = a.T * a.K;
+
+    for (int i = tid; i < E; i += kRouteThreads) {
+        s_count[i] = 0;
+        s_run[i] = 0;
+        for (int w = 0; w < kRouteWaves; ++w) s_tbl[w][i] = 0;
+    }
+    if (tid == 0) {
+        s_bad = 0;
+        s_nch = 0;
+    }
+    __syncthreads();
+
+    // 1. histogram of kept pairs per local expert
+    for (int p = tid; p < TK; p += kRouteThreads) {
+        const int t = p / a.K;
+        if (a.mask && !a.mask[t]) continue;
+        const int g = a.ids[p];
+        if (g < 0 || g >= a.E_g) {
+            atomicAdd(&s_bad, 1);
+            continue;
+        }
+        const int e = g - a.base;
+        if (e >= 0 && e < E) atomicAdd(&s_count[e], 1);
+    }
+    __syncthreads();
+
+    // 2. exclusive prefix sum of the counts
+    {
+        int total;
+        const int v = tid < E ? s_count[tid] : 0;
+        const int ex = block_exclusive_scan(v, s_tmp, &total);
+        if (tid < E) s_off[tid] = ex;
+        if (tid == 0) s_off[E] = total;
+    }
+    __syncthreads();
+    const int P = s_off[E];
+
+    // 3. stable placement, one round of 1024 pairs at a time
+    for (int base = 0; base < TK; base += kRouteThreads) {
+        const int p = base + tid;
+        int e = -1, t = 0;
+        if (p < TK) {
+            t = p / a.K;
+            if (!a.mask || a.mask[t]) {
+                const int g = a.ids[p];
+                if (g >= 0 && g < a.E_g) {
+                    e = g - a.base;
+                    if (e >= E) e = -1;
+                }
+            }
+        }
+        const bool valid = e >= 0;
+        unsigned long long peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 10; ++b) {  // expert ids < 1024
+            const bool bit = valid && ((e >> b) & 1);
+            const unsigned long long m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        const unsigned long long lower = peers & lanes_below(lane);
+        const int rank = __popcll(lower);
+        const int cnt = __popcll(peers);
+        const bool leader = valid && lower == 0ull;
+        if (leader) s_tbl[wave][e] = cnt;
+        __syncthreads();
+        if (p < TK) {
+            if (valid) {
+                int pre = 0;
+                for (int w = 0; w < wave; ++w) pre += s_tbl[w][e];
+                const int pos = s_off[e] + s_run[e] + pre + rank;
+                a.sorted_pair[pos] = p;
+                a.row_of_pair[p] = pos;
+                a.row_token[pos] = t;
+                a.row_group[pos] = e;
+            } else {
+                a.row_of_pair[p] = -1;
+            }
+        }
+        __syncthreads();
+        if (leader) {
+            atomicAdd(&s_run[e], cnt);
+            s_tbl[wave][e] = 0;
+        }
+        __syncthreads();
+    }
+
+    // 4. shared-expert rows: active tokens in token order, after the routed rows
+    int t_act = 0;
+    for (int base = 0; base < a.T; base += kRouteThreads) {
+        const int t = base + tid;
+        const bool act = t < a.T && (!a.mask || a.mask[t]);
+        int total;
+        const int ex = block_exclusive_scan(act ? 1 : 0, s_tmp, &total);
+        if (act) {
+            const int i = t_act + ex;
+            if (a.has_shared) {
+                a.row_token[P + i] = t;
+                a.row_group[P + i] = E;
+            }
+            if (a.dbg_shared_token) a.dbg_shared_token[i] = t;
+        }
+        t_act += total;
+    }
+
+    // 5. GEMM work items: each group's rows cut into chunks of kChunkRows
+    const int G = E + (a.has_shared ? 1 : 0);
+    for (int g0 = 0; g0 < G; g0 += kRouteThreads) {
+        const int g = g0 + tid;
+        int M = 0, row0 = 0;
+        if (g < G) {
+            M = g < E ? s_count[g] : t_act;
+            row0 = g < E ? s_off[g] : P;
+        }
+        const int nch = (M + kChunkRows - 1) / kChunkRows;
+        int total;
+        const int c = s_nch + block_exclusive_scan(nch, s_tmp, &total);
+        for (int i = 0; i < nch; ++i) {
+            const int r = i * kChunkRows;
+            a.chunks[c + i] = make_int4(g, row0 + r, min(kChunkRows, M - r), 0);
+        }
+        __syncthreads();
+        if (tid == 0) s_nch += total;
+        __syncthreads();
+    }
+
+    for (int e = tid; e < E; e += kRouteThreads) a.counts_out[e] = s_count[e];
+    for (int e = tid; e <= E; e += kRouteThreads) a.offsets[e] = s_off[e];
+    if (tid == 0) {
+        a.offsets[E + 1] = P + t_act;
+        a.meta[kMetaP] = P;
+        a.meta[kMetaTAct] = t_act;
+        a.meta[kMetaBad] = s_bad;
+        a.meta[kMetaChunks] = s_nch;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,158 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+on the same seeded inputs, stage by stage (tolerances in gpu_util.py).
+
+Small cases run the whole oracle; they span several MFMA row tiles, several
+64-row chunks per expert, ragged tails, masks, expert-parallel shares, smooth
+scales, a shared expert whose intermediate differs from the routed one, and
+the degenerate cases (T = 0, T = 1, every token masked, ids out of range).
+The five named workloads run at full size; the oracle then computes a sample
+of tokens (all of them where it finishes in seconds) and the routing outputs
+in full.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_ffn_route_amd as moe
+import oracle
+from moe_expert_ffn_route_amd import synth
+from gpu_util import check, compare, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def spec(**kw):
+    base = dict(name="parity", T=16, H=512, I=256, E_g=8, K=2, seed=101)
+    base.update(kw)
+    return synth.Spec(**base)
+
+
+SMALL = {
+    "cfg0_tiny": synth.CONFIGS[0],
+    "ragged_mask_smooth_shared": spec(T=37, H=768, I=512, I_s=256, E_g=16, K=4, active=29, smooth=True,
+                                      share_smooth=True, seed=102),
+    "ep_share_rank2": spec(T=50, H=512, I=512, E_g=32, K=6, ep_size=4, ep_rank=2, active=41, smooth=True, seed=103),
+    "skew_multi_chunk": spec(T=200, H=256, I=256, E_g=8, K=2, routing="zipf", zipf_s=2.0, I_s=512, seed=104),
+    "k1_single_expert": spec(T=70, H=256, I=256, E_g=1, K=1, seed=105),
+    "k16": spec(T=9, H=512, I=256, E_g=16, K=16, I_s=256, seed=106),
+    "t1": spec(T=1, H=1024, I=512, E_g=4, K=2, I_s=512, seed=107),
+    "wide_hidden": spec(T=5, H=4096, I=256, E_g=4, K=2, I_s=256, seed=108),
+    "wide_inter": spec(T=6, H=256, I=2048, E_g=4, K=2, I_s=768, seed=109),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_case_parity(name):
+    say(f"[parity] {name}: {SMALL[name]}")
+    stats, _, _ = check(synth.make_case(SMALL[name]))
+    say(f"[parity] {name}: {stats}")
+
+
+def test_zero_tokens():
+    s = spec(T=0, I_s=256)
+    c = synth.make_case(s)
+    gpu = run_gpu(c)
+    assert np.all(gpu["expert_token_nums"] == 0)
+    assert gpu["num_rows"][0] == 0 and gpu["num_rows"][1] == 0
+
+
+def test_all_tokens_masked():
+    s = spec(T=12, I_s=256, active=0, smooth=True)
+    c = synth.make_case(s)
+    stats, gpu, _ = check(c)
+    assert np.all(gpu["output"] == 0) and np.all(gpu["share_output"] == 0)
+
+
+def test_out_of_range_ids_are_dropped_and_counted():
+    c = synth.make_case(spec(T=20, E_g=8, K=3, I_s=256, seed=111))
+    ids = c.expert_ids.copy()
+    ids[3, 1] = -5
+    ids[7, 0] = 8
+    ids[11, 2] = 1 << 30
+    c = dataclasses.replace(c, expert_ids=ids)
+    stats, gpu, ref = check(c)
+    assert gpu["num_rows"][2] == 3 == ref["n_bad"]
+
+
+def test_duplicate_expert_in_topk():
+    c = synth.make_case(spec(T=10, E_g=4, K=3, seed=112))
+    ids = c.expert_ids.copy()
+    ids[:, 1] = ids[:, 0]
+    check(dataclasses.replace(c, expert_ids=ids))
+
+
+def test_deterministic_dirty_workspace_and_side_stream():
+    c = synth.make_case(spec(T=33, H=512, I=512, E_g=8, K=4, I_s=256, seed=113))
+    t = moe.upload(c)
+    a = run_gpu(c, tensors=t)
+    s = torch.cuda.Stream()
+    b = run_gpu(c, tensors=t, garbage_workspace=True, stream=s)
+    for k in ("output", "share_output", "expert_token_nums"):
+        assert np.array_equal(a[k], b[k]), k
+    # intermediates: only the defined part (rows in use; a shared row uses I_s columns)
+    P, Ta = int(a["num_rows"][0]), int(a["num_rows"][1])
+    for r in range(P + Ta):
+        n = c.spec.I if r < P else c.spec.I_s
+        for k, w in (("q_x", c.spec.H), ("acc1", 2 * n), ("h", n), ("q_h", n), ("acc2", c.spec.H)):
+            assert np.array_equal(a[k][r, :w], b[k][r, :w]), (k, r)
+
+
+def test_repeated_calls_shrinking_batch():
+    # one workspace, a large call then a smaller one: nothing stale leaks
+    big = spec(T=64, H=512, I=256, E_g=8, K=2, I_s=256, seed=114)
+    small = dataclasses.replace(big, T=5, seed=115)
+    cb, cs = synth.make_case(big), synth.make_case(small)
+    dims_b = moe.dims_of_case(cb)
+    runner = moe.Runner(dims_b)
+    runner(moe.upload(cb))
+    torch.cuda.synchronize()
+    dims_s = moe.dims_of_case(cs)
+    ts = moe.upload(cs)
+    out = torch.empty((5, 512), dtype=torch.bfloat16, device="cuda")
+    sout = torch.empty((5, 512), dtype=torch.bfloat16, device="cuda")
+    etn = torch.empty(8, dtype=torch.int32, device="cuda")
+    moe.moe_w8a8_forward(dims_s, output=out, share_output=sout, expert_token_nums=etn, workspace=runner.workspace,
+                         **ts)
+    torch.cuda.synchronize()
+    ref = oracle.forward(cs)
+    from gpu_util import out_close
+    out_close(out.view(torch.int16).cpu().numpy().view(np.uint16), ref["output"], "output")
+    out_close(sout.view(torch.int16).cpu().numpy().view(np.uint16), ref["share_output"], "share_output")
+    assert np.array_equal(etn.cpu().numpy(), ref["expert_token_nums"])
+
+
+# ------------------------------------------------------- full-size workloads
+
+_WEIGHTS = {}
+
+
+def weights_for(s):
+    key = (s.weight_seed, s.H, s.I, s.E_g, s.ep_size, s.ep_rank)
+    if key not in _WEIGHTS:
+        say(f"[parity] generating weights {key}")
+        w = synth.make_weights(s)
+        _WEIGHTS.clear()
+        _WEIGHTS[key] = w
+    return _WEIGHTS[key]
+
+
+# tokens sampled by the oracle (None = all); 1, 3 and 4 share one set of weights
+FULL = {1: None, 3: 24, 4: 12, 2: None}
+
+
+@pytest.mark.parametrize("cfg", list(FULL))
+def test_full_size_workload(cfg):
+    s = synth.CONFIGS[cfg]
+    say(f"[parity] config {cfg} {s.name}")
+    case = synth.config_case(cfg, weights=weights_for(s))
+    n = FULL[cfg]
+    tokens = None
+    if n is not None:
+        rng = np.random.default_rng(cfg)
+        tokens = np.sort(rng.choice(s.T, n, replace=False))
+    stats, gpu, ref = check(case, tokens=tokens)
+    say(f"[parity] config {cfg}: {stats}")
+    del gpu, ref
+    torch.cuda.empty_cache()
