@@ -78,7 +78,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=1, help="workload index (0-4); 1 is the headline decode step")
     ap.add_argument("--layers", type=int, default=4, help="weight copies cycled through to keep the cache cold")
+    ap.add_argument("--row-major", action="store_true",
+                    help="stream the weights in their row-major layout instead of the packed one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB 5 times (calibrates HBM byte counters)")
     ap.add_argument("--no-stage-events", action="store_true",
                     help="time the steps without per-stage events (stage times then come from a second pass)")
     args = ap.parse_args()
@@ -90,6 +94,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}), flush=True)
+        return
     moe.library()  # fail loudly if the HIP library is missing
 
     spec = synth.CONFIGS[args.config]
@@ -98,21 +112,31 @@ def main():
     case = synth.config_case(args.config)
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s; uploading")
     dev = moe.upload(case)
+    if not args.row_major:
+        dev = moe.pack_weights(dev)  # one-time re-layout at load time (moe_w8a8_pack_weights)
+        torch.cuda.synchronize()
     wkeys = [k for k in ("gmm1_weight", "gmm1_weight_scale", "gmm2_weight", "gmm2_weight_scale",
                          "share_gmm1_weight", "share_gmm1_weight_scale", "share_gmm2_weight",
                          "share_gmm2_weight_scale") if dev.get(k) is not None]
     layers = [dev] + [dict(dev, **{k: dev[k].clone() for k in wkeys}) for _ in range(max(0, args.layers - 1))]
     dims = moe.dims_of_case(case)
+    dims.weight_layout = moe.MOE_WEIGHT_ROW_MAJOR if args.row_major else moe.MOE_WEIGHT_PACKED
     runner = moe.Runner(dims)
     stream = torch.cuda.Stream()
     n_ev = len(binding.STAGES) + 1
+    G1 = 1 + binding.STAGES.index("gemm1")  # event after GEMM1; the one before it is G1 - 1
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    ev_ptrs = []
     for evs in events:
         for e in evs:
             e.record(stream)  # materialise the HIP event handles
-        ev_ptrs.append((ctypes.c_void_p * n_ev)(*[e.cuda_event for e in evs]))
     torch.cuda.synchronize()
+    # timed region: only the two events bracketing GEMM1 are recorded (by the
+    # library, on the launch stream); the per-stage pass below records all
+    g1_arrays = [(ctypes.c_void_p * n_ev)(*[e.cuda_event if j in (G1 - 1, G1) else None for j, e in enumerate(evs)])
+                 for evs in events]
+    all_arrays = [(ctypes.c_void_p * n_ev)(*[e.cuda_event for e in evs]) for evs in events]
+    g1_dbg = [binding.Debug(stage_events=ctypes.cast(p, ctypes.c_void_p).value) for p in g1_arrays]
+    all_dbg = [binding.Debug(stage_events=ctypes.cast(p, ctypes.c_void_p).value) for p in all_arrays]
 
     log(f"[bench] warmup {args.warmup} steps")
     with torch.cuda.stream(stream):
@@ -124,23 +148,28 @@ def main():
     log(f"[bench] timing {args.steps} steps")
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
-    dbgs = [binding.Debug(stage_events=ctypes.cast(p, ctypes.c_void_p).value) for p in ev_ptrs]
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         t_start.record(stream)
         for i in range(args.steps):
-            runner(layers[i % len(layers)], dbg=None if args.no_stage_events else dbgs[i], stream=stream)
+            runner(layers[i % len(layers)], dbg=None if args.no_stage_events else g1_dbg[i], stream=stream)
         t_stop.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_stop)
-    if args.no_stage_events:
-        with torch.cuda.stream(stream):
-            for i in range(args.steps):
-                runner(layers[i % len(layers)], dbg=dbgs[i], stream=stream)
-        torch.cuda.synchronize()
     ms_per_step = total_ms / args.steps
+    g1_us = None
+    if not args.no_stage_events:
+        g1_us = float(np.mean([events[i][G1 - 1].elapsed_time(events[i][G1]) for i in range(args.steps)])) * 1e3
+
+    log("[bench] per-stage pass")
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            runner(layers[i % len(layers)], dbg=all_dbg[i], stream=stream)
+    torch.cuda.synchronize()
     stage_us = {name: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]) * 1e3)
                 for j, name in enumerate(binding.STAGES)}
+    if g1_us is None:
+        g1_us = stage_us["gemm1"]
 
     out = runner.output.float()
     if not torch.isfinite(out).all():
@@ -148,7 +177,6 @@ def main():
 
     layer_bytes, gemm1_bytes, touched, rows = algorithmic_bytes(case, counts)
     us = ms_per_step * 1e3
-    g1_us = stage_us["gemm1"]
     g1_gbs = gemm1_bytes / (g1_us * 1e-6) / 1e9
     rec = {
         "metric": "µs per MoE layer (T=8 decode); achieved HBM GB/s in hbm_gbps",
@@ -165,10 +193,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": spec.name, "tokens": spec.T, "hidden": spec.H, "inter": spec.I,
                    "experts": spec.E_g, "topk": spec.K, "share_inter": spec.I_s,
-                   "touched_experts": touched, "grouped_rows": rows, "weight_copies": len(layers)},
+                   "touched_experts": touched, "grouped_rows": rows, "weight_copies": len(layers),
+                   "weight_layout": "row_major" if args.row_major else "packed"},
         "hbm_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
         "tokens_per_s": round(spec.T / (us * 1e-6), 1),
-        "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "stage_us": {k: round(v, 2) for k, v in stage_us.items()},  # separate pass, every stage bracketed
         "roofline": {"kernel": "gemm1_swiglu", "bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "algorithmic_bytes": gemm1_bytes, "avg_us": round(g1_us, 2)},

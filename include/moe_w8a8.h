@@ -81,7 +81,12 @@ typedef struct {
                             /*   [ep_rank_id*E_loc, (ep_rank_id+1)*E_loc)            */
     int32_t quant_mode;     /* 1 = per-token dynamic INT8 (the only mode)            */
     float amax_eps;         /* > 0: row amax floor (e.g. 1e-6)                       */
+    int32_t weight_layout;  /* MOE_WEIGHT_ROW_MAJOR: the layouts listed at           */
+                            /*   moe_w8a8_forward; MOE_WEIGHT_PACKED: all four       */
+                            /*   weight tensors come from moe_w8a8_pack_weights      */
 } moe_w8a8_dims_t;
+
+enum { MOE_WEIGHT_ROW_MAJOR = 0, MOE_WEIGHT_PACKED = 1 };
 
 /* Optional intermediates for testing (every field may be NULL; all are device
  * buffers written in stream order). Rows are "grouped rows": rows [0, P) are
@@ -102,9 +107,10 @@ typedef struct {
     float   *hs;            /* [R]     their per-row dequant scale             */
     int32_t *acc2;          /* [R, H]  GEMM2 int32 accumulators                */
     uint16_t *z;            /* [R, H]  bf16 GEMM2 output rows                  */
-    void   **stage_events;  /* [7] caller-created hipEvent_t, recorded on the
-                               stream before routing and after each stage:
-                               route, quant, GEMM1, requant, GEMM2, combine   */
+    void   **stage_events;  /* [7] caller-created hipEvent_t (NULL entries are
+                               skipped), recorded on the stream before routing
+                               and after each stage: route, quant, GEMM1,
+                               requant, GEMM2, combine                         */
 } moe_w8a8_debug_t;
 
 /* Workspace bytes that moe_w8a8_forward needs for these dims. The size depends
@@ -164,6 +170,23 @@ MOE_W8A8_API moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *dims,
                               size_t workspace_bytes,
                               const moe_w8a8_debug_t *dbg,
                               void *stream);
+
+/*
+ * Re-lay int8 weights once, at load time, into the order the GEMM kernels
+ * stream (the MI355X counterpart of the NZ weight format that FusedDeepMoE
+ * sec. 5.3 / 8.1 feeds its cube unit). Nothing is computed; bytes move.
+ *
+ *  src    int8 [groups, n, k], k contiguous (a gmm*_weight tensor: n = 2I, k = H
+ *         for GEMM1; n = H, k = I for GEMM2; groups = E_loc, or 1 for a shared
+ *         expert)
+ *  dst    int8, same size; for group g, 16-row tile j and 64-byte k step s, the
+ *         1024 bytes at ((g*(n/16) + j)*(k/64) + s)*1024 hold, at byte 16*l + b
+ *         (l in [0,64), b in [0,16)), src[g][16j + l%16][64s + 16*(l/16) + b]
+ *  n % 16 == 0, k % 64 == 0; src and dst 16-byte aligned and not overlapping.
+ *  Stream-ordered; returns MOE_ERR_INVALID_ARG for bad sizes or pointers.
+ */
+MOE_W8A8_API moe_status_t moe_w8a8_pack_weights(const int8_t *src, int8_t *dst, int64_t groups, int32_t n,
+                                                int32_t k, void *stream);
 
 /* Static description of a status code. Never NULL. */
 MOE_W8A8_API const char *moe_w8a8_status_string(moe_status_t status);

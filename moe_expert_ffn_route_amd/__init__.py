@@ -5,4 +5,5 @@ of include/moe_w8a8.h); `binding` is its ctypes front end and `synth` draws
 seeded synthetic inputs.
 """
 from .binding import (Debug, Dims, MoeError, Runner, debug_buffers, dims_of_case, library, make_dims,  # noqa: F401
-                      moe_w8a8_forward, moe_w8a8_status_string, moe_w8a8_workspace_size, upload)
+                      moe_w8a8_forward, moe_w8a8_pack_weights, moe_w8a8_status_string, moe_w8a8_workspace_size,
+                      pack_weights, upload, MOE_WEIGHT_PACKED, MOE_WEIGHT_ROW_MAJOR)

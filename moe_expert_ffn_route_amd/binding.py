@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(PKG, "libmoe_w8a8.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 
-EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_forward", "moe_w8a8_status_string")
+EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_forward", "moe_w8a8_pack_weights", "moe_w8a8_status_string")
+MOE_WEIGHT_ROW_MAJOR, MOE_WEIGHT_PACKED = 0, 1
 
 
 class MoeError(RuntimeError):
@@ -33,7 +34,7 @@ class Dims(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("share_inter", ctypes.c_int32), ("topk", ctypes.c_int32), ("moe_expert_num", ctypes.c_int32),
                 ("ep_rank_size", ctypes.c_int32), ("ep_rank_id", ctypes.c_int32), ("quant_mode", ctypes.c_int32),
-                ("amax_eps", ctypes.c_float)]
+                ("amax_eps", ctypes.c_float), ("weight_layout", ctypes.c_int32)]
 
     @property
     def e_loc(self) -> int:
@@ -42,7 +43,7 @@ class Dims(ctypes.Structure):
 
 DEBUG_FIELDS = ("sorted_pair", "row_of_pair", "group_offset", "shared_token", "num_rows", "q_x", "xs", "acc1",
                 "h", "q_h", "hs", "acc2", "z", "stage_events")
-STAGES = ("route", "quant", "gemm1", "requant", "gemm2", "combine")
+STAGES = ("route_quant", "smooth_quant", "gemm1", "requant", "gemm2", "combine")
 
 
 class Debug(ctypes.Structure):
@@ -65,6 +66,8 @@ def library() -> ctypes.CDLL:
         L.moe_w8a8_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_size_t)]
         L.moe_w8a8_forward.restype = ctypes.c_int
         L.moe_w8a8_forward.argtypes = ([ctypes.POINTER(Dims)] + [P] * 18 + [ctypes.c_size_t, ctypes.POINTER(Debug), P])
+        L.moe_w8a8_pack_weights.restype = ctypes.c_int
+        L.moe_w8a8_pack_weights.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P]
         L.moe_w8a8_status_string.restype = ctypes.c_char_p
         L.moe_w8a8_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -72,9 +75,9 @@ def library() -> ctypes.CDLL:
 
 
 def make_dims(num_tokens, hidden, inter, topk, moe_expert_num, share_inter=0, ep_rank_size=1, ep_rank_id=0,
-              quant_mode=1, amax_eps=1e-6) -> Dims:
+              quant_mode=1, amax_eps=1e-6, weight_layout=MOE_WEIGHT_ROW_MAJOR) -> Dims:
     return Dims(num_tokens, hidden, inter, share_inter, topk, moe_expert_num, ep_rank_size, ep_rank_id, quant_mode,
-                amax_eps)
+                amax_eps, weight_layout)
 
 
 def moe_w8a8_status_string(code: int) -> str:
@@ -87,6 +90,31 @@ def moe_w8a8_workspace_size(dims: Dims) -> int:
     if rc != MOE_OK:
         raise MoeError(rc, "moe_w8a8_workspace_size")
     return int(n.value)
+
+
+def moe_w8a8_pack_weights(src, dst=None, stream=None):
+    """Pack an int8 weight tensor [groups, n, k] or [n, k] (device) into the
+    kernels' streaming order; returns dst (allocated like src if None)."""
+    if dst is None:
+        dst = torch.empty_like(src)
+    shape = src.shape if src.dim() == 3 else (1, *src.shape)
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    rc = library().moe_w8a8_pack_weights(_ptr(src), _ptr(dst), shape[0], shape[1], shape[2], stream)
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_w8a8_pack_weights")
+    return dst
+
+
+def pack_weights(tensors: dict, stream=None) -> dict:
+    """Return a copy of an upload() dict whose four weight tensors are packed."""
+    out = dict(tensors)
+    for k in ("gmm1_weight", "gmm2_weight", "share_gmm1_weight", "share_gmm2_weight"):
+        if out.get(k) is not None:
+            out[k] = moe_w8a8_pack_weights(out[k], stream=stream)
+    return out
 
 
 def _ptr(t) -> Optional[int]:

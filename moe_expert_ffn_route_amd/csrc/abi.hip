@@ -1,7 +1,7 @@
 // C ABI of libmoe_w8a8: argument validation, workspace carve-up and the
 // stream-ordered launch sequence of the expert block
-//   route -> quant_gather -> GEMM1 (+dequant, SwiGLU) -> requant
-//         -> GEMM2 (+dequant to bf16) -> combine
+//   route + per-token quant -> [smooth quant] -> GEMM1 (+dequant, SwiGLU)
+//         -> requant -> GEMM2 (+dequant to bf16) -> combine
 // which is the unfused five-op chain of "FusedDeepMoE Kernel 深度分析报告"
 // sec. 9.3 with the dequant/SwiGLU/quant fused into the GEMMs' epilogues
 // (sec. 6.1, 6.2, 7.2). Nothing here allocates or synchronises.
@@ -31,6 +31,7 @@ moe_status_t check_dims(const moe_w8a8_dims_t *d) {
     if (d->moe_expert_num / d->ep_rank_size > kMaxLocalExperts) return MOE_ERR_UNSUPPORTED;
     if (d->hidden % 256 || d->inter % 256 || d->share_inter % 256) return MOE_ERR_UNSUPPORTED;
     if (d->hidden > 16384 || d->inter > 16384 || d->share_inter > 16384) return MOE_ERR_UNSUPPORTED;
+    if (d->weight_layout != MOE_WEIGHT_ROW_MAJOR && d->weight_layout != MOE_WEIGHT_PACKED) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
@@ -53,6 +54,8 @@ Layout make_layout(const moe_w8a8_dims_t *d) {
     L.row_token = o;   o = up256(o + sizeof(int32_t) * R);
     L.row_group = o;   o = up256(o + sizeof(int32_t) * R);
     L.chunks = o;      o = up256(o + sizeof(int4) * L.max_chunks);
+    L.q_tok = o;       o = up256(o + T * H);
+    L.xs_tok = o;      o = up256(o + sizeof(float) * T);
     L.q_x = o;         o = up256(o + R * H);
     L.xs = o;          o = up256(o + sizeof(float) * R);
     L.h = o;           o = up256(o + sizeof(float) * R * L.imax);
@@ -71,6 +74,17 @@ extern "C" moe_status_t moe_w8a8_workspace_size(const moe_w8a8_dims_t *dims, siz
     if (st != MOE_OK) return st;
     *bytes = make_layout(dims).total;
     return MOE_OK;
+}
+
+extern "C" moe_status_t moe_w8a8_pack_weights(const int8_t *src, int8_t *dst, int64_t groups, int32_t n, int32_t k,
+                                              void *stream) {
+    if (!src || !dst || groups < 0 || n <= 0 || k <= 0 || n % 16 || k % 64) return MOE_ERR_INVALID_ARG;
+    if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_INVALID_ARG;
+    const uint64_t bytes = static_cast<uint64_t>(groups) * n * k;
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return MOE_ERR_INVALID_ARG;  // overlap
+    if (bytes / 16 / 256 >= (1ull << 31)) return MOE_ERR_UNSUPPORTED;
+    return launch_pack(src, dst, groups, n, k, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 extern "C" const char *moe_w8a8_status_string(moe_status_t s) {
@@ -127,9 +141,16 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
     const moe_w8a8_debug_t nodbg = {};
     const moe_w8a8_debug_t &D = dbg ? *dbg : nodbg;
     auto mark = [&](int i) {
-        return !D.stage_events || hipEventRecord(static_cast<hipEvent_t>(D.stage_events[i]), s) == hipSuccess;
+        return !D.stage_events || !D.stage_events[i] ||
+               hipEventRecord(static_cast<hipEvent_t>(D.stage_events[i]), s) == hipSuccess;
     };
     if (!mark(0)) return MOE_ERR_HIP;
+
+    // GEMM1 input rows: per token (quantised once, in the routing launch)
+    // for groups without smooth scales, per grouped row otherwise
+    const bool routed_tok = expert_smooth_scales == nullptr;
+    const bool shared_tok = shared && share_smooth_scales == nullptr;
+    const bool any_smooth = !routed_tok || (shared && !shared_tok);
 
     RouteArgs ra;
     ra.ids = expert_ids;
@@ -149,7 +170,15 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
     ra.chunks = reinterpret_cast<int4 *>(ws + L.chunks);
     ra.meta = meta;
     ra.dbg_shared_token = D.shared_token;
-    if (launch_route(ra, s) != hipSuccess || !mark(1)) return MOE_ERR_HIP;
+    TokQuantArgs tq;
+    tq.x = static_cast<const uint16_t *>(x);
+    tq.mask = x_active_mask;
+    tq.T = T;
+    tq.H = H;
+    tq.eps = d->amax_eps;
+    tq.q = (T > 0 && (routed_tok || shared_tok)) ? reinterpret_cast<int8_t *>(ws + L.q_tok) : nullptr;
+    tq.scale = reinterpret_cast<float *>(ws + L.xs_tok);
+    if (launch_route_quant(ra, tq, s) != hipSuccess || !mark(1)) return MOE_ERR_HIP;
 
     if (T > 0) {
         QuantArgs qa;
@@ -166,12 +195,17 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         qa.eps = d->amax_eps;
         qa.q = reinterpret_cast<int8_t *>(ws + L.q_x);
         qa.scale = reinterpret_cast<float *>(ws + L.xs);
-        if (launch_quant(qa, s) != hipSuccess || !mark(2)) return MOE_ERR_HIP;
+        if (any_smooth && launch_quant(qa, s) != hipSuccess) return MOE_ERR_HIP;
+        if (!mark(2)) return MOE_ERR_HIP;
 
         GemmArgs g1 = {};
         g1.A = qa.q;
         g1.a_stride = H;
         g1.a_scale = qa.scale;
+        g1.A_tok = tq.q;
+        g1.a_scale_tok = tq.scale;
+        g1.routed_by_token = routed_tok;
+        g1.shared_by_token = shared_tok;
         g1.W = gmm1_weight;
         g1.Ws = gmm1_weight_scale;
         g1.W_sh = share_gmm1_weight;
@@ -183,6 +217,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g1.imax = L.imax;
         g1.g_lo = 0;
         g1.g_hi = E + 1;
+        g1.packed = d->weight_layout == MOE_WEIGHT_PACKED;
         g1.n_tiles = L.imax / kTileN;
         g1.chunks = ra.chunks;
         g1.meta = meta;
@@ -207,6 +242,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         if (launch_requant(rq, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;
 
         GemmArgs g2 = g1;
+        g2.routed_by_token = g2.shared_by_token = 0;
         g2.A = rq.q;
         g2.a_stride = L.imax;
         g2.a_scale = rq.scale;
@@ -257,12 +293,16 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         {D.row_of_pair, L.row_of_pair, sizeof(int32_t) * TK},
         {D.group_offset, L.offsets, sizeof(int32_t) * (E + 1)},
         {D.num_rows, L.meta, sizeof(int32_t) * kMetaWords},
-        {D.q_x, L.q_x, R * H},
-        {D.xs, L.xs, sizeof(float) * R},
         {D.h, L.h, sizeof(float) * R * L.imax},
         {D.q_h, L.q_h, R * L.imax},
         {D.hs, L.hs, sizeof(float) * R},
     };
+    if ((D.q_x || D.xs) &&
+        launch_dbg_gather(reinterpret_cast<int8_t *>(ws + L.q_tok), reinterpret_cast<float *>(ws + L.xs_tok),
+                          reinterpret_cast<int8_t *>(ws + L.q_x), reinterpret_cast<float *>(ws + L.xs),
+                          I32(L.row_token), I32(L.row_group), meta, E, routed_tok, shared_tok, shared, H, L.rows_max,
+                          D.q_x, D.xs, s) != hipSuccess)
+        return MOE_ERR_HIP;
     for (const Copy &c : copies)
         if (c.dst && c.bytes && hipMemcpyAsync(c.dst, ws + c.off, c.bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
             return MOE_ERR_HIP;

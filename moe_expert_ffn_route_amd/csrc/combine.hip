@@ -6,31 +6,41 @@
 // nothing, so such tokens get zero rows. The sum order is fixed per element,
 // so the result is deterministic.
 //
-// One workgroup per token; each thread owns 8 consecutive channels (16-byte
-// loads of each expert row, 16-byte stores). It also clears the shared-expert
-// rows of inactive tokens, which GEMM2 never writes.
+// Grid = tokens x (H / 1024): each thread owns 8 consecutive channels and
+// issues the 16-byte loads of all K rows before it sums them, so a token
+// costs one memory round trip. It also clears the shared-expert rows of
+// inactive tokens, which GEMM2 never writes.
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 128;
+constexpr int kChannels = kThreads * 8;  // channels per block
 
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     const int t = blockIdx.x;
-    const bool act = !a.mask || a.mask[t];
+    const int c = blockIdx.y * kChannels + threadIdx.x * 8;
+    if (c >= a.H) return;
     const int32_t *rop = a.row_of_pair + static_cast<size_t>(t) * a.K;
     const float *wt = a.scales + static_cast<size_t>(t) * a.K;
-    for (int c = threadIdx.x * 8; c < a.H; c += kThreads * 8) {
-        float sum[8];
+    uint4 raw[kMaxTopK];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sum[i] = 0.0f;
-        for (int k = 0; k < a.K; ++k) {
+    for (int k = 0; k < kMaxTopK; ++k) {
+        raw[k] = make_uint4(0, 0, 0, 0);
+        if (k < a.K) {
             const int row = rop[k];
-            if (row < 0) continue;
+            if (row >= 0) raw[k] = *reinterpret_cast<const uint4 *>(a.z + static_cast<size_t>(row) * a.H + c);
+        }
+    }
+    float sum[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum[i] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+        if (k < a.K && rop[k] >= 0) {
             const float wk = wt[k];
-            const uint4 raw = *reinterpret_cast<const uint4 *>(a.z + static_cast<size_t>(row) * a.H + c);
-            const uint32_t v[4] = {raw.x, raw.y, raw.z, raw.w};
+            const uint32_t v[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float m0 = bf16_to_f32(static_cast<uint16_t>(v[i] & 0xFFFFu)) * wk;
@@ -39,22 +49,23 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
                 sum[2 * i + 1] = sum[2 * i + 1] + m1;
             }
         }
-        uint4 o;
-        o.x = f32_to_bf16(sum[0]) | (static_cast<uint32_t>(f32_to_bf16(sum[1])) << 16);
-        o.y = f32_to_bf16(sum[2]) | (static_cast<uint32_t>(f32_to_bf16(sum[3])) << 16);
-        o.z = f32_to_bf16(sum[4]) | (static_cast<uint32_t>(f32_to_bf16(sum[5])) << 16);
-        o.w = f32_to_bf16(sum[6]) | (static_cast<uint32_t>(f32_to_bf16(sum[7])) << 16);
-        *reinterpret_cast<uint4 *>(a.out + static_cast<size_t>(t) * a.H + c) = o;
-        if (a.has_shared && !act)
-            *reinterpret_cast<uint4 *>(a.share_out + static_cast<size_t>(t) * a.H + c) = make_uint4(0, 0, 0, 0);
     }
+    uint4 o;
+    o.x = f32_to_bf16(sum[0]) | (static_cast<uint32_t>(f32_to_bf16(sum[1])) << 16);
+    o.y = f32_to_bf16(sum[2]) | (static_cast<uint32_t>(f32_to_bf16(sum[3])) << 16);
+    o.z = f32_to_bf16(sum[4]) | (static_cast<uint32_t>(f32_to_bf16(sum[5])) << 16);
+    o.w = f32_to_bf16(sum[6]) | (static_cast<uint32_t>(f32_to_bf16(sum[7])) << 16);
+    *reinterpret_cast<uint4 *>(a.out + static_cast<size_t>(t) * a.H + c) = o;
+    if (a.has_shared && a.mask && !a.mask[t])
+        *reinterpret_cast<uint4 *>(a.share_out + static_cast<size_t>(t) * a.H + c) = make_uint4(0, 0, 0, 0);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
     if (a.T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(kThreads), 0, s, a);
+    const dim3 grid(a.T, (a.H + kChannels - 1) / kChannels);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ struct Layout {
     int max_chunks;  // upper bound of GEMM work items
     int imax;        // max(I, I_s)
     size_t meta, offsets, sorted_pair, row_of_pair, row_token, row_group, chunks;
-    size_t q_x, xs, h, q_h, hs, z, total;
+    size_t q_tok, xs_tok, q_x, xs, h, q_h, hs, z, total;
 };
 
 struct RouteArgs {
@@ -43,6 +43,17 @@ struct RouteArgs {
     int32_t *dbg_shared_token;  // [T] or null
 };
 
+// per-token quantisation of x (groups without smooth scales read these rows)
+struct TokQuantArgs {
+    const uint16_t *x;     // bf16 [T, H]
+    const uint8_t *mask;   // [T] or null
+    int T, H;
+    float eps;
+    int8_t *q;             // [T, H]; null = not needed
+    float *scale;          // [T]
+};
+
+// per-grouped-row quantisation of x * smooth (rows of groups with smooth scales)
 struct QuantArgs {
     const uint16_t *x;       // bf16 [T, H]
     const int32_t *row_token;
@@ -67,10 +78,14 @@ struct RequantArgs {
 };
 
 struct GemmArgs {
-    // activations: grouped int8 rows and their per-row scale
+    // activations: grouped int8 rows and their per-row scale ...
     const int8_t *A;
     int a_stride;
     const float *a_scale;
+    // ... or, for groups flagged here, per-token rows picked by row_token
+    const int8_t *A_tok;
+    const float *a_scale_tok;
+    int routed_by_token, shared_by_token;
     // weights [E_loc, N, K] routed, [N, K] shared, and per-output-channel scales
     const int8_t *W;
     const float *Ws;
@@ -78,6 +93,7 @@ struct GemmArgs {
     const float *Ws_sh;
     int I, I_s, H, E_loc, imax;
     int g_lo, g_hi;   // only chunks of groups in [g_lo, g_hi)
+    int packed;       // weights in moe_w8a8_pack_weights order
     int n_tiles;      // work items per chunk along N
     const int4 *chunks;
     const int32_t *meta;
@@ -100,12 +116,18 @@ struct CombineArgs {
     uint16_t *share_out;
 };
 
-hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+hipError_t launch_route_quant(const RouteArgs &a, const TokQuantArgs &q, hipStream_t s);
 hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
 hipError_t launch_requant(const RequantArgs &a, hipStream_t s);
 hipError_t launch_gemm1(const GemmArgs &a, int max_chunks, hipStream_t s);
 hipError_t launch_gemm2(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+hipError_t launch_pack(const int8_t *src, int8_t *dst, int64_t groups, int n, int k, hipStream_t s);
+// debug only: expand per-token rows into the grouped-row q_x / xs dump
+hipError_t launch_dbg_gather(const int8_t *q_tok, const float *xs_tok, const int8_t *q_rows, const float *xs_rows,
+                             const int32_t *row_token, const int32_t *row_group, const int32_t *meta, int E_loc,
+                             int routed_by_token, int shared_by_token, int has_shared, int H, int rows_max,
+                             int8_t *dst_q, float *dst_xs, hipStream_t s);
 
 // bf16 helpers (round to nearest even)
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

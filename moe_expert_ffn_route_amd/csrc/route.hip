@@ -13,6 +13,7 @@
 // waves and of earlier rounds. No step depends on the order of atomics, so the
 // result is deterministic.
 #include "internal.h"
+#include "rowquant.h"
 
 namespace moe {
 namespace {
@@ -44,7 +45,7 @@ __device__ int block_exclusive_scan(int v, int *s_tmp, int *total) {
     return before + inc - v;
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
+__device__ void route_block(const RouteArgs &a) {
     __shared__ int s_count[kMaxLocalExperts + 1];
     __shared__ int s_off[kMaxLocalExperts + 2];
     __shared__ int s_run[kMaxLocalExperts];
@@ -192,10 +193,29 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     }
 }
 
+constexpr int kTokQuantSlots = kRouteThreads / kTPR;  // tokens quantised per block
+
+// Block 0 routes; blocks 1.. quantise x per token (groups without smooth
+// scales read these rows, FusedDeepMoE sec. 4.1 quantises in dispatch). The
+// two jobs are independent, so one launch runs both side by side.
+__global__ __launch_bounds__(kRouteThreads) void route_quant_kernel(RouteArgs a, TokQuantArgs q) {
+    if (blockIdx.x == 0) {
+        route_block(a);
+        return;
+    }
+    __shared__ float s_part[kTokQuantSlots * (kTPR / kWave)];
+    const int slot = threadIdx.x / kTPR, tr = threadIdx.x % kTPR;
+    const int t = (blockIdx.x - 1) * kTokQuantSlots + slot;
+    const bool active = t < q.T && (!q.mask || q.mask[t]);
+    const size_t tt = active ? t : 0;
+    quant_bf16_row(q.x + tt * q.H, nullptr, q.H, q.eps, q.q + tt * q.H, q.scale + tt, active, slot, tr, s_part);
+}
+
 }  // namespace
 
-hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, a);
+hipError_t launch_route_quant(const RouteArgs &a, const TokQuantArgs &q, hipStream_t s) {
+    const int qblocks = q.q ? (q.T + kTokQuantSlots - 1) / kTokQuantSlots : 0;
+    hipLaunchKernelGGL(route_quant_kernel, dim3(1 + qblocks), dim3(kRouteThreads), 0, s, a, q);
     return hipGetLastError();
 }
 

@@ -32,10 +32,13 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_gpu(case, tensors=None, dbg=True, stream=None, garbage_workspace=False):
+def run_gpu(case, tensors=None, dbg=True, stream=None, garbage_workspace=False, packed=False):
     dims = moe.dims_of_case(case)
     if tensors is None:
         tensors = moe.upload(case)
+    if packed:
+        tensors = moe.pack_weights(tensors)
+        dims.weight_layout = moe.MOE_WEIGHT_PACKED
     runner = moe.Runner(dims)
     if garbage_workspace:
         runner.workspace.fill_(0xA5)

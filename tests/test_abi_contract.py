@@ -93,6 +93,7 @@ def test_workspace_size(lib):
     (dict(share_inter=64), binding.MOE_ERR_UNSUPPORTED),
     (dict(moe_expert_num=1024), binding.MOE_ERR_UNSUPPORTED),
     (dict(num_tokens=70000), binding.MOE_ERR_UNSUPPORTED),
+    (dict(weight_layout=2), binding.MOE_ERR_INVALID_ARG),
 ])
 def test_bad_dims_rejected(lib, kw, code):
     n = ctypes.c_size_t(0)
@@ -144,6 +145,13 @@ def test_forward_rejects_bad_dims_and_shared_mismatch(lib):
     assert call(lib, sd) == binding.MOE_ERR_INVALID_ARG
     assert call(lib, sd, share_gmm1_weight=FAKE, share_gmm1_weight_scale=FAKE, share_gmm2_weight=FAKE,
                 share_gmm2_weight_scale=FAKE) == binding.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("src,dst,g,n,k", [
+    (None, FAKE, 1, 16, 64), (FAKE, None, 1, 16, 64), (FAKE, 2 * FAKE, 1, 24, 64), (FAKE, 2 * FAKE, 1, 16, 96),
+    (FAKE, 2 * FAKE, -1, 16, 64), (FAKE + 8, 2 * FAKE, 1, 16, 64), (FAKE, FAKE + 512, 1, 16, 64)])
+def test_pack_rejects_bad_arguments(lib, src, dst, g, n, k):
+    assert lib.moe_w8a8_pack_weights(src, dst, g, n, k, None) == binding.MOE_ERR_INVALID_ARG
 
 
 def test_status_strings(lib):

@@ -43,11 +43,29 @@ SMALL = {
 }
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_small_case_parity(name):
-    say(f"[parity] {name}: {SMALL[name]}")
-    stats, _, _ = check(synth.make_case(SMALL[name]))
+def test_small_case_parity(name, packed):
+    say(f"[parity] {name} packed={packed}: {SMALL[name]}")
+    stats, _, _ = check(synth.make_case(SMALL[name]), packed=packed)
     say(f"[parity] {name}: {stats}")
+
+
+def _pack_reference(w):
+    """The packed order written out with numpy, from its definition."""
+    G, n, k = w.shape
+    t = w.reshape(G, n // 16, 16, k // 64, 4, 16)          # g, tile, row-in-tile, step, lane-group, byte
+    t = t.transpose(0, 1, 3, 4, 2, 5)                      # g, tile, step, lane-group, row-in-tile, byte
+    return np.ascontiguousarray(t).reshape(-1)
+
+
+@pytest.mark.parametrize("shape", [(1, 16, 64), (3, 48, 192), (2, 4096, 512), (1, 512, 2048)])
+def test_pack_layout(shape):
+    rng = np.random.default_rng(7)
+    w = rng.integers(-127, 128, shape).astype(np.int8)
+    d = moe.moe_w8a8_pack_weights(torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(d.cpu().numpy().reshape(-1), _pack_reference(w))
 
 
 def test_zero_tokens():
@@ -152,7 +170,10 @@ def test_full_size_workload(cfg):
     if n is not None:
         rng = np.random.default_rng(cfg)
         tokens = np.sort(rng.choice(s.T, n, replace=False))
-    stats, gpu, ref = check(case, tokens=tokens)
-    say(f"[parity] config {cfg}: {stats}")
+    stats, gpu, ref = check(case, tokens=tokens, packed=True)
+    say(f"[parity] config {cfg} packed: {stats}")
+    if cfg in (1, 4):
+        stats, gpu, ref = check(case, tokens=tokens, packed=False)
+        say(f"[parity] config {cfg} row-major: {stats}")
     del gpu, ref
     torch.cuda.empty_cache()
