@@ -44,7 +44,9 @@ Layout make_layout(const moe_w8a8_dims_t *d) {
     L.imax = d->inter > d->share_inter ? d->inter : d->share_inter;
     L.rows_max = static_cast<int>(TK + T);
     const size_t nonempty = E < TK ? E : TK;
-    L.max_chunks = static_cast<int>(nonempty + TK / kChunkRows + (shared ? (T + kChunkRows - 1) / kChunkRows : 0));
+    L.chunk_rows = T <= kChunkRowsSmall ? kChunkRowsSmall : kChunkRowsLarge;
+    const size_t cr = L.chunk_rows;
+    L.max_chunks = static_cast<int>(nonempty + TK / cr + (shared ? (T + cr - 1) / cr : 0));
     const size_t R = L.rows_max;
     size_t o = 0;
     L.meta = o;        o = up256(o + sizeof(int32_t) * kMetaWords);
@@ -161,6 +163,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
     ra.E_loc = E;
     ra.base = d->ep_rank_id * E;
     ra.has_shared = shared;
+    ra.chunk_rows = L.chunk_rows;
     ra.counts_out = expert_token_nums;
     ra.offsets = I32(L.offsets);
     ra.sorted_pair = I32(L.sorted_pair);
@@ -218,6 +221,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g1.g_lo = 0;
         g1.g_hi = E + 1;
         g1.packed = d->weight_layout == MOE_WEIGHT_PACKED;
+        g1.mt = L.chunk_rows / kTileN;
         g1.n_tiles = L.imax / kTileN;
         g1.chunks = ra.chunks;
         g1.meta = meta;

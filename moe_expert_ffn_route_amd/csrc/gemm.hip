@@ -15,14 +15,16 @@
 // Decode is bound by the weight stream (each touched expert's bytes are read
 // once; per-expert rows M are 1..64), so the kernel is shaped around HBM, not
 // around MFMA throughput:
-//   - a work item is (chunk of <= 64 rows of one expert, 16-channel N tile
-//     pair); its 2 x 16 weight rows are split over the waves along K, and each
-//     wave pulls its whole K slice into registers with 16-byte loads up
-//     front, so a workgroup keeps 64-128 KB of weights in flight;
+//   - a work item is (chunk of <= 16*MT rows of one expert, 16-channel N tile
+//     pair); its 2 x 16 weight rows are split over the waves along K; each
+//     wave streams its K slice in batches of KSTEPS 64-byte steps, software
+//     pipelined (the next batch's loads are issued before this batch's
+//     MFMAs), with the whole loop unrolled so that the compiler's wait
+//     counters stay exact;
 //   - with packed weights (moe_w8a8_pack_weights) every wave load is one
 //     contiguous 1 KB block, read non-temporally;
-//   - the weights stay in registers while the chunk's 16-row MFMA tiles are
-//     swept, so a chunk reads its weight slice exactly once;
+//   - each weight batch is used for all of the chunk's 16-row MFMA tiles, so
+//     a chunk reads its weight slice exactly once;
 //   - the partial int32 tiles of the waves are summed in LDS (exact);
 //   - blockIdx maps linearly to (chunk, N tile), so the round-robin placement
 //     of blocks on the 8 XCDs gives each XCD an equal share of every expert;
@@ -37,25 +39,26 @@ namespace moe {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-constexpr int kMT = kChunkRows / kTileN;  // row tiles per chunk
 
 __device__ __forceinline__ v4i ld16(const int8_t *p) { return *reinterpret_cast<const v4i *>(p); }
 __device__ __forceinline__ v4i ld16_stream(const int8_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
 }
 
-template <int KIND, int WAVES, int KSTEPS, bool PACKED>
-__global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_dim, int n_pass) {
+// KIND 1 = GEMM1 + SwiGLU, 2 = GEMM2 + bf16. MT = 16-row MFMA tiles per
+// chunk. NPASS = K batches per wave (0: taken from n_pass_rt at run time).
+template <int KIND, int WAVES, int KSTEPS, bool PACKED, int MT, int NPASS>
+__global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_dim, int n_pass_rt) {
     constexpr int kThreads = WAVES * kWave;
     constexpr int kCols = KIND == 1 ? kTileN : 2 * kTileN;  // output columns of one work item
     constexpr int kElems = kTileN * kCols;                   // outputs of one 16-row tile
     constexpr int kEpt = (kElems + kThreads - 1) / kThreads; // outputs per thread per tile
+    const int n_pass = NPASS > 0 ? NPASS : n_pass_rt;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
     // Work item = (chunk, N tile), linear in blockIdx: the hardware deals
     // consecutive blocks round-robin to the 8 XCDs, so every XCD streams an
-    // equal share of every expert's weights (whole chunks per XCD left the
-    // XCDs up to one expert apart).
+    // equal share of every expert's weights.
     const int c = blockIdx.x / a.n_tiles;
     const int nt = blockIdx.x % a.n_tiles;
     const int4 ch = a.chunks[c];  // c < max_chunks: inside the chunk list even when unused
@@ -84,10 +87,50 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
     const int Kd = k_dim;
     const int r16 = lane & 15, kg = lane >> 4;
     const int step0 = wave * KSTEPS * n_pass;  // first 64-byte K step of this wave
+
+    // Issue order matters: vmcnt retires loads in issue order, so a wait for
+    // a small load issued after the weight stream would also wait for the
+    // weights. Independent small loads go first, then the first weight
+    // batch, then the loads that depend on the small ones, then the
+    // software-pipelined K loop. Scheduling barriers keep the compiler from
+    // reordering the phases.
+
+    // (1) independent small loads: token of each A row, epilogue rows' tokens
+    //     and the output channels' weight scales.
+    // GEMM1 rows of groups without smooth scales read the per-token rows of
+    // x (quantised once per token); every other A row is the grouped row.
+    // Lanes past the chunk's last row read that last row and are zeroed
+    // before the MFMA, so no load sits in a divergent branch.
+    const bool by_tok = KIND == 1 && (routed ? a.routed_by_token : a.shared_by_token);
+    const bool need_tok = by_tok || (KIND == 2 && !routed);
+    const int8_t *Abase = by_tok ? a.A_tok : a.A;
+    const float *Ascale = by_tok ? a.a_scale_tok : a.a_scale;
+    int arow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int lr = min(mt * kTileN + r16, rows - 1);
+        arow[mt] = by_tok ? a.row_token[row0 + lr] : row0 + lr;
+    }
+    // A thread's output column is the same in every row tile (kThreads is a
+    // multiple of kCols).
+    const int jc = tid % kCols;
+    const int col = (KIND == 1 ? nt * kTileN : nt * 2 * kTileN) + jc;
+    const float wsc0 = Ws[col];
+    const float wsc1 = KIND == 1 ? Ws[inter + col] : 0.0f;
+    int rrow[kEpt], rtok[kEpt];  // epilogue rows of the first row tile
+#pragma unroll
+    for (int e = 0; e < kEpt; ++e) {
+        rrow[e] = row0 + min(min(tid + e * kThreads, kElems - 1) / kCols, rows - 1);
+        rtok[e] = need_tok ? a.row_token[rrow[e]] : 0;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (2) first weight batch.
     // Row-major weights: lane reads 16 bytes of row (tile row + l%16) at byte
     // 64*step + 16*(l/16). Packed weights (moe_w8a8_pack_weights) hold exactly
     // those bytes as one contiguous 1 KB block per (16-row tile, step), so a
-    // wave's load is 1 KB contiguous and consecutive steps are adjacent.
+    // wave's load is 1 KB contiguous and consecutive steps are adjacent;
+    // those are read non-temporally, 64-byte row segments with plain loads.
     const int8_t *pw0, *pw1;
     size_t wstep;
     if (PACKED) {
@@ -100,81 +143,77 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
         pw1 = W + static_cast<size_t>(rowB + r16) * Kd + step0 * 64 + kg * 16;
         wstep = 64;
     }
-    // GEMM1 rows of groups without smooth scales read the per-token rows of
-    // x (quantised once per token); every other A row is the grouped row.
-    const bool by_tok = KIND == 1 && (routed ? a.routed_by_token : a.shared_by_token);
-    const int8_t *Abase = by_tok ? a.A_tok : a.A;
-    const float *Ascale = by_tok ? a.a_scale_tok : a.a_scale;
-    int arow[kMT];  // source row of this lane's A operand in each row tile
+    v4i wbuf[2][2][KSTEPS];
+    auto ldw = [&](v4i (&w)[2][KSTEPS], int pass) {
+        const size_t sp = static_cast<size_t>(pass) * KSTEPS;
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
-        const int lr = mt * kTileN + r16;
-        arow[mt] = lr < rows ? (by_tok ? a.row_token[row0 + lr] : row0 + lr) : 0;
-    }
-
-    // Epilogue operands of the first row tile, fetched before the weight
-    // stream so that their latency hides under it. A thread's output column
-    // is the same in every row tile (kThreads is a multiple of kCols).
-    const int jc = tid % kCols;
-    const int col = (KIND == 1 ? nt * kTileN : nt * 2 * kTileN) + jc;
-    float wsc0 = 0.0f, wsc1 = 0.0f;
-    if (tid < kElems) {
-        wsc0 = Ws[col];
-        if (KIND == 1) wsc1 = Ws[inter + col];
-    }
-    float rsc[kEpt];
-    int rtok[kEpt];
-#pragma unroll
-    for (int e = 0; e < kEpt; ++e) {
-        const int m = (tid + e * kThreads) / kCols;
-        rsc[e] = 0.0f;
-        rtok[e] = 0;
-        if (tid + e * kThreads < kElems && m < rows) {
-            rsc[e] = Ascale[by_tok ? a.row_token[row0 + m] : row0 + m];
-            if (KIND == 2 && !routed) rtok[e] = a.row_token[row0 + m];
+        for (int i = 0; i < KSTEPS; ++i) {
+            if (PACKED) {
+                w[0][i] = ld16_stream(pw0 + (sp + i) * wstep);
+                w[1][i] = ld16_stream(pw1 + (sp + i) * wstep);
+            } else {
+                w[0][i] = ld16(pw0 + (sp + i) * wstep);
+                w[1][i] = ld16(pw1 + (sp + i) * wstep);
+            }
         }
-    }
+    };
+    ldw(wbuf[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
 
-    v4i acc0[kMT], acc1[kMT];
+    // (3) loads that depend on (1): the first row tile's row scales
+    float rsc[kEpt];
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
+    for (int e = 0; e < kEpt; ++e) rsc[e] = Ascale[by_tok ? rtok[e] : rrow[e]];
+    __builtin_amdgcn_sched_barrier(0);
+
+    v4i acc0[MT], acc1[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
         acc0[mt] = v4i{0, 0, 0, 0};
         acc1[mt] = v4i{0, 0, 0, 0};
     }
-
-    for (int pass = 0; pass < n_pass; ++pass) {
-        v4i w0[KSTEPS], w1[KSTEPS];
-        const int sp = pass * KSTEPS;
+    // One K batch: this batch's A rows, then (if any) the next weight batch,
+    // then the MFMAs, which wait only for this batch's loads.
+    auto batch = [&](const v4i (&w)[2][KSTEPS], v4i (&nxt)[2][KSTEPS], int pass, bool has_next) {
+        v4i x[MT][KSTEPS];
 #pragma unroll
-        for (int i = 0; i < KSTEPS; ++i) {
-            // streamed weights: non-temporal when each wave load is a whole
-            // contiguous 1 KB block, plain loads for 64-byte row segments
-            if (PACKED) {
-                w0[i] = ld16_stream(pw0 + (sp + i) * wstep);
-                w1[i] = ld16_stream(pw1 + (sp + i) * wstep);
-            } else {
-                w0[i] = ld16(pw0 + (sp + i) * wstep);
-                w1[i] = ld16(pw1 + (sp + i) * wstep);
+        for (int mt = 0; mt < MT; ++mt) {
+            if (MT == 1 || mt * kTileN < rows) {  // uniform
+                const int8_t *pam =
+                    Abase + static_cast<size_t>(arow[mt]) * a.a_stride + (step0 + pass * KSTEPS) * 64 + kg * 16;
+#pragma unroll
+                for (int i = 0; i < KSTEPS; ++i) x[mt][i] = ld16(pam + i * 64);
             }
         }
+        if (has_next) ldw(nxt, pass + 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-            if (mt * kTileN < rows) {
+        for (int mt = 0; mt < MT; ++mt) {
+            if (MT == 1 || mt * kTileN < rows) {
                 const bool av = mt * kTileN + r16 < rows;
-                const int8_t *pam = Abase + static_cast<size_t>(arow[mt]) * a.a_stride + (step0 + sp) * 64 + kg * 16;
 #pragma unroll
                 for (int i = 0; i < KSTEPS; ++i) {
-                    const v4i x = av ? ld16(pam + i * 64) : v4i{0, 0, 0, 0};
-                    acc0[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x, w0[i], acc0[mt], 0, 0, 0);
-                    acc1[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x, w1[i], acc1[mt], 0, 0, 0);
+                    const v4i xi = av ? x[mt][i] : v4i{0, 0, 0, 0};
+                    acc0[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xi, w[0][i], acc0[mt], 0, 0, 0);
+                    acc1[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xi, w[1][i], acc1[mt], 0, 0, 0);
                 }
             }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (NPASS > 0) {
+#pragma unroll
+        for (int pass = 0; pass < NPASS; ++pass) batch(wbuf[pass & 1], wbuf[(pass + 1) & 1], pass, pass + 1 < NPASS);
+    } else {
+        for (int pass = 0; pass < n_pass; pass += 2) {
+            batch(wbuf[0], wbuf[1], pass, pass + 1 < n_pass);
+            if (pass + 1 < n_pass) batch(wbuf[1], wbuf[0], pass + 1, pass + 2 < n_pass);
         }
     }
 
     __shared__ int red[WAVES][2][kTileN][kTileN];
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
         if (mt * kTileN >= rows) break;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -235,51 +274,73 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
 // the number of 64-byte K steps a wave loads per batch (fewer steps per batch
 // = fewer VGPRs = more resident waves streaming).
 #ifndef MOE_GEMM1_WAVES
-#define MOE_GEMM1_WAVES 4
+#define MOE_GEMM1_WAVES 8
 #endif
 #ifndef MOE_GEMM1_KSTEPS
-#define MOE_GEMM1_KSTEPS 4
+#define MOE_GEMM1_KSTEPS 8
 #endif
 #ifndef MOE_GEMM2_WAVES
 #define MOE_GEMM2_WAVES 8
 #endif
 #ifndef MOE_GEMM2_KSTEPS
-#define MOE_GEMM2_KSTEPS 1
+#define MOE_GEMM2_KSTEPS 4
+#endif
+#ifndef MOE_GEMM1_KSTEPS_MT4
+#define MOE_GEMM1_KSTEPS_MT4 2
+#endif
+#ifndef MOE_GEMM2_KSTEPS_MT4
+#define MOE_GEMM2_KSTEPS_MT4 2
 #endif
 
-template <int KIND, int WAVES, bool PACKED>
-hipError_t launch_impl(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s) {
-    const int steps = k_dim / (64 * WAVES);
-    int ks = KIND == 1 ? MOE_GEMM1_KSTEPS : MOE_GEMM2_KSTEPS;
-    while (ks > 1 && steps % ks) ks >>= 1;
-    const int n_pass = steps / ks;
-    const long grid = static_cast<long>(max_chunks) * a.n_tiles;
-    if (grid <= 0) return hipSuccess;
+template <int KIND, int WAVES, int KSTEPS, bool PACKED, int MT>
+hipError_t launch_np(const GemmArgs &a, dim3 grid, int k_dim, int n_pass, hipStream_t s) {
     const dim3 blk(WAVES * kWave);
-    switch (ks) {
-        case 16: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, 16, PACKED>), dim3(grid), blk, 0, s, a, k_dim, n_pass); break;
-        case 8: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, 8, PACKED>), dim3(grid), blk, 0, s, a, k_dim, n_pass); break;
-        case 4: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, 4, PACKED>), dim3(grid), blk, 0, s, a, k_dim, n_pass); break;
-        case 2: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, 2, PACKED>), dim3(grid), blk, 0, s, a, k_dim, n_pass); break;
-        default: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, 1, PACKED>), dim3(grid), blk, 0, s, a, k_dim, n_pass); break;
+    switch (n_pass) {
+        case 1: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, 1>), grid, blk, 0, s, a, k_dim, 1); break;
+        case 2: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, 2>), grid, blk, 0, s, a, k_dim, 2); break;
+        case 4: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, 4>), grid, blk, 0, s, a, k_dim, 4); break;
+        case 8: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, 8>), grid, blk, 0, s, a, k_dim, 8); break;
+        default: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, 0>), grid, blk, 0, s, a, k_dim, n_pass); break;
     }
     return hipGetLastError();
 }
 
+// k_dim is a multiple of 256 (64-byte MFMA K step x 4 waves). A wave walks
+// k_dim / (64 * waves) steps in batches of KS1 (one row tile per chunk) or
+// KS4 (four row tiles: fewer steps per batch keep the A tiles in registers),
+// or of 1 step when that does not divide the steps.
+template <int KIND, int WAVES, int KS1, int KS4>
+hipError_t launch_w(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s) {
+    const long blocks = static_cast<long>(max_chunks) * a.n_tiles;
+    if (blocks <= 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    const int steps = k_dim / (64 * WAVES);
+    if (a.mt == 1) {
+        if (steps % KS1 == 0)
+            return a.packed ? launch_np<KIND, WAVES, KS1, true, 1>(a, grid, k_dim, steps / KS1, s)
+                            : launch_np<KIND, WAVES, KS1, false, 1>(a, grid, k_dim, steps / KS1, s);
+        return a.packed ? launch_np<KIND, WAVES, 1, true, 1>(a, grid, k_dim, steps, s)
+                        : launch_np<KIND, WAVES, 1, false, 1>(a, grid, k_dim, steps, s);
+    }
+    if (steps % KS4 == 0)
+        return a.packed ? launch_np<KIND, WAVES, KS4, true, 4>(a, grid, k_dim, steps / KS4, s)
+                        : launch_np<KIND, WAVES, KS4, false, 4>(a, grid, k_dim, steps / KS4, s);
+    return a.packed ? launch_np<KIND, WAVES, 1, true, 4>(a, grid, k_dim, steps, s)
+                    : launch_np<KIND, WAVES, 1, false, 4>(a, grid, k_dim, steps, s);
+}
+
 template <int KIND>
 hipError_t launch_kind(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s) {
-    // k_dim is a multiple of 256 (64-byte MFMA K step x 4 waves)
-    if constexpr ((KIND == 1 ? MOE_GEMM1_WAVES : MOE_GEMM2_WAVES) == 8) {
-        if (k_dim % 512 == 0)
-            return a.packed ? launch_impl<KIND, 8, true>(a, max_chunks, k_dim, s)
-                            : launch_impl<KIND, 8, false>(a, max_chunks, k_dim, s);
+    constexpr int W = KIND == 1 ? MOE_GEMM1_WAVES : MOE_GEMM2_WAVES;
+    constexpr int KS1 = KIND == 1 ? MOE_GEMM1_KSTEPS : MOE_GEMM2_KSTEPS;
+    constexpr int KS4 = KIND == 1 ? MOE_GEMM1_KSTEPS_MT4 : MOE_GEMM2_KSTEPS_MT4;
+    if constexpr (W == 8) {
+        if (k_dim % 512 == 0) return launch_w<KIND, 8, KS1, KS4>(a, max_chunks, k_dim, s);
     }
-    return a.packed ? launch_impl<KIND, 4, true>(a, max_chunks, k_dim, s)
-                    : launch_impl<KIND, 4, false>(a, max_chunks, k_dim, s);
+    return launch_w<KIND, 4, KS1, KS4>(a, max_chunks, k_dim, s);
 }
 
 }  // namespace
-
 hipError_t launch_gemm1(const GemmArgs &a, int max_chunks, hipStream_t s) {
     return launch_kind<1>(a, max_chunks, a.H, s);
 }

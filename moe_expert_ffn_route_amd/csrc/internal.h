@@ -11,7 +11,8 @@ constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kMaxLocalExperts = 512;
 constexpr int kRouteThreads = 1024;  // the routing kernel runs as one workgroup
 constexpr int kRouteWaves = kRouteThreads / kWave;
-constexpr int kChunkRows = 64;       // grouped rows per GEMM work item (4 MFMA row tiles)
+constexpr int kChunkRowsSmall = 16;  // grouped rows per GEMM work item when T <= 16 (1 MFMA row tile)
+constexpr int kChunkRowsLarge = 64;  // otherwise (4 MFMA row tiles)
 constexpr int kTileN = 16;           // MFMA 16x16x64 output tile edge
 constexpr int kMaxTopK = 16;
 constexpr int kMaxTokens = 1 << 16;
@@ -23,6 +24,7 @@ enum { kMetaP = 0, kMetaTAct = 1, kMetaBad = 2, kMetaChunks = 3, kMetaWords = 4 
 struct Layout {
     int rows_max;    // T*K + T grouped-row capacity
     int max_chunks;  // upper bound of GEMM work items
+    int chunk_rows;  // rows per GEMM work item
     int imax;        // max(I, I_s)
     size_t meta, offsets, sorted_pair, row_of_pair, row_token, row_group, chunks;
     size_t q_tok, xs_tok, q_x, xs, h, q_h, hs, z, total;
@@ -32,6 +34,7 @@ struct RouteArgs {
     const int32_t *ids;
     const uint8_t *mask;
     int T, K, E_g, E_loc, base, has_shared;
+    int chunk_rows;        // rows per GEMM work item
     int32_t *counts_out;   // expert_token_nums [E_loc]
     int32_t *offsets;      // [E_loc + 2]
     int32_t *sorted_pair;  // [T*K]
@@ -94,6 +97,7 @@ struct GemmArgs {
     int I, I_s, H, E_loc, imax;
     int g_lo, g_hi;   // only chunks of groups in [g_lo, g_hi)
     int packed;       // weights in moe_w8a8_pack_weights order
+    int mt;           // 16-row MFMA tiles per chunk: 1 or 4
     int n_tiles;      // work items per chunk along N
     const int4 *chunks;
     const int32_t *meta;

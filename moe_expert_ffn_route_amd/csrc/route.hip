@@ -161,7 +161,7 @@ __device__ void route_block(const RouteArgs &a) {
         t_act += total;
     }
 
-    // 5. GEMM work items: each group's rows cut into chunks of kChunkRows
+    // 5. GEMM work items: each group's rows cut into chunks of chunk_rows
     const int G = E + (a.has_shared ? 1 : 0);
     for (int g0 = 0; g0 < G; g0 += kRouteThreads) {
         const int g = g0 + tid;
@@ -170,12 +170,12 @@ __device__ void route_block(const RouteArgs &a) {
             M = g < E ? s_count[g] : t_act;
             row0 = g < E ? s_off[g] : P;
         }
-        const int nch = (M + kChunkRows - 1) / kChunkRows;
+        const int nch = (M + a.chunk_rows - 1) / a.chunk_rows;
         int total;
         const int c = s_nch + block_exclusive_scan(nch, s_tmp, &total);
         for (int i = 0; i < nch; ++i) {
-            const int r = i * kChunkRows;
-            a.chunks[c + i] = make_int4(g, row0 + r, min(kChunkRows, M - r), 0);
+            const int r = i * a.chunk_rows;
+            a.chunks[c + i] = make_int4(g, row0 + r, min(a.chunk_rows, M - r), 0);
         }
         __syncthreads();
         if (tid == 0) s_nch += total;
