@@ -51,6 +51,25 @@ def test_small_case_parity(name, packed):
     say(f"[parity] {name}: {stats}")
 
 
+# The production tile shapes (hidden 4096, intermediate 2048: one K batch per
+# wave in GEMM1) at small T: 16-row chunks (T <= 16) and 64-row chunks
+# (T > 16), including an expert with more than one chunk.
+H4096 = {
+    "h4096_t6_shared": spec(T=6, H=4096, I=2048, E_g=8, K=2, I_s=2048, seed=121),
+    "h4096_mask_smooth": spec(T=10, H=4096, I=2048, E_g=4, K=2, active=7, smooth=True, seed=122),
+    "h4096_mt4_shared": spec(T=40, H=4096, I=2048, E_g=4, K=2, I_s=2048, seed=123),
+    "h4096_mt4_multichunk": spec(T=80, H=4096, I=2048, E_g=2, K=2, seed=124),
+}
+
+
+@pytest.mark.parametrize("packed", [True, False], ids=["packed", "rowmajor"])
+@pytest.mark.parametrize("name", list(H4096))
+def test_production_tile_parity(name, packed):
+    say(f"[parity] {name} packed={packed}: {H4096[name]}")
+    stats, gpu, _ = check(synth.make_case(H4096[name]), packed=packed)
+    say(f"[parity] {name}: {stats}")
+
+
 def _pack_reference(w):
     """The packed order written out with numpy, from its definition."""
     G, n, k = w.shape
