@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB 5 times (calibrates HBM byte counters)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step per weight copy into HIP graphs and time their replays")
     ap.add_argument("--no-stage-events", action="store_true",
                     help="time the steps without per-stage events (stage times then come from a second pass)")
     args = ap.parse_args()
@@ -172,6 +174,20 @@ def main():
     torch.cuda.synchronize()
     counts = runner.expert_token_nums.cpu().numpy()
 
+    graphs = []
+    if args.graph:
+        # one graph per weight copy; the GEMM1 events of the timed region are
+        # not recorded inside graphs (stage times come from the per-stage pass)
+        for li in range(len(layers)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                runner(layers[li], stream=stream)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+
     log(f"[bench] timing {args.steps} steps")
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
@@ -179,13 +195,16 @@ def main():
     with torch.cuda.stream(stream):
         t_start.record(stream)
         for i in range(args.steps):
-            runner(layers[i % len(layers)], dbg=None if args.no_stage_events else g1_dbg[i], stream=stream)
+            if graphs:
+                graphs[i % len(graphs)].replay()
+            else:
+                runner(layers[i % len(layers)], dbg=None if args.no_stage_events else g1_dbg[i], stream=stream)
         t_stop.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_stop)
     ms_per_step = total_ms / args.steps
     g1_us = None
-    if not args.no_stage_events:
+    if not args.no_stage_events and not graphs:
         g1_us = float(np.mean([events[i][G1 - 1].elapsed_time(events[i][G1]) for i in range(args.steps)])) * 1e3
 
     log("[bench] per-stage pass")
@@ -222,7 +241,8 @@ def main():
         "config": {"workload": spec.name, "tokens": spec.T, "hidden": spec.H, "inter": spec.I,
                    "experts": spec.E_g, "topk": spec.K, "share_inter": spec.I_s,
                    "touched_experts": touched, "grouped_rows": rows, "weight_copies": len(layers),
-                   "weight_layout": "row_major" if args.row_major else "packed"},
+                   "weight_layout": "row_major" if args.row_major else "packed",
+                   "launch": "hip_graph" if graphs else "stream"},
         "hbm_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
         "tokens_per_s": round(spec.T / (us * 1e-6), 1),
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},  # separate pass, every stage bracketed

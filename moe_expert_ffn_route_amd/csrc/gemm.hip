@@ -285,11 +285,11 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
 #ifndef MOE_GEMM2_KSTEPS
 #define MOE_GEMM2_KSTEPS 4
 #endif
-#ifndef MOE_GEMM1_KSTEPS_MT4
-#define MOE_GEMM1_KSTEPS_MT4 2
+#ifndef MOE_GEMM1_KSTEPS_LARGE
+#define MOE_GEMM1_KSTEPS_LARGE 4
 #endif
-#ifndef MOE_GEMM2_KSTEPS_MT4
-#define MOE_GEMM2_KSTEPS_MT4 2
+#ifndef MOE_GEMM2_KSTEPS_LARGE
+#define MOE_GEMM2_KSTEPS_LARGE 4
 #endif
 
 template <int KIND, int WAVES, int KSTEPS, bool PACKED, int MT>
@@ -307,7 +307,7 @@ hipError_t launch_np(const GemmArgs &a, dim3 grid, int k_dim, int n_pass, hipStr
 
 // k_dim is a multiple of 256 (64-byte MFMA K step x 4 waves). A wave walks
 // k_dim / (64 * waves) steps in batches of KS1 (one row tile per chunk) or
-// KS4 (four row tiles: fewer steps per batch keep the A tiles in registers),
+// KS4 (MOE_LARGE_MT row tiles: fewer steps per batch keep the A tiles in registers),
 // or of 1 step when that does not divide the steps.
 template <int KIND, int WAVES, int KS1, int KS4>
 hipError_t launch_w(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s) {
@@ -322,18 +322,19 @@ hipError_t launch_w(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s)
         return a.packed ? launch_np<KIND, WAVES, 1, true, 1>(a, grid, k_dim, steps, s)
                         : launch_np<KIND, WAVES, 1, false, 1>(a, grid, k_dim, steps, s);
     }
+    constexpr int MTL = MOE_LARGE_MT;
     if (steps % KS4 == 0)
-        return a.packed ? launch_np<KIND, WAVES, KS4, true, 4>(a, grid, k_dim, steps / KS4, s)
-                        : launch_np<KIND, WAVES, KS4, false, 4>(a, grid, k_dim, steps / KS4, s);
-    return a.packed ? launch_np<KIND, WAVES, 1, true, 4>(a, grid, k_dim, steps, s)
-                    : launch_np<KIND, WAVES, 1, false, 4>(a, grid, k_dim, steps, s);
+        return a.packed ? launch_np<KIND, WAVES, KS4, true, MTL>(a, grid, k_dim, steps / KS4, s)
+                        : launch_np<KIND, WAVES, KS4, false, MTL>(a, grid, k_dim, steps / KS4, s);
+    return a.packed ? launch_np<KIND, WAVES, 1, true, MTL>(a, grid, k_dim, steps, s)
+                    : launch_np<KIND, WAVES, 1, false, MTL>(a, grid, k_dim, steps, s);
 }
 
 template <int KIND>
 hipError_t launch_kind(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s) {
     constexpr int W = KIND == 1 ? MOE_GEMM1_WAVES : MOE_GEMM2_WAVES;
     constexpr int KS1 = KIND == 1 ? MOE_GEMM1_KSTEPS : MOE_GEMM2_KSTEPS;
-    constexpr int KS4 = KIND == 1 ? MOE_GEMM1_KSTEPS_MT4 : MOE_GEMM2_KSTEPS_MT4;
+    constexpr int KS4 = KIND == 1 ? MOE_GEMM1_KSTEPS_LARGE : MOE_GEMM2_KSTEPS_LARGE;
     if constexpr (W == 8) {
         if (k_dim % 512 == 0) return launch_w<KIND, 8, KS1, KS4>(a, max_chunks, k_dim, s);
     }

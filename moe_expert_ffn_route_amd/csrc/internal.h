@@ -11,8 +11,13 @@ constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kMaxLocalExperts = 512;
 constexpr int kRouteThreads = 1024;  // the routing kernel runs as one workgroup
 constexpr int kRouteWaves = kRouteThreads / kWave;
-constexpr int kChunkRowsSmall = 16;  // grouped rows per GEMM work item when T <= 16 (1 MFMA row tile)
-constexpr int kChunkRowsLarge = 64;  // otherwise (4 MFMA row tiles)
+// Grouped rows per GEMM work item: one 16-row MFMA tile when T <= 16 (decode),
+// MOE_LARGE_MT tiles otherwise.
+#ifndef MOE_LARGE_MT
+#define MOE_LARGE_MT 2
+#endif
+constexpr int kChunkRowsSmall = 16;
+constexpr int kChunkRowsLarge = 16 * MOE_LARGE_MT;
 constexpr int kTileN = 16;           // MFMA 16x16x64 output tile edge
 constexpr int kMaxTopK = 16;
 constexpr int kMaxTokens = 1 << 16;

@@ -87,6 +87,26 @@ def test_pack_layout(shape):
     assert np.array_equal(d.cpu().numpy().reshape(-1), _pack_reference(w))
 
 
+# Size limits of the C ABI: 512 local experts, top-16, hidden and intermediate
+# 16384, and many routing rounds (32768 pairs); the oracle computes a sample of
+# tokens where the full batch would take long, the routing always in full.
+LIMITS = {
+    "e512_k16": (spec(T=64, H=256, I=256, E_g=512, K=16, I_s=256, seed=131), None),
+    "hidden_16384": (spec(T=3, H=16384, I=256, E_g=4, K=2, I_s=256, seed=132), None),
+    "inter_16384": (spec(T=3, H=256, I=16384, E_g=4, K=2, I_s=512, seed=133), None),
+    "pairs_32768": (spec(T=2048, H=256, I=256, E_g=64, K=16, active=1900, seed=134), [0, 5, 777, 2047]),
+}
+
+
+@pytest.mark.parametrize("packed", [True, False], ids=["packed", "rowmajor"])
+@pytest.mark.parametrize("name", list(LIMITS))
+def test_size_limits(name, packed):
+    sp, tokens = LIMITS[name]
+    say(f"[parity] {name} packed={packed}: {sp}")
+    stats, _, _ = check(synth.make_case(sp), tokens=tokens, packed=packed)
+    say(f"[parity] {name}: {stats}")
+
+
 def test_zero_tokens():
     s = spec(T=0, I_s=256)
     c = synth.make_case(s)
@@ -134,6 +154,36 @@ def test_deterministic_dirty_workspace_and_side_stream():
         n = c.spec.I if r < P else c.spec.I_s
         for k, w in (("q_x", c.spec.H), ("acc1", 2 * n), ("h", n), ("q_h", n), ("acc2", c.spec.H)):
             assert np.array_equal(a[k][r, :w], b[k][r, :w]), (k, r)
+
+
+def test_hip_graph_capture_and_replay():
+    # the production path launches kernels only (no memset, no allocation), so
+    # a caller can capture it; every replay must match the eager result, with
+    # other eager work and synchronisations between replays
+    c = synth.make_case(spec(T=12, H=512, I=256, E_g=8, K=2, I_s=256, active=10, seed=116))
+    t = moe.pack_weights(moe.upload(c))
+    dims = moe.dims_of_case(c)
+    dims.weight_layout = moe.MOE_WEIGHT_PACKED
+    runner = moe.Runner(dims)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        runner(t, stream=s)
+    torch.cuda.synchronize()
+    eager = (runner.output.clone(), runner.share_output.clone(), runner.expert_token_nums.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        runner(t, stream=s)
+    for i in range(4):
+        runner.output.fill_(3)
+        runner.share_output.fill_(3)
+        runner.expert_token_nums.fill_(-1)
+        runner.workspace.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(runner.output, eager[0]), i
+        assert torch.equal(runner.share_output, eager[1]), i
+        assert torch.equal(runner.expert_token_nums, eager[2]), i
 
 
 def test_repeated_calls_shrinking_batch():
