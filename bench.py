@@ -12,9 +12,9 @@ i % layers, as consecutive MoE layers of a model would, so every step streams
 its experts' weights from HBM rather than from the 256 MB last-level cache.
 
 Prints one JSON line: the metric (µs per MoE layer), the achieved HBM GB/s of
-the layer, the roofline of the dominant kernel (GEMM1) from HIP events
-recorded on the launch stream around that kernel in every timed step, and the
-CPU oracle's time on this host as a baseline.
+the layer, the roofline of the dominant kernel (GEMM1) from HIP events bound
+to that kernel's launch (hipExtLaunchKernel) in every timed step, and the CPU
+oracle's time on this host as a baseline.
 """
 from __future__ import annotations
 
@@ -35,6 +35,9 @@ import moe_expert_ffn_route_amd as moe  # noqa: E402
 from moe_expert_ffn_route_amd import binding, synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix rate, published (no sparsity)
+MFMA_I8_OPS_PER_CLK_CU = 8192  # the per-CU rate at which 256 CUs at 2.4 GHz reach the published figure
+HIP_ATTR_CLOCK_RATE = 5  # hipDeviceAttributeClockRate (peak clock, kHz) in hip_runtime_api.h
 
 
 def log(*a):
@@ -53,9 +56,44 @@ def algorithmic_bytes(case, counts):
     if case.smooth is not None:
         act += 4 * s.E_loc * H
     gemm1 = touched * (2 * I * H + 8 * I) + ((2 * Is * H + 8 * Is) if Is else 0)
-    rows = int(counts.sum()) + (T if Is else 0)
+    routed_rows = int(counts.sum())
+    t_act = T if case.mask is None else int(np.count_nonzero(case.mask))
+    rows = routed_rows + (t_act if Is else 0)
     gemm1 += rows * (H + 4 + 4 * max(I, Is))  # q_x and xs read, h written
-    return touched * per_expert + shared + act, gemm1, touched, rows
+    gemm2 = touched * (H * I + 4 * H) + ((H * Is + 4 * H) if Is else 0)
+    gemm2 += routed_rows * (I + 4 + 2 * H) + ((t_act * (Is + 4 + 2 * H)) if Is else 0)  # q_h, hs in; z out
+    return touched * per_expert + shared + act, gemm1, gemm2, touched, rows
+
+
+def layer_ops(case, counts):
+    """Integer multiply-adds (x2) of the two GEMMs: 2 * rows * 3 * H * I for
+    the routed rows and the same with I_s for the shared rows."""
+    s = case.spec
+    routed = int(counts.sum())
+    t_act = s.T if case.mask is None else int(np.count_nonzero(case.mask))
+    return 2 * 3 * s.H * (routed * s.I + (t_act * s.I_s if s.I_s else 0))
+
+
+def mfma_peak_on_device():
+    """int8 MFMA peak re-derived from the device: CUs x peak clock x the
+    per-CU rate; None when the clock cannot be read."""
+    props = torch.cuda.get_device_properties(0)
+    for name in ("libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"):
+        try:
+            hip = ctypes.CDLL(name)
+            break
+        except OSError:
+            hip = None
+    if hip is None:
+        return None
+    khz = ctypes.c_int(0)
+    if hip.hipDeviceGetAttribute(ctypes.byref(khz), HIP_ATTR_CLOCK_RATE, torch.cuda.current_device()) != 0:
+        return None
+    if not 500_000 <= khz.value <= 5_000_000:
+        return None
+    cus = props.multi_processor_count
+    return {"cus": cus, "clock_mhz": khz.value / 1e3,
+            "tops": round(cus * khz.value * 1e3 * MFMA_I8_OPS_PER_CLK_CU / 1e12, 1)}
 
 
 def gemm1_traffic(workload):
@@ -112,8 +150,9 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB 5 times (calibrates HBM byte counters)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step per weight copy into HIP graphs and time their replays")
-    ap.add_argument("--no-stage-events", action="store_true",
-                    help="time the steps without per-stage events (stage times then come from a second pass)")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time the steps without the GEMM kernel events (GEMM times then come from the "
+                         "per-stage pass)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -153,19 +192,23 @@ def main():
     runner = moe.Runner(dims)
     stream = torch.cuda.Stream()
     n_ev = len(binding.STAGES) + 1
-    G1 = 1 + binding.STAGES.index("gemm1")  # event after GEMM1; the one before it is G1 - 1
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    for evs in events:
+    kevents = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for evs in events + kevents:
         for e in evs:
             e.record(stream)  # materialise the HIP event handles
     torch.cuda.synchronize()
-    # timed region: only the two events bracketing GEMM1 are recorded (by the
-    # library, on the launch stream); the per-stage pass below records all
-    g1_arrays = [(ctypes.c_void_p * n_ev)(*[e.cuda_event if j in (G1 - 1, G1) else None for j, e in enumerate(evs)])
-                 for evs in events]
+    # timed region: the library binds two events to the GEMM1 launch itself
+    # (its start and end); the per-stage pass below records a marker event
+    # between every two stages and binds GEMM2's pair
+    # (GEMM1 only: each bound event costs a few µs of the step)
+    k_arrays = [(ctypes.c_void_p * 4)(evs[0].cuda_event, evs[1].cuda_event, None, None) for evs in kevents]
+    k2_arrays = [(ctypes.c_void_p * 4)(None, None, evs[2].cuda_event, evs[3].cuda_event) for evs in kevents]
     all_arrays = [(ctypes.c_void_p * n_ev)(*[e.cuda_event for e in evs]) for evs in events]
-    g1_dbg = [binding.Debug(stage_events=ctypes.cast(p, ctypes.c_void_p).value) for p in g1_arrays]
-    all_dbg = [binding.Debug(stage_events=ctypes.cast(p, ctypes.c_void_p).value) for p in all_arrays]
+    k_dbg = [binding.Debug(kernel_events=ctypes.cast(p, ctypes.c_void_p).value) for p in k_arrays]
+    all_dbg = [binding.Debug(stage_events=ctypes.cast(p, ctypes.c_void_p).value,
+                             kernel_events=ctypes.cast(q, ctypes.c_void_p).value)
+               for p, q in zip(all_arrays, k2_arrays)]
 
     log(f"[bench] warmup {args.warmup} steps")
     with torch.cuda.stream(stream):
@@ -198,14 +241,14 @@ def main():
             if graphs:
                 graphs[i % len(graphs)].replay()
             else:
-                runner(layers[i % len(layers)], dbg=None if args.no_stage_events else g1_dbg[i], stream=stream)
+                runner(layers[i % len(layers)], dbg=None if args.no_kernel_events else k_dbg[i], stream=stream)
         t_stop.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_stop)
     ms_per_step = total_ms / args.steps
-    g1_us = None
-    if not args.no_stage_events and not graphs:
-        g1_us = float(np.mean([events[i][G1 - 1].elapsed_time(events[i][G1]) for i in range(args.steps)])) * 1e3
+    g1_us = g2_us = None
+    if not args.no_kernel_events and not graphs:
+        g1_us = float(np.mean([kevents[i][0].elapsed_time(kevents[i][1]) for i in range(args.steps)])) * 1e3
 
     log("[bench] per-stage pass")
     with torch.cuda.stream(stream):
@@ -214,17 +257,35 @@ def main():
     torch.cuda.synchronize()
     stage_us = {name: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]) * 1e3)
                 for j, name in enumerate(binding.STAGES)}
+    g2_us = float(np.mean([kevents[i][2].elapsed_time(kevents[i][3]) for i in range(args.steps)])) * 1e3
+    timing = "kernel-bound HIP events in the timed steps"
     if g1_us is None:
         g1_us = stage_us["gemm1"]
+        timing = "marker HIP events between stages (per-stage pass)"
+
+    log("[bench] per-step distribution pass")
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    with torch.cuda.stream(stream):
+        bounds[0].record(stream)
+        for i in range(args.steps):
+            if graphs:
+                graphs[i % len(graphs)].replay()
+            else:
+                runner(layers[i % len(layers)], stream=stream)
+            bounds[i + 1].record(stream)
+    torch.cuda.synchronize()
+    step_samples = [bounds[i].elapsed_time(bounds[i + 1]) * 1e3 for i in range(args.steps)]
+    p10, p50, p90 = (float(v) for v in np.percentile(step_samples, [10, 50, 90]))
 
     out = runner.output.float()
     if not torch.isfinite(out).all():
         raise RuntimeError("non-finite output")
 
-    layer_bytes, gemm1_bytes, touched, rows = algorithmic_bytes(case, counts)
+    layer_bytes, gemm1_bytes, gemm2_bytes, touched, rows = algorithmic_bytes(case, counts)
     us = ms_per_step * 1e3
     g1_gbs = gemm1_bytes / (g1_us * 1e-6) / 1e9
     traffic = None if args.row_major else gemm1_traffic(spec.name)
+    tops = layer_ops(case, counts) / (us * 1e-6) / 1e12
     rec = {
         "metric": "µs per MoE layer (T=8 decode); achieved HBM GB/s in hbm_gbps",
         "value": round(us, 2),
@@ -245,10 +306,16 @@ def main():
                    "launch": "hip_graph" if graphs else "stream"},
         "hbm_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
         "tokens_per_s": round(spec.T / (us * 1e-6), 1),
+        "step_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],  # one event per step boundary
+        "tops": round(tops, 2),
+        "mfma_i8_frac": round(tops / MFMA_I8_PEAK_TOPS, 5),
+        "mfma_i8_peak_derived": mfma_peak_on_device(),
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},  # separate pass, every stage bracketed
         "roofline": {"kernel": "gemm1_swiglu", "bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes": gemm1_bytes, "avg_us": round(g1_us, 2)},
+                     "algorithmic_bytes": gemm1_bytes, "avg_us": round(g1_us, 2), "timing": timing},
+        "gemm2": {"achieved": round(gemm2_bytes / (g2_us * 1e-6) / 1e9, 1), "unit": "GB/s",
+                  "algorithmic_bytes": gemm2_bytes, "avg_us": round(g2_us, 2)},
     }
     if args.no_cpu_baseline:
         rec["cpu_baseline"] = None

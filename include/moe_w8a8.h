@@ -111,6 +111,13 @@ typedef struct {
                                skipped), recorded on the stream before routing
                                and after each stage: route, quant, GEMM1,
                                requant, GEMM2, combine                         */
+    void   **kernel_events; /* [4] caller-created hipEvent_t (NULL entries are
+                               skipped) bound to the GEMM kernels themselves
+                               (hipExtLaunchKernel): start and end of the GEMM1
+                               launch, start of the first and end of the last
+                               GEMM2 launch. Unlike stage_events they add no
+                               marker between kernels, so their elapsed times
+                               are the kernels' own durations.               */
 } moe_w8a8_debug_t;
 
 /* Workspace bytes that moe_w8a8_forward needs for these dims. The size depends

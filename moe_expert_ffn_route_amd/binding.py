@@ -42,7 +42,7 @@ class Dims(ctypes.Structure):
 
 
 DEBUG_FIELDS = ("sorted_pair", "row_of_pair", "group_offset", "shared_token", "num_rows", "q_x", "xs", "acc1",
-                "h", "q_h", "hs", "acc2", "z", "stage_events")
+                "h", "q_h", "hs", "acc2", "z", "stage_events", "kernel_events")
 STAGES = ("route_quant", "smooth_quant", "gemm1", "requant", "gemm2", "combine")
 
 

@@ -147,6 +147,9 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
                hipEventRecord(static_cast<hipEvent_t>(D.stage_events[i]), s) == hipSuccess;
     };
     if (!mark(0)) return MOE_ERR_HIP;
+    auto kev = [&](int i) {
+        return D.kernel_events ? static_cast<hipEvent_t>(D.kernel_events[i]) : static_cast<hipEvent_t>(nullptr);
+    };
 
     // GEMM1 input rows: per token (quantised once, in the routing launch)
     // for groups without smooth scales, per grouped row otherwise
@@ -228,7 +231,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g1.row_token = ra.row_token;
         g1.h = reinterpret_cast<float *>(ws + L.h);
         g1.dbg_acc = D.acc1;
-        if (launch_gemm1(g1, L.max_chunks, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
+        if (launch_gemm1(g1, L.max_chunks, s, kev(0), kev(1)) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
 
         RequantArgs rq;
         rq.h = g1.h;
@@ -262,13 +265,14 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g2.dbg_z = D.z;
         // the contraction length of GEMM2 is the group's intermediate size
         if (!shared || d->share_inter == d->inter) {
-            if (launch_gemm2(g2, L.max_chunks, d->inter, s) != hipSuccess) return MOE_ERR_HIP;
+            if (launch_gemm2(g2, L.max_chunks, d->inter, s, kev(2), kev(3)) != hipSuccess) return MOE_ERR_HIP;
         } else {
             g2.g_hi = E;
-            if (launch_gemm2(g2, L.max_chunks, d->inter, s) != hipSuccess) return MOE_ERR_HIP;
+            if (launch_gemm2(g2, L.max_chunks, d->inter, s, kev(2), nullptr) != hipSuccess) return MOE_ERR_HIP;
             g2.g_lo = E;
             g2.g_hi = E + 1;
-            if (launch_gemm2(g2, L.max_chunks, d->share_inter, s) != hipSuccess) return MOE_ERR_HIP;
+            if (launch_gemm2(g2, L.max_chunks, d->share_inter, s, nullptr, kev(3)) != hipSuccess)
+                return MOE_ERR_HIP;
         }
         if (!mark(5)) return MOE_ERR_HIP;
 

@@ -35,6 +35,8 @@
 // holds D[4 * (l / 16) + i][l % 16].
 #include "internal.h"
 
+#include <hip/hip_ext.h>
+
 namespace moe {
 namespace {
 
@@ -292,15 +294,25 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
 #define MOE_GEMM2_KSTEPS_LARGE 4
 #endif
 
-template <int KIND, int WAVES, int KSTEPS, bool PACKED, int MT>
-hipError_t launch_np(const GemmArgs &a, dim3 grid, int k_dim, int n_pass, hipStream_t s) {
+template <int KIND, int WAVES, int KSTEPS, bool PACKED, int MT, int NPASS>
+void launch_one(const GemmArgs &a, dim3 grid, int k_dim, int n_pass, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const dim3 blk(WAVES * kWave);
+    if (e0 || e1)
+        hipExtLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, NPASS>), grid, blk, 0, s, e0, e1, 0, a,
+                              k_dim, n_pass);
+    else
+        hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, NPASS>), grid, blk, 0, s, a, k_dim, n_pass);
+}
+
+template <int KIND, int WAVES, int KSTEPS, bool PACKED, int MT>
+hipError_t launch_np(const GemmArgs &a, dim3 grid, int k_dim, int n_pass, hipStream_t s, hipEvent_t e0,
+                     hipEvent_t e1) {
     switch (n_pass) {
-        case 1: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, 1>), grid, blk, 0, s, a, k_dim, 1); break;
-        case 2: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, 2>), grid, blk, 0, s, a, k_dim, 2); break;
-        case 4: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, 4>), grid, blk, 0, s, a, k_dim, 4); break;
-        case 8: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, 8>), grid, blk, 0, s, a, k_dim, 8); break;
-        default: hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, 0>), grid, blk, 0, s, a, k_dim, n_pass); break;
+        case 1: launch_one<KIND, WAVES, KSTEPS, PACKED, MT, 1>(a, grid, k_dim, 1, s, e0, e1); break;
+        case 2: launch_one<KIND, WAVES, KSTEPS, PACKED, MT, 2>(a, grid, k_dim, 2, s, e0, e1); break;
+        case 4: launch_one<KIND, WAVES, KSTEPS, PACKED, MT, 4>(a, grid, k_dim, 4, s, e0, e1); break;
+        case 8: launch_one<KIND, WAVES, KSTEPS, PACKED, MT, 8>(a, grid, k_dim, 8, s, e0, e1); break;
+        default: launch_one<KIND, WAVES, KSTEPS, PACKED, MT, 0>(a, grid, k_dim, n_pass, s, e0, e1); break;
     }
     return hipGetLastError();
 }
@@ -310,44 +322,45 @@ hipError_t launch_np(const GemmArgs &a, dim3 grid, int k_dim, int n_pass, hipStr
 // KS4 (MOE_LARGE_MT row tiles: fewer steps per batch keep the A tiles in registers),
 // or of 1 step when that does not divide the steps.
 template <int KIND, int WAVES, int KS1, int KS4>
-hipError_t launch_w(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s) {
+hipError_t launch_w(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const long blocks = static_cast<long>(max_chunks) * a.n_tiles;
     if (blocks <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(blocks));
     const int steps = k_dim / (64 * WAVES);
     if (a.mt == 1) {
         if (steps % KS1 == 0)
-            return a.packed ? launch_np<KIND, WAVES, KS1, true, 1>(a, grid, k_dim, steps / KS1, s)
-                            : launch_np<KIND, WAVES, KS1, false, 1>(a, grid, k_dim, steps / KS1, s);
-        return a.packed ? launch_np<KIND, WAVES, 1, true, 1>(a, grid, k_dim, steps, s)
-                        : launch_np<KIND, WAVES, 1, false, 1>(a, grid, k_dim, steps, s);
+            return a.packed ? launch_np<KIND, WAVES, KS1, true, 1>(a, grid, k_dim, steps / KS1, s, e0, e1)
+                            : launch_np<KIND, WAVES, KS1, false, 1>(a, grid, k_dim, steps / KS1, s, e0, e1);
+        return a.packed ? launch_np<KIND, WAVES, 1, true, 1>(a, grid, k_dim, steps, s, e0, e1)
+                        : launch_np<KIND, WAVES, 1, false, 1>(a, grid, k_dim, steps, s, e0, e1);
     }
     constexpr int MTL = MOE_LARGE_MT;
     if (steps % KS4 == 0)
-        return a.packed ? launch_np<KIND, WAVES, KS4, true, MTL>(a, grid, k_dim, steps / KS4, s)
-                        : launch_np<KIND, WAVES, KS4, false, MTL>(a, grid, k_dim, steps / KS4, s);
-    return a.packed ? launch_np<KIND, WAVES, 1, true, MTL>(a, grid, k_dim, steps, s)
-                    : launch_np<KIND, WAVES, 1, false, MTL>(a, grid, k_dim, steps, s);
+        return a.packed ? launch_np<KIND, WAVES, KS4, true, MTL>(a, grid, k_dim, steps / KS4, s, e0, e1)
+                        : launch_np<KIND, WAVES, KS4, false, MTL>(a, grid, k_dim, steps / KS4, s, e0, e1);
+    return a.packed ? launch_np<KIND, WAVES, 1, true, MTL>(a, grid, k_dim, steps, s, e0, e1)
+                    : launch_np<KIND, WAVES, 1, false, MTL>(a, grid, k_dim, steps, s, e0, e1);
 }
 
 template <int KIND>
-hipError_t launch_kind(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s) {
+hipError_t launch_kind(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     constexpr int W = KIND == 1 ? MOE_GEMM1_WAVES : MOE_GEMM2_WAVES;
     constexpr int KS1 = KIND == 1 ? MOE_GEMM1_KSTEPS : MOE_GEMM2_KSTEPS;
     constexpr int KS4 = KIND == 1 ? MOE_GEMM1_KSTEPS_LARGE : MOE_GEMM2_KSTEPS_LARGE;
     if constexpr (W == 8) {
-        if (k_dim % 512 == 0) return launch_w<KIND, 8, KS1, KS4>(a, max_chunks, k_dim, s);
+        if (k_dim % 512 == 0) return launch_w<KIND, 8, KS1, KS4>(a, max_chunks, k_dim, s, e0, e1);
     }
-    return launch_w<KIND, 4, KS1, KS4>(a, max_chunks, k_dim, s);
+    return launch_w<KIND, 4, KS1, KS4>(a, max_chunks, k_dim, s, e0, e1);
 }
 
 }  // namespace
-hipError_t launch_gemm1(const GemmArgs &a, int max_chunks, hipStream_t s) {
-    return launch_kind<1>(a, max_chunks, a.H, s);
+hipError_t launch_gemm1(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+    return launch_kind<1>(a, max_chunks, a.H, s, ev_start, ev_stop);
 }
 
-hipError_t launch_gemm2(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s) {
-    return launch_kind<2>(a, max_chunks, k_dim, s);
+hipError_t launch_gemm2(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
+                        hipEvent_t ev_stop) {
+    return launch_kind<2>(a, max_chunks, k_dim, s, ev_start, ev_stop);
 }
 
 }  // namespace moe

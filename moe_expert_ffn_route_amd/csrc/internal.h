@@ -102,7 +102,7 @@ struct GemmArgs {
     int I, I_s, H, E_loc, imax;
     int g_lo, g_hi;   // only chunks of groups in [g_lo, g_hi)
     int packed;       // weights in moe_w8a8_pack_weights order
-    int mt;           // 16-row MFMA tiles per chunk: 1 or 4
+    int mt;           // 16-row MFMA tiles per chunk: 1 or MOE_LARGE_MT
     int n_tiles;      // work items per chunk along N
     const int4 *chunks;
     const int32_t *meta;
@@ -128,8 +128,10 @@ struct CombineArgs {
 hipError_t launch_route_quant(const RouteArgs &a, const TokQuantArgs &q, hipStream_t s);
 hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
 hipError_t launch_requant(const RequantArgs &a, hipStream_t s);
-hipError_t launch_gemm1(const GemmArgs &a, int max_chunks, hipStream_t s);
-hipError_t launch_gemm2(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s);
+// ev_start / ev_stop (may be null) are bound to the kernel launch itself.
+hipError_t launch_gemm1(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_gemm2(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
+                        hipEvent_t ev_stop);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_pack(const int8_t *src, int8_t *dst, int64_t groups, int n, int k, hipStream_t s);
 // debug only: expand per-token rows into the grouped-row q_x / xs dump

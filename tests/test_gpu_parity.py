@@ -40,6 +40,7 @@ SMALL = {
     "t1": spec(T=1, H=1024, I=512, E_g=4, K=2, I_s=512, seed=107),
     "wide_hidden": spec(T=5, H=4096, I=256, E_g=4, K=2, I_s=256, seed=108),
     "wide_inter": spec(T=6, H=256, I=2048, E_g=4, K=2, I_s=768, seed=109),
+    "t16_full_tiles": spec(T=16, H=512, I=512, E_g=2, K=2, I_s=256, seed=110),
 }
 
 
@@ -184,6 +185,43 @@ def test_hip_graph_capture_and_replay():
         assert torch.equal(runner.output, eager[0]), i
         assert torch.equal(runner.share_output, eager[1]), i
         assert torch.equal(runner.expert_token_nums, eager[2]), i
+
+
+@pytest.mark.parametrize("I_s", [256, 512], ids=["split_gemm2", "one_gemm2"])
+def test_timing_events(I_s):
+    # stage events (markers between stages) and kernel events (bound to the
+    # GEMM launches) leave the results unchanged; each GEMM's own duration
+    # lies inside the markers around its stage
+    import ctypes
+    from moe_expert_ffn_route_amd import binding
+    c = synth.make_case(spec(T=24, H=1024, I=512, E_g=16, K=4, I_s=I_s, seed=117))
+    t = moe.pack_weights(moe.upload(c))
+    dims = moe.dims_of_case(c)
+    dims.weight_layout = moe.MOE_WEIGHT_PACKED
+    runner = moe.Runner(dims)
+    runner(t)
+    torch.cuda.synchronize()
+    plain = (runner.output.clone(), runner.share_output.clone())
+    stage = [torch.cuda.Event(enable_timing=True) for _ in range(len(binding.STAGES) + 1)]
+    kern = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in stage + kern:
+        e.record()
+    torch.cuda.synchronize()
+    sa = (ctypes.c_void_p * len(stage))(*[e.cuda_event for e in stage])
+    ka = (ctypes.c_void_p * 4)(*[e.cuda_event for e in kern])
+    d = binding.Debug(stage_events=ctypes.cast(sa, ctypes.c_void_p).value,
+                      kernel_events=ctypes.cast(ka, ctypes.c_void_p).value)
+    runner.output.fill_(0)
+    runner(t, dbg=d)
+    torch.cuda.synchronize()
+    assert torch.equal(runner.output, plain[0]) and torch.equal(runner.share_output, plain[1])
+    g1 = binding.STAGES.index("gemm1")
+    g2 = binding.STAGES.index("gemm2")
+    k1, k2 = kern[0].elapsed_time(kern[1]), kern[2].elapsed_time(kern[3])
+    s1, s2 = stage[g1].elapsed_time(stage[g1 + 1]), stage[g2].elapsed_time(stage[g2 + 1])
+    say(f"[parity] gemm1 kernel {k1 * 1e3:.1f} us (stage {s1 * 1e3:.1f}), gemm2 {k2 * 1e3:.1f} us (stage {s2 * 1e3:.1f})")
+    assert 0 < k1 <= s1 * 1.05 + 2e-3 and 0 < k2 <= s2 * 1.05 + 2e-3
+    assert stage[g1].elapsed_time(kern[0]) >= -1e-3 and kern[1].elapsed_time(stage[g1 + 1]) >= -1e-3
 
 
 def test_repeated_calls_shrinking_batch():
