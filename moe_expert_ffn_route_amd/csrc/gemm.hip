@@ -61,11 +61,24 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
     // Work item = (chunk, N tile), linear in blockIdx: the hardware deals
     // consecutive blocks round-robin to the 8 XCDs, so every XCD streams an
     // equal share of every expert's weights.
-    const int c = blockIdx.x / a.n_tiles;
-    const int nt = blockIdx.x % a.n_tiles;
-    const int4 ch = a.chunks[c];  // c < max_chunks: inside the chunk list even when unused
+    int c = blockIdx.x / a.n_tiles;
+    int nt = blockIdx.x % a.n_tiles;
+    int4 ch = a.chunks[c];  // c < max_chunks: inside the chunk list even when unused
     if (c >= a.meta[kMetaChunks]) return;
-    const int g = ch.x, row0 = ch.y, rows = ch.z;
+    const int nch = ch.z >> kChunkCountShift;
+    if (nch > 1 && (a.n_tiles & 7) == 0) {
+        // A group of several chunks owns blocks [c0 * n_tiles, (c0 + nch) *
+        // n_tiles). Within that range the nch chunks of one N tile are put 8
+        // blocks apart: on the same XCD and in flight together, so the tile's
+        // weights come from HBM once and are shared through that XCD's L2.
+        const int c0 = c - ch.w;
+        const int i = blockIdx.x - c0 * a.n_tiles;
+        const int q = i / (8 * nch), rem = i - q * 8 * nch;
+        c = c0 + rem / 8;
+        nt = q * 8 + rem % 8;
+        ch = a.chunks[c];
+    }
+    const int g = ch.x, row0 = ch.y, rows = ch.z & kChunkRowsMask;
     if (g < a.g_lo || g >= a.g_hi) return;
     const bool routed = g < a.E_loc;
     const int inter = routed ? a.I : a.I_s;

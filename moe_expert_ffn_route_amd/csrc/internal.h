@@ -19,6 +19,11 @@ constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kChunkRowsSmall = 16;
 constexpr int kChunkRowsLarge = 16 * MOE_LARGE_MT;
 constexpr int kTileN = 16;           // MFMA 16x16x64 output tile edge
+// A chunk entry's third word holds its row count (<= 64) in the low bits and
+// the number of chunks of its group above kChunkCountShift.
+constexpr int kChunkCountShift = 8;
+constexpr int kChunkRowsMask = (1 << kChunkCountShift) - 1;
+static_assert(kChunkRowsLarge <= kChunkRowsMask, "chunk rows must fit below the count bits");
 constexpr int kMaxTopK = 16;
 constexpr int kMaxTokens = 1 << 16;
 
@@ -46,7 +51,7 @@ struct RouteArgs {
     int32_t *row_of_pair;  // [T*K]
     int32_t *row_token;    // [rows_max]
     int32_t *row_group;    // [rows_max]
-    int4 *chunks;          // [max_chunks] (group, first row, rows, 0)
+    int4 *chunks;          // [max_chunks] (group, first row, rows | count << 8, index)
     int32_t *meta;         // [kMetaWords]
     int32_t *dbg_shared_token;  // [T] or null
 };

@@ -161,7 +161,8 @@ __device__ void route_block(const RouteArgs &a) {
         t_act += total;
     }
 
-    // 5. GEMM work items: each group's rows cut into chunks of chunk_rows
+    // 5. GEMM work items: each group's rows cut into chunks of chunk_rows;
+    //    an entry also carries the group's chunk count and its own index in it
     const int G = E + (a.has_shared ? 1 : 0);
     for (int g0 = 0; g0 < G; g0 += kRouteThreads) {
         const int g = g0 + tid;
@@ -175,7 +176,7 @@ __device__ void route_block(const RouteArgs &a) {
         const int c = s_nch + block_exclusive_scan(nch, s_tmp, &total);
         for (int i = 0; i < nch; ++i) {
             const int r = i * a.chunk_rows;
-            a.chunks[c + i] = make_int4(g, row0 + r, min(a.chunk_rows, M - r), 0);
+            a.chunks[c + i] = make_int4(g, row0 + r, min(a.chunk_rows, M - r) | (nch << kChunkCountShift), i);
         }
         __syncthreads();
         if (tid == 0) s_nch += total;
