@@ -225,13 +225,17 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g1.g_hi = E + 1;
         g1.packed = d->weight_layout == MOE_WEIGHT_PACKED;
         g1.mt = L.chunk_rows / kTileN;
-        g1.n_tiles = L.imax / kTileN;
+        const bool wide = g1.mt > 1;
+        const int nw = wide ? wide_waves() : 1;
+        g1.n_tiles = L.imax / kTileN / nw;
         g1.chunks = ra.chunks;
         g1.meta = meta;
         g1.row_token = ra.row_token;
         g1.h = reinterpret_cast<float *>(ws + L.h);
         g1.dbg_acc = D.acc1;
-        if (launch_gemm1(g1, L.max_chunks, s, kev(0), kev(1)) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
+        const hipError_t e1 = wide ? launch_gemm1_wide(g1, L.max_chunks, s, kev(0), kev(1))
+                                   : launch_gemm1(g1, L.max_chunks, s, kev(0), kev(1));
+        if (e1 != hipSuccess || !mark(3)) return MOE_ERR_HIP;
 
         RequantArgs rq;
         rq.h = g1.h;
@@ -243,6 +247,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         rq.imax = L.imax;
         rq.has_shared = shared;
         rq.rows_max = L.rows_max;
+        rq.load_early = d->ep_rank_size == 1;  // then nearly every grouped row is in use
         rq.eps = d->amax_eps;
         rq.q = reinterpret_cast<int8_t *>(ws + L.q_h);
         rq.scale = reinterpret_cast<float *>(ws + L.hs);
@@ -257,22 +262,25 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g2.Ws = gmm2_weight_scale;
         g2.W_sh = share_gmm2_weight;
         g2.Ws_sh = share_gmm2_weight_scale;
-        g2.n_tiles = H / (2 * kTileN);
+        g2.n_tiles = H / (2 * kTileN) / nw;
         g2.h = nullptr;
         g2.z = reinterpret_cast<uint16_t *>(ws + L.z);
         g2.share_out = static_cast<uint16_t *>(share_output);
         g2.dbg_acc = D.acc2;
         g2.dbg_z = D.z;
         // the contraction length of GEMM2 is the group's intermediate size
+        auto gemm2 = [&](int k_dim, hipEvent_t e0, hipEvent_t e1) {
+            return wide ? launch_gemm2_wide(g2, L.max_chunks, k_dim, s, e0, e1)
+                        : launch_gemm2(g2, L.max_chunks, k_dim, s, e0, e1);
+        };
         if (!shared || d->share_inter == d->inter) {
-            if (launch_gemm2(g2, L.max_chunks, d->inter, s, kev(2), kev(3)) != hipSuccess) return MOE_ERR_HIP;
+            if (gemm2(d->inter, kev(2), kev(3)) != hipSuccess) return MOE_ERR_HIP;
         } else {
             g2.g_hi = E;
-            if (launch_gemm2(g2, L.max_chunks, d->inter, s, kev(2), nullptr) != hipSuccess) return MOE_ERR_HIP;
+            if (gemm2(d->inter, kev(2), nullptr) != hipSuccess) return MOE_ERR_HIP;
             g2.g_lo = E;
             g2.g_hi = E + 1;
-            if (launch_gemm2(g2, L.max_chunks, d->share_inter, s, nullptr, kev(3)) != hipSuccess)
-                return MOE_ERR_HIP;
+            if (gemm2(d->share_inter, nullptr, kev(3)) != hipSuccess) return MOE_ERR_HIP;
         }
         if (!mark(5)) return MOE_ERR_HIP;
 

@@ -12,10 +12,11 @@
 //     expert (sec. 6.2: the shared expert's rows go to memory, routed rows on
 //     to combine).
 //
-// Decode is bound by the weight stream (each touched expert's bytes are read
-// once; per-expert rows M are 1..64), so the kernel is shaped around HBM, not
-// around MFMA throughput:
-//   - a work item is (chunk of <= 16*MT rows of one expert, 16-channel N tile
+// Decode (at most 16 tokens, so at most 16 rows per expert; larger batches
+// go to gemm_wide.hip) is bound by the weight stream: each touched expert's
+// bytes are read once, so the kernel is shaped around HBM, not around MFMA
+// throughput:
+//   - a work item is (chunk of <= 16 rows of one expert, 16-channel N tile
 //     pair); its 2 x 16 weight rows are split over the waves along K; each
 //     wave streams its K slice in batches of KSTEPS 64-byte steps, software
 //     pipelined (the next batch's loads are issued before this batch's
@@ -23,8 +24,9 @@
 //     counters stay exact;
 //   - with packed weights (moe_w8a8_pack_weights) every wave load is one
 //     contiguous 1 KB block, read non-temporally;
-//   - each weight batch is used for all of the chunk's 16-row MFMA tiles, so
-//     a chunk reads its weight slice exactly once;
+//   - the kernel takes MT row tiles per chunk as a parameter (each weight
+//     batch feeds all of them, so a chunk reads its weights once); the
+//     library instantiates MT = 1;
 //   - the partial int32 tiles of the waves are summed in LDS (exact);
 //   - blockIdx maps linearly to (chunk, N tile), so the round-robin placement
 //     of blocks on the 8 XCDs gives each XCD an equal share of every expert;
@@ -300,13 +302,6 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
 #ifndef MOE_GEMM2_KSTEPS
 #define MOE_GEMM2_KSTEPS 4
 #endif
-#ifndef MOE_GEMM1_KSTEPS_LARGE
-#define MOE_GEMM1_KSTEPS_LARGE 4
-#endif
-#ifndef MOE_GEMM2_KSTEPS_LARGE
-#define MOE_GEMM2_KSTEPS_LARGE 4
-#endif
-
 template <int KIND, int WAVES, int KSTEPS, bool PACKED, int MT, int NPASS>
 void launch_one(const GemmArgs &a, dim3 grid, int k_dim, int n_pass, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const dim3 blk(WAVES * kWave);
@@ -331,39 +326,31 @@ hipError_t launch_np(const GemmArgs &a, dim3 grid, int k_dim, int n_pass, hipStr
 }
 
 // k_dim is a multiple of 256 (64-byte MFMA K step x 4 waves). A wave walks
-// k_dim / (64 * waves) steps in batches of KS1 (one row tile per chunk) or
-// KS4 (MOE_LARGE_MT row tiles: fewer steps per batch keep the A tiles in registers),
-// or of 1 step when that does not divide the steps.
-template <int KIND, int WAVES, int KS1, int KS4>
+// k_dim / (64 * waves) steps in batches of KS steps, or of 1 step when KS does
+// not divide them. Work items here are single 16-row tiles (decode batches);
+// chunks of several tiles go to gemm_wide.hip.
+template <int KIND, int WAVES, int KS>
 hipError_t launch_w(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    if (a.mt != 1) return hipErrorInvalidValue;
     const long blocks = static_cast<long>(max_chunks) * a.n_tiles;
     if (blocks <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(blocks));
     const int steps = k_dim / (64 * WAVES);
-    if (a.mt == 1) {
-        if (steps % KS1 == 0)
-            return a.packed ? launch_np<KIND, WAVES, KS1, true, 1>(a, grid, k_dim, steps / KS1, s, e0, e1)
-                            : launch_np<KIND, WAVES, KS1, false, 1>(a, grid, k_dim, steps / KS1, s, e0, e1);
-        return a.packed ? launch_np<KIND, WAVES, 1, true, 1>(a, grid, k_dim, steps, s, e0, e1)
-                        : launch_np<KIND, WAVES, 1, false, 1>(a, grid, k_dim, steps, s, e0, e1);
-    }
-    constexpr int MTL = MOE_LARGE_MT;
-    if (steps % KS4 == 0)
-        return a.packed ? launch_np<KIND, WAVES, KS4, true, MTL>(a, grid, k_dim, steps / KS4, s, e0, e1)
-                        : launch_np<KIND, WAVES, KS4, false, MTL>(a, grid, k_dim, steps / KS4, s, e0, e1);
-    return a.packed ? launch_np<KIND, WAVES, 1, true, MTL>(a, grid, k_dim, steps, s, e0, e1)
-                    : launch_np<KIND, WAVES, 1, false, MTL>(a, grid, k_dim, steps, s, e0, e1);
+    if (steps % KS == 0)
+        return a.packed ? launch_np<KIND, WAVES, KS, true, 1>(a, grid, k_dim, steps / KS, s, e0, e1)
+                        : launch_np<KIND, WAVES, KS, false, 1>(a, grid, k_dim, steps / KS, s, e0, e1);
+    return a.packed ? launch_np<KIND, WAVES, 1, true, 1>(a, grid, k_dim, steps, s, e0, e1)
+                    : launch_np<KIND, WAVES, 1, false, 1>(a, grid, k_dim, steps, s, e0, e1);
 }
 
 template <int KIND>
 hipError_t launch_kind(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     constexpr int W = KIND == 1 ? MOE_GEMM1_WAVES : MOE_GEMM2_WAVES;
-    constexpr int KS1 = KIND == 1 ? MOE_GEMM1_KSTEPS : MOE_GEMM2_KSTEPS;
-    constexpr int KS4 = KIND == 1 ? MOE_GEMM1_KSTEPS_LARGE : MOE_GEMM2_KSTEPS_LARGE;
+    constexpr int KS = KIND == 1 ? MOE_GEMM1_KSTEPS : MOE_GEMM2_KSTEPS;
     if constexpr (W == 8) {
-        if (k_dim % 512 == 0) return launch_w<KIND, 8, KS1, KS4>(a, max_chunks, k_dim, s, e0, e1);
+        if (k_dim % 512 == 0) return launch_w<KIND, 8, KS>(a, max_chunks, k_dim, s, e0, e1);
     }
-    return launch_w<KIND, 4, KS1, KS4>(a, max_chunks, k_dim, s, e0, e1);
+    return launch_w<KIND, 4, KS>(a, max_chunks, k_dim, s, e0, e1);
 }
 
 }  // namespace

@@ -1,0 +1,364 @@
+// Grouped INT8 GEMMs for work items of several 16-row MFMA tiles (more than
+// 16 tokens in the batch), with the same fused epilogues as gemm.hip:
+//   GEMM1 ("FusedDeepMoE Kernel 深度分析报告" sec. 3.3 / 6.1): gate and up
+//     accumulators of one row and channel meet in one lane, which applies
+//     y = (float(acc) * w1s[n]) * xs[r] to both and writes
+//     h = (y_g / (1 + exp(-y_g))) * y_u as fp32;
+//   GEMM2 (sec. 3.4 / 6.2): z = bf16((float(acc) * w2s[n]) * hs[r]), to the
+//     routed row buffer or, for the shared expert, straight to share_output.
+//
+// Here the rows of a chunk (up to 16 * MT) are reused across many weight
+// rows, so the chunk's activations are shared by the waves of a workgroup
+// instead of being fetched by each wave:
+//   - the workgroup covers NW pairs of 16-row weight tiles; wave w owns pair
+//     w and walks the whole K range, streaming its weights straight from
+//     memory into registers (a ring of SLAB 64-byte K steps: the load of
+//     step s + SLAB is issued right after the MFMAs of step s consumed its
+//     slot), so every weight byte is read once and only by one wave;
+//   - the activation rows go through LDS in slabs of SLAB K steps, double
+//     buffered: the waves load slab s + 1 into registers while they multiply
+//     slab s, write it to LDS at the end of the slab and meet at one
+//     workgroup barrier per slab;
+//   - with no K split there is no cross-wave reduction: each lane holds the
+//     finished int32 sums of its (row, channel) outputs.
+// LDS layout: one 1 KB unit per (K step, row tile), in MFMA operand order
+// (lane l's 16 bytes are row l % 16, byte 16 * (l / 16) of the step), so both
+// the writes and the MFMA operand reads are whole, conflict-free 1 KB rows.
+#include "internal.h"
+
+#include <hip/hip_ext.h>
+
+namespace moe {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4i ld16(const int8_t *p) { return *reinterpret_cast<const v4i *>(p); }
+__device__ __forceinline__ v4i ld16_stream(const int8_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+}
+
+// What a wave knows about its work item once the block has decoded it.
+struct WideItem {
+    const int8_t *wb0, *wb1;  // wave-uniform bases of the two weight tiles
+    const float *Ws;
+    const int8_t *Abase;
+    const float *Ascale;
+    uint32_t wlane;           // lane offset of a weight load
+    int wstep;                // bytes between consecutive K steps of a tile
+    int rowA, rowB;           // first weight row (= output channel) of each tile
+    int row0, rows, S, inter;
+    bool routed, by_tok, need_tok;
+};
+
+// The K loop and epilogue for MTA active row tiles (the chunk's rows, rounded
+// up to whole tiles). Runs the same sequence in every wave of the block.
+template <int KIND, int NW, int MTA, int SLAB, int RING, bool PACKED>
+__device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it, v4i (*s_a)[kWave]) {
+    constexpr int kUnits = SLAB * MTA;             // 1 KB activation units per slab
+    constexpr int kUpw = (kUnits + NW - 1) / NW;   // units each wave loads per slab
+    constexpr int kSlabsPerRing = RING / SLAB;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int rows = it.rows, row0 = it.row0;
+
+    // (1) independent small loads: the token of each activation row this
+    //     wave stages and of each output row it finishes (4 * (lane / 16) + i
+    //     of every row tile), and the channel scales
+    const int8_t *asrc[kUpw];
+#pragma unroll
+    for (int j = 0; j < kUpw; ++j) {
+        const int u = wave + j * NW;
+        const int mt = u % MTA, st = u / MTA;
+        const int lr = min(mt * kTileN + r16, rows - 1);  // rows past the chunk repeat its last row
+        const int ar = it.by_tok ? a.row_token[row0 + lr] : row0 + lr;
+        asrc[j] = it.Abase + static_cast<size_t>(ar) * a.a_stride + st * 64 + kg * 16;
+    }
+    // a token indexes the row scale of per-token rows and the share_output
+    // row of the shared expert's GEMM2
+    int otok[MTA][4];
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int lr = min(mt * kTileN + 4 * kg + i, rows - 1);
+            otok[mt][i] = it.need_tok ? a.row_token[row0 + lr] : 0;
+        }
+    const float ws0 = it.Ws[it.rowA + r16];
+    const float ws1 = it.Ws[it.rowB + r16];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (2) the first activation slab, then the first ring of weight steps
+    auto ldw = [&](const int8_t *base, int step) {
+        const int8_t *p = base + static_cast<size_t>(step) * it.wstep + it.wlane;
+        return PACKED ? ld16_stream(p) : ld16(p);
+    };
+    v4i stage[kUpw];
+    auto load_slab = [&](int s) {
+#pragma unroll
+        for (int j = 0; j < kUpw; ++j)
+            if (kUnits % NW == 0 || wave + j * NW < kUnits) stage[j] = ld16(asrc[j] + s * SLAB * 64);
+    };
+    auto store_slab = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < kUpw; ++j)
+            if (kUnits % NW == 0 || wave + j * NW < kUnits) s_a[buf * kUnits + wave + j * NW][lane] = stage[j];
+    };
+    load_slab(0);
+    __builtin_amdgcn_sched_barrier(0);
+    v4i w0[RING], w1[RING];
+#pragma unroll
+    for (int i = 0; i < RING; ++i) {
+        w0[i] = ldw(it.wb0, i);
+        w1[i] = ldw(it.wb1, i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (3) loads that depend on (1): the row scales of this lane's output rows
+    float rsc[MTA][4];
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            rsc[mt][i] = it.Ascale[it.by_tok ? otok[mt][i] : row0 + min(mt * kTileN + 4 * kg + i, rows - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+
+    store_slab(0);
+    __syncthreads();
+
+    v4i acc0[MTA], acc1[MTA];
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt) {
+        acc0[mt] = v4i{0, 0, 0, 0};
+        acc1[mt] = v4i{0, 0, 0, 0};
+    }
+    // One slab of SLAB K steps at ring position h: the next slab's activation
+    // loads, then for each step the MFMAs of all row tiles followed by the
+    // weight load that refills the step's ring slot (RING steps ahead); at the
+    // end the next slab goes to the other LDS buffer. Scheduling barriers keep
+    // each refill right after its step's MFMAs (left alone, the compiler sinks
+    // the refills to the end of the slab).
+    auto slab = [&](int s, int h, bool more_a, bool more_w) {
+        const int cur = s & 1;
+        if (more_a) load_slab(s + 1);
+        const int wnext = s * SLAB + RING;
+#pragma unroll
+        for (int i = 0; i < SLAB; ++i) {
+            const int slot = h * SLAB + i;
+            v4i x[MTA];
+#pragma unroll
+            for (int mt = 0; mt < MTA; ++mt) x[mt] = s_a[cur * kUnits + i * MTA + mt][lane];
+#pragma unroll
+            for (int mt = 0; mt < MTA; ++mt) {
+                acc0[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x[mt], w0[slot], acc0[mt], 0, 0, 0);
+                acc1[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x[mt], w1[slot], acc1[mt], 0, 0, 0);
+            }
+            if (more_w) {
+                w0[slot] = ldw(it.wb0, wnext + i);
+                w1[slot] = ldw(it.wb1, wnext + i);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (more_a) store_slab(cur ^ 1);
+        __syncthreads();
+    };
+    // Every row tile is multiplied, also past the chunk's last row: those A
+    // rows repeat the last row, and since an MFMA output row depends only on
+    // its own A row, they only produce outputs that are never stored.
+    const int ncyc = it.S / RING;
+    for (int cyc = 0; cyc + 1 < ncyc; ++cyc) {
+#pragma unroll
+        for (int h = 0; h < kSlabsPerRing; ++h) slab(cyc * kSlabsPerRing + h, h, true, true);
+    }
+#pragma unroll
+    for (int h = 0; h < kSlabsPerRing; ++h)
+        slab((ncyc - 1) * kSlabsPerRing + h, h, h + 1 < kSlabsPerRing, false);
+
+    // Epilogue: lane l holds rows 4 * (l / 16) + i of every row tile, at
+    // channel l % 16 of both weight tiles.
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt) {
+        if (KIND == 1) {
+            const int col = it.rowA + r16;  // gate channel index = h column
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int lr = mt * kTileN + 4 * kg + i;
+                if (lr < rows) {
+                    const int r = row0 + lr;
+                    float yg = static_cast<float>(acc0[mt][i]) * ws0;
+                    yg = yg * rsc[mt][i];
+                    float yu = static_cast<float>(acc1[mt][i]) * ws1;
+                    yu = yu * rsc[mt][i];
+                    const float ex = expf(-yg);
+                    const float den = 1.0f + ex;
+                    const float sg = yg / den;
+                    a.h[static_cast<size_t>(r) * a.imax + col] = sg * yu;
+                    if (a.dbg_acc) {
+                        a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + col] = acc0[mt][i];
+                        a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + it.inter + col] = acc1[mt][i];
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int lr = mt * kTileN + 4 * kg + i;
+                float y0 = static_cast<float>(acc0[mt][i]) * ws0;
+                y0 = y0 * rsc[mt][i];
+                float y1 = static_cast<float>(acc1[mt][i]) * ws1;
+                y1 = y1 * rsc[mt][i];
+                const uint32_t b0 = f32_to_bf16(y0), b1 = f32_to_bf16(y1);
+                // pair up neighbouring channels for 4-byte stores: even lanes
+                // take channels (c, c + 1) of tile A, odd lanes (c - 1, c) of
+                // tile B, so 16 lanes store 64 contiguous bytes of the row
+                const uint32_t p0 = __shfl_xor(static_cast<int>(b0), 1, kWave);
+                const uint32_t p1 = __shfl_xor(static_cast<int>(b1), 1, kWave);
+                const bool even = (r16 & 1) == 0;
+                const uint32_t word = even ? (b0 | (p0 << 16)) : (p1 | (b1 << 16));
+                const int wcol = even ? it.rowA + r16 : it.rowB + r16 - 1;
+                if (lr < rows) {
+                    const int r = row0 + lr;
+                    uint16_t *dst = it.routed ? a.z + static_cast<size_t>(r) * a.H
+                                              : a.share_out + static_cast<size_t>(otok[mt][i]) * a.H;
+                    *reinterpret_cast<uint32_t *>(dst + wcol) = word;
+                    if (a.dbg_acc) {
+                        a.dbg_acc[static_cast<size_t>(r) * a.H + it.rowA + r16] = acc0[mt][i];
+                        a.dbg_acc[static_cast<size_t>(r) * a.H + it.rowB + r16] = acc1[mt][i];
+                    }
+                    if (a.dbg_z) *reinterpret_cast<uint32_t *>(a.dbg_z + static_cast<size_t>(r) * a.H + wcol) = word;
+                }
+            }
+        }
+    }
+}
+
+// MT = row tiles per chunk (the chunk size); a block runs the body for the
+// tiles its chunk actually fills.
+template <int KIND, int NW, int MT, int SLAB, int RING, bool PACKED>
+__global__ __launch_bounds__(NW * kWave) void gemm_wide_kernel(GemmArgs a, int k_dim) {
+    __shared__ v4i s_a[2 * SLAB * MT][kWave];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    int c = blockIdx.x / a.n_tiles;
+    int nt = blockIdx.x % a.n_tiles;
+    int4 ch = a.chunks[c];  // c < max_chunks: inside the chunk list even when unused
+    if (c >= a.meta[kMetaChunks]) return;
+    const int nch = ch.z >> kChunkCountShift;
+    if (nch > 1 && (a.n_tiles & 7) == 0) {
+        // the chunks of one N tile run 8 blocks apart, on one XCD (gemm.hip)
+        const int c0 = c - ch.w;
+        const int i = blockIdx.x - c0 * a.n_tiles;
+        const int q = i / (8 * nch), rem = i - q * 8 * nch;
+        c = c0 + rem / 8;
+        nt = q * 8 + rem % 8;
+        ch = a.chunks[c];
+    }
+    WideItem it;
+    const int g = ch.x;
+    it.row0 = ch.y;
+    it.rows = ch.z & kChunkRowsMask;
+    if (g < a.g_lo || g >= a.g_hi) return;
+    it.routed = g < a.E_loc;
+    it.inter = it.routed ? a.I : a.I_s;
+    // inter and H are multiples of 256, so a block either has work for all of
+    // its waves or for none
+    if (KIND == 1 && nt * NW * kTileN >= it.inter) return;
+
+    const int8_t *W;
+    const int tp = nt * NW + wave;  // this wave's pair of 16-row weight tiles
+    if (KIND == 1) {
+        W = it.routed ? a.W + static_cast<size_t>(g) * 2 * it.inter * a.H : a.W_sh;
+        it.Ws = it.routed ? a.Ws + static_cast<size_t>(g) * 2 * it.inter : a.Ws_sh;
+        it.rowA = tp * kTileN;             // gate channels
+        it.rowB = it.inter + tp * kTileN;  // matching up channels
+    } else {
+        W = it.routed ? a.W + static_cast<size_t>(g) * a.H * it.inter : a.W_sh;
+        it.Ws = it.routed ? a.Ws + static_cast<size_t>(g) * a.H : a.Ws_sh;
+        it.rowA = tp * 2 * kTileN;
+        it.rowB = it.rowA + kTileN;
+    }
+    it.S = k_dim / 64;  // 64-byte K steps; a multiple of RING (host-checked)
+    // weight addresses: a wave-uniform base plus a 32-bit lane offset
+    if (PACKED) {
+        it.wb0 = W + static_cast<size_t>(it.rowA / kTileN) * it.S * 1024;
+        it.wb1 = W + static_cast<size_t>(it.rowB / kTileN) * it.S * 1024;
+        it.wlane = lane * 16;
+        it.wstep = 1024;
+    } else {
+        it.wb0 = W + static_cast<size_t>(it.rowA) * k_dim;
+        it.wb1 = W + static_cast<size_t>(it.rowB) * k_dim;
+        it.wlane = (lane & 15) * k_dim + (lane >> 4) * 16;
+        it.wstep = 64;
+    }
+    it.by_tok = KIND == 1 && (it.routed ? a.routed_by_token : a.shared_by_token);
+    it.need_tok = it.by_tok || (KIND == 2 && !it.routed);
+    it.Abase = it.by_tok ? a.A_tok : a.A;
+    it.Ascale = it.by_tok ? a.a_scale_tok : a.a_scale;
+
+    const int tiles = (it.rows + kTileN - 1) / kTileN;
+    if constexpr (MT > 2) {
+        if (tiles > 2) return wide_body<KIND, NW, MT, SLAB, RING, PACKED>(a, it, s_a);
+    }
+    if constexpr (MT > 1) {
+        if (tiles > 1) return wide_body<KIND, NW, 2, SLAB, RING, PACKED>(a, it, s_a);
+    }
+    wide_body<KIND, NW, 1, SLAB, RING, PACKED>(a, it, s_a);
+}
+
+#ifndef MOE_WIDE_WAVES
+#define MOE_WIDE_WAVES 2
+#endif
+#ifndef MOE_WIDE_SLAB
+#define MOE_WIDE_SLAB 4
+#endif
+#ifndef MOE_WIDE_RING
+#define MOE_WIDE_RING 8
+#endif
+
+template <int KIND, int NW, int MT, int SLAB, int RING>
+hipError_t launch_wide_t(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    const long blocks = static_cast<long>(max_chunks) * a.n_tiles;
+    if (blocks <= 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(blocks)), blk(NW * kWave);
+    if (a.packed) {
+        if (e0 || e1)
+            hipExtLaunchKernelGGL((gemm_wide_kernel<KIND, NW, MT, SLAB, RING, true>), grid, blk, 0, s, e0, e1, 0, a,
+                                  k_dim);
+        else
+            hipLaunchKernelGGL((gemm_wide_kernel<KIND, NW, MT, SLAB, RING, true>), grid, blk, 0, s, a, k_dim);
+    } else {
+        if (e0 || e1)
+            hipExtLaunchKernelGGL((gemm_wide_kernel<KIND, NW, MT, SLAB, RING, false>), grid, blk, 0, s, e0, e1, 0, a,
+                                  k_dim);
+        else
+            hipLaunchKernelGGL((gemm_wide_kernel<KIND, NW, MT, SLAB, RING, false>), grid, blk, 0, s, a, k_dim);
+    }
+    return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_wide(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    constexpr int NW = MOE_WIDE_WAVES, MT = kWideTiles, SL = MOE_WIDE_SLAB, RG = MOE_WIDE_RING;
+    static_assert(RG % SL == 0, "the weight ring holds whole activation slabs");
+    // k_dim is a multiple of 256, so rings of 4 steps always divide it
+    if ((k_dim / 64) % RG == 0) return launch_wide_t<KIND, NW, MT, SL, RG>(a, max_chunks, k_dim, s, e0, e1);
+    return launch_wide_t<KIND, NW, MT, 4, 4>(a, max_chunks, k_dim, s, e0, e1);
+}
+
+}  // namespace
+
+hipError_t launch_gemm1_wide(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start,
+                             hipEvent_t ev_stop) {
+    return launch_wide<1>(a, max_chunks, a.H, s, ev_start, ev_stop);
+}
+
+hipError_t launch_gemm2_wide(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
+                             hipEvent_t ev_stop) {
+    return launch_wide<2>(a, max_chunks, k_dim, s, ev_start, ev_stop);
+}
+
+int wide_waves() { return MOE_WIDE_WAVES; }
+
+}  // namespace moe

@@ -11,13 +11,15 @@ constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kMaxLocalExperts = 512;
 constexpr int kRouteThreads = 1024;  // the routing kernel runs as one workgroup
 constexpr int kRouteWaves = kRouteThreads / kWave;
-// Grouped rows per GEMM work item: one 16-row MFMA tile when T <= 16 (decode),
-// MOE_LARGE_MT tiles otherwise.
-#ifndef MOE_LARGE_MT
-#define MOE_LARGE_MT 2
+// Grouped rows per GEMM work item: one 16-row MFMA tile when T <= 16
+// (decode; gemm.hip), MOE_WIDE_MT tiles otherwise (gemm_wide.hip, which
+// shares each chunk's activations across the waves of a workgroup).
+#ifndef MOE_WIDE_MT
+#define MOE_WIDE_MT 2
 #endif
+constexpr int kWideTiles = MOE_WIDE_MT;
 constexpr int kChunkRowsSmall = 16;
-constexpr int kChunkRowsLarge = 16 * MOE_LARGE_MT;
+constexpr int kChunkRowsLarge = 16 * MOE_WIDE_MT;
 constexpr int kTileN = 16;           // MFMA 16x16x64 output tile edge
 // A chunk entry's third word holds its row count (<= 64) in the low bits and
 // the number of chunks of its group above kChunkCountShift.
@@ -85,6 +87,7 @@ struct RequantArgs {
     const int32_t *row_group;
     const int32_t *meta;
     int E_loc, I, I_s, imax, has_shared, rows_max;
+    int load_early;  // read each h row before the row count is known (all pairs local)
     float eps;
     int8_t *q;     // [rows_max, imax]
     float *scale;  // [rows_max]
@@ -107,7 +110,7 @@ struct GemmArgs {
     int I, I_s, H, E_loc, imax;
     int g_lo, g_hi;   // only chunks of groups in [g_lo, g_hi)
     int packed;       // weights in moe_w8a8_pack_weights order
-    int mt;           // 16-row MFMA tiles per chunk: 1 or MOE_LARGE_MT
+    int mt;           // 16-row MFMA tiles per chunk
     int n_tiles;      // work items per chunk along N
     const int4 *chunks;
     const int32_t *meta;
@@ -137,6 +140,13 @@ hipError_t launch_requant(const RequantArgs &a, hipStream_t s);
 hipError_t launch_gemm1(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_gemm2(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
                         hipEvent_t ev_stop);
+// Work items of several row tiles (gemm_wide.hip); n_tiles counts groups of
+// wide_waves() pairs of 16-row weight tiles.
+hipError_t launch_gemm1_wide(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start,
+                             hipEvent_t ev_stop);
+hipError_t launch_gemm2_wide(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
+                             hipEvent_t ev_stop);
+int wide_waves();
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_pack(const int8_t *src, int8_t *dst, int64_t groups, int n, int k, hipStream_t s);
 // debug only: expand per-token rows into the grouped-row q_x / xs dump

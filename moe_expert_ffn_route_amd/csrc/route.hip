@@ -45,6 +45,24 @@ __device__ int block_exclusive_scan(int v, int *s_tmp, int *total) {
     return before + inc - v;
 }
 
+// Pairs held in registers by the routing block (rounds of kRouteThreads);
+// enough for every pair at T = 512, top-8.
+constexpr int kRouteRegRounds = 4;
+constexpr int kPairDropped = -1;  // inactive token or expert of another rank
+constexpr int kPairBad = -2;      // expert id outside [0, E_g)
+
+// Local expert of a pair with global id `g`, or kPairDropped / kPairBad.
+__device__ __forceinline__ int classify_id(const RouteArgs &a, int g, bool active) {
+    if (!active) return kPairDropped;
+    if (g < 0 || g >= a.E_g) return kPairBad;
+    const int e = g - a.base;
+    return e >= 0 && e < a.E_loc ? e : kPairDropped;
+}
+
+__device__ __forceinline__ int classify_pair(const RouteArgs &a, int p) {
+    return classify_id(a, a.ids[p], !a.mask || a.mask[p / a.K]);
+}
+
 __device__ void route_block(const RouteArgs &a) {
     __shared__ int s_count[kMaxLocalExperts + 1];
     __shared__ int s_off[kMaxLocalExperts + 2];
@@ -58,6 +76,25 @@ __device__ void route_block(const RouteArgs &a) {
     const int lane = tid & (kWave - 1), wave = tid / kWave;
     const int E = a.E_loc, TK = a.T * a.K;
 
+    // 0. Every global input the routing needs, fetched at once: the first
+    //    kRouteRegRounds rounds of pairs are classified into registers, and the
+    //    first round of tokens' mask bits is read alongside (rounds beyond
+    //    those are read again where they are used).
+    int e_reg[kRouteRegRounds];
+    {
+        int id_v[kRouteRegRounds];
+        bool act_v[kRouteRegRounds];
+#pragma unroll
+        for (int j = 0; j < kRouteRegRounds; ++j) {
+            const int p = j * kRouteThreads + tid;
+            id_v[j] = p < TK ? a.ids[p] : 0;
+            act_v[j] = p < TK && (!a.mask || a.mask[p / a.K]);
+        }
+#pragma unroll
+        for (int j = 0; j < kRouteRegRounds; ++j) e_reg[j] = classify_id(a, id_v[j], act_v[j]);
+    }
+    const bool tok_act0 = tid < a.T && (!a.mask || a.mask[tid]);
+
     for (int i = tid; i < E; i += kRouteThreads) {
         s_count[i] = 0;
         s_run[i] = 0;
@@ -70,17 +107,13 @@ __device__ void route_block(const RouteArgs &a) {
     __syncthreads();
 
     // 1. histogram of kept pairs per local expert
-    for (int p = tid; p < TK; p += kRouteThreads) {
-        const int t = p / a.K;
-        if (a.mask && !a.mask[t]) continue;
-        const int g = a.ids[p];
-        if (g < 0 || g >= a.E_g) {
-            atomicAdd(&s_bad, 1);
-            continue;
-        }
-        const int e = g - a.base;
-        if (e >= 0 && e < E) atomicAdd(&s_count[e], 1);
-    }
+    auto count = [&](int e) {
+        if (e == kPairBad) atomicAdd(&s_bad, 1);
+        else if (e >= 0) atomicAdd(&s_count[e], 1);
+    };
+#pragma unroll
+    for (int j = 0; j < kRouteRegRounds; ++j) count(e_reg[j]);
+    for (int p = kRouteRegRounds * kRouteThreads + tid; p < TK; p += kRouteThreads) count(classify_pair(a, p));
     __syncthreads();
 
     // 2. exclusive prefix sum of the counts
@@ -95,19 +128,8 @@ __device__ void route_block(const RouteArgs &a) {
     const int P = s_off[E];
 
     // 3. stable placement, one round of 1024 pairs at a time
-    for (int base = 0; base < TK; base += kRouteThreads) {
+    auto place = [&](int base, int e) {
         const int p = base + tid;
-        int e = -1, t = 0;
-        if (p < TK) {
-            t = p / a.K;
-            if (!a.mask || a.mask[t]) {
-                const int g = a.ids[p];
-                if (g >= 0 && g < a.E_g) {
-                    e = g - a.base;
-                    if (e >= E) e = -1;
-                }
-            }
-        }
         const bool valid = e >= 0;
         unsigned long long peers = __ballot(valid);
 #pragma unroll
@@ -129,7 +151,7 @@ __device__ void route_block(const RouteArgs &a) {
                 const int pos = s_off[e] + s_run[e] + pre + rank;
                 a.sorted_pair[pos] = p;
                 a.row_of_pair[p] = pos;
-                a.row_token[pos] = t;
+                a.row_token[pos] = p / a.K;
                 a.row_group[pos] = e;
             } else {
                 a.row_of_pair[p] = -1;
@@ -141,13 +163,18 @@ __device__ void route_block(const RouteArgs &a) {
             s_tbl[wave][e] = 0;
         }
         __syncthreads();
-    }
+    };
+#pragma unroll
+    for (int j = 0; j < kRouteRegRounds; ++j)
+        if (j * kRouteThreads < TK) place(j * kRouteThreads, e_reg[j]);  // uniform
+    for (int base = kRouteRegRounds * kRouteThreads; base < TK; base += kRouteThreads)
+        place(base, base + tid < TK ? classify_pair(a, base + tid) : kPairDropped);
 
     // 4. shared-expert rows: active tokens in token order, after the routed rows
     int t_act = 0;
     for (int base = 0; base < a.T; base += kRouteThreads) {
         const int t = base + tid;
-        const bool act = t < a.T && (!a.mask || a.mask[t]);
+        const bool act = base == 0 ? tok_act0 : t < a.T && (!a.mask || a.mask[t]);
         int total;
         const int ex = block_exclusive_scan(act ? 1 : 0, s_tmp, &total);
         if (act) {
