@@ -41,6 +41,10 @@ SMALL = {
     "wide_hidden": spec(T=5, H=4096, I=256, E_g=4, K=2, I_s=256, seed=108),
     "wide_inter": spec(T=6, H=256, I=2048, E_g=4, K=2, I_s=768, seed=109),
     "t16_full_tiles": spec(T=16, H=512, I=512, E_g=2, K=2, I_s=256, seed=110),
+    # more than 16 tokens with K step counts (H / 64 = 12, I / 64 = 4) that the
+    # larger-batch kernel's 8-step weight ring does not divide
+    "t40_short_ring": spec(T=40, H=768, I=256, E_g=4, K=2, I_s=768, seed=111),
+    "t17_one_row_past_decode": spec(T=17, H=512, I=256, E_g=2, K=1, I_s=256, seed=112),
 }
 
 
@@ -96,6 +100,8 @@ LIMITS = {
     "hidden_16384": (spec(T=3, H=16384, I=256, E_g=4, K=2, I_s=256, seed=132), None),
     "inter_16384": (spec(T=3, H=256, I=16384, E_g=4, K=2, I_s=512, seed=133), None),
     "pairs_32768": (spec(T=2048, H=256, I=256, E_g=64, K=16, active=1900, seed=134), [0, 5, 777, 2047]),
+    "t24_hidden_16384": (spec(T=24, H=16384, I=256, E_g=4, K=2, I_s=256, seed=135), None),
+    "t24_inter_16384": (spec(T=24, H=256, I=16384, E_g=4, K=2, I_s=512, seed=136), None),
 }
 
 
