@@ -44,7 +44,10 @@ Layout make_layout(const moe_w8a8_dims_t *d) {
     L.imax = d->inter > d->share_inter ? d->inter : d->share_inter;
     L.rows_max = static_cast<int>(TK + T);
     const size_t nonempty = E < TK ? E : TK;
-    L.chunk_rows = T <= kChunkRowsSmall ? kChunkRowsSmall : kChunkRowsLarge;
+    // rows per GEMM work item: 16 for decode batches; 128 (tall items) when
+    // the routed experts average kTallMinRows rows or more; 32 otherwise
+    const bool tall = T >= kTallMinRows && TK >= static_cast<size_t>(kTallMinRows) * E;
+    L.chunk_rows = T <= kChunkRowsSmall ? kChunkRowsSmall : tall ? kChunkRowsTall : kChunkRowsLarge;
     const size_t cr = L.chunk_rows;
     L.max_chunks = static_cast<int>(nonempty + TK / cr + (shared ? (T + cr - 1) / cr : 0));
     const size_t R = L.rows_max;
@@ -226,9 +229,10 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g1.packed = d->weight_layout == MOE_WEIGHT_PACKED;
         g1.mt = L.chunk_rows / kTileN;
         const bool wide = g1.mt > 1;
-        const int nw = wide ? wide_waves() : 1;
+        const int nw = wide ? wide_tile_pairs(g1.mt) : 1;  // tile pairs per work item
         g1.n_tiles = L.imax / kTileN / nw;
         g1.chunks = ra.chunks;
+        g1.count_word = kMetaChunks;
         g1.meta = meta;
         g1.row_token = ra.row_token;
         g1.h = reinterpret_cast<float *>(ws + L.h);

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
     int c = blockIdx.x / a.n_tiles;
     int nt = blockIdx.x % a.n_tiles;
     int4 ch = a.chunks[c];  // c < max_chunks: inside the chunk list even when unused
-    if (c >= a.meta[kMetaChunks]) return;
+    if (c >= a.meta[a.count_word]) return;
     const int nch = ch.z >> kChunkCountShift;
     if (nch > 1 && (a.n_tiles & 7) == 0) {
         // A group of several chunks owns blocks [c0 * n_tiles, (c0 + nch) *

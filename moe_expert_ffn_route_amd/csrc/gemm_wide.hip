@@ -40,24 +40,30 @@ __device__ __forceinline__ v4i ld16_stream(const int8_t *p) {
 
 // What a wave knows about its work item once the block has decoded it.
 struct WideItem {
-    const int8_t *wb0, *wb1;  // wave-uniform bases of the two weight tiles
+    const int8_t *wb0, *wb1;  // wave-uniform bases of the first pair of weight tiles
+    size_t jstride;           // bytes from one of the wave's tile pairs to the next
     const float *Ws;
     const int8_t *Abase;
     const float *Ascale;
     uint32_t wlane;           // lane offset of a weight load
     int wstep;                // bytes between consecutive K steps of a tile
-    int rowA, rowB;           // first weight row (= output channel) of each tile
+    int rowA, rowB;           // first weight row (= output channel) of the first pair
+    int jcol;                 // channels from one tile pair to the next
     int row0, rows, S, inter;
     bool routed, by_tok, need_tok;
 };
 
 // The K loop and epilogue for MTA active row tiles (the chunk's rows, rounded
-// up to whole tiles). Runs the same sequence in every wave of the block.
-template <int KIND, int NW, int MTA, int SLAB, int RING, bool PACKED>
+// up to whole tiles) and NT pairs of weight tiles per wave. Runs the same
+// sequence in every wave of the block.
+template <int KIND, int NW, int NT, int MTA, int SLAB, int RING, bool PACKED>
 __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it, v4i (*s_a)[kWave]) {
     constexpr int kUnits = SLAB * MTA;             // 1 KB activation units per slab
     constexpr int kUpw = (kUnits + NW - 1) / NW;   // units each wave loads per slab
     constexpr int kSlabsPerRing = RING / SLAB;
+    // with many row tiles the epilogue's per-row tokens and scales are read
+    // after the K loop, into registers the weight ring no longer needs
+    constexpr bool kLateRows = MTA > 2;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int r16 = lane & 15, kg = lane >> 4;
@@ -77,21 +83,37 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
     }
     // a token indexes the row scale of per-token rows and the share_output
     // row of the shared expert's GEMM2
+    constexpr int kER = kLateRows ? 1 : MTA;  // row tiles whose epilogue rows are read early
     int otok[MTA][4];
+    float rsc[MTA][4];
+    auto load_tokens = [&](int mt0, int mt1) {
 #pragma unroll
-    for (int mt = 0; mt < MTA; ++mt)
+        for (int mt = mt0; mt < mt1; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int lr = min(mt * kTileN + 4 * kg + i, rows - 1);
-            otok[mt][i] = it.need_tok ? a.row_token[row0 + lr] : 0;
-        }
-    const float ws0 = it.Ws[it.rowA + r16];
-    const float ws1 = it.Ws[it.rowB + r16];
+            for (int i = 0; i < 4; ++i) {
+                const int lr = min(mt * kTileN + 4 * kg + i, rows - 1);
+                otok[mt][i] = it.need_tok ? a.row_token[row0 + lr] : 0;
+            }
+    };
+    auto load_scales = [&](int mt0, int mt1) {
+#pragma unroll
+        for (int mt = mt0; mt < mt1; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                rsc[mt][i] = it.Ascale[it.by_tok ? otok[mt][i] : row0 + min(mt * kTileN + 4 * kg + i, rows - 1)];
+    };
+    if (!kLateRows) load_tokens(0, kER);
+    float ws0[NT], ws1[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        ws0[j] = it.Ws[it.rowA + j * it.jcol + r16];
+        ws1[j] = it.Ws[it.rowB + j * it.jcol + r16];
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // (2) the first activation slab, then the first ring of weight steps
-    auto ldw = [&](const int8_t *base, int step) {
-        const int8_t *p = base + static_cast<size_t>(step) * it.wstep + it.wlane;
+    auto ldw = [&](const int8_t *base, int j, int step) {
+        const int8_t *p = base + j * it.jstride + static_cast<size_t>(step) * it.wstep + it.wlane;
         return PACKED ? ld16_stream(p) : ld16(p);
     };
     v4i stage[kUpw];
@@ -107,35 +129,34 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
     };
     load_slab(0);
     __builtin_amdgcn_sched_barrier(0);
-    v4i w0[RING], w1[RING];
+    v4i w0[RING][NT], w1[RING][NT];
 #pragma unroll
-    for (int i = 0; i < RING; ++i) {
-        w0[i] = ldw(it.wb0, i);
-        w1[i] = ldw(it.wb1, i);
-    }
+    for (int i = 0; i < RING; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            w0[i][j] = ldw(it.wb0, j, i);
+            w1[i][j] = ldw(it.wb1, j, i);
+        }
     __builtin_amdgcn_sched_barrier(0);
 
     // (3) loads that depend on (1): the row scales of this lane's output rows
-    float rsc[MTA][4];
-#pragma unroll
-    for (int mt = 0; mt < MTA; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            rsc[mt][i] = it.Ascale[it.by_tok ? otok[mt][i] : row0 + min(mt * kTileN + 4 * kg + i, rows - 1)];
+    if (!kLateRows) load_scales(0, kER);
     __builtin_amdgcn_sched_barrier(0);
 
     store_slab(0);
     __syncthreads();
 
-    v4i acc0[MTA], acc1[MTA];
+    v4i acc0[MTA][NT], acc1[MTA][NT];
 #pragma unroll
-    for (int mt = 0; mt < MTA; ++mt) {
-        acc0[mt] = v4i{0, 0, 0, 0};
-        acc1[mt] = v4i{0, 0, 0, 0};
-    }
+    for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            acc0[mt][j] = v4i{0, 0, 0, 0};
+            acc1[mt][j] = v4i{0, 0, 0, 0};
+        }
     // One slab of SLAB K steps at ring position h: the next slab's activation
     // loads, then for each step the MFMAs of all row tiles followed by the
-    // weight load that refills the step's ring slot (RING steps ahead); at the
+    // weight loads that refill the step's ring slot (RING steps ahead); at the
     // end the next slab goes to the other LDS buffer. Scheduling barriers keep
     // each refill right after its step's MFMAs (left alone, the compiler sinks
     // the refills to the end of the slab).
@@ -146,17 +167,21 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
 #pragma unroll
         for (int i = 0; i < SLAB; ++i) {
             const int slot = h * SLAB + i;
-            v4i x[MTA];
-#pragma unroll
-            for (int mt = 0; mt < MTA; ++mt) x[mt] = s_a[cur * kUnits + i * MTA + mt][lane];
 #pragma unroll
             for (int mt = 0; mt < MTA; ++mt) {
-                acc0[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x[mt], w0[slot], acc0[mt], 0, 0, 0);
-                acc1[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x[mt], w1[slot], acc1[mt], 0, 0, 0);
+                const v4i x = s_a[cur * kUnits + i * MTA + mt][lane];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    acc0[mt][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x, w0[slot][j], acc0[mt][j], 0, 0, 0);
+                    acc1[mt][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x, w1[slot][j], acc1[mt][j], 0, 0, 0);
+                }
             }
             if (more_w) {
-                w0[slot] = ldw(it.wb0, wnext + i);
-                w1[slot] = ldw(it.wb1, wnext + i);
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    w0[slot][j] = ldw(it.wb0, j, wnext + i);
+                    w1[slot][j] = ldw(it.wb1, j, wnext + i);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -175,115 +200,129 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
     for (int h = 0; h < kSlabsPerRing; ++h)
         slab((ncyc - 1) * kSlabsPerRing + h, h, h + 1 < kSlabsPerRing, false);
 
+    if (kLateRows) {
+        load_tokens(0, MTA);
+        load_scales(0, MTA);
+    }
+
     // Epilogue: lane l holds rows 4 * (l / 16) + i of every row tile, at
-    // channel l % 16 of both weight tiles.
+    // channel l % 16 of every weight tile.
 #pragma unroll
     for (int mt = 0; mt < MTA; ++mt) {
-        if (KIND == 1) {
-            const int col = it.rowA + r16;  // gate channel index = h column
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int lr = mt * kTileN + 4 * kg + i;
-                if (lr < rows) {
-                    const int r = row0 + lr;
-                    float yg = static_cast<float>(acc0[mt][i]) * ws0;
-                    yg = yg * rsc[mt][i];
-                    float yu = static_cast<float>(acc1[mt][i]) * ws1;
-                    yu = yu * rsc[mt][i];
-                    const float ex = expf(-yg);
-                    const float den = 1.0f + ex;
-                    const float sg = yg / den;
-                    a.h[static_cast<size_t>(r) * a.imax + col] = sg * yu;
-                    if (a.dbg_acc) {
-                        a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + col] = acc0[mt][i];
-                        a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + it.inter + col] = acc1[mt][i];
+        for (int j = 0; j < NT; ++j) {
+            const int rowA = it.rowA + j * it.jcol, rowB = it.rowB + j * it.jcol;
+            if (KIND == 1) {
+                const int col = rowA + r16;  // gate channel index = h column
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int lr = mt * kTileN + 4 * kg + i;
+                    if (lr < rows) {
+                        const int r = row0 + lr;
+                        float yg = static_cast<float>(acc0[mt][j][i]) * ws0[j];
+                        yg = yg * rsc[mt][i];
+                        float yu = static_cast<float>(acc1[mt][j][i]) * ws1[j];
+                        yu = yu * rsc[mt][i];
+                        const float ex = expf(-yg);
+                        const float den = 1.0f + ex;
+                        const float sg = yg / den;
+                        a.h[static_cast<size_t>(r) * a.imax + col] = sg * yu;
+                        if (a.dbg_acc) {
+                            a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + col] = acc0[mt][j][i];
+                            a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + it.inter + col] = acc1[mt][j][i];
+                        }
                     }
                 }
-            }
-        } else {
+            } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int lr = mt * kTileN + 4 * kg + i;
-                float y0 = static_cast<float>(acc0[mt][i]) * ws0;
-                y0 = y0 * rsc[mt][i];
-                float y1 = static_cast<float>(acc1[mt][i]) * ws1;
-                y1 = y1 * rsc[mt][i];
-                const uint32_t b0 = f32_to_bf16(y0), b1 = f32_to_bf16(y1);
-                // pair up neighbouring channels for 4-byte stores: even lanes
-                // take channels (c, c + 1) of tile A, odd lanes (c - 1, c) of
-                // tile B, so 16 lanes store 64 contiguous bytes of the row
-                const uint32_t p0 = __shfl_xor(static_cast<int>(b0), 1, kWave);
-                const uint32_t p1 = __shfl_xor(static_cast<int>(b1), 1, kWave);
-                const bool even = (r16 & 1) == 0;
-                const uint32_t word = even ? (b0 | (p0 << 16)) : (p1 | (b1 << 16));
-                const int wcol = even ? it.rowA + r16 : it.rowB + r16 - 1;
-                if (lr < rows) {
-                    const int r = row0 + lr;
-                    uint16_t *dst = it.routed ? a.z + static_cast<size_t>(r) * a.H
-                                              : a.share_out + static_cast<size_t>(otok[mt][i]) * a.H;
-                    *reinterpret_cast<uint32_t *>(dst + wcol) = word;
-                    if (a.dbg_acc) {
-                        a.dbg_acc[static_cast<size_t>(r) * a.H + it.rowA + r16] = acc0[mt][i];
-                        a.dbg_acc[static_cast<size_t>(r) * a.H + it.rowB + r16] = acc1[mt][i];
+                for (int i = 0; i < 4; ++i) {
+                    const int lr = mt * kTileN + 4 * kg + i;
+                    float y0 = static_cast<float>(acc0[mt][j][i]) * ws0[j];
+                    y0 = y0 * rsc[mt][i];
+                    float y1 = static_cast<float>(acc1[mt][j][i]) * ws1[j];
+                    y1 = y1 * rsc[mt][i];
+                    const uint32_t b0 = f32_to_bf16(y0), b1 = f32_to_bf16(y1);
+                    // pair up neighbouring channels for 4-byte stores: even
+                    // lanes take channels (c, c + 1) of tile A, odd lanes
+                    // (c - 1, c) of tile B, so 16 lanes store 64 contiguous
+                    // bytes of the row
+                    const uint32_t p0 = __shfl_xor(static_cast<int>(b0), 1, kWave);
+                    const uint32_t p1 = __shfl_xor(static_cast<int>(b1), 1, kWave);
+                    const bool even = (r16 & 1) == 0;
+                    const uint32_t word = even ? (b0 | (p0 << 16)) : (p1 | (b1 << 16));
+                    const int wcol = even ? rowA + r16 : rowB + r16 - 1;
+                    if (lr < rows) {
+                        const int r = row0 + lr;
+                        uint16_t *dst = it.routed ? a.z + static_cast<size_t>(r) * a.H
+                                                  : a.share_out + static_cast<size_t>(otok[mt][i]) * a.H;
+                        *reinterpret_cast<uint32_t *>(dst + wcol) = word;
+                        if (a.dbg_acc) {
+                            a.dbg_acc[static_cast<size_t>(r) * a.H + rowA + r16] = acc0[mt][j][i];
+                            a.dbg_acc[static_cast<size_t>(r) * a.H + rowB + r16] = acc1[mt][j][i];
+                        }
+                        if (a.dbg_z)
+                            *reinterpret_cast<uint32_t *>(a.dbg_z + static_cast<size_t>(r) * a.H + wcol) = word;
                     }
-                    if (a.dbg_z) *reinterpret_cast<uint32_t *>(a.dbg_z + static_cast<size_t>(r) * a.H + wcol) = word;
                 }
             }
         }
     }
 }
 
-// MT = row tiles per chunk (the chunk size); a block runs the body for the
-// tiles its chunk actually fills.
-template <int KIND, int NW, int MT, int SLAB, int RING, bool PACKED>
-__global__ __launch_bounds__(NW * kWave) void gemm_wide_kernel(GemmArgs a, int k_dim) {
-    __shared__ v4i s_a[2 * SLAB * MT][kWave];
-
+// Decodes the work item of block index b of one item class (chunk list,
+// chunk count word, N groups per chunk) into `it`, for a block of NW waves
+// holding NT tile pairs each. Returns false when the block has no work.
+template <int KIND, int NW, int NT, bool PACKED>
+__device__ __forceinline__ bool decode_item(const GemmArgs &a, const int4 *chunks, int count_word, int n_tiles,
+                                            int b, int k_dim, WideItem &it) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    int c = blockIdx.x / a.n_tiles;
-    int nt = blockIdx.x % a.n_tiles;
-    int4 ch = a.chunks[c];  // c < max_chunks: inside the chunk list even when unused
-    if (c >= a.meta[kMetaChunks]) return;
+    int c = b / n_tiles;
+    int nt = b % n_tiles;
+    int4 ch = chunks[c];  // c < the class's capacity: inside the list even when unused
+    if (c >= a.meta[count_word]) return false;
     const int nch = ch.z >> kChunkCountShift;
-    if (nch > 1 && (a.n_tiles & 7) == 0) {
+    if (nch > 1 && (n_tiles & 7) == 0) {
         // the chunks of one N tile run 8 blocks apart, on one XCD (gemm.hip)
         const int c0 = c - ch.w;
-        const int i = blockIdx.x - c0 * a.n_tiles;
+        const int i = b - c0 * n_tiles;
         const int q = i / (8 * nch), rem = i - q * 8 * nch;
         c = c0 + rem / 8;
         nt = q * 8 + rem % 8;
-        ch = a.chunks[c];
+        ch = chunks[c];
     }
-    WideItem it;
     const int g = ch.x;
     it.row0 = ch.y;
     it.rows = ch.z & kChunkRowsMask;
-    if (g < a.g_lo || g >= a.g_hi) return;
+    if (g < a.g_lo || g >= a.g_hi) return false;
     it.routed = g < a.E_loc;
     it.inter = it.routed ? a.I : a.I_s;
-    // inter and H are multiples of 256, so a block either has work for all of
-    // its waves or for none
-    if (KIND == 1 && nt * NW * kTileN >= it.inter) return;
+    // inter and H are multiples of 256 and a block covers at most 256
+    // channels, so a block either has work for all of its waves or for none
+    if (KIND == 1 && nt * NW * NT * kTileN >= it.inter) return false;
 
     const int8_t *W;
-    const int tp = nt * NW + wave;  // this wave's pair of 16-row weight tiles
+    const int tp = (nt * NW + wave) * NT;  // this wave's first pair of 16-row weight tiles
+    it.S = k_dim / 64;                     // 64-byte K steps; a multiple of the ring (host-checked)
+    const size_t tile_bytes = static_cast<size_t>(kTileN) * k_dim;
     if (KIND == 1) {
         W = it.routed ? a.W + static_cast<size_t>(g) * 2 * it.inter * a.H : a.W_sh;
         it.Ws = it.routed ? a.Ws + static_cast<size_t>(g) * 2 * it.inter : a.Ws_sh;
         it.rowA = tp * kTileN;             // gate channels
         it.rowB = it.inter + tp * kTileN;  // matching up channels
+        it.jcol = kTileN;
     } else {
         W = it.routed ? a.W + static_cast<size_t>(g) * a.H * it.inter : a.W_sh;
         it.Ws = it.routed ? a.Ws + static_cast<size_t>(g) * a.H : a.Ws_sh;
         it.rowA = tp * 2 * kTileN;
         it.rowB = it.rowA + kTileN;
+        it.jcol = 2 * kTileN;
     }
-    it.S = k_dim / 64;  // 64-byte K steps; a multiple of RING (host-checked)
+    it.jstride = (it.jcol / kTileN) * tile_bytes;  // a tile is 16 rows x k_dim bytes in both layouts
     // weight addresses: a wave-uniform base plus a 32-bit lane offset
     if (PACKED) {
-        it.wb0 = W + static_cast<size_t>(it.rowA / kTileN) * it.S * 1024;
-        it.wb1 = W + static_cast<size_t>(it.rowB / kTileN) * it.S * 1024;
+        it.wb0 = W + static_cast<size_t>(it.rowA / kTileN) * tile_bytes;
+        it.wb1 = W + static_cast<size_t>(it.rowB / kTileN) * tile_bytes;
         it.wlane = lane * 16;
         it.wstep = 1024;
     } else {
@@ -296,69 +335,97 @@ __global__ __launch_bounds__(NW * kWave) void gemm_wide_kernel(GemmArgs a, int k
     it.need_tok = it.by_tok || (KIND == 2 && !it.routed);
     it.Abase = it.by_tok ? a.A_tok : a.A;
     it.Ascale = it.by_tok ? a.a_scale_tok : a.a_scale;
-
-    const int tiles = (it.rows + kTileN - 1) / kTileN;
-    if constexpr (MT > 2) {
-        if (tiles > 2) return wide_body<KIND, NW, MT, SLAB, RING, PACKED>(a, it, s_a);
-    }
-    if constexpr (MT > 1) {
-        if (tiles > 1) return wide_body<KIND, NW, 2, SLAB, RING, PACKED>(a, it, s_a);
-    }
-    wide_body<KIND, NW, 1, SLAB, RING, PACKED>(a, it, s_a);
+    return true;
 }
 
-#ifndef MOE_WIDE_WAVES
-#define MOE_WIDE_WAVES 2
+// Tile parameters of the two chunk sizes. Wide items (chunks of up to
+// 16 * kWideTiles rows): 2 waves of one tile pair each, activation slabs of
+// 4 K steps, a weight ring of 8 steps (4 where 8 does not divide K). Tall
+// items (chunks of up to 16 * kTallTiles rows, when experts average hundreds
+// of rows): 4 waves of two tile pairs each, so each activation fragment read
+// from LDS feeds four MFMAs; slabs of 1 step and a ring of 4 keep the
+// 128-row accumulators within two waves' registers per SIMD. (Measured on
+// the compute-bound probe: one tile pair per wave is 25 % slower; slabs of 2
+// steps 1.5 % slower.)
+#ifndef MOE_TALL_WAVES
+#define MOE_TALL_WAVES 4
 #endif
-#ifndef MOE_WIDE_SLAB
-#define MOE_WIDE_SLAB 4
+#ifndef MOE_TALL_NT
+#define MOE_TALL_NT 2
 #endif
-#ifndef MOE_WIDE_RING
-#define MOE_WIDE_RING 8
+#ifndef MOE_TALL_SLAB
+#define MOE_TALL_SLAB 1
 #endif
+#ifndef MOE_TALL_RING
+#define MOE_TALL_RING 4
+#endif
+constexpr int kWideWaves = 2, kWideSlab = 4;
+constexpr int kTallWaves = MOE_TALL_WAVES, kTallNT = MOE_TALL_NT, kTallSlab = MOE_TALL_SLAB,
+              kTallRing = MOE_TALL_RING;
 
-template <int KIND, int NW, int MT, int SLAB, int RING>
-hipError_t launch_wide_t(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+template <int KIND, int NW, int NT, int MT, int SLAB, int RING, bool PACKED>
+__global__ __launch_bounds__(NW * kWave, 2) void gemm_wide_kernel(GemmArgs a, int k_dim) {
+    __shared__ v4i s_a[2 * SLAB * MT][kWave];
+    WideItem it;
+    if (!decode_item<KIND, NW, NT, PACKED>(a, a.chunks, a.count_word, a.n_tiles, blockIdx.x, k_dim, it)) return;
+    // run the body for the row tiles the chunk actually fills
+    const int tiles = (it.rows + kTileN - 1) / kTileN;
+    if constexpr (MT > 4) {
+        if (tiles > 4) return wide_body<KIND, NW, NT, MT, SLAB, RING, PACKED>(a, it, s_a);
+    }
+    if constexpr (MT > 2) {
+        if (tiles > 2) return wide_body<KIND, NW, NT, (MT > 4 ? 4 : MT), SLAB, RING, PACKED>(a, it, s_a);
+    }
+    if constexpr (MT > 1) {
+        if (tiles > 1) return wide_body<KIND, NW, NT, 2, SLAB, RING, PACKED>(a, it, s_a);
+    }
+    wide_body<KIND, NW, NT, 1, SLAB, RING, PACKED>(a, it, s_a);
+}
+
+template <int KIND, int NW, int NT, int MT, int SLAB, int RING>
+hipError_t launch_t(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const long blocks = static_cast<long>(max_chunks) * a.n_tiles;
     if (blocks <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(blocks)), blk(NW * kWave);
     if (a.packed) {
         if (e0 || e1)
-            hipExtLaunchKernelGGL((gemm_wide_kernel<KIND, NW, MT, SLAB, RING, true>), grid, blk, 0, s, e0, e1, 0, a,
-                                  k_dim);
+            hipExtLaunchKernelGGL((gemm_wide_kernel<KIND, NW, NT, MT, SLAB, RING, true>), grid, blk, 0, s, e0, e1, 0,
+                                  a, k_dim);
         else
-            hipLaunchKernelGGL((gemm_wide_kernel<KIND, NW, MT, SLAB, RING, true>), grid, blk, 0, s, a, k_dim);
+            hipLaunchKernelGGL((gemm_wide_kernel<KIND, NW, NT, MT, SLAB, RING, true>), grid, blk, 0, s, a, k_dim);
     } else {
         if (e0 || e1)
-            hipExtLaunchKernelGGL((gemm_wide_kernel<KIND, NW, MT, SLAB, RING, false>), grid, blk, 0, s, e0, e1, 0, a,
-                                  k_dim);
+            hipExtLaunchKernelGGL((gemm_wide_kernel<KIND, NW, NT, MT, SLAB, RING, false>), grid, blk, 0, s, e0, e1,
+                                  0, a, k_dim);
         else
-            hipLaunchKernelGGL((gemm_wide_kernel<KIND, NW, MT, SLAB, RING, false>), grid, blk, 0, s, a, k_dim);
+            hipLaunchKernelGGL((gemm_wide_kernel<KIND, NW, NT, MT, SLAB, RING, false>), grid, blk, 0, s, a, k_dim);
     }
     return hipGetLastError();
 }
 
+// k_dim is a multiple of 256, so rings of 4 steps always divide it
 template <int KIND>
-hipError_t launch_wide(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    constexpr int NW = MOE_WIDE_WAVES, MT = kWideTiles, SL = MOE_WIDE_SLAB, RG = MOE_WIDE_RING;
-    static_assert(RG % SL == 0, "the weight ring holds whole activation slabs");
-    // k_dim is a multiple of 256, so rings of 4 steps always divide it
-    if ((k_dim / 64) % RG == 0) return launch_wide_t<KIND, NW, MT, SL, RG>(a, max_chunks, k_dim, s, e0, e1);
-    return launch_wide_t<KIND, NW, MT, 4, 4>(a, max_chunks, k_dim, s, e0, e1);
+hipError_t launch_items(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    if (a.mt == kTallTiles)
+        return launch_t<KIND, kTallWaves, kTallNT, kTallTiles, kTallSlab, kTallRing>(a, max_chunks, k_dim, s, e0, e1);
+    if (a.mt != kWideTiles) return hipErrorInvalidValue;
+    if ((k_dim / 64) % 8 == 0)
+        return launch_t<KIND, kWideWaves, 1, kWideTiles, kWideSlab, 8>(a, max_chunks, k_dim, s, e0, e1);
+    return launch_t<KIND, kWideWaves, 1, kWideTiles, kWideSlab, 4>(a, max_chunks, k_dim, s, e0, e1);
 }
 
 }  // namespace
 
 hipError_t launch_gemm1_wide(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start,
                              hipEvent_t ev_stop) {
-    return launch_wide<1>(a, max_chunks, a.H, s, ev_start, ev_stop);
+    return launch_items<1>(a, max_chunks, a.H, s, ev_start, ev_stop);
 }
 
 hipError_t launch_gemm2_wide(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
                              hipEvent_t ev_stop) {
-    return launch_wide<2>(a, max_chunks, k_dim, s, ev_start, ev_stop);
+    return launch_items<2>(a, max_chunks, k_dim, s, ev_start, ev_stop);
 }
 
-int wide_waves() { return MOE_WIDE_WAVES; }
+int wide_tile_pairs(int mt) { return mt == kTallTiles ? kTallWaves * kTallNT : kWideWaves; }
 
 }  // namespace moe

@@ -20,12 +20,26 @@ constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kWideTiles = MOE_WIDE_MT;
 constexpr int kChunkRowsSmall = 16;
 constexpr int kChunkRowsLarge = 16 * MOE_WIDE_MT;
+// When the routed experts average at least kTallMinRows rows (T * K >=
+// kTallMinRows * E_loc), every group is cut into chunks of kChunkRowsTall rows
+// instead: tall work items of gemm_wide.hip, whose waves each hold two weight
+// tile pairs, so that every activation fragment read from LDS feeds more MFMAs.
+#ifndef MOE_TALL_MT
+#define MOE_TALL_MT 8
+#endif
+#ifndef MOE_TALL_MIN_ROWS
+#define MOE_TALL_MIN_ROWS 256
+#endif
+constexpr int kTallTiles = MOE_TALL_MT;
+constexpr int kChunkRowsTall = 16 * MOE_TALL_MT;
+constexpr int kTallMinRows = MOE_TALL_MIN_ROWS;
 constexpr int kTileN = 16;           // MFMA 16x16x64 output tile edge
 // A chunk entry's third word holds its row count (<= 64) in the low bits and
 // the number of chunks of its group above kChunkCountShift.
 constexpr int kChunkCountShift = 8;
 constexpr int kChunkRowsMask = (1 << kChunkCountShift) - 1;
-static_assert(kChunkRowsLarge <= kChunkRowsMask, "chunk rows must fit below the count bits");
+static_assert(kChunkRowsLarge <= kChunkRowsMask && kChunkRowsTall <= kChunkRowsMask,
+              "chunk rows must fit below the count bits");
 constexpr int kMaxTopK = 16;
 constexpr int kMaxTokens = 1 << 16;
 
@@ -113,6 +127,7 @@ struct GemmArgs {
     int mt;           // 16-row MFMA tiles per chunk
     int n_tiles;      // work items per chunk along N
     const int4 *chunks;
+    int count_word;   // meta word holding the number of chunks
     const int32_t *meta;
     const int32_t *row_token;
     // outputs
@@ -140,13 +155,14 @@ hipError_t launch_requant(const RequantArgs &a, hipStream_t s);
 hipError_t launch_gemm1(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_gemm2(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
                         hipEvent_t ev_stop);
-// Work items of several row tiles (gemm_wide.hip); n_tiles counts groups of
-// wide_waves() pairs of 16-row weight tiles.
+// Work items of several row tiles (gemm_wide.hip; a.mt = kWideTiles or
+// kTallTiles): n_tiles counts groups of wide_tile_pairs(a.mt) pairs of 16-row
+// weight tiles.
 hipError_t launch_gemm1_wide(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start,
                              hipEvent_t ev_stop);
 hipError_t launch_gemm2_wide(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
                              hipEvent_t ev_stop);
-int wide_waves();
+int wide_tile_pairs(int mt);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_pack(const int8_t *src, int8_t *dst, int64_t groups, int n, int k, hipStream_t s);
 // debug only: expand per-token rows into the grouped-row q_x / xs dump

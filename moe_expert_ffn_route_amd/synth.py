@@ -71,7 +71,7 @@ class Spec:
         return self.seed if self.wseed is None else self.wseed
 
 
-# The five workloads. Configs 1, 3 and 4 are one model (same expert shapes),
+# The five workloads (and a probe). Configs 1, 3 and 4 are one model (same expert shapes),
 # so they share a weight seed and one set of resident weights serves all three.
 CONFIGS = {
     0: Spec("tiny_w8a8_moe", T=8, H=512, I=256, E_g=8, K=2, seed=1234),
@@ -83,6 +83,11 @@ CONFIGS = {
             routing="zipf", zipf_s=1.2, seed=1237, wseed=1235),
     4: Spec("large_batch_t512", T=512, H=4096, I=2048, E_g=256, K=8, I_s=2048,
             seed=1238, wseed=1235),
+    # Supplementary compute-bound probe (not one of the pages' workloads):
+    # every token picks all 8 experts, so each expert multiplies 512 rows and
+    # the GEMMs do 2 * 512 int8 operations per weight byte, above the MI355X
+    # ridge of about 625; it exercises the grouped GEMMs' MFMA throughput.
+    5: Spec("mfma_probe_t512_e8", T=512, H=4096, I=2048, E_g=8, K=8, seed=1239),
 }
 
 

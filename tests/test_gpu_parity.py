@@ -45,6 +45,14 @@ SMALL = {
     # larger-batch kernel's 8-step weight ring does not divide
     "t40_short_ring": spec(T=40, H=768, I=256, E_g=4, K=2, I_s=768, seed=111),
     "t17_one_row_past_decode": spec(T=17, H=512, I=256, E_g=2, K=1, I_s=256, seed=112),
+    # experts averaging 256 rows or more: every group is cut into tall work
+    # items (128-row chunks, the last one ragged, filling 1 to 8 row tiles)
+    "tall_ragged_shared": spec(T=300, H=512, I=256, E_g=2, K=2, I_s=256, seed=113),
+    "tall_exact_two_chunks": spec(T=256, H=512, I=512, E_g=1, K=1, seed=114),
+    "tall_mask_smooth_split_gemm2": spec(T=290, H=768, I=256, E_g=2, K=2, I_s=512, active=270, smooth=True,
+                                         share_smooth=True, seed=115),
+    "tall_skewed": spec(T=600, H=256, I=256, E_g=2, K=1, routing="zipf", zipf_s=2.0, I_s=256, seed=116),
+    "tall_tail_two_tiles": spec(T=280, H=512, I=256, E_g=1, K=1, I_s=256, seed=117),
 }
 
 
@@ -270,7 +278,7 @@ def weights_for(s):
 
 
 # tokens sampled by the oracle (None = all); 1, 3 and 4 share one set of weights
-FULL = {1: None, 3: 24, 4: 12, 2: None}
+FULL = {1: None, 3: 24, 4: 12, 2: None, 5: 6}
 
 
 @pytest.mark.parametrize("cfg", list(FULL))
