@@ -21,9 +21,7 @@
 //     workgroup barrier per slab;
 //   - with no K split there is no cross-wave reduction: each lane holds the
 //     finished int32 sums of its (row, channel) outputs.
-// LDS layout: one 1 KB unit per (K step, row tile), in MFMA operand order
-// (lane l's 16 bytes are row l % 16, byte 16 * (l / 16) of the step), so both
-// the writes and the MFMA operand reads are whole, conflict-free 1 KB rows.
+// LDS layout: the slab's rows, each padded by 16 bytes (see wide_body).
 #include "internal.h"
 
 #include <hip/hip_ext.h>
@@ -57,10 +55,21 @@ struct WideItem {
 // up to whole tiles) and NT pairs of weight tiles per wave. Runs the same
 // sequence in every wave of the block.
 template <int KIND, int NW, int NT, int MTA, int SLAB, int RING, bool PACKED>
-__device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it, v4i (*s_a)[kWave]) {
-    constexpr int kUnits = SLAB * MTA;             // 1 KB activation units per slab
-    constexpr int kUpw = (kUnits + NW - 1) / NW;   // units each wave loads per slab
+__device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it, v4i *s_a) {
+    // Activation slab layout in LDS: the chunk's 16 * MTA rows, each holding
+    // the slab's SLAB * 64 bytes plus 16 bytes of padding. A load instruction
+    // reads kRpi whole row segments (contiguous, so every 128-byte line it
+    // touches is used in full), a store writes them unchanged, and the
+    // padding spreads the 16 rows an MFMA operand read gathers over distinct
+    // LDS banks.
+    constexpr int kLpr = 4 * SLAB;                 // lanes per row segment (16 bytes each)
+    constexpr int kRpi = kWave / kLpr;             // row segments per load instruction
+    constexpr int kStr = kLpr + 1;                 // LDS row stride, in 16-byte units
+    constexpr int kBuf = kTileN * MTA * kStr;      // one slab buffer
+    constexpr int kUnits = kTileN * MTA / kRpi;    // load instructions per slab (= SLAB * MTA)
+    constexpr int kUpw = (kUnits + NW - 1) / NW;   // of them, per wave
     constexpr int kSlabsPerRing = RING / SLAB;
+    static_assert(kWave % kLpr == 0, "a load instruction covers whole row segments");
     // with many row tiles the epilogue's per-row tokens and scales are read
     // after the K loop, into registers the weight ring no longer needs
     constexpr bool kLateRows = MTA > 2;
@@ -73,13 +82,13 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
     //     wave stages and of each output row it finishes (4 * (lane / 16) + i
     //     of every row tile), and the channel scales
     const int8_t *asrc[kUpw];
+    const int seg = lane % kLpr;  // this lane's 16 bytes within a row segment
 #pragma unroll
     for (int j = 0; j < kUpw; ++j) {
         const int u = wave + j * NW;
-        const int mt = u % MTA, st = u / MTA;
-        const int lr = min(mt * kTileN + r16, rows - 1);  // rows past the chunk repeat its last row
+        const int lr = min(u * kRpi + lane / kLpr, rows - 1);  // rows past the chunk repeat its last row
         const int ar = it.by_tok ? a.row_token[row0 + lr] : row0 + lr;
-        asrc[j] = it.Abase + static_cast<size_t>(ar) * a.a_stride + st * 64 + kg * 16;
+        asrc[j] = it.Abase + static_cast<size_t>(ar) * a.a_stride + seg * 16;
     }
     // a token indexes the row scale of per-token rows and the share_output
     // row of the shared expert's GEMM2
@@ -125,7 +134,8 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
     auto store_slab = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < kUpw; ++j)
-            if (kUnits % NW == 0 || wave + j * NW < kUnits) s_a[buf * kUnits + wave + j * NW][lane] = stage[j];
+            if (kUnits % NW == 0 || wave + j * NW < kUnits)
+                s_a[buf * kBuf + ((wave + j * NW) * kRpi + lane / kLpr) * kStr + seg] = stage[j];
     };
     load_slab(0);
     __builtin_amdgcn_sched_barrier(0);
@@ -169,7 +179,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
             const int slot = h * SLAB + i;
 #pragma unroll
             for (int mt = 0; mt < MTA; ++mt) {
-                const v4i x = s_a[cur * kUnits + i * MTA + mt][lane];
+                const v4i x = s_a[cur * kBuf + (mt * kTileN + r16) * kStr + i * 4 + kg];
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     acc0[mt][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x, w0[slot][j], acc0[mt][j], 0, 0, 0);
@@ -365,7 +375,7 @@ constexpr int kTallWaves = MOE_TALL_WAVES, kTallNT = MOE_TALL_NT, kTallSlab = MO
 
 template <int KIND, int NW, int NT, int MT, int SLAB, int RING, bool PACKED>
 __global__ __launch_bounds__(NW * kWave, 2) void gemm_wide_kernel(GemmArgs a, int k_dim) {
-    __shared__ v4i s_a[2 * SLAB * MT][kWave];
+    __shared__ v4i s_a[2 * kTileN * MT * (4 * SLAB + 1)];
     WideItem it;
     if (!decode_item<KIND, NW, NT, PACKED>(a, a.chunks, a.count_word, a.n_tiles, blockIdx.x, k_dim, it)) return;
     // run the body for the row tiles the chunk actually fills
