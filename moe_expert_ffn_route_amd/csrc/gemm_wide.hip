@@ -369,7 +369,13 @@ __device__ __forceinline__ bool decode_item(const GemmArgs &a, const int4 *chunk
 #ifndef MOE_TALL_RING
 #define MOE_TALL_RING 4
 #endif
-constexpr int kWideWaves = 2, kWideSlab = 4;
+#ifndef MOE_WIDE_WAVES
+#define MOE_WIDE_WAVES 2
+#endif
+#ifndef MOE_WIDE_SLAB
+#define MOE_WIDE_SLAB 4
+#endif
+constexpr int kWideWaves = MOE_WIDE_WAVES, kWideSlab = MOE_WIDE_SLAB;
 constexpr int kTallWaves = MOE_TALL_WAVES, kTallNT = MOE_TALL_NT, kTallSlab = MOE_TALL_SLAB,
               kTallRing = MOE_TALL_RING;
 
