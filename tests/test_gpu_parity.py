@@ -171,11 +171,21 @@ def test_deterministic_dirty_workspace_and_side_stream():
             assert np.array_equal(a[k][r, :w], b[k][r, :w]), (k, r)
 
 
-def test_hip_graph_capture_and_replay():
+GRAPH_CASES = {
+    "decode": spec(T=12, H=512, I=256, E_g=8, K=2, I_s=256, active=10, seed=116),
+    "wide": spec(T=40, H=512, I=256, E_g=8, K=2, I_s=512, active=37, seed=118),
+    "tall": spec(T=300, H=512, I=256, E_g=2, K=2, I_s=256, seed=119),
+}
+
+
+@pytest.mark.parametrize("name", list(GRAPH_CASES))
+def test_hip_graph_capture_and_replay(name):
     # the production path launches kernels only (no memset, no allocation), so
     # a caller can capture it; every replay must match the eager result, with
-    # other eager work and synchronisations between replays
-    c = synth.make_case(spec(T=12, H=512, I=256, E_g=8, K=2, I_s=256, active=10, seed=116))
+    # other eager work and synchronisations between replays (each GEMM kernel
+    # family: decode, 32-row and 128-row work items)
+    say(f"[graph] {name}: {GRAPH_CASES[name]}")
+    c = synth.make_case(GRAPH_CASES[name])
     t = moe.pack_weights(moe.upload(c))
     dims = moe.dims_of_case(c)
     dims.weight_layout = moe.MOE_WEIGHT_PACKED
