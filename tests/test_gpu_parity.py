@@ -83,6 +83,44 @@ def test_production_tile_parity(name, packed):
     say(f"[parity] {name}: {stats}")
 
 
+def _random_specs(n, seed=2024):
+    """Seeded random small shapes over every option of the block: batch sizes
+    on both sides of the decode / 32-row / 128-row work-item choice, hidden and
+    intermediate sizes, a shared expert or none (with a differing
+    intermediate), expert-parallel shares, masks, smooth scales, uniform and
+    skewed routing, both weight layouts."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E_g = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        ep = int(rng.choice([d for d in (1, 2, 4) if E_g % d == 0]))
+        K = int(rng.integers(1, min(E_g, 8) + 1))
+        T = int(rng.choice([1, 3, 8, 16, 17, 40, 100, 260, 300]))
+        I_s = int(rng.choice([0, 256, 512]))
+        kw = dict(name=f"random{i}", T=T, H=int(rng.choice([256, 512, 768, 1024])), I=int(rng.choice([256, 512])),
+                  E_g=E_g, K=K, I_s=I_s, ep_size=ep, ep_rank=int(rng.integers(0, ep)),
+                  routing=str(rng.choice(["uniform", "zipf"])), zipf_s=1.5, seed=200 + i)
+        if rng.random() < 0.4:
+            kw["active"] = int(rng.integers(0, T + 1))
+        if rng.random() < 0.4:
+            kw["smooth"] = True
+        if I_s and rng.random() < 0.4:
+            kw["share_smooth"] = True
+        out.append((synth.Spec(**kw), bool(i % 2)))
+    return out
+
+
+RANDOM = _random_specs(24)
+
+
+@pytest.mark.parametrize("i", range(len(RANDOM)))
+def test_random_shapes_parity(i):
+    sp, packed = RANDOM[i]
+    say(f"[parity] random {i} packed={packed}: {sp}")
+    stats, _, _ = check(synth.make_case(sp), packed=packed)
+    say(f"[parity] random {i}: {stats}")
+
+
 def _pack_reference(w):
     """The packed order written out with numpy, from its definition."""
     G, n, k = w.shape
