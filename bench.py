@@ -186,10 +186,10 @@ def main():
         return
     moe.library()  # fail loudly if the HIP library is missing
 
-    spec = synth.CONFIGS[args.config]
+    spec = synth.WORKLOADS[args.config]
     log(f"[bench] workload {spec.name}: generating inputs")
     t0 = time.perf_counter()
-    case = synth.config_case(args.config)
+    case = synth.workload_case(args.config)
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s; uploading")
     dev = moe.upload(case)
     if not args.row_major:

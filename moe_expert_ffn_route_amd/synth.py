@@ -71,9 +71,9 @@ class Spec:
         return self.seed if self.wseed is None else self.wseed
 
 
-# The five workloads (and a probe). Configs 1, 3 and 4 are one model (same expert shapes),
+# The five workloads (and a probe). Workloads 1, 3 and 4 are one model (same expert shapes),
 # so they share a weight seed and one set of resident weights serves all three.
-CONFIGS = {
+WORKLOADS = {
     0: Spec("tiny_w8a8_moe", T=8, H=512, I=256, E_g=8, K=2, seed=1234),
     1: Spec("v4flash_decode_t8", T=8, H=4096, I=2048, E_g=256, K=8, I_s=2048,
             seed=1235, wseed=1235),
@@ -247,5 +247,5 @@ def make_case(spec: Spec, weights=None) -> Case:
     return Case(spec, x, ids, esc, w1, w1s, w2, w2s, sw1, sw1s, sw2, sw2s, smooth, ssm, mask)
 
 
-def config_case(i: int, weights=None) -> Case:
-    return make_case(CONFIGS[i], weights)
+def workload_case(i: int, weights=None) -> Case:
+    return make_case(WORKLOADS[i], weights)

@@ -23,7 +23,7 @@ def digest(a):
 
 
 def main():
-    case = synth.config_case(0)
+    case = synth.workload_case(0)
     r = oracle.forward(case, trace=True)
     P = r["P"]
     rec = {

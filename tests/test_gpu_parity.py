@@ -30,7 +30,7 @@ def spec(**kw):
 
 
 SMALL = {
-    "cfg0_tiny": synth.CONFIGS[0],
+    "cfg0_tiny": synth.WORKLOADS[0],
     "ragged_mask_smooth_shared": spec(T=37, H=768, I=512, I_s=256, E_g=16, K=4, active=29, smooth=True,
                                       share_smooth=True, seed=102),
     "ep_share_rank2": spec(T=50, H=512, I=512, E_g=32, K=6, ep_size=4, ep_rank=2, active=41, smooth=True, seed=103),
@@ -331,9 +331,9 @@ FULL = {1: None, 3: 24, 4: 12, 2: None, 5: 6}
 
 @pytest.mark.parametrize("cfg", list(FULL))
 def test_full_size_workload(cfg):
-    s = synth.CONFIGS[cfg]
+    s = synth.WORKLOADS[cfg]
     say(f"[parity] config {cfg} {s.name}")
-    case = synth.config_case(cfg, weights=weights_for(s))
+    case = synth.workload_case(cfg, weights=weights_for(s))
     n = FULL[cfg]
     tokens = None
     if n is not None:

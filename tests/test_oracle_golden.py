@@ -14,7 +14,7 @@ GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "cfg0_
 def test_oracle_matches_recorded_fixture():
     with open(GOLD) as f:
         g = json.load(f)
-    r = oracle.forward(synth.config_case(0), trace=True)
+    r = oracle.forward(synth.workload_case(0), trace=True)
     P = r["P"]
     h = lambda a: hashlib.sha256(a.tobytes()).hexdigest()
     assert r["expert_token_nums"].tolist() == g["expert_token_nums"]

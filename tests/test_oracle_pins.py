@@ -78,7 +78,7 @@ def pin_route_bruteforce():
 
 def pin_route_count_invariant():
     # sum(expert_token_nums) = active tokens x top-k when every expert is local
-    for i, spec in synth.CONFIGS.items():
+    for i, spec in synth.WORKLOADS.items():
         x, ids, esc, mask, _, _ = synth.make_activations(spec)
         d = oracle.dims_of(spec.T, spec.H, spec.I, spec.K, spec.E_g, spec.I_s, spec.ep_size, spec.ep_rank)
         got = oracle.route(d, ids, mask)

@@ -26,7 +26,7 @@ def spec(**kw):
 
 
 CASES = {
-    "tiny": synth.CONFIGS[0],
+    "tiny": synth.WORKLOADS[0],
     "t0": spec(T=0),
     "t1_shared": spec(T=1, I_s=512),
     "all_masked": spec(T=9, active=0, I_s=256),
