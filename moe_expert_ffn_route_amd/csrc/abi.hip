@@ -61,8 +61,8 @@ Layout make_layout(const moe_w8a8_dims_t *d) {
     L.chunks = o;      o = up256(o + sizeof(int4) * L.max_chunks);
     L.q_tok = o;       o = up256(o + T * H);
     L.xs_tok = o;      o = up256(o + sizeof(float) * T);
-    L.q_x = o;         o = up256(o + R * H);
-    L.xs = o;          o = up256(o + sizeof(float) * R);
+    L.q_sm = o;        o = up256(o + R * H);  // per-pair rows [0, T*K), per-token shared rows after
+    L.s_sm = o;        o = up256(o + sizeof(float) * R);
     L.h = o;           o = up256(o + sizeof(float) * R * L.imax);
     L.q_h = o;         o = up256(o + R * L.imax);
     L.hs = o;          o = up256(o + sizeof(float) * R);
@@ -158,7 +158,6 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
     // for groups without smooth scales, per grouped row otherwise
     const bool routed_tok = expert_smooth_scales == nullptr;
     const bool shared_tok = shared && share_smooth_scales == nullptr;
-    const bool any_smooth = !routed_tok || (shared && !shared_tok);
 
     RouteArgs ra;
     ra.ids = expert_ids;
@@ -185,36 +184,41 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
     tq.T = T;
     tq.H = H;
     tq.eps = d->amax_eps;
-    tq.q = (T > 0 && (routed_tok || shared_tok)) ? reinterpret_cast<int8_t *>(ws + L.q_tok) : nullptr;
-    tq.scale = reinterpret_cast<float *>(ws + L.xs_tok);
+    tq.ids = expert_ids;
+    tq.K = K;
+    tq.E_g = d->moe_expert_num;
+    tq.E_loc = E;
+    tq.base = ra.base;
+    tq.q_tok = (T > 0 && (routed_tok || shared_tok)) ? reinterpret_cast<int8_t *>(ws + L.q_tok) : nullptr;
+    tq.s_tok = reinterpret_cast<float *>(ws + L.xs_tok);
+    tq.smooth = T > 0 ? expert_smooth_scales : nullptr;
+    tq.share_smooth = T > 0 && shared ? share_smooth_scales : nullptr;
+    tq.q_sm = reinterpret_cast<int8_t *>(ws + L.q_sm);
+    tq.s_sm = reinterpret_cast<float *>(ws + L.s_sm);
     if (launch_route_quant(ra, tq, s) != hipSuccess || !mark(1)) return MOE_ERR_HIP;
 
+    // GEMM1's activation rows: per token (q_tok, index row_token) or per
+    // (token, expert) pair (q_sm, index sorted_pair) for routed rows; per
+    // token, plain (q_tok) or with the shared smooth scales (q_sm rows T*K..),
+    // for shared rows
+    auto gemm1_inputs = [&] {
+        GemmArgs g = {};
+        const size_t sh_row0 = static_cast<size_t>(T) * K;
+        g.a_stride = H;
+        g.H = H;
+        g.E_loc = E;
+        g.row_token = ra.row_token;
+        g.A_r = routed_tok ? tq.q_tok : tq.q_sm;
+        g.a_scale_r = routed_tok ? tq.s_tok : tq.s_sm;
+        g.idx_r = routed_tok ? ra.row_token : ra.sorted_pair;
+        g.A_s = shared_tok ? tq.q_tok : tq.q_sm + sh_row0 * H;
+        g.a_scale_s = shared_tok ? tq.s_tok : tq.s_sm + sh_row0;
+        return g;
+    };
     if (T > 0) {
-        QuantArgs qa;
-        qa.x = static_cast<const uint16_t *>(x);
-        qa.row_token = ra.row_token;
-        qa.row_group = ra.row_group;
-        qa.meta = meta;
-        qa.smooth = expert_smooth_scales;
-        qa.share_smooth = share_smooth_scales;
-        qa.E_loc = E;
-        qa.H = H;
-        qa.has_shared = shared;
-        qa.rows_max = L.rows_max;
-        qa.eps = d->amax_eps;
-        qa.q = reinterpret_cast<int8_t *>(ws + L.q_x);
-        qa.scale = reinterpret_cast<float *>(ws + L.xs);
-        if (any_smooth && launch_quant(qa, s) != hipSuccess) return MOE_ERR_HIP;
-        if (!mark(2)) return MOE_ERR_HIP;
+        if (!mark(2)) return MOE_ERR_HIP;  // (stage 2, a separate smooth quantisation, no longer exists)
 
-        GemmArgs g1 = {};
-        g1.A = qa.q;
-        g1.a_stride = H;
-        g1.a_scale = qa.scale;
-        g1.A_tok = tq.q;
-        g1.a_scale_tok = tq.scale;
-        g1.routed_by_token = routed_tok;
-        g1.shared_by_token = shared_tok;
+        GemmArgs g1 = gemm1_inputs();
         g1.W = gmm1_weight;
         g1.Ws = gmm1_weight_scale;
         g1.W_sh = share_gmm1_weight;
@@ -258,7 +262,6 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         if (launch_requant(rq, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;
 
         GemmArgs g2 = g1;
-        g2.routed_by_token = g2.shared_by_token = 0;
         g2.A = rq.q;
         g2.a_stride = L.imax;
         g2.a_scale = rq.scale;
@@ -318,10 +321,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         {D.hs, L.hs, sizeof(float) * R},
     };
     if ((D.q_x || D.xs) &&
-        launch_dbg_gather(reinterpret_cast<int8_t *>(ws + L.q_tok), reinterpret_cast<float *>(ws + L.xs_tok),
-                          reinterpret_cast<int8_t *>(ws + L.q_x), reinterpret_cast<float *>(ws + L.xs),
-                          I32(L.row_token), I32(L.row_group), meta, E, routed_tok, shared_tok, shared, H, L.rows_max,
-                          D.q_x, D.xs, s) != hipSuccess)
+        launch_dbg_gather(gemm1_inputs(), I32(L.row_group), meta, shared, L.rows_max, D.q_x, D.xs, s) != hipSuccess)
         return MOE_ERR_HIP;
     for (const Copy &c : copies)
         if (c.dst && c.bytes && hipMemcpyAsync(c.dst, ws + c.off, c.bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)

@@ -114,19 +114,21 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
 
     // (1) independent small loads: token of each A row, epilogue rows' tokens
     //     and the output channels' weight scales.
-    // GEMM1 rows of groups without smooth scales read the per-token rows of
-    // x (quantised once per token); every other A row is the grouped row.
-    // Lanes past the chunk's last row read that last row and are zeroed
-    // before the MFMA, so no load sits in a divergent branch.
-    const bool by_tok = KIND == 1 && (routed ? a.routed_by_token : a.shared_by_token);
-    const bool need_tok = by_tok || (KIND == 2 && !routed);
-    const int8_t *Abase = by_tok ? a.A_tok : a.A;
-    const float *Ascale = by_tok ? a.a_scale_tok : a.a_scale;
+    // GEMM1 row r reads its activations through an index (routed rows: the
+    // token's or the (token, expert) pair's quantised row; shared rows: the
+    // token's); GEMM2 row r reads row r. Lanes past the chunk's last row read
+    // that last row and are zeroed before the MFMA, so no load sits in a
+    // divergent branch.
+    const int32_t *aidx = KIND == 1 ? (routed ? a.idx_r : a.row_token) : nullptr;
+    const bool need_tok = KIND == 1 || !routed;
+    const int32_t *tidx = KIND == 1 ? aidx : a.row_token;  // epilogue rows: scale index / share_output row
+    const int8_t *Abase = KIND == 1 ? (routed ? a.A_r : a.A_s) : a.A;
+    const float *Ascale = KIND == 1 ? (routed ? a.a_scale_r : a.a_scale_s) : a.a_scale;
     int arow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int lr = min(mt * kTileN + r16, rows - 1);
-        arow[mt] = by_tok ? a.row_token[row0 + lr] : row0 + lr;
+        arow[mt] = KIND == 1 ? aidx[row0 + lr] : row0 + lr;
     }
     // A thread's output column is the same in every row tile (kThreads is a
     // multiple of kCols).
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) {
         rrow[e] = row0 + min(min(tid + e * kThreads, kElems - 1) / kCols, rows - 1);
-        rtok[e] = need_tok ? a.row_token[rrow[e]] : 0;
+        rtok[e] = need_tok ? tidx[rrow[e]] : 0;
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
     // (3) loads that depend on (1): the first row tile's row scales
     float rsc[kEpt];
 #pragma unroll
-    for (int e = 0; e < kEpt; ++e) rsc[e] = Ascale[by_tok ? rtok[e] : rrow[e]];
+    for (int e = 0; e < kEpt; ++e) rsc[e] = Ascale[KIND == 1 ? rtok[e] : rrow[e]];
     __builtin_amdgcn_sched_barrier(0);
 
     v4i acc0[MT], acc1[MT];
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
             const int lr = mt * kTileN + m;
             if (idx < kElems && lr < rows) {
                 const int r = row0 + lr;
-                const float rs = mt == 0 ? rsc[e] : Ascale[by_tok ? a.row_token[r] : r];
+                const float rs = mt == 0 ? rsc[e] : Ascale[KIND == 1 ? aidx[r] : r];
                 if (KIND == 1) {
                     int ag = 0, au = 0;
 #pragma unroll

@@ -48,7 +48,9 @@ struct WideItem {
     int rowA, rowB;           // first weight row (= output channel) of the first pair
     int jcol;                 // channels from one tile pair to the next
     int row0, rows, S, inter;
-    bool routed, by_tok, need_tok;
+    const int32_t *aidx;        // GEMM1: where row r's activations are (null: row r)
+    const int32_t *tidx;        // epilogue rows' scale index / share_output row (null: none)
+    bool routed;
 };
 
 // The K loop and epilogue for MTA active row tiles (the chunk's rows, rounded
@@ -87,7 +89,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
     for (int j = 0; j < kUpw; ++j) {
         const int u = wave + j * NW;
         const int lr = min(u * kRpi + lane / kLpr, rows - 1);  // rows past the chunk repeat its last row
-        const int ar = it.by_tok ? a.row_token[row0 + lr] : row0 + lr;
+        const int ar = it.aidx ? it.aidx[row0 + lr] : row0 + lr;
         asrc[j] = it.Abase + static_cast<size_t>(ar) * a.a_stride + seg * 16;
     }
     // a token indexes the row scale of per-token rows and the share_output
@@ -101,7 +103,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int lr = min(mt * kTileN + 4 * kg + i, rows - 1);
-                otok[mt][i] = it.need_tok ? a.row_token[row0 + lr] : 0;
+                otok[mt][i] = it.tidx ? it.tidx[row0 + lr] : 0;
             }
     };
     auto load_scales = [&](int mt0, int mt1) {
@@ -109,7 +111,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
         for (int mt = mt0; mt < mt1; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                rsc[mt][i] = it.Ascale[it.by_tok ? otok[mt][i] : row0 + min(mt * kTileN + 4 * kg + i, rows - 1)];
+                rsc[mt][i] = it.Ascale[it.aidx ? otok[mt][i] : row0 + min(mt * kTileN + 4 * kg + i, rows - 1)];
     };
     if (!kLateRows) load_tokens(0, kER);
     float ws0[NT], ws1[NT];
@@ -341,10 +343,13 @@ __device__ __forceinline__ bool decode_item(const GemmArgs &a, const int4 *chunk
         it.wlane = (lane & 15) * k_dim + (lane >> 4) * 16;
         it.wstep = 64;
     }
-    it.by_tok = KIND == 1 && (it.routed ? a.routed_by_token : a.shared_by_token);
-    it.need_tok = it.by_tok || (KIND == 2 && !it.routed);
-    it.Abase = it.by_tok ? a.A_tok : a.A;
-    it.Ascale = it.by_tok ? a.a_scale_tok : a.a_scale;
+    // GEMM1 row r reads its activations through an index (routed rows: the
+    // token's or the (token, expert) pair's quantised row; shared rows: the
+    // token's); GEMM2 row r reads row r
+    it.aidx = KIND == 1 ? (it.routed ? a.idx_r : a.row_token) : nullptr;
+    it.tidx = KIND == 1 ? it.aidx : (it.routed ? nullptr : a.row_token);
+    it.Abase = KIND == 1 ? (it.routed ? a.A_r : a.A_s) : a.A;
+    it.Ascale = KIND == 1 ? (it.routed ? a.a_scale_r : a.a_scale_s) : a.a_scale;
     return true;
 }
 

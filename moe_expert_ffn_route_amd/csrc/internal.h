@@ -53,7 +53,7 @@ struct Layout {
     int chunk_rows;  // rows per GEMM work item
     int imax;        // max(I, I_s)
     size_t meta, offsets, sorted_pair, row_of_pair, row_token, row_group, chunks;
-    size_t q_tok, xs_tok, q_x, xs, h, q_h, hs, z, total;
+    size_t q_tok, xs_tok, q_sm, s_sm, h, q_h, hs, z, total;
 };
 
 struct RouteArgs {
@@ -72,28 +72,25 @@ struct RouteArgs {
     int32_t *dbg_shared_token;  // [T] or null
 };
 
-// per-token quantisation of x (groups without smooth scales read these rows)
+// Quantisation of x in the routing launch, which needs no routing result:
+//   - per token (x[t]) into q_tok, for groups without smooth scales;
+//   - per (token, expert) pair p = t * K + k (x[t] * smooth[e]) into rows
+//     [0, T*K) of q_sm, for routed rows when expert smooth scales are given
+//     (pairs that are not kept are skipped);
+//   - per token (x[t] * share_smooth) into rows [T*K, T*K + T) of q_sm, for
+//     the shared expert when its smooth scales are given.
 struct TokQuantArgs {
     const uint16_t *x;     // bf16 [T, H]
     const uint8_t *mask;   // [T] or null
-    int T, H;
+    const int32_t *ids;    // [T, K] global expert ids
+    int T, K, H, E_g, E_loc, base;
     float eps;
-    int8_t *q;             // [T, H]; null = not needed
-    float *scale;          // [T]
-};
-
-// per-grouped-row quantisation of x * smooth (rows of groups with smooth scales)
-struct QuantArgs {
-    const uint16_t *x;       // bf16 [T, H]
-    const int32_t *row_token;
-    const int32_t *row_group;
-    const int32_t *meta;
+    int8_t *q_tok;         // [T, H]; null = not needed
+    float *s_tok;          // [T]
     const float *smooth;        // [E_loc, H] or null
     const float *share_smooth;  // [H] or null
-    int E_loc, H, has_shared, rows_max;
-    float eps;
-    int8_t *q;    // [rows_max, H]
-    float *scale; // [rows_max]
+    int8_t *q_sm;          // [T*K + T, H]
+    float *s_sm;           // [T*K + T]
 };
 
 struct RequantArgs {
@@ -108,14 +105,16 @@ struct RequantArgs {
 };
 
 struct GemmArgs {
-    // activations: grouped int8 rows and their per-row scale ...
+    // GEMM2 activations: grouped int8 rows (row r of A) and their scales
     const int8_t *A;
     int a_stride;
     const float *a_scale;
-    // ... or, for groups flagged here, per-token rows picked by row_token
-    const int8_t *A_tok;
-    const float *a_scale_tok;
-    int routed_by_token, shared_by_token;
+    // GEMM1 activations: routed row r reads row idx_r[r] of A_r (the token's
+    // row of q_tok, or the pair's row of q_sm), a shared row reads row
+    // row_token[r] of A_s
+    const int8_t *A_r, *A_s;
+    const float *a_scale_r, *a_scale_s;
+    const int32_t *idx_r;
     // weights [E_loc, N, K] routed, [N, K] shared, and per-output-channel scales
     const int8_t *W;
     const float *Ws;
@@ -149,7 +148,6 @@ struct CombineArgs {
 };
 
 hipError_t launch_route_quant(const RouteArgs &a, const TokQuantArgs &q, hipStream_t s);
-hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
 hipError_t launch_requant(const RequantArgs &a, hipStream_t s);
 // ev_start / ev_stop (may be null) are bound to the kernel launch itself.
 hipError_t launch_gemm1(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
@@ -165,11 +163,9 @@ hipError_t launch_gemm2_wide(const GemmArgs &a, int max_chunks, int k_dim, hipSt
 int wide_tile_pairs(int mt);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_pack(const int8_t *src, int8_t *dst, int64_t groups, int n, int k, hipStream_t s);
-// debug only: expand per-token rows into the grouped-row q_x / xs dump
-hipError_t launch_dbg_gather(const int8_t *q_tok, const float *xs_tok, const int8_t *q_rows, const float *xs_rows,
-                             const int32_t *row_token, const int32_t *row_group, const int32_t *meta, int E_loc,
-                             int routed_by_token, int shared_by_token, int has_shared, int H, int rows_max,
-                             int8_t *dst_q, float *dst_xs, hipStream_t s);
+// debug only: the GEMM1 input rows of every grouped row (q_x / xs dump)
+hipError_t launch_dbg_gather(const GemmArgs &g1, const int32_t *row_group, const int32_t *meta, int has_shared,
+                             int rows_max, int8_t *dst_q, float *dst_xs, hipStream_t s);
 
 // bf16 helpers (round to nearest even)
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -221,11 +221,54 @@ __device__ void route_block(const RouteArgs &a) {
     }
 }
 
-constexpr int kTokQuantSlots = kRouteThreads / kTPR;  // tokens quantised per block
+constexpr int kTokQuantSlots = kRouteThreads / kTPR;  // rows quantised per block
 
-// Block 0 routes; blocks 1.. quantise x per token (groups without smooth
-// scales read these rows, FusedDeepMoE sec. 4.1 quantises in dispatch). The
-// two jobs are independent, so one launch runs both side by side.
+// Rows the quantisation blocks of the routing launch work on: the tokens (when
+// some group reads plain per-token rows), then the (token, expert) pairs (when
+// expert smooth scales are given), then the tokens again (when the shared
+// expert has smooth scales).
+__device__ __forceinline__ void quant_unit(const TokQuantArgs &q, int u, int slot, int tr, float *s_part) {
+    const int n_tok = q.q_tok ? q.T : 0;
+    const int n_pair = q.smooth ? q.T * q.K : 0;
+    const uint16_t *src = q.x;
+    const float *sm = nullptr;
+    int8_t *dst = nullptr;
+    float *scale = nullptr;
+    bool active = false;
+    if (u < n_tok) {
+        active = !q.mask || q.mask[u];
+        src += static_cast<size_t>(u) * q.H;
+        dst = q.q_tok + static_cast<size_t>(u) * q.H;
+        scale = q.s_tok + u;
+    } else if (u < n_tok + n_pair) {
+        const int p = u - n_tok, t = p / q.K;
+        const int g = q.ids[p];
+        const int e = g - q.base;
+        // only kept pairs are read later: active token, id in range, local expert
+        active = (!q.mask || q.mask[t]) && g >= 0 && g < q.E_g && e >= 0 && e < q.E_loc;
+        src += static_cast<size_t>(t) * q.H;
+        sm = q.smooth + static_cast<size_t>(active ? e : 0) * q.H;
+        dst = q.q_sm + static_cast<size_t>(p) * q.H;
+        scale = q.s_sm + p;
+    } else {
+        const int t = u - n_tok - n_pair;
+        active = t < q.T && (!q.mask || q.mask[t]);
+        src += static_cast<size_t>(active ? t : 0) * q.H;
+        sm = q.share_smooth;
+        const size_t row = static_cast<size_t>(q.T) * q.K + (active ? t : 0);
+        dst = q.q_sm + row * q.H;
+        scale = q.s_sm + row;
+    }
+    quant_bf16_row(src, sm, q.H, q.eps, dst, scale, active, slot, tr, s_part);
+}
+
+__device__ __forceinline__ int quant_units(const TokQuantArgs &q) {
+    return (q.q_tok ? q.T : 0) + (q.smooth ? q.T * q.K : 0) + (q.share_smooth ? q.T : 0);
+}
+
+// Block 0 routes; blocks 1.. quantise rows of x (FusedDeepMoE sec. 4.1
+// quantises in dispatch). Neither job needs the other's result, so one launch
+// runs both side by side.
 __global__ __launch_bounds__(kRouteThreads) void route_quant_kernel(RouteArgs a, TokQuantArgs q) {
     if (blockIdx.x == 0) {
         route_block(a);
@@ -233,16 +276,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_quant_kernel(RouteArgs a,
     }
     __shared__ float s_part[kTokQuantSlots * (kTPR / kWave)];
     const int slot = threadIdx.x / kTPR, tr = threadIdx.x % kTPR;
-    const int t = (blockIdx.x - 1) * kTokQuantSlots + slot;
-    const bool active = t < q.T && (!q.mask || q.mask[t]);
-    const size_t tt = active ? t : 0;
-    quant_bf16_row(q.x + tt * q.H, nullptr, q.H, q.eps, q.q + tt * q.H, q.scale + tt, active, slot, tr, s_part);
+    const int u = (blockIdx.x - 1) * kTokQuantSlots + slot;
+    // units past the end take part in the block's barrier only
+    if (u < quant_units(q)) {
+        quant_unit(q, u, slot, tr, s_part);
+    } else {
+        quant_bf16_row(q.x, nullptr, q.H, q.eps, nullptr, nullptr, false, slot, tr, s_part);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_route_quant(const RouteArgs &a, const TokQuantArgs &q, hipStream_t s) {
-    const int qblocks = q.q ? (q.T + kTokQuantSlots - 1) / kTokQuantSlots : 0;
+    const int units = (q.q_tok ? q.T : 0) + (q.smooth ? q.T * q.K : 0) + (q.share_smooth ? q.T : 0);
+    const int qblocks = (units + kTokQuantSlots - 1) / kTokQuantSlots;
     hipLaunchKernelGGL(route_quant_kernel, dim3(1 + qblocks), dim3(kRouteThreads), 0, s, a, q);
     return hipGetLastError();
 }
