@@ -44,6 +44,60 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence in hip_runtime_api.h
+_hip_rt = None
+
+
+def hip_runtime() -> ctypes.CDLL:
+    """The HIP runtime torch has loaded (the same library instance, so its
+    events and streams are shared with torch and libmoe_w8a8)."""
+    global _hip_rt
+    if _hip_rt is None:
+        torch.cuda.init()
+        with open("/proc/self/maps") as f:
+            paths = [ln.split()[-1] for ln in f if "libamdhip64" in ln]
+        if not paths:
+            raise RuntimeError("the HIP runtime is not loaded")
+        _hip_rt = ctypes.CDLL(paths[0])
+        P = ctypes.c_void_p
+        _hip_rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(P), ctypes.c_uint]
+        _hip_rt.hipEventRecord.argtypes = [P, P]
+        _hip_rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+        _hip_rt.hipEventDestroy.argtypes = [P]
+    return _hip_rt
+
+
+class TimingEvent:
+    """A HIP event used only for timing, created with hipEventDisableSystemFence
+    so that recording it (or binding it to a kernel launch) adds no
+    system-scope cache writeback and invalidation to the stream. The host reads
+    results only after a device synchronisation, so nothing relies on the
+    fence. Offers what this file uses of torch.cuda.Event: record(stream),
+    elapsed_time(end) in ms and the raw handle `cuda_event`."""
+
+    def __init__(self, fence_free: bool = True):
+        rt = hip_runtime()
+        h = ctypes.c_void_p()
+        flags = HIP_EVENT_DISABLE_SYSTEM_FENCE if fence_free else 0
+        if rt.hipEventCreateWithFlags(ctypes.byref(h), flags) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.cuda_event = h.value
+
+    def record(self, stream):
+        if hip_runtime().hipEventRecord(self.cuda_event, stream.cuda_stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        ms = ctypes.c_float()
+        if hip_runtime().hipEventElapsedTime(ctypes.byref(ms), self.cuda_event, end.cuda_event) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        if _hip_rt is not None and self.cuda_event:
+            _hip_rt.hipEventDestroy(self.cuda_event)
+
+
 def algorithmic_bytes(case, counts):
     """Bytes the layer must move at least once: every touched expert's weights
     and scales, the shared expert's, the activations in and out."""
@@ -162,6 +216,9 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB 5 times (calibrates HBM byte counters)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step per weight copy into HIP graphs and time their replays")
+    ap.add_argument("--fenced-events", action="store_true",
+                    help="time with default HIP events (each record adds a system-scope cache writeback) "
+                         "instead of events created with hipEventDisableSystemFence")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the GEMM kernel events (GEMM times then come from the "
                          "per-stage pass)")
@@ -203,9 +260,10 @@ def main():
     dims.weight_layout = moe.MOE_WEIGHT_ROW_MAJOR if args.row_major else moe.MOE_WEIGHT_PACKED
     runner = moe.Runner(dims)
     stream = torch.cuda.Stream()
+    fence_free = not args.fenced_events
     n_ev = len(binding.STAGES) + 1
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    kevents = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[TimingEvent(fence_free) for _ in range(n_ev)] for _ in range(args.steps)]
+    kevents = [[TimingEvent(fence_free) for _ in range(4)] for _ in range(args.steps)]
     for evs in events + kevents:
         for e in evs:
             e.record(stream)  # materialise the HIP event handles
@@ -244,8 +302,8 @@ def main():
         torch.cuda.synchronize()
 
     log(f"[bench] timing {args.steps} steps")
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
+    t_start = TimingEvent(fence_free)
+    t_stop = TimingEvent(fence_free)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         t_start.record(stream)
@@ -274,9 +332,10 @@ def main():
     if g1_us is None:
         g1_us = stage_us["gemm1"]
         timing = "marker HIP events between stages (per-stage pass)"
+    timing += ", default event flags" if args.fenced_events else ", hipEventDisableSystemFence"
 
     log("[bench] per-step distribution pass")
-    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    bounds = [TimingEvent(fence_free) for _ in range(args.steps + 1)]
     with torch.cuda.stream(stream):
         bounds[0].record(stream)
         for i in range(args.steps):

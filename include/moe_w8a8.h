@@ -107,10 +107,11 @@ typedef struct {
     float   *hs;            /* [R]     their per-row dequant scale             */
     int32_t *acc2;          /* [R, H]  GEMM2 int32 accumulators                */
     uint16_t *z;            /* [R, H]  bf16 GEMM2 output rows                  */
-    void   **stage_events;  /* [7] caller-created hipEvent_t (NULL entries are
+    void   **stage_events;  /* [6] caller-created hipEvent_t (NULL entries are
                                skipped), recorded on the stream before routing
-                               and after each stage: route, quant, GEMM1,
-                               requant, GEMM2, combine                         */
+                               and after each stage: routing with the
+                               quantisation of x, GEMM1, requant, GEMM2,
+                               combine                                        */
     void   **kernel_events; /* [4] caller-created hipEvent_t (NULL entries are
                                skipped) bound to the GEMM kernels themselves
                                (hipExtLaunchKernel): start and end of the GEMM1

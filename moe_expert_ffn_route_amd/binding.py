@@ -43,7 +43,7 @@ class Dims(ctypes.Structure):
 
 DEBUG_FIELDS = ("sorted_pair", "row_of_pair", "group_offset", "shared_token", "num_rows", "q_x", "xs", "acc1",
                 "h", "q_h", "hs", "acc2", "z", "stage_events", "kernel_events")
-STAGES = ("route_quant", "smooth_quant", "gemm1", "requant", "gemm2", "combine")
+STAGES = ("route_quant", "gemm1", "requant", "gemm2", "combine")
 
 
 class Debug(ctypes.Structure):

@@ -216,8 +216,6 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         return g;
     };
     if (T > 0) {
-        if (!mark(2)) return MOE_ERR_HIP;  // (stage 2, a separate smooth quantisation, no longer exists)
-
         GemmArgs g1 = gemm1_inputs();
         g1.W = gmm1_weight;
         g1.Ws = gmm1_weight_scale;
@@ -243,7 +241,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g1.dbg_acc = D.acc1;
         const hipError_t e1 = wide ? launch_gemm1_wide(g1, L.max_chunks, s, kev(0), kev(1))
                                    : launch_gemm1(g1, L.max_chunks, s, kev(0), kev(1));
-        if (e1 != hipSuccess || !mark(3)) return MOE_ERR_HIP;
+        if (e1 != hipSuccess || !mark(2)) return MOE_ERR_HIP;
 
         RequantArgs rq;
         rq.h = g1.h;
@@ -259,7 +257,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         rq.eps = d->amax_eps;
         rq.q = reinterpret_cast<int8_t *>(ws + L.q_h);
         rq.scale = reinterpret_cast<float *>(ws + L.hs);
-        if (launch_requant(rq, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;
+        if (launch_requant(rq, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
 
         GemmArgs g2 = g1;
         g2.A = rq.q;
@@ -289,7 +287,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
             g2.g_hi = E + 1;
             if (gemm2(d->share_inter, nullptr, kev(3)) != hipSuccess) return MOE_ERR_HIP;
         }
-        if (!mark(5)) return MOE_ERR_HIP;
+        if (!mark(4)) return MOE_ERR_HIP;
 
         CombineArgs ca;
         ca.z = g2.z;
@@ -302,9 +300,9 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         ca.has_shared = shared;
         ca.out = static_cast<uint16_t *>(output);
         ca.share_out = static_cast<uint16_t *>(share_output);
-        if (launch_combine(ca, s) != hipSuccess || !mark(6)) return MOE_ERR_HIP;
+        if (launch_combine(ca, s) != hipSuccess || !mark(5)) return MOE_ERR_HIP;
     } else {
-        for (int i = 2; i < 7; ++i)
+        for (int i = 2; i < 6; ++i)
             if (!mark(i)) return MOE_ERR_HIP;
     }
 
