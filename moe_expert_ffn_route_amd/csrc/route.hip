@@ -48,6 +48,14 @@ __device__ int block_exclusive_scan(int v, int *s_tmp, int *total) {
 // Pairs held in registers by the routing block (rounds of kRouteThreads);
 // enough for every pair at T = 512, top-8.
 constexpr int kRouteRegRounds = 4;
+// Routed rows whose (expert, pair) entries are collected in LDS and written
+// out in row order, as coalesced stores, when P fits (a store per row at its
+// scattered position would cost the one routing workgroup a cache-line write
+// per row and array). Entry = expert << kStagePairBits | pair.
+constexpr int kRouteStage = 4096;
+constexpr int kStagePairBits = 20;
+static_assert(static_cast<long>(kMaxTokens) * kMaxTopK <= (1l << kStagePairBits), "pair ids fit the entry");
+static_assert(kMaxLocalExperts <= (1 << (31 - kStagePairBits)), "expert ids fit the entry");
 constexpr int kPairDropped = -1;  // inactive token or expert of another rank
 constexpr int kPairBad = -2;      // expert id outside [0, E_g)
 
@@ -71,6 +79,7 @@ __device__ void route_block(const RouteArgs &a) {
     __shared__ int s_tmp[kRouteWaves];
     __shared__ int s_bad;
     __shared__ int s_nch;  // chunks emitted so far
+    __shared__ uint32_t s_stage[kRouteStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -126,6 +135,7 @@ __device__ void route_block(const RouteArgs &a) {
     }
     __syncthreads();
     const int P = s_off[E];
+    const bool staged = P <= kRouteStage;
 
     // 3. stable placement, one round of 1024 pairs at a time
     auto place = [&](int base, int e) {
@@ -149,10 +159,14 @@ __device__ void route_block(const RouteArgs &a) {
                 int pre = 0;
                 for (int w = 0; w < wave; ++w) pre += s_tbl[w][e];
                 const int pos = s_off[e] + s_run[e] + pre + rank;
-                a.sorted_pair[pos] = p;
                 a.row_of_pair[p] = pos;
-                a.row_token[pos] = p / a.K;
-                a.row_group[pos] = e;
+                if (staged) {
+                    s_stage[pos] = (static_cast<uint32_t>(e) << kStagePairBits) | static_cast<uint32_t>(p);
+                } else {
+                    a.sorted_pair[pos] = p;
+                    a.row_token[pos] = p / a.K;
+                    a.row_group[pos] = e;
+                }
             } else {
                 a.row_of_pair[p] = -1;
             }
@@ -169,6 +183,15 @@ __device__ void route_block(const RouteArgs &a) {
         if (j * kRouteThreads < TK) place(j * kRouteThreads, e_reg[j]);  // uniform
     for (int base = kRouteRegRounds * kRouteThreads; base < TK; base += kRouteThreads)
         place(base, base + tid < TK ? classify_pair(a, base + tid) : kPairDropped);
+    if (staged) {  // place() ends with a barrier, so every entry is in LDS
+        for (int r = tid; r < P; r += kRouteThreads) {
+            const uint32_t v = s_stage[r];
+            const int p = static_cast<int>(v & ((1u << kStagePairBits) - 1u));
+            a.sorted_pair[r] = p;
+            a.row_token[r] = p / a.K;
+            a.row_group[r] = static_cast<int>(v >> kStagePairBits);
+        }
+    }
 
     // 4. shared-expert rows: active tokens in token order, after the routed rows
     int t_act = 0;
