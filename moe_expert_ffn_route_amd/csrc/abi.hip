@@ -230,8 +230,10 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g1.g_hi = E + 1;
         g1.packed = d->weight_layout == MOE_WEIGHT_PACKED;
         g1.mt = L.chunk_rows / kTileN;
-        const bool wide = g1.mt > 1;
-        const int nw = wide ? wide_tile_pairs(g1.mt) : 1;  // tile pairs per work item
+        // three kernels by chunk size: decode (gemm.hip), wide (gemm_wide.hip)
+        // and tall (gemm_tall.hip) work items
+        const bool tall = g1.mt == kTallTiles, wide = g1.mt == kWideTiles;
+        const int nw = tall ? kTallPairs : wide ? wide_tile_pairs() : 1;  // tile pairs per work item
         g1.n_tiles = L.imax / kTileN / nw;
         g1.chunks = ra.chunks;
         g1.count_word = kMetaChunks;
@@ -239,8 +241,9 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g1.row_token = ra.row_token;
         g1.h = reinterpret_cast<float *>(ws + L.h);
         g1.dbg_acc = D.acc1;
-        const hipError_t e1 = wide ? launch_gemm1_wide(g1, L.max_chunks, s, kev(0), kev(1))
-                                   : launch_gemm1(g1, L.max_chunks, s, kev(0), kev(1));
+        const hipError_t e1 = tall   ? launch_gemm1_tall(g1, L.max_chunks, s, kev(0), kev(1))
+                              : wide ? launch_gemm1_wide(g1, L.max_chunks, s, kev(0), kev(1))
+                                     : launch_gemm1(g1, L.max_chunks, s, kev(0), kev(1));
         if (e1 != hipSuccess || !mark(2)) return MOE_ERR_HIP;
 
         RequantArgs rq;
@@ -275,8 +278,9 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g2.dbg_z = D.z;
         // the contraction length of GEMM2 is the group's intermediate size
         auto gemm2 = [&](int k_dim, hipEvent_t e0, hipEvent_t e1) {
-            return wide ? launch_gemm2_wide(g2, L.max_chunks, k_dim, s, e0, e1)
-                        : launch_gemm2(g2, L.max_chunks, k_dim, s, e0, e1);
+            return tall   ? launch_gemm2_tall(g2, L.max_chunks, k_dim, s, e0, e1)
+                   : wide ? launch_gemm2_wide(g2, L.max_chunks, k_dim, s, e0, e1)
+                          : launch_gemm2(g2, L.max_chunks, k_dim, s, e0, e1);
         };
         if (!shared || d->share_inter == d->inter) {
             if (gemm2(d->inter, kev(2), kev(3)) != hipSuccess) return MOE_ERR_HIP;

@@ -1,0 +1,310 @@
+// Grouped INT8 GEMMs for experts of hundreds of rows (tall work items), with
+// the fused epilogues of the other GEMM kernels:
+//   GEMM1 ("FusedDeepMoE Kernel 深度分析报告" sec. 3.3 / 6.1): gate and up
+//     accumulators of one row and channel meet in one lane, which applies
+//     y = (float(acc) * w1s[n]) * xs[r] to both and writes
+//     h = (y_g / (1 + exp(-y_g))) * y_u as fp32;
+//   GEMM2 (sec. 3.4 / 6.2): z = bf16((float(acc) * w2s[n]) * hs[r]), to the
+//     routed row buffer or, for the shared expert, straight to share_output.
+//
+// When an expert holds hundreds of rows its weights are re-read by every
+// chunk of rows, and the GEMM can be fed from on-chip memory at the MFMA
+// rate. A work item is a 256-row chunk times 8 pairs of 16-row weight tiles
+// (GEMM1: 128 gate tiles' channels with their up tiles; GEMM2: 256 output
+// channels). Its 16 waves form a 4 x 4 grid: wave (wm, wn) multiplies rows
+// [64 wm, 64 wm + 64) by the 2 tile pairs [2 wn, 2 wn + 2), so it holds
+// 4 x 4 MFMA tiles of int32 sums and four waves share a SIMD. Both operands
+// go through LDS one 64-byte K step (a stage) at a time, double buffered,
+// with the global loads two stages ahead: each stage, a thread issues its
+// 16-byte shares of stage s + 2 into registers, the waves run the stage's
+// MFMAs from LDS, and the thread writes its (already loaded) shares of stage
+// s + 1 to the other buffer; one workgroup barrier per stage publishes it.
+// Every activation fragment read from LDS feeds 4 MFMAs and every weight
+// fragment 4.
+//
+// LDS stage layout, all in MFMA lane order (1 KB blocks, lane l at byte
+// 16 l: row l % 16, bytes 16 (l / 16) .. +16 of the K step): the chunk's 16
+// activation row tiles, then the block's 16 weight tiles as (pair, half)
+// blocks. Lane-ordered reads and writes are free of bank conflicts.
+#include "internal.h"
+
+#include <hip/hip_ext.h>
+
+namespace moe {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kTWaves = 16;                         // a grid of kTWM (rows) x kTWN (weight tiles)
+constexpr int kTThreads = kTWaves * kWave;
+constexpr int kTWN = 4;
+constexpr int kTWM = kTWaves / kTWN;
+constexpr int kTMT = kChunkRowsTall / kTileN / kTWM;  // 16-row tiles per wave
+constexpr int kTQ = 2;                              // tile pairs per wave
+constexpr int kTPairs = kTWN * kTQ;                 // tile pairs per block
+constexpr int kTSteps = 1;                          // 64-byte K steps per stage
+constexpr int kTRowTiles = kChunkRowsTall / kTileN;
+constexpr int kTAStage = kTRowTiles * kTSteps * 1024;
+constexpr int kTWStage = 2 * kTPairs * kTSteps * 1024;
+constexpr int kTStage = kTAStage + kTWStage;
+constexpr int kTLoads = kTAStage / 1024 / kTWaves;  // 1 KB blocks per operand, wave and stage
+static_assert(kTRowTiles == kTWM * kTMT, "a chunk is kTWM waves' rows");
+static_assert(kTPairs == kTallPairs, "the host sizes the grid with kTallPairs");
+static_assert(kTAStage == kTLoads * kTWaves * 1024 && kTWStage == kTLoads * kTWaves * 1024,
+              "a stage is kTLoads blocks per operand and wave");
+
+__device__ __forceinline__ v4i ld16(const int8_t *p) { return *reinterpret_cast<const v4i *>(p); }
+__device__ __forceinline__ v4i ld16_stream(const int8_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+}
+
+template <int KIND, bool PACKED>
+__global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int k_dim) {
+    __shared__ __attribute__((aligned(16))) int8_t s_b0[kTStage];
+    __shared__ __attribute__((aligned(16))) int8_t s_b1[kTStage];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave % kTWM, wn = wave / kTWM;
+    const int r16 = lane & 15, kg = lane >> 4;
+
+    // Work item = (chunk, group of 8 tile pairs), linear in blockIdx; a
+    // group of several chunks puts the chunks of one N group 8 blocks apart
+    // (same XCD, in flight together: the weights come from HBM once).
+    int c = blockIdx.x / a.n_tiles;
+    int nt = blockIdx.x % a.n_tiles;
+    int4 ch = a.chunks[c];  // c < max_chunks: inside the chunk list even when unused
+    if (c >= a.meta[a.count_word]) return;
+    const int nch = ch.z >> kChunkCountShift;
+    if (nch > 1 && (a.n_tiles & 7) == 0) {
+        const int c0 = c - ch.w;
+        const int i = blockIdx.x - c0 * a.n_tiles;
+        const int q = i / (8 * nch), rem = i - q * 8 * nch;
+        c = c0 + rem / 8;
+        nt = q * 8 + rem % 8;
+        ch = a.chunks[c];
+    }
+    const int g = ch.x, row0 = ch.y, rows = ch.z & kChunkRowsMask;
+    if (g < a.g_lo || g >= a.g_hi) return;
+    const bool routed = g < a.E_loc;
+    const int inter = routed ? a.I : a.I_s;
+    if (KIND == 1 && nt * kTPairs * kTileN >= inter) return;  // inter is a multiple of 256: all or nothing
+
+    const size_t tile_bytes = static_cast<size_t>(kTileN) * k_dim;
+    const int8_t *W;
+    const float *Ws;
+    if (KIND == 1) {
+        W = routed ? a.W + static_cast<size_t>(g) * 2 * inter * a.H : a.W_sh;
+        Ws = routed ? a.Ws + static_cast<size_t>(g) * 2 * inter : a.Ws_sh;
+    } else {
+        W = routed ? a.W + static_cast<size_t>(g) * a.H * inter : a.W_sh;
+        Ws = routed ? a.Ws + static_cast<size_t>(g) * a.H : a.Ws_sh;
+    }
+    // first weight row (= output channel) of each tile of the block's pair q
+    auto row_a = [&](int q) { return KIND == 1 ? (nt * kTPairs + q) * kTileN : nt * 2 * kTPairs * kTileN + q * 32; };
+    auto row_b = [&](int q) { return KIND == 1 ? inter + row_a(q) : row_a(q) + kTileN; };
+
+    // Global -> LDS copy of a stage: block j = 8 i + wave (i < kTLoads) of
+    // each operand. Activations: block j is row tile j / 2, step j % 2; lane l
+    // reads 16 bytes of row 16 (j / 2) + l % 16 (rows past the chunk repeat
+    // its last row; their outputs are never stored). Weights: block j is
+    // (pair j / 4, half (j / 2) % 2, step j % 2), 1 KB contiguous in the
+    // packed layout.
+    const int wstep = PACKED ? 1024 : 64;  // bytes between K steps of a tile
+    const int wlane = PACKED ? lane * 16 : r16 * k_dim + kg * 16;
+    const int8_t *wsrc[kTLoads];
+    const int8_t *asrc[kTLoads];
+    const int32_t *aidx = KIND == 1 ? (routed ? a.idx_r : a.row_token) : nullptr;
+    const int8_t *Abase = KIND == 1 ? (routed ? a.A_r : a.A_s) : a.A;
+    const float *Ascale = KIND == 1 ? (routed ? a.a_scale_r : a.a_scale_s) : a.a_scale;
+#pragma unroll
+    for (int i = 0; i < kTLoads; ++i) {
+        const int j = i * kTWaves + wave;
+        const int wrow = ((j / kTSteps) & 1) ? row_b(j / (2 * kTSteps)) : row_a(j / (2 * kTSteps));
+        wsrc[i] = W + static_cast<size_t>(wrow / kTileN) * tile_bytes + (j % kTSteps) * wstep + wlane;
+        const int lr = min((j / kTSteps) * kTileN + r16, rows - 1);
+        const int ar = KIND == 1 ? aidx[row0 + lr] : row0 + lr;
+        asrc[i] = Abase + static_cast<size_t>(ar) * a.a_stride + (j % kTSteps) * 64 + kg * 16;
+    }
+    // a stage's share of this thread, held in registers between its global
+    // loads and its LDS stores
+    struct Stage {
+        v4i a[kTLoads], w[kTLoads];
+    };
+    auto gload = [&](Stage &r, int s) {
+#pragma unroll
+        for (int i = 0; i < kTLoads; ++i) {
+            const int8_t *pw = wsrc[i] + static_cast<size_t>(s) * kTSteps * wstep;
+            r.w[i] = PACKED ? ld16_stream(pw) : ld16(pw);
+            r.a[i] = ld16(asrc[i] + s * kTSteps * 64);
+        }
+    };
+    auto lstore = [&](const Stage &r, int8_t *base) {
+#pragma unroll
+        for (int i = 0; i < kTLoads; ++i) {
+            const int j = i * kTWaves + wave;
+            *reinterpret_cast<v4i *>(base + j * 1024 + lane * 16) = r.a[i];
+            *reinterpret_cast<v4i *>(base + kTAStage + j * 1024 + lane * 16) = r.w[i];
+        }
+    };
+
+    v4i acc0[kTMT][kTQ], acc1[kTMT][kTQ];
+#pragma unroll
+    for (int mt = 0; mt < kTMT; ++mt)
+#pragma unroll
+        for (int q = 0; q < kTQ; ++q) {
+            acc0[mt][q] = v4i{0, 0, 0, 0};
+            acc1[mt][q] = v4i{0, 0, 0, 0};
+        }
+    // Stage s: the loads of stage s + 2 go out into the register set that
+    // stage s filled, then the MFMAs of stage s run from LDS, then stage
+    // s + 1 (loaded during stage s - 1) goes from registers to the other LDS
+    // buffer, and a workgroup barrier publishes it. Two register sets and two
+    // LDS buffers alternate, so the loop runs two stages per turn.
+    const int n_stages = k_dim / (kTSteps * 64);  // even: k_dim is a multiple of 256
+    Stage r0, r1;
+    // The loads and stores run unconditionally (the last stages reload the
+    // last stage, which nobody reads), so that the compiler can count the
+    // loads in flight exactly and wait only for the ones a store needs.
+    auto stage = [&](int s, Stage &mine, const Stage &next, const int8_t *cur, int8_t *other) {
+        gload(mine, min(s + 2, n_stages - 1));
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+#pragma unroll
+        for (int st = 0; st < kTSteps; ++st) {
+            v4i b0[kTQ], b1[kTQ], x[kTMT];
+#pragma unroll
+            for (int q = 0; q < kTQ; ++q) {
+                const int pq = wn * kTQ + q;
+                b0[q] = *reinterpret_cast<const v4i *>(cur + kTAStage + ((pq * 2 + 0) * kTSteps + st) * 1024 + lane * 16);
+                b1[q] = *reinterpret_cast<const v4i *>(cur + kTAStage + ((pq * 2 + 1) * kTSteps + st) * 1024 + lane * 16);
+            }
+#pragma unroll
+            for (int mt = 0; mt < kTMT; ++mt)
+                x[mt] = *reinterpret_cast<const v4i *>(cur + ((wm * kTMT + mt) * kTSteps + st) * 1024 + lane * 16);
+#pragma unroll
+            for (int mt = 0; mt < kTMT; ++mt)
+#pragma unroll
+                for (int q = 0; q < kTQ; ++q) {
+                    acc0[mt][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x[mt], b0[q], acc0[mt][q], 0, 0, 0);
+                    acc1[mt][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x[mt], b1[q], acc1[mt][q], 0, 0, 0);
+                }
+        }
+        lstore(next, other);
+        __syncthreads();
+    };
+    gload(r0, 0);
+    gload(r1, 1);  // n_stages >= 4
+    lstore(r0, s_b0);
+    __syncthreads();
+    for (int s = 0; s < n_stages; s += 2) {
+        stage(s, r0, r1, s_b0, s_b1);
+        stage(s + 1, r1, r0, s_b1, s_b0);
+    }
+
+    // Epilogue: lane l holds rows 4 (l / 16) + i of each of the wave's row
+    // tiles, at channel l % 16 of each weight tile.
+    const int32_t *tidx = KIND == 1 ? aidx : (routed ? nullptr : a.row_token);
+#pragma unroll
+    for (int mt = 0; mt < kTMT; ++mt) {
+        int otok[4];
+        float rsc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int lr = min(wm * kTMT * kTileN + mt * kTileN + 4 * kg + i, rows - 1);
+            otok[i] = tidx ? tidx[row0 + lr] : 0;
+            rsc[i] = Ascale[KIND == 1 ? otok[i] : row0 + lr];
+        }
+#pragma unroll
+        for (int q = 0; q < kTQ; ++q) {
+            const int pq = wn * kTQ + q;
+            const int rowA = row_a(pq), rowB = row_b(pq);
+            const float ws0 = Ws[rowA + r16], ws1 = Ws[rowB + r16];
+            if (KIND == 1) {
+                const int col = rowA + r16;  // gate channel index = h column
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int lr = wm * kTMT * kTileN + mt * kTileN + 4 * kg + i;
+                    if (lr < rows) {
+                        const int r = row0 + lr;
+                        float yg = static_cast<float>(acc0[mt][q][i]) * ws0;
+                        yg = yg * rsc[i];
+                        float yu = static_cast<float>(acc1[mt][q][i]) * ws1;
+                        yu = yu * rsc[i];
+                        const float ex = expf(-yg);
+                        const float den = 1.0f + ex;
+                        const float sg = yg / den;
+                        a.h[static_cast<size_t>(r) * a.imax + col] = sg * yu;
+                        if (a.dbg_acc) {
+                            a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + col] = acc0[mt][q][i];
+                            a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + inter + col] = acc1[mt][q][i];
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int lr = wm * kTMT * kTileN + mt * kTileN + 4 * kg + i;
+                    float y0 = static_cast<float>(acc0[mt][q][i]) * ws0;
+                    y0 = y0 * rsc[i];
+                    float y1 = static_cast<float>(acc1[mt][q][i]) * ws1;
+                    y1 = y1 * rsc[i];
+                    const uint32_t h0 = f32_to_bf16(y0), h1 = f32_to_bf16(y1);
+                    // neighbouring channels share a 4-byte store: even lanes
+                    // take channels (c, c + 1) of tile A, odd lanes (c - 1, c)
+                    // of tile B, so 16 lanes store 64 contiguous bytes
+                    const uint32_t p0 = __shfl_xor(static_cast<int>(h0), 1, kWave);
+                    const uint32_t p1 = __shfl_xor(static_cast<int>(h1), 1, kWave);
+                    const bool even = (r16 & 1) == 0;
+                    const uint32_t word = even ? (h0 | (p0 << 16)) : (p1 | (h1 << 16));
+                    const int wcol = even ? rowA + r16 : rowB + r16 - 1;
+                    if (lr < rows) {
+                        const int r = row0 + lr;
+                        uint16_t *dst = routed ? a.z + static_cast<size_t>(r) * a.H
+                                               : a.share_out + static_cast<size_t>(otok[i]) * a.H;
+                        *reinterpret_cast<uint32_t *>(dst + wcol) = word;
+                        if (a.dbg_acc) {
+                            a.dbg_acc[static_cast<size_t>(r) * a.H + rowA + r16] = acc0[mt][q][i];
+                            a.dbg_acc[static_cast<size_t>(r) * a.H + rowB + r16] = acc1[mt][q][i];
+                        }
+                        if (a.dbg_z)
+                            *reinterpret_cast<uint32_t *>(a.dbg_z + static_cast<size_t>(r) * a.H + wcol) = word;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int KIND>
+hipError_t launch_tall(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    if (k_dim % (2 * kTSteps * 64) != 0) return hipErrorInvalidValue;  // whole pairs of stages
+    const long blocks = static_cast<long>(max_chunks) * a.n_tiles;
+    if (blocks <= 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(blocks)), blk(kTThreads);
+    if (a.packed) {
+        if (e0 || e1)
+            hipExtLaunchKernelGGL((gemm_tall_kernel<KIND, true>), grid, blk, 0, s, e0, e1, 0, a, k_dim);
+        else
+            hipLaunchKernelGGL((gemm_tall_kernel<KIND, true>), grid, blk, 0, s, a, k_dim);
+    } else {
+        if (e0 || e1)
+            hipExtLaunchKernelGGL((gemm_tall_kernel<KIND, false>), grid, blk, 0, s, e0, e1, 0, a, k_dim);
+        else
+            hipLaunchKernelGGL((gemm_tall_kernel<KIND, false>), grid, blk, 0, s, a, k_dim);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm1_tall(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start,
+                             hipEvent_t ev_stop) {
+    return launch_tall<1>(a, max_chunks, a.H, s, ev_start, ev_stop);
+}
+
+hipError_t launch_gemm2_tall(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
+                             hipEvent_t ev_stop) {
+    return launch_tall<2>(a, max_chunks, k_dim, s, ev_start, ev_stop);
+}
+
+}  // namespace moe

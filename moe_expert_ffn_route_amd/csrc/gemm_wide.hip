@@ -353,27 +353,8 @@ __device__ __forceinline__ bool decode_item(const GemmArgs &a, const int4 *chunk
     return true;
 }
 
-// Tile parameters of the two chunk sizes. Wide items (chunks of up to
-// 16 * kWideTiles rows): 2 waves of one tile pair each, activation slabs of
-// 4 K steps, a weight ring of 8 steps (4 where 8 does not divide K). Tall
-// items (chunks of up to 16 * kTallTiles rows, when experts average hundreds
-// of rows): 4 waves of two tile pairs each, so each activation fragment read
-// from LDS feeds four MFMAs; slabs of 1 step and a ring of 4 keep the
-// 128-row accumulators within two waves' registers per SIMD. (Measured on
-// the compute-bound probe: one tile pair per wave is 25 % slower; slabs of 2
-// steps 1.5 % slower.)
-#ifndef MOE_TALL_WAVES
-#define MOE_TALL_WAVES 4
-#endif
-#ifndef MOE_TALL_NT
-#define MOE_TALL_NT 2
-#endif
-#ifndef MOE_TALL_SLAB
-#define MOE_TALL_SLAB 1
-#endif
-#ifndef MOE_TALL_RING
-#define MOE_TALL_RING 4
-#endif
+// Tile parameters: 2 waves of one tile pair each, activation slabs of 4 K
+// steps, a weight ring of 8 steps (4 where 8 does not divide K).
 #ifndef MOE_WIDE_WAVES
 #define MOE_WIDE_WAVES 2
 #endif
@@ -381,8 +362,6 @@ __device__ __forceinline__ bool decode_item(const GemmArgs &a, const int4 *chunk
 #define MOE_WIDE_SLAB 4
 #endif
 constexpr int kWideWaves = MOE_WIDE_WAVES, kWideSlab = MOE_WIDE_SLAB;
-constexpr int kTallWaves = MOE_TALL_WAVES, kTallNT = MOE_TALL_NT, kTallSlab = MOE_TALL_SLAB,
-              kTallRing = MOE_TALL_RING;
 
 template <int KIND, int NW, int NT, int MT, int SLAB, int RING, bool PACKED>
 __global__ __launch_bounds__(NW * kWave, 2) void gemm_wide_kernel(GemmArgs a, int k_dim) {
@@ -427,8 +406,6 @@ hipError_t launch_t(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s,
 // k_dim is a multiple of 256, so rings of 4 steps always divide it
 template <int KIND>
 hipError_t launch_items(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    if (a.mt == kTallTiles)
-        return launch_t<KIND, kTallWaves, kTallNT, kTallTiles, kTallSlab, kTallRing>(a, max_chunks, k_dim, s, e0, e1);
     if (a.mt != kWideTiles) return hipErrorInvalidValue;
     if ((k_dim / 64) % 8 == 0)
         return launch_t<KIND, kWideWaves, 1, kWideTiles, kWideSlab, 8>(a, max_chunks, k_dim, s, e0, e1);
@@ -447,6 +424,6 @@ hipError_t launch_gemm2_wide(const GemmArgs &a, int max_chunks, int k_dim, hipSt
     return launch_items<2>(a, max_chunks, k_dim, s, ev_start, ev_stop);
 }
 
-int wide_tile_pairs(int mt) { return mt == kTallTiles ? kTallWaves * kTallNT : kWideWaves; }
+int wide_tile_pairs() { return kWideWaves; }
 
 }  // namespace moe

@@ -22,21 +22,19 @@ constexpr int kChunkRowsSmall = 16;
 constexpr int kChunkRowsLarge = 16 * MOE_WIDE_MT;
 // When the routed experts average at least kTallMinRows rows (T * K >=
 // kTallMinRows * E_loc), every group is cut into chunks of kChunkRowsTall rows
-// instead: tall work items of gemm_wide.hip, whose waves each hold two weight
-// tile pairs, so that every activation fragment read from LDS feeds more MFMAs.
-#ifndef MOE_TALL_MT
-#define MOE_TALL_MT 8
-#endif
+// instead: tall work items (gemm_tall.hip), each covering kTallPairs pairs of
+// 16-row weight tiles with both operands staged through LDS.
 #ifndef MOE_TALL_MIN_ROWS
 #define MOE_TALL_MIN_ROWS 256
 #endif
-constexpr int kTallTiles = MOE_TALL_MT;
-constexpr int kChunkRowsTall = 16 * MOE_TALL_MT;
+constexpr int kTallTiles = 16;
+constexpr int kChunkRowsTall = 16 * kTallTiles;
+constexpr int kTallPairs = 8;
 constexpr int kTallMinRows = MOE_TALL_MIN_ROWS;
 constexpr int kTileN = 16;           // MFMA 16x16x64 output tile edge
-// A chunk entry's third word holds its row count (<= 64) in the low bits and
+// A chunk entry's third word holds its row count (<= 256) in the low bits and
 // the number of chunks of its group above kChunkCountShift.
-constexpr int kChunkCountShift = 8;
+constexpr int kChunkCountShift = 9;
 constexpr int kChunkRowsMask = (1 << kChunkCountShift) - 1;
 static_assert(kChunkRowsLarge <= kChunkRowsMask && kChunkRowsTall <= kChunkRowsMask,
               "chunk rows must fit below the count bits");
@@ -153,14 +151,18 @@ hipError_t launch_requant(const RequantArgs &a, hipStream_t s);
 hipError_t launch_gemm1(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_gemm2(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
                         hipEvent_t ev_stop);
-// Work items of several row tiles (gemm_wide.hip; a.mt = kWideTiles or
-// kTallTiles): n_tiles counts groups of wide_tile_pairs(a.mt) pairs of 16-row
-// weight tiles.
+// Wide work items (gemm_wide.hip; a.mt = kWideTiles): n_tiles counts groups
+// of wide_tile_pairs() pairs of 16-row weight tiles.
 hipError_t launch_gemm1_wide(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start,
                              hipEvent_t ev_stop);
 hipError_t launch_gemm2_wide(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
                              hipEvent_t ev_stop);
-int wide_tile_pairs(int mt);
+int wide_tile_pairs();
+// Tall work items (gemm_tall.hip; a.mt = kTallTiles): n_tiles counts groups
+// of kTallPairs pairs of 16-row weight tiles.
+hipError_t launch_gemm1_tall(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_gemm2_tall(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
+                             hipEvent_t ev_stop);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_pack(const int8_t *src, int8_t *dst, int64_t groups, int n, int k, hipStream_t s);
 // debug only: the GEMM1 input rows of every grouped row (q_x / xs dump)

@@ -46,9 +46,14 @@ SMALL = {
     "t40_short_ring": spec(T=40, H=768, I=256, E_g=4, K=2, I_s=768, seed=111),
     "t17_one_row_past_decode": spec(T=17, H=512, I=256, E_g=2, K=1, I_s=256, seed=112),
     # experts averaging 256 rows or more: every group is cut into tall work
-    # items (128-row chunks, the last one ragged, filling 1 to 8 row tiles)
+    # items (256-row chunks, the last one ragged; rows past it repeat the
+    # chunk's last row)
     "tall_ragged_shared": spec(T=300, H=512, I=256, E_g=2, K=2, I_s=256, seed=113),
-    "tall_exact_two_chunks": spec(T=256, H=512, I=512, E_g=1, K=1, seed=114),
+    "tall_exact_one_chunk": spec(T=256, H=512, I=512, E_g=1, K=1, seed=114),
+    # two full chunks of one expert; with I = 1024 a chunk has 8 groups of
+    # weight tiles, so the two chunks of a group run 8 blocks apart
+    "tall_two_chunks_grouped": spec(T=512, H=256, I=1024, E_g=1, K=1, I_s=256, seed=141),
+    "tall_three_chunks_ragged": spec(T=700, H=512, I=256, E_g=1, K=1, seed=142),
     "tall_mask_smooth_split_gemm2": spec(T=290, H=768, I=256, E_g=2, K=2, I_s=512, active=270, smooth=True,
                                          share_smooth=True, seed=115),
     "tall_skewed": spec(T=600, H=256, I=256, E_g=2, K=1, routing="zipf", zipf_s=2.0, I_s=256, seed=116),
@@ -85,7 +90,7 @@ def test_production_tile_parity(name, packed):
 
 def _random_specs(n, seed=2024):
     """Seeded random small shapes over every option of the block: batch sizes
-    on both sides of the decode / 32-row / 128-row work-item choice, hidden and
+    on both sides of the decode / 32-row / 256-row work-item choice, hidden and
     intermediate sizes, a shared expert or none (with a differing
     intermediate), expert-parallel shares, masks, smooth scales, uniform and
     skewed routing, both weight layouts."""
