@@ -1,6 +1,6 @@
 // C ABI of libmoe_w8a8: argument validation, workspace carve-up and the
 // stream-ordered launch sequence of the expert block
-//   route + per-token quant -> [smooth quant] -> GEMM1 (+dequant, SwiGLU)
+//   route + quantisation of x -> GEMM1 (+dequant, SwiGLU)
 //         -> requant -> GEMM2 (+dequant to bf16) -> combine
 // which is the unfused five-op chain of "FusedDeepMoE Kernel 深度分析报告"
 // sec. 9.3 with the dequant/SwiGLU/quant fused into the GEMMs' epilogues

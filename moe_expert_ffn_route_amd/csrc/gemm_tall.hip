@@ -156,19 +156,8 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
             acc0[mt][q] = v4i{0, 0, 0, 0};
             acc1[mt][q] = v4i{0, 0, 0, 0};
         }
-    // Stage s: the loads of stage s + 2 go out into the register set that
-    // stage s filled, then the MFMAs of stage s run from LDS, then stage
-    // s + 1 (loaded during stage s - 1) goes from registers to the other LDS
-    // buffer, and a workgroup barrier publishes it. Two register sets and two
-    // LDS buffers alternate, so the loop runs two stages per turn.
-    const int n_stages = k_dim / (kTSteps * 64);  // even: k_dim is a multiple of 256
-    Stage r0, r1;
-    // The loads and stores run unconditionally (the last stages reload the
-    // last stage, which nobody reads), so that the compiler can count the
-    // loads in flight exactly and wait only for the ones a store needs.
-    auto stage = [&](int s, Stage &mine, const Stage &next, const int8_t *cur, int8_t *other) {
-        gload(mine, min(s + 2, n_stages - 1));
-        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+    // the MFMAs of one stage, from the LDS buffer that holds it
+    auto compute = [&](const int8_t *cur) {
 #pragma unroll
         for (int st = 0; st < kTSteps; ++st) {
             v4i b0[kTQ], b1[kTQ], x[kTMT];
@@ -189,6 +178,21 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
                     acc1[mt][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x[mt], b1[q], acc1[mt][q], 0, 0, 0);
                 }
         }
+    };
+    const int n_stages = k_dim / (kTSteps * 64);  // even: k_dim is a multiple of 256
+    // Stage s: the loads of stage s + 2 go out into the register set that
+    // stage s filled, then the MFMAs of stage s run from LDS, then stage
+    // s + 1 (loaded during stage s - 1) goes from registers to the other LDS
+    // buffer, and a workgroup barrier publishes it. Two register sets and two
+    // LDS buffers alternate, so the loop runs two stages per turn. The loads
+    // and stores run unconditionally (the last stages reload the last stage,
+    // which nobody reads), so that the compiler can count the loads in flight
+    // exactly and wait only for the ones a store needs.
+    Stage r0, r1;
+    auto stage = [&](int s, Stage &mine, const Stage &next, const int8_t *cur, int8_t *other) {
+        gload(mine, min(s + 2, n_stages - 1));
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+        compute(cur);
         lstore(next, other);
         __syncthreads();
     };

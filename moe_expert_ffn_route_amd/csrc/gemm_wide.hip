@@ -72,9 +72,6 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
     constexpr int kUpw = (kUnits + NW - 1) / NW;   // of them, per wave
     constexpr int kSlabsPerRing = RING / SLAB;
     static_assert(kWave % kLpr == 0, "a load instruction covers whole row segments");
-    // with many row tiles the epilogue's per-row tokens and scales are read
-    // after the K loop, into registers the weight ring no longer needs
-    constexpr bool kLateRows = MTA > 2;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int r16 = lane & 15, kg = lane >> 4;
@@ -94,26 +91,25 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
     }
     // a token indexes the row scale of per-token rows and the share_output
     // row of the shared expert's GEMM2
-    constexpr int kER = kLateRows ? 1 : MTA;  // row tiles whose epilogue rows are read early
     int otok[MTA][4];
     float rsc[MTA][4];
-    auto load_tokens = [&](int mt0, int mt1) {
+    auto load_tokens = [&] {
 #pragma unroll
-        for (int mt = mt0; mt < mt1; ++mt)
+        for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int lr = min(mt * kTileN + 4 * kg + i, rows - 1);
                 otok[mt][i] = it.tidx ? it.tidx[row0 + lr] : 0;
             }
     };
-    auto load_scales = [&](int mt0, int mt1) {
+    auto load_scales = [&] {
 #pragma unroll
-        for (int mt = mt0; mt < mt1; ++mt)
+        for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 rsc[mt][i] = it.Ascale[it.aidx ? otok[mt][i] : row0 + min(mt * kTileN + 4 * kg + i, rows - 1)];
     };
-    if (!kLateRows) load_tokens(0, kER);
+    load_tokens();
     float ws0[NT], ws1[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -152,7 +148,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
     __builtin_amdgcn_sched_barrier(0);
 
     // (3) loads that depend on (1): the row scales of this lane's output rows
-    if (!kLateRows) load_scales(0, kER);
+    load_scales();
     __builtin_amdgcn_sched_barrier(0);
 
     store_slab(0);
@@ -211,11 +207,6 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
 #pragma unroll
     for (int h = 0; h < kSlabsPerRing; ++h)
         slab((ncyc - 1) * kSlabsPerRing + h, h, h + 1 < kSlabsPerRing, false);
-
-    if (kLateRows) {
-        load_tokens(0, MTA);
-        load_scales(0, MTA);
-    }
 
     // Epilogue: lane l holds rows 4 * (l / 16) + i of every row tile, at
     // channel l % 16 of every weight tile.
@@ -369,13 +360,8 @@ __global__ __launch_bounds__(NW * kWave, 2) void gemm_wide_kernel(GemmArgs a, in
     WideItem it;
     if (!decode_item<KIND, NW, NT, PACKED>(a, a.chunks, a.count_word, a.n_tiles, blockIdx.x, k_dim, it)) return;
     // run the body for the row tiles the chunk actually fills
+    static_assert(MT <= 2, "items of one or two row tiles");
     const int tiles = (it.rows + kTileN - 1) / kTileN;
-    if constexpr (MT > 4) {
-        if (tiles > 4) return wide_body<KIND, NW, NT, MT, SLAB, RING, PACKED>(a, it, s_a);
-    }
-    if constexpr (MT > 2) {
-        if (tiles > 2) return wide_body<KIND, NW, NT, (MT > 4 ? 4 : MT), SLAB, RING, PACKED>(a, it, s_a);
-    }
     if constexpr (MT > 1) {
         if (tiles > 1) return wide_body<KIND, NW, NT, 2, SLAB, RING, PACKED>(a, it, s_a);
     }
