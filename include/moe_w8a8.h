@@ -187,14 +187,20 @@ MOE_W8A8_API moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *dims,
  *  src    int8 [groups, n, k], k contiguous (a gmm*_weight tensor: n = 2I, k = H
  *         for GEMM1; n = H, k = I for GEMM2; groups = E_loc, or 1 for a shared
  *         expert)
- *  dst    int8, same size; for group g, 16-row tile j and 64-byte k step s, the
- *         1024 bytes at ((g*(n/16) + j)*(k/64) + s)*1024 hold, at byte 16*l + b
- *         (l in [0,64), b in [0,16)), src[g][16j + l%16][64s + 16*(l/16) + b]
- *  n % 16 == 0, k % 64 == 0; src and dst 16-byte aligned and not overlapping.
- *  Stream-ordered; returns MOE_ERR_INVALID_ARG for bad sizes or pointers.
+ *  which  MOE_PACK_GMM1 for a gmm1 tensor, MOE_PACK_GMM2 for a gmm2 tensor
+ *  dst    int8, same size; for group g, tile position p and 64-byte k step s,
+ *         the 1024 bytes at ((g*(n/16) + p)*(k/64) + s)*1024 hold, at byte
+ *         16*l + b (l in [0,64), b in [0,16)), src[g][16j + l%16][64s +
+ *         16*(l/16) + b], where j = p for GEMM2 and, for GEMM1 (gate tiles
+ *         j < n/32, up tiles after them), j = p/2 for even p and n/32 + p/2
+ *         for odd p: gate tile j and up tile j follow each other
+ *  n % 32 == 0, k % 64 == 0; src and dst 16-byte aligned and not overlapping.
+ *  Stream-ordered; returns MOE_ERR_INVALID_ARG for bad sizes, pointers or
+ *  `which`.
  */
+enum { MOE_PACK_GMM1 = 1, MOE_PACK_GMM2 = 2 };
 MOE_W8A8_API moe_status_t moe_w8a8_pack_weights(const int8_t *src, int8_t *dst, int64_t groups, int32_t n,
-                                                int32_t k, void *stream);
+                                                int32_t k, int32_t which, void *stream);
 
 /* Static description of a status code. Never NULL. */
 MOE_W8A8_API const char *moe_w8a8_status_string(moe_status_t status);

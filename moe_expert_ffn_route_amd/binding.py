@@ -21,6 +21,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 
 EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_forward", "moe_w8a8_pack_weights", "moe_w8a8_status_string")
 MOE_WEIGHT_ROW_MAJOR, MOE_WEIGHT_PACKED = 0, 1
+MOE_PACK_GMM1, MOE_PACK_GMM2 = 1, 2
 
 
 class MoeError(RuntimeError):
@@ -67,7 +68,7 @@ def library() -> ctypes.CDLL:
         L.moe_w8a8_forward.restype = ctypes.c_int
         L.moe_w8a8_forward.argtypes = ([ctypes.POINTER(Dims)] + [P] * 18 + [ctypes.c_size_t, ctypes.POINTER(Debug), P])
         L.moe_w8a8_pack_weights.restype = ctypes.c_int
-        L.moe_w8a8_pack_weights.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P]
+        L.moe_w8a8_pack_weights.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
         L.moe_w8a8_status_string.restype = ctypes.c_char_p
         L.moe_w8a8_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -92,9 +93,10 @@ def moe_w8a8_workspace_size(dims: Dims) -> int:
     return int(n.value)
 
 
-def moe_w8a8_pack_weights(src, dst=None, stream=None):
+def moe_w8a8_pack_weights(src, which, dst=None, stream=None):
     """Pack an int8 weight tensor [groups, n, k] or [n, k] (device) into the
-    kernels' streaming order; returns dst (allocated like src if None)."""
+    kernels' streaming order; `which` is MOE_PACK_GMM1 for a gmm1 tensor and
+    MOE_PACK_GMM2 for a gmm2 tensor. Returns dst (allocated like src if None)."""
     if dst is None:
         dst = torch.empty_like(src)
     shape = src.shape if src.dim() == 3 else (1, *src.shape)
@@ -102,7 +104,7 @@ def moe_w8a8_pack_weights(src, dst=None, stream=None):
         stream = torch.cuda.current_stream().cuda_stream
     elif isinstance(stream, torch.cuda.Stream):
         stream = stream.cuda_stream
-    rc = library().moe_w8a8_pack_weights(_ptr(src), _ptr(dst), shape[0], shape[1], shape[2], stream)
+    rc = library().moe_w8a8_pack_weights(_ptr(src), _ptr(dst), shape[0], shape[1], shape[2], which, stream)
     if rc != MOE_OK:
         raise MoeError(rc, "moe_w8a8_pack_weights")
     return dst
@@ -113,7 +115,7 @@ def pack_weights(tensors: dict, stream=None) -> dict:
     out = dict(tensors)
     for k in ("gmm1_weight", "gmm2_weight", "share_gmm1_weight", "share_gmm2_weight"):
         if out.get(k) is not None:
-            out[k] = moe_w8a8_pack_weights(out[k], stream=stream)
+            out[k] = moe_w8a8_pack_weights(out[k], MOE_PACK_GMM1 if "gmm1" in k else MOE_PACK_GMM2, stream=stream)
     return out
 
 

@@ -82,14 +82,16 @@ extern "C" moe_status_t moe_w8a8_workspace_size(const moe_w8a8_dims_t *dims, siz
 }
 
 extern "C" moe_status_t moe_w8a8_pack_weights(const int8_t *src, int8_t *dst, int64_t groups, int32_t n, int32_t k,
-                                              void *stream) {
-    if (!src || !dst || groups < 0 || n <= 0 || k <= 0 || n % 16 || k % 64) return MOE_ERR_INVALID_ARG;
+                                              int32_t which, void *stream) {
+    if (!src || !dst || groups < 0 || n <= 0 || k <= 0 || n % 32 || k % 64) return MOE_ERR_INVALID_ARG;
+    if (which != MOE_PACK_GMM1 && which != MOE_PACK_GMM2) return MOE_ERR_INVALID_ARG;
     if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_INVALID_ARG;
     const uint64_t bytes = static_cast<uint64_t>(groups) * n * k;
     const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
     if (s0 < d0 + bytes && d0 < s0 + bytes) return MOE_ERR_INVALID_ARG;  // overlap
     if (bytes / 16 / 256 >= (1ull << 31)) return MOE_ERR_UNSUPPORTED;
-    return launch_pack(src, dst, groups, n, k, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return launch_pack(src, dst, groups, n, k, which, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK
+                                                                                                  : MOE_ERR_HIP;
 }
 
 extern "C" const char *moe_w8a8_status_string(moe_status_t s) {

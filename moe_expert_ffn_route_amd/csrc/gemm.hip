@@ -154,8 +154,10 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
     size_t wstep;
     if (PACKED) {
         const size_t steps_k = Kd / 64;
-        pw0 = W + ((rowA / kTileN) * steps_k + step0) * 1024 + lane * 16;
-        pw1 = W + ((rowB / kTileN) * steps_k + step0) * 1024 + lane * 16;
+        const size_t ta = KIND == 1 ? g1_tile_pos(rowA / kTileN, inter / kTileN) : rowA / kTileN;
+        const size_t tb = KIND == 1 ? g1_tile_pos(rowB / kTileN, inter / kTileN) : rowB / kTileN;
+        pw0 = W + (ta * steps_k + step0) * 1024 + lane * 16;
+        pw1 = W + (tb * steps_k + step0) * 1024 + lane * 16;
         wstep = 1024;
     } else {
         pw0 = W + static_cast<size_t>(rowA + r16) * Kd + step0 * 64 + kg * 16;

@@ -121,7 +121,8 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
     for (int i = 0; i < kTLoads; ++i) {
         const int j = i * kTWaves + wave;
         const int wrow = ((j / kTSteps) & 1) ? row_b(j / (2 * kTSteps)) : row_a(j / (2 * kTSteps));
-        wsrc[i] = W + static_cast<size_t>(wrow / kTileN) * tile_bytes + (j % kTSteps) * wstep + wlane;
+        const size_t wt = KIND == 1 && PACKED ? g1_tile_pos(wrow / kTileN, inter / kTileN) : wrow / kTileN;
+        wsrc[i] = W + wt * tile_bytes + (j % kTSteps) * wstep + wlane;
         const int lr = min((j / kTSteps) * kTileN + r16, rows - 1);
         const int ar = KIND == 1 ? aidx[row0 + lr] : row0 + lr;
         asrc[i] = Abase + static_cast<size_t>(ar) * a.a_stride + (j % kTSteps) * 64 + kg * 16;

@@ -324,8 +324,14 @@ __device__ __forceinline__ bool decode_item(const GemmArgs &a, const int4 *chunk
     it.jstride = (it.jcol / kTileN) * tile_bytes;  // a tile is 16 rows x k_dim bytes in both layouts
     // weight addresses: a wave-uniform base plus a 32-bit lane offset
     if (PACKED) {
-        it.wb0 = W + static_cast<size_t>(it.rowA / kTileN) * tile_bytes;
-        it.wb1 = W + static_cast<size_t>(it.rowB / kTileN) * tile_bytes;
+        if (KIND == 1) {
+            it.wb0 = W + g1_tile_pos(it.rowA / kTileN, it.inter / kTileN) * tile_bytes;
+            it.wb1 = W + g1_tile_pos(it.rowB / kTileN, it.inter / kTileN) * tile_bytes;
+            it.jstride = 2 * tile_bytes;  // the next gate tile
+        } else {
+            it.wb0 = W + static_cast<size_t>(it.rowA / kTileN) * tile_bytes;
+            it.wb1 = W + static_cast<size_t>(it.rowB / kTileN) * tile_bytes;
+        }
         it.wlane = lane * 16;
         it.wstep = 1024;
     } else {

@@ -164,10 +164,17 @@ hipError_t launch_gemm1_tall(const GemmArgs &a, int max_chunks, hipStream_t s, h
 hipError_t launch_gemm2_tall(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
                              hipEvent_t ev_stop);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
-hipError_t launch_pack(const int8_t *src, int8_t *dst, int64_t groups, int n, int k, hipStream_t s);
+hipError_t launch_pack(const int8_t *src, int8_t *dst, int64_t groups, int n, int k, int which, hipStream_t s);
 // debug only: the GEMM1 input rows of every grouped row (q_x / xs dump)
 hipError_t launch_dbg_gather(const GemmArgs &g1, const int32_t *row_group, const int32_t *meta, int has_shared,
                              int rows_max, int8_t *dst_q, float *dst_xs, hipStream_t s);
+
+// Position of 16-row tile t in a packed GEMM1 weight whose gate half holds
+// `half` tiles: gate and up tiles alternate (gate j, up j, gate j + 1, ...),
+// so the two tiles a GEMM1 work item streams lie side by side.
+__host__ __device__ __forceinline__ size_t g1_tile_pos(int t, int half) {
+    return t < half ? 2 * static_cast<size_t>(t) : 2 * static_cast<size_t>(t - half) + 1;
+}
 
 // bf16 helpers (round to nearest even)
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -147,11 +147,13 @@ def test_forward_rejects_bad_dims_and_shared_mismatch(lib):
                 share_gmm2_weight_scale=FAKE) == binding.MOE_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("src,dst,g,n,k", [
-    (None, FAKE, 1, 16, 64), (FAKE, None, 1, 16, 64), (FAKE, 2 * FAKE, 1, 24, 64), (FAKE, 2 * FAKE, 1, 16, 96),
-    (FAKE, 2 * FAKE, -1, 16, 64), (FAKE + 8, 2 * FAKE, 1, 16, 64), (FAKE, FAKE + 512, 1, 16, 64)])
-def test_pack_rejects_bad_arguments(lib, src, dst, g, n, k):
-    assert lib.moe_w8a8_pack_weights(src, dst, g, n, k, None) == binding.MOE_ERR_INVALID_ARG
+@pytest.mark.parametrize("src,dst,g,n,k,which", [
+    (None, FAKE, 1, 32, 64, 1), (FAKE, None, 1, 32, 64, 1), (FAKE, 2 * FAKE, 1, 16, 64, 1),
+    (FAKE, 2 * FAKE, 1, 48, 64, 2), (FAKE, 2 * FAKE, 1, 32, 96, 1), (FAKE, 2 * FAKE, -1, 32, 64, 2),
+    (FAKE + 8, 2 * FAKE, 1, 32, 64, 1), (FAKE, FAKE + 512, 1, 32, 64, 2), (FAKE, 2 * FAKE, 1, 32, 64, 0),
+    (FAKE, 2 * FAKE, 1, 32, 64, 3)])
+def test_pack_rejects_bad_arguments(lib, src, dst, g, n, k, which):
+    assert lib.moe_w8a8_pack_weights(src, dst, g, n, k, which, None) == binding.MOE_ERR_INVALID_ARG
 
 
 def test_status_strings(lib):
