@@ -104,12 +104,13 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
     auto row_a = [&](int q) { return KIND == 1 ? (nt * kTPairs + q) * kTileN : nt * 2 * kTPairs * kTileN + q * 32; };
     auto row_b = [&](int q) { return KIND == 1 ? inter + row_a(q) : row_a(q) + kTileN; };
 
-    // Global -> LDS copy of a stage: block j = 8 i + wave (i < kTLoads) of
-    // each operand. Activations: block j is row tile j / 2, step j % 2; lane l
-    // reads 16 bytes of row 16 (j / 2) + l % 16 (rows past the chunk repeat
-    // its last row; their outputs are never stored). Weights: block j is
-    // (pair j / 4, half (j / 2) % 2, step j % 2), 1 KB contiguous in the
-    // packed layout.
+    // Global -> LDS copy of a stage: thread t copies the 16 bytes of lane
+    // t % 64 of 1 KB block j = kTWaves i + wave (i < kTLoads) of each operand.
+    // Activation block j is row tile j / kTSteps, K step j % kTSteps: lane l
+    // reads row 16 (j / kTSteps) + l % 16 (rows past the chunk repeat its last
+    // row; their outputs are never stored). Weight block j is tile pair
+    // j / (2 kTSteps), half (j / kTSteps) % 2, K step j % kTSteps: 1 KB
+    // contiguous in the packed layout.
     const int wstep = PACKED ? 1024 : 64;  // bytes between K steps of a tile
     const int wlane = PACKED ? lane * 16 : r16 * k_dim + kg * 16;
     const int8_t *wsrc[kTLoads];
