@@ -238,7 +238,7 @@ def test_hip_graph_capture_and_replay(name):
     # the production path launches kernels only (no memset, no allocation), so
     # a caller can capture it; every replay must match the eager result, with
     # other eager work and synchronisations between replays (each GEMM kernel
-    # family: decode, 32-row and 128-row work items)
+    # family: decode, 32-row and 256-row work items)
     say(f"[graph] {name}: {GRAPH_CASES[name]}")
     c = synth.make_case(GRAPH_CASES[name])
     t = moe.pack_weights(moe.upload(c))
