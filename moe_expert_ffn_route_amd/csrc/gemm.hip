@@ -257,14 +257,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
                         ag += red[w][0][m][jc];
                         au += red[w][1][m][jc];
                     }
-                    float yg = static_cast<float>(ag) * wsc0;
-                    yg = yg * rs;
-                    float yu = static_cast<float>(au) * wsc1;
-                    yu = yu * rs;
-                    const float ex = expf(-yg);
-                    const float den = 1.0f + ex;
-                    const float sg = yg / den;
-                    a.h[static_cast<size_t>(r) * a.imax + col] = sg * yu;
+                    a.h[static_cast<size_t>(r) * a.imax + col] = swiglu(ag, au, wsc0, wsc1, rs);
                     if (a.dbg_acc) {
                         a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + col] = ag;
                         a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + inter + col] = au;
@@ -273,9 +266,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
                     int acc = 0;
 #pragma unroll
                     for (int w = 0; w < WAVES; ++w) acc += red[w][jc / kTileN][m][jc % kTileN];
-                    float y = static_cast<float>(acc) * wsc0;
-                    y = y * rs;
-                    const uint16_t zb = f32_to_bf16(y);
+                    const uint16_t zb = f32_to_bf16(dequant(acc, wsc0, rs));
                     if (routed) {
                         a.z[static_cast<size_t>(r) * a.H + col] = zb;
                     } else {

@@ -232,14 +232,8 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
                     const int lr = wm * kTMT * kTileN + mt * kTileN + 4 * kg + i;
                     if (lr < rows) {
                         const int r = row0 + lr;
-                        float yg = static_cast<float>(acc0[mt][q][i]) * ws0;
-                        yg = yg * rsc[i];
-                        float yu = static_cast<float>(acc1[mt][q][i]) * ws1;
-                        yu = yu * rsc[i];
-                        const float ex = expf(-yg);
-                        const float den = 1.0f + ex;
-                        const float sg = yg / den;
-                        a.h[static_cast<size_t>(r) * a.imax + col] = sg * yu;
+                        a.h[static_cast<size_t>(r) * a.imax + col] =
+                            swiglu(acc0[mt][q][i], acc1[mt][q][i], ws0, ws1, rsc[i]);
                         if (a.dbg_acc) {
                             a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + col] = acc0[mt][q][i];
                             a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + inter + col] = acc1[mt][q][i];
@@ -250,11 +244,8 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int lr = wm * kTMT * kTileN + mt * kTileN + 4 * kg + i;
-                    float y0 = static_cast<float>(acc0[mt][q][i]) * ws0;
-                    y0 = y0 * rsc[i];
-                    float y1 = static_cast<float>(acc1[mt][q][i]) * ws1;
-                    y1 = y1 * rsc[i];
-                    const uint32_t h0 = f32_to_bf16(y0), h1 = f32_to_bf16(y1);
+                    const uint32_t h0 = f32_to_bf16(dequant(acc0[mt][q][i], ws0, rsc[i]));
+                    const uint32_t h1 = f32_to_bf16(dequant(acc1[mt][q][i], ws1, rsc[i]));
                     // neighbouring channels share a 4-byte store: even lanes
                     // take channels (c, c + 1) of tile A, odd lanes (c - 1, c)
                     // of tile B, so 16 lanes store 64 contiguous bytes

@@ -222,14 +222,8 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
                     const int lr = mt * kTileN + 4 * kg + i;
                     if (lr < rows) {
                         const int r = row0 + lr;
-                        float yg = static_cast<float>(acc0[mt][j][i]) * ws0[j];
-                        yg = yg * rsc[mt][i];
-                        float yu = static_cast<float>(acc1[mt][j][i]) * ws1[j];
-                        yu = yu * rsc[mt][i];
-                        const float ex = expf(-yg);
-                        const float den = 1.0f + ex;
-                        const float sg = yg / den;
-                        a.h[static_cast<size_t>(r) * a.imax + col] = sg * yu;
+                        a.h[static_cast<size_t>(r) * a.imax + col] =
+                            swiglu(acc0[mt][j][i], acc1[mt][j][i], ws0[j], ws1[j], rsc[mt][i]);
                         if (a.dbg_acc) {
                             a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + col] = acc0[mt][j][i];
                             a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + it.inter + col] = acc1[mt][j][i];
@@ -240,11 +234,8 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int lr = mt * kTileN + 4 * kg + i;
-                    float y0 = static_cast<float>(acc0[mt][j][i]) * ws0[j];
-                    y0 = y0 * rsc[mt][i];
-                    float y1 = static_cast<float>(acc1[mt][j][i]) * ws1[j];
-                    y1 = y1 * rsc[mt][i];
-                    const uint32_t b0 = f32_to_bf16(y0), b1 = f32_to_bf16(y1);
+                    const uint32_t b0 = f32_to_bf16(dequant(acc0[mt][j][i], ws0[j], rsc[mt][i]));
+                    const uint32_t b1 = f32_to_bf16(dequant(acc1[mt][j][i], ws1[j], rsc[mt][i]));
                     // pair up neighbouring channels for 4-byte stores: even
                     // lanes take channels (c, c + 1) of tile A, odd lanes
                     // (c - 1, c) of tile B, so 16 lanes store 64 contiguous

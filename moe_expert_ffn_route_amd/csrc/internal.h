@@ -187,4 +187,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// GEMM epilogues, one fp32 operation per step in this order (every GEMM
+// kernel uses these, so all of them round alike):
+//   dequant ("FusedDeepMoE Kernel 深度分析报告" sec. 6.1, 6.2):
+//     y = (float(acc) * w_scale[n]) * row_scale[r];
+//   SwiGLU (sec. 6.1): h = (y_g / (1 + exp(-y_g))) * y_u.
+__device__ __forceinline__ float dequant(int acc, float w_scale, float row_scale) {
+    const float y = static_cast<float>(acc) * w_scale;
+    return y * row_scale;
+}
+__device__ __forceinline__ float swiglu(int acc_g, int acc_u, float ws_g, float ws_u, float row_scale) {
+    const float yg = dequant(acc_g, ws_g, row_scale);
+    const float yu = dequant(acc_u, ws_u, row_scale);
+    const float ex = expf(-yg);
+    const float den = 1.0f + ex;
+    const float sg = yg / den;
+    return sg * yu;
+}
+
 }  // namespace moe
