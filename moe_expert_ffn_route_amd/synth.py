@@ -61,6 +61,7 @@ class Spec:
     seed: int = 1234
     wseed: Optional[int] = None    # weight seed (defaults to seed)
     eps: float = AMAX_EPS
+    fuse_route_scale: bool = False  # routing weight folded into the GEMM2 row scale
 
     @property
     def E_loc(self) -> int:

@@ -35,7 +35,8 @@ def build(force: bool = False) -> str:
 class _Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("I_s", ctypes.c_int32), ("K", ctypes.c_int32), ("E_g", ctypes.c_int32),
-                ("ep_size", ctypes.c_int32), ("ep_rank", ctypes.c_int32), ("eps", ctypes.c_float)]
+                ("ep_size", ctypes.c_int32), ("ep_rank", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("fuse_route_scale", ctypes.c_int32)]
 
 
 class _Trace(ctypes.Structure):
@@ -102,12 +103,13 @@ def _c(a, dtype):
     return None if a is None else np.ascontiguousarray(a, dtype=dtype)
 
 
-def dims_of(T, H, I, K, E_g, I_s=0, ep_size=1, ep_rank=0, eps=1e-6) -> _Dims:
-    return _Dims(T, H, I, I_s, K, E_g, ep_size, ep_rank, eps)
+def dims_of(T, H, I, K, E_g, I_s=0, ep_size=1, ep_rank=0, eps=1e-6, fuse_route_scale=False) -> _Dims:
+    return _Dims(T, H, I, I_s, K, E_g, ep_size, ep_rank, eps, int(bool(fuse_route_scale)))
 
 
 def _spec_dims(spec) -> _Dims:
-    return dims_of(spec.T, spec.H, spec.I, spec.K, spec.E_g, spec.I_s, spec.ep_size, spec.ep_rank, spec.eps)
+    return dims_of(spec.T, spec.H, spec.I, spec.K, spec.E_g, spec.I_s, spec.ep_size, spec.ep_rank, spec.eps,
+                   spec.fuse_route_scale)
 
 
 def route(d: _Dims, expert_ids: np.ndarray, mask: Optional[np.ndarray] = None) -> dict:

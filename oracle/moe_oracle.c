@@ -162,8 +162,12 @@ typedef struct {
 } expert_view;
 
 /* One grouped row through quant -> GEMM1 -> dequant/SwiGLU -> requant ->
- * GEMM2 -> dequant -> bf16 (FusedDeepMoE sec. 7.1 data flow). */
+ * GEMM2 -> dequant -> bf16 (FusedDeepMoE sec. 7.1 data flow). With `fold`
+ * the GEMM2 row scale is fl(hs * route_w), the routing weight folded in
+ * ("DeepSeek V4 Decode Optimization" sec. 2.3: one fused row scale);
+ * otherwise it is hs. */
 static int32_t run_row(const moe_oracle_dims *d, const uint16_t *xrow, const expert_view *ev,
+                       int fold, float route_w,
                        int32_t row, int32_t Imax, moe_oracle_trace *tr, uint16_t *zrow,
                        float *vbuf, int8_t *qx, int32_t *acc1, float *y, float *h,
                        int8_t *qh, int32_t *acc2) {
@@ -181,7 +185,8 @@ static int32_t run_row(const moe_oracle_dims *d, const uint16_t *xrow, const exp
     moe_oracle_swiglu(y, I, h);
     moe_oracle_quant_row(h, I, d->eps, qh, &hs);
     rc |= moe_oracle_gemm_i8(qh, ev->w2, 1, H, I, acc2);
-    dequant_row(acc2, ev->w2s, hs, H, vbuf);
+    const float rs2 = fold ? hs * route_w : hs;
+    dequant_row(acc2, ev->w2s, rs2, H, vbuf);
     for (int32_t n = 0; n < H; ++n) zrow[n] = moe_oracle_f32_to_bf16(vbuf[n]);
     if (tr) {
         if (tr->q_x) memcpy(tr->q_x + (size_t)row * H, qx, (size_t)H);
@@ -264,19 +269,22 @@ int32_t moe_oracle_forward(const moe_oracle_dims *d, const uint16_t *x,
             expert_view ev = {w1 + (size_t)e * 2 * I * H, w1s + (size_t)e * 2 * I,
                               w2 + (size_t)e * H * I, w2s + (size_t)e * H,
                               smooth ? smooth + (size_t)e * H : NULL, I};
-            rc |= run_row(d, xrow, &ev, row, Imax, tr, zk + (size_t)k * H, vbuf, qx, acc1, y,
-                          h, qh, acc2);
+            rc |= run_row(d, xrow, &ev, d->fuse_route_scale != 0, expert_scales[t * K + k], row, Imax,
+                          tr, zk + (size_t)k * H, vbuf, qx, acc1, y, h, qh, acc2);
         }
         /* 7. combine: fp32 sum from zero over kept pairs, k ascending, then
          * one bf16 cast (FusedDeepMoE sec. 4.2 LocalWindowCopy). Tokens with
-         * no kept pair (masked off, or all pairs non-local) give zero rows. */
+         * no kept pair (masked off, or all pairs non-local) give zero rows.
+         * Each row is weighted here, unless its weight was folded into its
+         * GEMM2 row scale. */
         for (int32_t n = 0; n < H; ++n) sum[n] = 0.0f;
         for (int32_t k = 0; k < K; ++k) {
             if (row_of_pair[t * K + k] < 0) continue;
             const float s = expert_scales[t * K + k];
             const uint16_t *zr = zk + (size_t)k * H;
             for (int32_t n = 0; n < H; ++n) {
-                float m = moe_oracle_bf16_to_f32(zr[n]) * s;
+                float m = moe_oracle_bf16_to_f32(zr[n]);
+                if (!d->fuse_route_scale) m = m * s;
                 sum[n] = sum[n] + m;
             }
         }
@@ -290,7 +298,7 @@ int32_t moe_oracle_forward(const moe_oracle_dims *d, const uint16_t *x,
                 for (int32_t n = 0; n < H; ++n) so[n] = 0;
             } else {
                 expert_view ev = {sw1, sw1s, sw2, sw2s, share_smooth, Is};
-                rc |= run_row(d, xrow, &ev, shared_row[t], Imax, tr, so, vbuf, qx, acc1, y, h,
+                rc |= run_row(d, xrow, &ev, 0, 1.0f, shared_row[t], Imax, tr, so, vbuf, qx, acc1, y, h,
                               qh, acc2);
             }
         }

@@ -39,6 +39,9 @@ typedef struct {
     int32_t ep_size;  /* E_loc = E_g / ep_size                    */
     int32_t ep_rank;  /* local experts [ep_rank*E_loc, +E_loc)    */
     float eps;        /* amax floor                               */
+    int32_t fuse_route_scale; /* 1: routing weight folded into the GEMM2
+                                 row scale, combine only sums (DeepSeek V4
+                                 Decode Optimization sec. 2.3)            */
 } moe_oracle_dims;
 
 /* Optional intermediates, indexed by grouped row: routed rows [0, P) in

@@ -22,8 +22,11 @@ MUTANTS = {
     "gemm_weight_transposed": [("s += (int64_t)a[k] * (int64_t)b[k];",
                                 "s += (int64_t)a[k] * (int64_t)B[(size_t)k * N + n];")],
     "bf16_truncates": [("u += 0x7FFFu + lsb;", "u += 0u * lsb;")],
-    "combine_ignores_weight": [("float m = moe_oracle_bf16_to_f32(zr[n]) * s;",
-                                "float m = moe_oracle_bf16_to_f32(zr[n]);")],
+    "combine_ignores_weight": [("if (!d->fuse_route_scale) m = m * s;", "")],
+    "fused_scale_drops_weight": [("const float rs2 = fold ? hs * route_w : hs;", "const float rs2 = hs;")],
+    "fused_combine_weights_again": [("if (!d->fuse_route_scale) m = m * s;", "m = m * s;")],
+    "fused_weight_of_first_k": [("d->fuse_route_scale != 0, expert_scales[t * K + k]",
+                                 "d->fuse_route_scale != 0, expert_scales[t * K]")],
     "combine_skips_first_k": [("if (row_of_pair[t * K + k] < 0) continue;\n            const float s",
                                "if (k == 0 || row_of_pair[t * K + k] < 0) continue;\n            const float s")],
     "route_unstable_order": [("int32_t row = cursor[e]++;", "int32_t row = offsets[e + 1] - 1 - (cursor[e]++ - offsets[e]);")],

@@ -312,6 +312,45 @@ def pin_combine():
     assert np.all(np.abs(F32(r["output"]) - ref) <= bound)
 
 
+def _bf16_rne(v32):
+    """float32 -> bf16 bits, round to nearest even, through torch."""
+    return torch.from_numpy(np.ascontiguousarray(v32, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(
+        np.uint16)
+
+
+def pin_fused_route_scale():
+    # "DeepSeek V4 Decode Optimization" sec. 2.3: the routing weight folded
+    # into the GEMM2 row scale, combine only sums
+    spec = small_spec(T=9, E_g=8, K=3, I_s=32, active=7, wseed=11)
+    fused = dataclasses.replace(spec, fuse_route_scale=True)
+    # (a) with unit weights the fused path is the plain path, bit for bit
+    c1 = _replace(synth.make_case(spec), expert_scales=np.ones((9, 3), np.float32))
+    c1f = _replace(synth.make_case(fused), expert_scales=np.ones((9, 3), np.float32))
+    a, b = run(c1, trace=True), run(c1f, trace=True)
+    assert np.array_equal(a["output"], b["output"]) and np.array_equal(a["z"], b["z"])
+    assert np.array_equal(a["share_output"], b["share_output"])
+    # (b) power-of-two weights scale the output exactly
+    cf = synth.make_case(fused)
+    r = run(cf, trace=True)
+    r4 = run(_replace(cf, expert_scales=cf.expert_scales * np.float32(4.0)))
+    assert np.array_equal(F32(r4["output"]), F32(r["output"]) * 4.0)
+    assert np.array_equal(r4["share_output"], r["share_output"])
+    # (c) each routed row's bf16 output is rounded from acc2 * w2s scaled by
+    #     hs times the weight of that row's own (token, k) pair; torch rounds
+    P = r["P"]
+    w_pair = cf.expert_scales.reshape(-1)[r["sorted_pair"]].astype(np.float32)        # [P]
+    e_row = np.repeat(np.arange(cf.spec.E_loc), r["expert_token_nums"])              # [P]
+    y = r["acc2"][:P].astype(np.float32) * cf.w2s[e_row]
+    y = y * (r["hs"][:P] * w_pair)[:, None]
+    assert np.array_equal(r["z"][:P], _bf16_rne(y))
+    # (d) each output is the plain fp32 sum over k of those rows
+    zr = F32(r["z"][r["row_of_pair"].reshape(9, 3)]).astype(np.float64)
+    zr[r["row_of_pair"].reshape(9, 3) < 0] = 0.0
+    ref = zr.sum(1)
+    bound = 2.0 ** -8 * np.abs(ref) + 4 * 2.0 ** -24 * np.abs(zr).sum(1) + 1e-30
+    assert np.all(np.abs(F32(r["output"]) - ref) <= bound)
+
+
 def pin_mask_and_ep_share():
     spec = small_spec(T=10, E_g=8, K=3, I_s=32, active=6, wseed=5)
     c = synth.make_case(spec)
@@ -389,7 +428,8 @@ def pin_subset_and_empty():
 PINS = [pin_route_bruteforce, pin_route_count_invariant, pin_quant_closed_forms, pin_quant_ties_to_even, pin_quant_zero_and_eps,
         pin_quant_integer_rows, pin_quant_pow2_invariance, pin_gemm_exact, pin_swiglu_vs_torch,
         pin_dense_swiglu_ffn, pin_scale_linearity, pin_permutation_invariance, pin_combine,
-        pin_mask_and_ep_share, pin_shared_matches_routed, pin_smooth_scales, pin_subset_and_empty]
+        pin_mask_and_ep_share, pin_shared_matches_routed, pin_smooth_scales, pin_subset_and_empty,
+        pin_fused_route_scale]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
