@@ -216,6 +216,8 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB 5 times (calibrates HBM byte counters)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step per weight copy into HIP graphs and time their replays")
+    ap.add_argument("--fuse-route-scale", action="store_true",
+                    help="fold the routing weight into the GEMM2 row scale (combine only sums)")
     ap.add_argument("--fenced-events", action="store_true",
                     help="time with default HIP events (each record adds a system-scope cache writeback) "
                          "instead of events created with hipEventDisableSystemFence")
@@ -258,6 +260,7 @@ def main():
     layers = [dev] + [dict(dev, **{k: dev[k].clone() for k in wkeys}) for _ in range(max(0, args.layers - 1))]
     dims = moe.dims_of_case(case)
     dims.weight_layout = moe.MOE_WEIGHT_ROW_MAJOR if args.row_major else moe.MOE_WEIGHT_PACKED
+    dims.fuse_route_scale = int(args.fuse_route_scale)
     runner = moe.Runner(dims)
     stream = torch.cuda.Stream()
     fence_free = not args.fenced_events
@@ -387,6 +390,7 @@ def main():
                    "experts": spec.E_g, "topk": spec.K, "share_inter": spec.I_s,
                    "touched_experts": touched, "grouped_rows": rows, "weight_copies": len(layers),
                    "weight_layout": "row_major" if args.row_major else "packed",
+                   "route_scale": "fused_gemm2" if args.fuse_route_scale else "combine",
                    "launch": "hip_graph" if graphs else "stream"},
         "hbm_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
         "tokens_per_s": round(spec.T / (us * 1e-6), 1),

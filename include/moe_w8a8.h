@@ -84,6 +84,11 @@ typedef struct {
     int32_t weight_layout;  /* MOE_WEIGHT_ROW_MAJOR: the layouts listed at           */
                             /*   moe_w8a8_forward; MOE_WEIGHT_PACKED: all four       */
                             /*   weight tensors come from moe_w8a8_pack_weights      */
+    int32_t fuse_route_scale; /* 0: combine multiplies each routed bf16 row by its   */
+                            /*   routing weight (FusedDeepMoE sec. 4.2); 1: the     */
+                            /*   weight is folded into the row's GEMM2 dequant scale */
+                            /*   (fl(hs * w), "DeepSeek V4 Decode Optimization" sec. */
+                            /*   2.3) and combine only sums; z rows then carry it    */
 } moe_w8a8_dims_t;
 
 enum { MOE_WEIGHT_ROW_MAJOR = 0, MOE_WEIGHT_PACKED = 1 };

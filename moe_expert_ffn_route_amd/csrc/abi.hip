@@ -32,6 +32,7 @@ moe_status_t check_dims(const moe_w8a8_dims_t *d) {
     if (d->hidden % 256 || d->inter % 256 || d->share_inter % 256) return MOE_ERR_UNSUPPORTED;
     if (d->hidden > 16384 || d->inter > 16384 || d->share_inter > 16384) return MOE_ERR_UNSUPPORTED;
     if (d->weight_layout != MOE_WEIGHT_ROW_MAJOR && d->weight_layout != MOE_WEIGHT_PACKED) return MOE_ERR_INVALID_ARG;
+    if (d->fuse_route_scale != 0 && d->fuse_route_scale != 1) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
@@ -66,6 +67,7 @@ Layout make_layout(const moe_w8a8_dims_t *d) {
     L.h = o;           o = up256(o + sizeof(float) * R * L.imax);
     L.q_h = o;         o = up256(o + R * L.imax);
     L.hs = o;          o = up256(o + sizeof(float) * R);
+    L.hs2 = o;         o = up256(o + sizeof(float) * R);  // GEMM2 row scales with the routing weight folded in
     L.z = o;           o = up256(o + sizeof(uint16_t) * TK * H);
     L.total = o;
     return L;
@@ -262,12 +264,16 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         rq.eps = d->amax_eps;
         rq.q = reinterpret_cast<int8_t *>(ws + L.q_h);
         rq.scale = reinterpret_cast<float *>(ws + L.hs);
+        const bool fused = d->fuse_route_scale != 0;
+        rq.scale2 = fused ? reinterpret_cast<float *>(ws + L.hs2) : nullptr;
+        rq.route_w = expert_scales;
+        rq.sorted_pair = ra.sorted_pair;
         if (launch_requant(rq, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
 
         GemmArgs g2 = g1;
         g2.A = rq.q;
         g2.a_stride = L.imax;
-        g2.a_scale = rq.scale;
+        g2.a_scale = fused ? rq.scale2 : rq.scale;
         g2.W = gmm2_weight;
         g2.Ws = gmm2_weight_scale;
         g2.W_sh = share_gmm2_weight;
@@ -304,6 +310,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         ca.K = K;
         ca.H = H;
         ca.has_shared = shared;
+        ca.fused = fused;
         ca.out = static_cast<uint16_t *>(output);
         ca.share_out = static_cast<uint16_t *>(share_output);
         if (launch_combine(ca, s) != hipSuccess || !mark(5)) return MOE_ERR_HIP;

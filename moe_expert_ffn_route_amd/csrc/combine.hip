@@ -1,7 +1,9 @@
 // Weighted top-k combine ("FusedDeepMoE Kernel 深度分析报告" sec. 4.2,
 // LocalWindowCopy): for each token, an fp32 sum that starts at zero and adds,
 // for k = 0..K-1 in order, the expert's bf16 row (cast to fp32) times the
-// routing weight; one round-to-nearest-even cast to bf16 at the end. Pairs
+// routing weight (unless the weight was folded into the row's GEMM2 row
+// scale: then the rows are summed as they are); one round-to-nearest-even
+// cast to bf16 at the end. Pairs
 // that were dropped (inactive token, non-local expert, bad id) contribute
 // nothing, so such tokens get zero rows. The sum order is fixed per element,
 // so the result is deterministic.
@@ -43,8 +45,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
             const uint32_t v[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float m0 = bf16_to_f32(static_cast<uint16_t>(v[i] & 0xFFFFu)) * wk;
-                const float m1 = bf16_to_f32(static_cast<uint16_t>(v[i] >> 16)) * wk;
+                float m0 = bf16_to_f32(static_cast<uint16_t>(v[i] & 0xFFFFu));
+                float m1 = bf16_to_f32(static_cast<uint16_t>(v[i] >> 16));
+                if (!a.fused) {
+                    m0 = m0 * wk;
+                    m1 = m1 * wk;
+                }
                 sum[2 * i] = sum[2 * i] + m0;
                 sum[2 * i + 1] = sum[2 * i + 1] + m1;
             }

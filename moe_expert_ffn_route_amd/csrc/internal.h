@@ -51,7 +51,7 @@ struct Layout {
     int chunk_rows;  // rows per GEMM work item
     int imax;        // max(I, I_s)
     size_t meta, offsets, sorted_pair, row_of_pair, row_token, row_group, chunks;
-    size_t q_tok, xs_tok, q_sm, s_sm, h, q_h, hs, z, total;
+    size_t q_tok, xs_tok, q_sm, s_sm, h, q_h, hs, hs2, z, total;
 };
 
 struct RouteArgs {
@@ -100,6 +100,11 @@ struct RequantArgs {
     float eps;
     int8_t *q;     // [rows_max, imax]
     float *scale;  // [rows_max]
+    // fused route scale: scale2[r] = scale[r] * route_w[sorted_pair[r]] for
+    // routed rows, scale[r] for shared rows (null: not fused)
+    float *scale2;
+    const float *route_w;        // [T*K]
+    const int32_t *sorted_pair;  // [P]
 };
 
 struct GemmArgs {
@@ -141,6 +146,7 @@ struct CombineArgs {
     const float *scales;
     const uint8_t *mask;
     int T, K, H, has_shared;
+    int fused;  // the routing weights are already in the z rows: only sum
     uint16_t *out;
     uint16_t *share_out;
 };

@@ -23,6 +23,10 @@ __global__ __launch_bounds__(kTPR) void requant_kernel(RequantArgs a) {
     const int n = a.row_group[r] < a.E_loc ? a.I : a.I_s;
     quant_f32_row(a.h + static_cast<size_t>(r) * a.imax, n, a.eps, a.q + static_cast<size_t>(r) * a.imax,
                   a.scale + r, true, 0, threadIdx.x, s_part);
+    if (a.scale2 && threadIdx.x == 0) {  // the thread that wrote scale[r]
+        const float hs = a.scale[r];
+        a.scale2[r] = r < a.meta[kMetaP] ? hs * a.route_w[a.sorted_pair[r]] : hs;
+    }
 }
 
 constexpr int kRowsPerBlock = 4;  // one wavefront per row
@@ -71,7 +75,11 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void requant_wave_kernel(Req
         const int i = (lane + j * kWave) * 4;
         if (i < n) *reinterpret_cast<uint32_t *>(dst + i) = quant4(v[j].x, v[j].y, v[j].z, v[j].w, inv);
     }
-    if (lane == 0) a.scale[r] = ap * (1.0f / 127.0f);
+    if (lane == 0) {
+        const float hs = ap * (1.0f / 127.0f);
+        a.scale[r] = hs;
+        if (a.scale2) a.scale2[r] = r < P ? hs * a.route_w[a.sorted_pair[r]] : hs;
+    }
 }
 
 // Debug dump of GEMM1's input rows in grouped-row order: row r is copied from

@@ -184,7 +184,7 @@ class Case:
         s = self.spec
         return dict(num_tokens=s.T, hidden=s.H, inter=s.I, share_inter=s.I_s, topk=s.K,
                     moe_expert_num=s.E_g, ep_rank_size=s.ep_size, ep_rank_id=s.ep_rank,
-                    quant_mode=1, amax_eps=s.eps)
+                    quant_mode=1, amax_eps=s.eps, fuse_route_scale=int(s.fuse_route_scale))
 
 
 def _threads() -> int:

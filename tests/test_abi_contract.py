@@ -94,6 +94,8 @@ def test_workspace_size(lib):
     (dict(moe_expert_num=1024), binding.MOE_ERR_UNSUPPORTED),
     (dict(num_tokens=70000), binding.MOE_ERR_UNSUPPORTED),
     (dict(weight_layout=2), binding.MOE_ERR_INVALID_ARG),
+    (dict(fuse_route_scale=2), binding.MOE_ERR_INVALID_ARG),
+    (dict(fuse_route_scale=-1), binding.MOE_ERR_INVALID_ARG),
 ])
 def test_bad_dims_rejected(lib, kw, code):
     n = ctypes.c_size_t(0)

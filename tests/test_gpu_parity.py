@@ -58,6 +58,14 @@ SMALL = {
                                          share_smooth=True, seed=115),
     "tall_skewed": spec(T=600, H=256, I=256, E_g=2, K=1, routing="zipf", zipf_s=2.0, I_s=256, seed=116),
     "tall_tail_two_tiles": spec(T=280, H=512, I=256, E_g=1, K=1, I_s=256, seed=117),
+    # the routing weight folded into the GEMM2 row scale (combine only sums),
+    # on each item size, with masks, an EP share, smooth scales and a split
+    # GEMM2 (I_s != I)
+    "fused_decode_shared_mask": spec(T=12, H=512, I=256, E_g=8, K=3, I_s=256, active=10, fuse_route_scale=True,
+                                     seed=151),
+    "fused_wide_ep_smooth": spec(T=60, H=512, I=256, E_g=16, K=4, ep_size=2, ep_rank=1, active=50, smooth=True,
+                                 fuse_route_scale=True, seed=152),
+    "fused_tall_split_gemm2": spec(T=300, H=512, I=256, E_g=2, K=2, I_s=512, fuse_route_scale=True, seed=153),
 }
 
 
@@ -93,7 +101,7 @@ def _random_specs(n, seed=2024):
     on both sides of the decode / 32-row / 256-row work-item choice, hidden and
     intermediate sizes, a shared expert or none (with a differing
     intermediate), expert-parallel shares, masks, smooth scales, uniform and
-    skewed routing, both weight layouts."""
+    skewed routing, both weight layouts, the fused route scale."""
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -111,6 +119,8 @@ def _random_specs(n, seed=2024):
             kw["smooth"] = True
         if I_s and rng.random() < 0.4:
             kw["share_smooth"] = True
+        if rng.random() < 0.3:
+            kw["fuse_route_scale"] = True
         out.append((synth.Spec(**kw), bool(i % 2)))
     return out
 

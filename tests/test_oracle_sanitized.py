@@ -35,6 +35,7 @@ CASES = {
     "ep_share": spec(T=50, E_g=32, K=6, ep_size=4, ep_rank=3, active=41, smooth=True),
     "zipf_multi_chunk": spec(T=200, E_g=8, K=2, routing="zipf", zipf_s=2.0, I_s=512),
     "k16_e512": spec(T=20, E_g=512, K=16, I_s=256),
+    "fused_route_scale": spec(T=30, E_g=16, K=4, I_s=256, active=25, fuse_route_scale=True),
 }
 
 
