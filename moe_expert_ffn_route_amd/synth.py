@@ -20,6 +20,10 @@ Distributions (one recipe for every case):
   expert_scales   softmax over the K chosen experts of N(0, 1) logits
   smooth scales   fp32 ~ U[0.5, 2]
   x_active_mask   exactly `active` tokens set, at random positions
+  FP4 weights     (weight_format "mxfp4") E2M1 codes uniform over all 16, two
+                  per byte; E8M0 block scales (one per 32 K elements) uniform
+                  over exponents 124..130 (2^-3 .. 2^3); fp32 per-channel
+                  scales as above
 
 Every array comes from its own numpy PCG64 stream keyed by
 SeedSequence([seed, stream, index]); expert weights are drawn per global
@@ -37,6 +41,7 @@ import numpy as np
 # stream ids of SeedSequence([seed, stream, index])
 S_IDS, S_ESCALE, S_X, S_W1, S_W1S, S_W2, S_W2S, S_MASK, S_SMOOTH = range(1, 10)
 S_SW1, S_SW1S, S_SW2, S_SW2S, S_SSMOOTH, S_PERM = range(10, 16)
+S_W1B, S_W2B, S_SW1B, S_SW2B = range(16, 20)
 
 AMAX_EPS = 1e-6
 
@@ -62,6 +67,7 @@ class Spec:
     wseed: Optional[int] = None    # weight seed (defaults to seed)
     eps: float = AMAX_EPS
     fuse_route_scale: bool = False  # routing weight folded into the GEMM2 row scale
+    weight_format: str = "int8"     # "int8" | "mxfp4" (FP4 weights, FP8 activations)
 
     @property
     def E_loc(self) -> int:
@@ -119,6 +125,15 @@ def _uniform_f32(rng: np.random.Generator, n: int, lo: float, hi: float) -> np.n
     return rng.uniform(lo, hi, n).astype(np.float32)
 
 
+def _fp4_pairs(rng: np.random.Generator, n: int) -> np.ndarray:
+    """n / 2 bytes, each two E2M1 codes drawn uniformly over all 16."""
+    return rng.integers(0, 256, n // 2, dtype=np.uint8)
+
+
+def _e8m0(rng: np.random.Generator, n: int) -> np.ndarray:
+    return rng.integers(124, 131, n, dtype=np.uint8)
+
+
 def _routing(spec: Spec) -> np.ndarray:
     """[T, K] int32 global expert ids, K distinct per token."""
     T, K, E = spec.T, spec.K, spec.E_g
@@ -160,6 +175,19 @@ def expert_weights(spec: Spec, g: int):
     return w1, w1s, w2, w2s
 
 
+def expert_weights_mx(spec: Spec, g: int):
+    """FP4 weights of global expert g: (w1 [2I, H/2] u8, w1b [2I, H/32] u8,
+    w1s [2I] f32, w2 [H, I/2] u8, w2b [H, I/32] u8, w2s [H] f32)."""
+    s, H, I = spec.weight_seed, spec.H, spec.I
+    w1 = _fp4_pairs(_rng(s, S_W1, g), 2 * I * H).reshape(2 * I, H // 2)
+    w1b = _e8m0(_rng(s, S_W1B, g), 2 * I * H // 32).reshape(2 * I, H // 32)
+    w1s = _uniform_f32(_rng(s, S_W1S, g), 2 * I, 1e-3, 1e-2)
+    w2 = _fp4_pairs(_rng(s, S_W2, g), H * I).reshape(H, I // 2)
+    w2b = _e8m0(_rng(s, S_W2B, g), H * I // 32).reshape(H, I // 32)
+    w2s = _uniform_f32(_rng(s, S_W2S, g), H, 1e-3, 1e-2)
+    return w1, w1b, w1s, w2, w2b, w2s
+
+
 @dataclasses.dataclass
 class Case:
     """One batch of inputs, all host numpy arrays in the ABI's layouts."""
@@ -178,6 +206,12 @@ class Case:
     smooth: Optional[np.ndarray] = None        # fp32 [E_loc, H]
     share_smooth: Optional[np.ndarray] = None  # fp32 [H]
     mask: Optional[np.ndarray] = None          # uint8 [T]
+    # weight_format "mxfp4": w1 / w2 / sw1 / sw2 hold E2M1 code pairs (uint8,
+    # last dimension halved) and these their E8M0 block scales
+    w1b: Optional[np.ndarray] = None   # uint8 [E_loc, 2I, H/32]
+    w2b: Optional[np.ndarray] = None   # uint8 [E_loc, H, I/32]
+    sw1b: Optional[np.ndarray] = None  # uint8 [2I_s, H/32]
+    sw2b: Optional[np.ndarray] = None  # uint8 [H, I_s/32]
 
     @property
     def dims(self) -> dict:
@@ -240,8 +274,29 @@ def make_activations(spec: Spec):
     return x, ids, esc, mask, smooth, ssm
 
 
+def make_case_mx(spec: Spec) -> Case:
+    """A case with FP4 weights (weight_format "mxfp4")."""
+    x, ids, esc, mask, smooth, ssm = make_activations(spec)
+    E, H, I, Is = spec.E_loc, spec.H, spec.I, spec.I_s
+    parts = [expert_weights_mx(spec, spec.ep_rank * E + e) for e in range(E)]
+    w1, w1b, w1s, w2, w2b, w2s = (np.stack([p[i] for p in parts]) if E else None for i in range(6))
+    sw = [None] * 6
+    if Is:
+        s = spec.weight_seed
+        sw = [_fp4_pairs(_rng(s, S_SW1), 2 * Is * H).reshape(2 * Is, H // 2),
+              _e8m0(_rng(s, S_SW1B), 2 * Is * H // 32).reshape(2 * Is, H // 32),
+              _uniform_f32(_rng(s, S_SW1S), 2 * Is, 1e-3, 1e-2),
+              _fp4_pairs(_rng(s, S_SW2), H * Is).reshape(H, Is // 2),
+              _e8m0(_rng(s, S_SW2B), H * Is // 32).reshape(H, Is // 32),
+              _uniform_f32(_rng(s, S_SW2S), H, 1e-3, 1e-2)]
+    return Case(spec, x, ids, esc, w1, w1s, w2, w2s, sw[0], sw[2], sw[3], sw[5], smooth, ssm, mask,
+                w1b=w1b, w2b=w2b, sw1b=sw[1], sw2b=sw[4])
+
+
 def make_case(spec: Spec, weights=None) -> Case:
     """Materialise a whole case. `weights` may pass a cached make_weights() result."""
+    if spec.weight_format == "mxfp4":
+        return make_case_mx(spec)
     x, ids, esc, mask, smooth, ssm = make_activations(spec)
     w1, w1s, w2, w2s = weights if weights is not None else make_weights(spec)
     sw1, sw1s, sw2, sw2s = shared_weights(spec)

@@ -66,6 +66,18 @@ def load(path: str):
     L.moe_oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
     L.moe_oracle_f32_to_bf16.restype = ctypes.c_uint16
     L.moe_oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+    L.moe_oracle_forward_mx.restype = ctypes.c_int32
+    L.moe_oracle_forward_mx.argtypes = [ctypes.POINTER(_Dims)] + [P] * 19 + [ctypes.c_int32] + [P] * 4
+    L.moe_oracle_f32_to_e4m3.restype = ctypes.c_uint8
+    L.moe_oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+    L.moe_oracle_e4m3_to_f32.restype = ctypes.c_float
+    L.moe_oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+    L.moe_oracle_e2m1_to_f32.restype = ctypes.c_float
+    L.moe_oracle_e2m1_to_f32.argtypes = [ctypes.c_uint8]
+    L.moe_oracle_quant_row_fp8.restype = None
+    L.moe_oracle_quant_row_fp8.argtypes = [P, ctypes.c_int32, ctypes.c_float, P, P]
+    L.moe_oracle_gemm_mx.restype = None
+    L.moe_oracle_gemm_mx.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
     return L
 
 
@@ -196,13 +208,23 @@ def forward(case, tokens: Optional[Sequence[int]] = None, trace: bool = False) -
                    acc2=np.zeros((rows_max, H), np.int32), z=np.zeros((rows_max, H), np.uint16))
         tr = _Trace(**{k: _p(v) for k, v in res.items()})
     sub = None if tokens is None else np.ascontiguousarray(tokens, np.int32)
-    keep = [_c(case.x, np.uint16), _c(case.expert_ids, np.int32), _c(case.expert_scales, np.float32),
-            _c(case.w1, np.int8), _c(case.w1s, np.float32), _c(case.w2, np.int8), _c(case.w2s, np.float32),
-            _c(case.sw1, np.int8), _c(case.sw1s, np.float32), _c(case.sw2, np.int8), _c(case.sw2s, np.float32),
-            _c(case.smooth, np.float32), _c(case.share_smooth, np.float32), _c(case.mask, np.uint8)]
-    rc = lib().moe_oracle_forward(ctypes.byref(d), *[_p(a) for a in keep], _p(sub),
-                                  0 if sub is None else len(sub), _p(out), _p(sout), _p(etn),
-                                  ctypes.byref(tr) if tr is not None else None)
+    mx = getattr(s, "weight_format", "int8") == "mxfp4"
+    if mx:
+        keep = [_c(case.x, np.uint16), _c(case.expert_ids, np.int32), _c(case.expert_scales, np.float32),
+                _c(case.w1, np.uint8), _c(case.w1b, np.uint8), _c(case.w1s, np.float32),
+                _c(case.w2, np.uint8), _c(case.w2b, np.uint8), _c(case.w2s, np.float32),
+                _c(case.sw1, np.uint8), _c(case.sw1b, np.uint8), _c(case.sw1s, np.float32),
+                _c(case.sw2, np.uint8), _c(case.sw2b, np.uint8), _c(case.sw2s, np.float32),
+                _c(case.smooth, np.float32), _c(case.share_smooth, np.float32), _c(case.mask, np.uint8)]
+        fwd = lib().moe_oracle_forward_mx
+    else:
+        keep = [_c(case.x, np.uint16), _c(case.expert_ids, np.int32), _c(case.expert_scales, np.float32),
+                _c(case.w1, np.int8), _c(case.w1s, np.float32), _c(case.w2, np.int8), _c(case.w2s, np.float32),
+                _c(case.sw1, np.int8), _c(case.sw1s, np.float32), _c(case.sw2, np.int8), _c(case.sw2s, np.float32),
+                _c(case.smooth, np.float32), _c(case.share_smooth, np.float32), _c(case.mask, np.uint8)]
+        fwd = lib().moe_oracle_forward
+    rc = fwd(ctypes.byref(d), *[_p(a) for a in keep], _p(sub), 0 if sub is None else len(sub), _p(out), _p(sout),
+             _p(etn), ctypes.byref(tr) if tr is not None else None)
     if rc != 0:
         raise RuntimeError(f"oracle forward failed: {rc}")
     res.update(output=out, share_output=sout, expert_token_nums=etn)
@@ -211,4 +233,46 @@ def forward(case, tokens: Optional[Sequence[int]] = None, trace: bool = False) -
         res["sorted_pair"] = res["sorted_pair"][:P]
         res["shared_token"] = res["shared_token"][:Ta]
         res["P"], res["T_act"], res["n_bad"] = P, Ta, int(res["num_rows"][2])
+        if mx:  # E4M3 codes and fp32 accumulators
+            for k in ("q_x", "q_h"):
+                res[k] = res[k].view(np.uint8)
+            for k in ("acc1", "acc2"):
+                res[k] = res[k].view(np.float32)
     return res
+
+
+# FP8 / FP4 helpers of the FP4-weight variant (elementwise through the C oracle)
+def f32_to_e4m3(a) -> np.ndarray:
+    f = lib().moe_oracle_f32_to_e4m3
+    a = np.asarray(a, np.float32)
+    return np.array([f(float(v)) for v in a.reshape(-1)], np.uint8).reshape(a.shape)
+
+
+def e4m3_to_f32(c) -> np.ndarray:
+    f = lib().moe_oracle_e4m3_to_f32
+    c = np.asarray(c, np.uint8)
+    return np.array([f(int(v)) for v in c.reshape(-1)], np.float32).reshape(c.shape)
+
+
+def e2m1_to_f32(c) -> np.ndarray:
+    f = lib().moe_oracle_e2m1_to_f32
+    c = np.asarray(c, np.uint8)
+    return np.array([f(int(v)) for v in c.reshape(-1)], np.float32).reshape(c.shape)
+
+
+def quant_row_fp8(v: np.ndarray, eps: float = 1e-6):
+    v = np.ascontiguousarray(v, np.float32)
+    q = np.zeros(v.shape, np.uint8)
+    sc = np.zeros(1, np.float32)
+    lib().moe_oracle_quant_row_fp8(_p(v), v.size, eps, _p(q), _p(sc))
+    return q, float(sc[0])
+
+
+def gemm_mx(A: np.ndarray, B: np.ndarray, S: np.ndarray) -> np.ndarray:
+    """A [M, K] E4M3 codes, B [N, K/2] E2M1 pairs, S [N, K/32] E8M0 -> fp32 [M, N]."""
+    A, B, S = (np.ascontiguousarray(x, np.uint8) for x in (A, B, S))
+    M, K = A.shape
+    N = B.shape[0]
+    C = np.zeros((M, N), np.float32)
+    lib().moe_oracle_gemm_mx(_p(A), _p(B), _p(S), M, N, K, _p(C))
+    return C

@@ -144,6 +144,88 @@ void moe_oracle_swiglu(const float *y, int32_t n_half, float *h) {
     }
 }
 
+/* FP8 E4M3 from fp32: round to nearest, ties to even, on the E4M3 grid
+ * (subnormal step 2^-9, normal values (8 + m) * 2^(e - 10)); magnitudes that
+ * round above 448 saturate to 448. */
+uint8_t moe_oracle_f32_to_e4m3(float f) {
+    if (isnan(f)) return 0x7F;
+    const uint8_t sign = signbit(f) ? 0x80 : 0x00;
+    const float a = fabsf(f);
+    if (a >= 448.0f) return sign | 0x7E;
+    if (a < 0.015625f) {                     /* below 2^-6: subnormal codes m * 2^-9 */
+        const float m = rintf(a * 512.0f);   /* exact scaling; m == 8 is the smallest normal */
+        return sign | (uint8_t)m;
+    }
+    int e2;
+    (void)frexpf(a, &e2);                     /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;                           /* unbiased exponent, -6..8 */
+    float m = rintf(ldexpf(a, 3 - E));        /* significand in eighths, 8..16 */
+    if (m == 16.0f) { m = 8.0f; E += 1; }
+    if (E > 8 || (E == 8 && m > 14.0f)) return sign | 0x7E;
+    return sign | (uint8_t)(((E + 7) << 3) | ((int)m - 8));
+}
+
+float moe_oracle_e4m3_to_f32(uint8_t c) {
+    const int e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    const float v = e == 0 ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), e - 10);
+    return (c & 0x80) ? -v : v;
+}
+
+float moe_oracle_e2m1_to_f32(uint8_t nib) {
+    const int e = (nib >> 1) & 3, m = nib & 1;
+    const float v = e == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+    return (nib & 8) ? -v : v;
+}
+
+/* Per-row dynamic FP8 quantisation: the int8 rule with 448 (the largest E4M3
+ * value) in place of 127 and E4M3 rounding in place of rint. */
+void moe_oracle_quant_row_fp8(const float *v, int32_t n, float eps, uint8_t *q, float *scale) {
+    float a = 0.0f;
+    for (int32_t i = 0; i < n; ++i) {
+        float m = fabsf(v[i]);
+        if (m > a) a = m;
+    }
+    if (a < eps) a = eps;
+    const float inv = 1.0f / a;
+    const float inv448 = 1.0f / 448.0f;
+    *scale = a * inv448;
+    for (int32_t i = 0; i < n; ++i) {
+        float t = v[i] * 448.0f;
+        t = t * inv;
+        q[i] = moe_oracle_f32_to_e4m3(t);
+    }
+}
+
+/* Integer forms: an E4M3 value is qa * 2^-9 and an E2M1 value qb * 2^-1 with
+ * integers qa, qb, so a 32-element block sum is an exact int64 times
+ * 2^(E - 127 - 10). */
+static int32_t e4m3_units(uint8_t c) { return (int32_t)ldexpf(moe_oracle_e4m3_to_f32(c), 9); }
+static int32_t e2m1_units(uint8_t nib) { return (int32_t)(2.0f * moe_oracle_e2m1_to_f32(nib)); }
+
+void moe_oracle_gemm_mx(const uint8_t *A, const uint8_t *B, const uint8_t *S, int32_t M, int32_t N,
+                        int32_t Kd, float *C) {
+    const int32_t nb = Kd / 32;
+    for (int32_t m = 0; m < M; ++m) {
+        const uint8_t *a = A + (size_t)m * Kd;
+        for (int32_t n = 0; n < N; ++n) {
+            const uint8_t *b = B + (size_t)n * (Kd / 2);
+            const uint8_t *sc = S + (size_t)n * nb;
+            double acc = 0.0;
+            for (int32_t blk = 0; blk < nb; ++blk) {
+                int64_t s = 0;
+                for (int32_t k = blk * 32; k < blk * 32 + 32; ++k) {
+                    const uint8_t byte = b[k / 2];
+                    const uint8_t nib = (k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+                    s += (int64_t)e4m3_units(a[k]) * (int64_t)e2m1_units(nib);
+                }
+                acc += ldexp((double)s, (int)sc[blk] - 127 - 10);
+            }
+            C[(size_t)m * N + n] = (float)acc;
+        }
+    }
+}
+
 /* Dequantise one int32 accumulator row: fl(fl(float(acc) * w_scale[n]) * row_scale)
  * (FusedDeepMoE sec. 6.1 steps 2-4 and sec. 6.2 steps 1-4; int32 -> fp32 with
  * round-to-nearest-even). */
@@ -156,9 +238,20 @@ static void dequant_row(const int32_t *acc, const float *wscale, float row_scale
     }
 }
 
+/* The same with an fp32 accumulator (FP4/FP8 GEMMs). */
+static void dequant_row_f(const float *acc, const float *wscale, float row_scale, int32_t n, float *y) {
+    for (int32_t i = 0; i < n; ++i) {
+        float f = acc[i] * wscale[i];
+        y[i] = f * row_scale;
+    }
+}
+
+/* One expert's weights: int8 [N][K] (w1b == NULL), or FP4 nibble pairs
+ * [N][K/2] with E8M0 block scales w1b / w2b [N][K/32]. */
 typedef struct {
-    const int8_t *w1; const float *w1s; const int8_t *w2; const float *w2s;
+    const void *w1; const float *w1s; const void *w2; const float *w2s;
     const float *smooth; int32_t inter;
+    const uint8_t *w1b, *w2b;
 } expert_view;
 
 /* One grouped row through quant -> GEMM1 -> dequant/SwiGLU -> requant ->
@@ -179,14 +272,31 @@ static int32_t run_row(const moe_oracle_dims *d, const uint16_t *xrow, const exp
         if (ev->smooth) v = v * ev->smooth[i];
         vbuf[i] = v;
     }
-    moe_oracle_quant_row(vbuf, H, d->eps, qx, &xs);
-    rc |= moe_oracle_gemm_i8(qx, ev->w1, 1, 2 * I, H, acc1);
-    dequant_row(acc1, ev->w1s, xs, 2 * I, y);
+    const int mx = ev->w1b != NULL;
+    /* (fp32 accumulators of the FP4 path live in the int32 buffers, bit for bit) */
+    float *acc1f = (float *)(void *)acc1, *acc2f = (float *)(void *)acc2;
+    if (mx) {
+        moe_oracle_quant_row_fp8(vbuf, H, d->eps, (uint8_t *)qx, &xs);
+        moe_oracle_gemm_mx((const uint8_t *)qx, (const uint8_t *)ev->w1, ev->w1b, 1, 2 * I, H, acc1f);
+        dequant_row_f(acc1f, ev->w1s, xs, 2 * I, y);
+    } else {
+        moe_oracle_quant_row(vbuf, H, d->eps, qx, &xs);
+        rc |= moe_oracle_gemm_i8(qx, (const int8_t *)ev->w1, 1, 2 * I, H, acc1);
+        dequant_row(acc1, ev->w1s, xs, 2 * I, y);
+    }
     moe_oracle_swiglu(y, I, h);
-    moe_oracle_quant_row(h, I, d->eps, qh, &hs);
-    rc |= moe_oracle_gemm_i8(qh, ev->w2, 1, H, I, acc2);
+    if (mx) {
+        moe_oracle_quant_row_fp8(h, I, d->eps, (uint8_t *)qh, &hs);
+        moe_oracle_gemm_mx((const uint8_t *)qh, (const uint8_t *)ev->w2, ev->w2b, 1, H, I, acc2f);
+    } else {
+        moe_oracle_quant_row(h, I, d->eps, qh, &hs);
+        rc |= moe_oracle_gemm_i8(qh, (const int8_t *)ev->w2, 1, H, I, acc2);
+    }
     const float rs2 = fold ? hs * route_w : hs;
-    dequant_row(acc2, ev->w2s, rs2, H, vbuf);
+    if (mx)
+        dequant_row_f(acc2f, ev->w2s, rs2, H, vbuf);
+    else
+        dequant_row(acc2, ev->w2s, rs2, H, vbuf);
     for (int32_t n = 0; n < H; ++n) zrow[n] = moe_oracle_f32_to_bf16(vbuf[n]);
     if (tr) {
         if (tr->q_x) memcpy(tr->q_x + (size_t)row * H, qx, (size_t)H);
@@ -201,17 +311,18 @@ static int32_t run_row(const moe_oracle_dims *d, const uint16_t *xrow, const exp
     return rc;
 }
 
-int32_t moe_oracle_forward(const moe_oracle_dims *d, const uint16_t *x,
-                           const int32_t *expert_ids, const float *expert_scales,
-                           const int8_t *w1, const float *w1s,
-                           const int8_t *w2, const float *w2s,
-                           const int8_t *sw1, const float *sw1s,
-                           const int8_t *sw2, const float *sw2s,
-                           const float *smooth, const float *share_smooth,
-                           const uint8_t *mask,
-                           const int32_t *token_subset, int32_t n_subset,
-                           uint16_t *output, uint16_t *share_output,
-                           int32_t *expert_token_nums, moe_oracle_trace *tr) {
+/* Weights are int8 when w1b is NULL, FP4 with E8M0 block scales otherwise. */
+static int32_t forward_impl(const moe_oracle_dims *d, const uint16_t *x,
+                            const int32_t *expert_ids, const float *expert_scales,
+                            const void *w1, const uint8_t *w1b, const float *w1s,
+                            const void *w2, const uint8_t *w2b, const float *w2s,
+                            const void *sw1, const uint8_t *sw1b, const float *sw1s,
+                            const void *sw2, const uint8_t *sw2b, const float *sw2s,
+                            const float *smooth, const float *share_smooth,
+                            const uint8_t *mask,
+                            const int32_t *token_subset, int32_t n_subset,
+                            uint16_t *output, uint16_t *share_output,
+                            int32_t *expert_token_nums, moe_oracle_trace *tr) {
     if (!d || d->T < 0 || d->H <= 0 || d->I <= 0 || d->K <= 0 || d->E_g <= 0 ||
         d->ep_size <= 0 || d->E_g % d->ep_size || d->ep_rank < 0 || d->ep_rank >= d->ep_size)
         return -1;
@@ -266,9 +377,13 @@ int32_t moe_oracle_forward(const moe_oracle_dims *d, const uint16_t *x,
             const int32_t row = row_of_pair[t * K + k];
             if (row < 0) continue;
             const int32_t e = expert_ids[t * K + k] - d->ep_rank * E;
-            expert_view ev = {w1 + (size_t)e * 2 * I * H, w1s + (size_t)e * 2 * I,
-                              w2 + (size_t)e * H * I, w2s + (size_t)e * H,
-                              smooth ? smooth + (size_t)e * H : NULL, I};
+            const int mx = w1b != NULL;
+            const size_t wb1 = (size_t)e * 2 * I * H / (mx ? 2 : 1), wb2 = (size_t)e * H * I / (mx ? 2 : 1);
+            expert_view ev = {(const uint8_t *)w1 + wb1, w1s + (size_t)e * 2 * I,
+                              (const uint8_t *)w2 + wb2, w2s + (size_t)e * H,
+                              smooth ? smooth + (size_t)e * H : NULL, I,
+                              mx ? w1b + (size_t)e * 2 * I * (H / 32) : NULL,
+                              mx ? w2b + (size_t)e * H * (I / 32) : NULL};
             rc |= run_row(d, xrow, &ev, d->fuse_route_scale != 0, expert_scales[t * K + k], row, Imax,
                           tr, zk + (size_t)k * H, vbuf, qx, acc1, y, h, qh, acc2);
         }
@@ -297,7 +412,7 @@ int32_t moe_oracle_forward(const moe_oracle_dims *d, const uint16_t *x,
             if (shared_row[t] < 0) {
                 for (int32_t n = 0; n < H; ++n) so[n] = 0;
             } else {
-                expert_view ev = {sw1, sw1s, sw2, sw2s, share_smooth, Is};
+                expert_view ev = {sw1, sw1s, sw2, sw2s, share_smooth, Is, sw1b, sw2b};
                 rc |= run_row(d, xrow, &ev, 0, 1.0f, shared_row[t], Imax, tr, so, vbuf, qx, acc1, y, h,
                               qh, acc2);
             }
@@ -306,4 +421,38 @@ int32_t moe_oracle_forward(const moe_oracle_dims *d, const uint16_t *x,
     free(counts); free(offsets); free(sorted_pair); free(row_of_pair); free(shared_row);
     free(vbuf); free(qx); free(acc1); free(y); free(h); free(qh); free(acc2); free(zk); free(sum);
     return rc;
+}
+
+int32_t moe_oracle_forward(const moe_oracle_dims *d, const uint16_t *x,
+                           const int32_t *expert_ids, const float *expert_scales,
+                           const int8_t *w1, const float *w1s,
+                           const int8_t *w2, const float *w2s,
+                           const int8_t *sw1, const float *sw1s,
+                           const int8_t *sw2, const float *sw2s,
+                           const float *smooth, const float *share_smooth,
+                           const uint8_t *mask,
+                           const int32_t *token_subset, int32_t n_subset,
+                           uint16_t *output, uint16_t *share_output,
+                           int32_t *expert_token_nums, moe_oracle_trace *tr) {
+    return forward_impl(d, x, expert_ids, expert_scales, w1, NULL, w1s, w2, NULL, w2s, sw1, NULL, sw1s, sw2, NULL,
+                        sw2s, smooth, share_smooth, mask, token_subset, n_subset, output, share_output,
+                        expert_token_nums, tr);
+}
+
+int32_t moe_oracle_forward_mx(const moe_oracle_dims *d, const uint16_t *x,
+                              const int32_t *expert_ids, const float *expert_scales,
+                              const uint8_t *w1, const uint8_t *w1b, const float *w1s,
+                              const uint8_t *w2, const uint8_t *w2b, const float *w2s,
+                              const uint8_t *sw1, const uint8_t *sw1b, const float *sw1s,
+                              const uint8_t *sw2, const uint8_t *sw2b, const float *sw2s,
+                              const float *smooth, const float *share_smooth,
+                              const uint8_t *mask,
+                              const int32_t *token_subset, int32_t n_subset,
+                              uint16_t *output, uint16_t *share_output,
+                              int32_t *expert_token_nums, moe_oracle_trace *tr) {
+    if (!w1b || !w2b || (d && d->I_s > 0 && (!sw1b || !sw2b))) return -2;
+    if (d && (d->H % 32 || d->I % 32 || d->I_s % 32)) return -1;
+    return forward_impl(d, x, expert_ids, expert_scales, w1, w1b, w1s, w2, w2b, w2s, sw1, sw1b, sw1s, sw2, sw2b,
+                        sw2s, smooth, share_smooth, mask, token_subset, n_subset, output, share_output,
+                        expert_token_nums, tr);
 }

@@ -84,6 +84,29 @@ int32_t moe_oracle_gemm_i8(const int8_t *A, const int8_t *B, int32_t M, int32_t 
 /* SwiGLU of one dequantised GEMM1 row: h[j] = silu(y[j]) * y[n_half + j]. */
 void moe_oracle_swiglu(const float *y, int32_t n_half, float *h);
 
+/* --- FP4 weights / FP8 activations (the FP8/FP4 variant of the expert GEMMs,
+ *     "FIFO Pipeline Analysis ... Mega MoE": FP8 GEMMs, FP8 cast after
+ *     SwiGLU, FP4 weights). Formats are the OCP microscaling ones:
+ *   E4M3 (activations): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits, no
+ *     infinities, largest finite 448, code 0x7F / 0xFF NaN;
+ *   E2M1 (weights): 1 sign, 2 exponent bits (bias 1), 1 mantissa bit, values
+ *     0, 0.5, 1, 1.5, 2, 3, 4, 6; two per byte, element 2j in the low nibble;
+ *   E8M0 (weight block scales): 2^(e - 127), one per 32 consecutive K elements
+ *     of a weight row (e = 255 is NaN and not used). */
+uint8_t moe_oracle_f32_to_e4m3(float f);   /* round to nearest even, saturating at 448 */
+float   moe_oracle_e4m3_to_f32(uint8_t c);
+float   moe_oracle_e2m1_to_f32(uint8_t nibble);
+
+/* Per-row dynamic FP8 quantisation of v[0..n): a' = max(max|v|, eps);
+ * scale = a' * (1/448); q_i = e4m3((v_i * 448) * (1/a')). */
+void moe_oracle_quant_row_fp8(const float *v, int32_t n, float eps, uint8_t *q, float *scale);
+
+/* C[m][n] = sum_k e4m3(A[m][k]) * e2m1(B[n], k) * 2^(S[n][k/32] - 127): block
+ * sums exact in int64, blocks combined in double, then one rounding to fp32.
+ * A [M][Kd] codes, B [N][Kd/2] nibble pairs, S [N][Kd/32]; Kd % 32 == 0. */
+void moe_oracle_gemm_mx(const uint8_t *A, const uint8_t *B, const uint8_t *S, int32_t M, int32_t N,
+                        int32_t Kd, float *C);
+
 /* Whole block. token_subset (n_subset entries, NULL = every token) selects
  * which output rows are computed; others are left untouched. Returns 0 or a
  * negative value on bad arguments. All pointers are host pointers. */
@@ -98,6 +121,24 @@ int32_t moe_oracle_forward(const moe_oracle_dims *d, const uint16_t *x,
                            const int32_t *token_subset, int32_t n_subset,
                            uint16_t *output, uint16_t *share_output,
                            int32_t *expert_token_nums, moe_oracle_trace *tr);
+
+/* The same block with FP4 weights (E2M1 nibble pairs [.., N, K/2] plus E8M0
+ * block scales [.., N, K/32]; the fp32 per-channel scales stay) and FP8 (E4M3)
+ * activations: x and h are quantised to E4M3 per row, the GEMMs accumulate in
+ * fp32 (exact here, then rounded once), everything else as in
+ * moe_oracle_forward. Trace: q_x / q_h hold E4M3 codes, acc1 / acc2 the bits
+ * of the fp32 accumulators. */
+int32_t moe_oracle_forward_mx(const moe_oracle_dims *d, const uint16_t *x,
+                              const int32_t *expert_ids, const float *expert_scales,
+                              const uint8_t *w1, const uint8_t *w1b, const float *w1s,
+                              const uint8_t *w2, const uint8_t *w2b, const float *w2s,
+                              const uint8_t *sw1, const uint8_t *sw1b, const float *sw1s,
+                              const uint8_t *sw2, const uint8_t *sw2b, const float *sw2s,
+                              const float *smooth, const float *share_smooth,
+                              const uint8_t *mask,
+                              const int32_t *token_subset, int32_t n_subset,
+                              uint16_t *output, uint16_t *share_output,
+                              int32_t *expert_token_nums, moe_oracle_trace *tr);
 
 #ifdef __cplusplus
 }

@@ -35,9 +35,17 @@ MUTANTS = {
                               ("    for (int32_t t = 0; t < T; ++t) {\n        if (mask && !mask[t]) continue;\n        for (int32_t k = 0; k < K; ++k) {\n            int32_t g = expert_ids[t * K + k];\n            if (g < 0 || g >= d->E_g) continue;",
                                "    for (int32_t t = 0; t < T; ++t) {\n        for (int32_t k = 0; k < K; ++k) {\n            int32_t g = expert_ids[t * K + k];\n            if (g < 0 || g >= d->E_g) continue;")],
     "smooth_after_quant": [("if (ev->smooth) v = v * ev->smooth[i];", "")],
-    "shared_uses_routed_smooth": [("expert_view ev = {sw1, sw1s, sw2, sw2s, share_smooth, Is};",
-                                   "expert_view ev = {sw1, sw1s, sw2, sw2s, smooth, Is};")],
+    "shared_uses_routed_smooth": [("expert_view ev = {sw1, sw1s, sw2, sw2s, share_smooth, Is, sw1b, sw2b};",
+                                   "expert_view ev = {sw1, sw1s, sw2, sw2s, smooth, Is, sw1b, sw2b};")],
     "ep_rank_offset_ignored": [("const int32_t base = d->ep_rank * E;", "const int32_t base = 0;")],
+    # the FP4-weight / FP8-activation variant
+    "e4m3_truncates": [("float m = rintf(ldexpf(a, 3 - E));", "float m = truncf(ldexpf(a, 3 - E));")],
+    "e4m3_subnormal_step": [("const float m = rintf(a * 512.0f);", "const float m = rintf(a * 256.0f);")],
+    "e2m1_bias_off": [("ldexpf(1.0f + 0.5f * (float)m, e - 1)", "ldexpf(1.0f + 0.5f * (float)m, e)")],
+    "mx_nibble_order_swapped": [("(k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15)",
+                                 "(k & 1) ? (uint8_t)(byte & 15) : (uint8_t)(byte >> 4)")],
+    "mx_block_scale_bias": [("(int)sc[blk] - 127 - 10", "(int)sc[blk] - 128 - 10")],
+    "fp8_quant_uses_127": [("float t = v[i] * 448.0f;", "float t = v[i] * 127.0f;")],
 }
 
 

@@ -351,6 +351,117 @@ def pin_fused_route_scale():
     assert np.all(np.abs(F32(r["output"]) - ref) <= bound)
 
 
+# -------------------------------------------- FP4 weights / FP8 activations
+# OCP microscaling formats: E4M3 activations (torch.float8_e4m3fn is the
+# reference), E2M1 weights (the spec's value table), E8M0 block scales 2^(e-127).
+
+E2M1_VALUES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _e4m3_torch(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).float().numpy()
+
+
+def pin_e4m3_codes_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours, ref = oracle.e4m3_to_f32(codes), _e4m3_torch(codes)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+    # encoding: random values, exact ties, subnormals and the top of the range
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.standard_normal(4000).astype(np.float32) * np.float32(30),
+                        rng.uniform(-2e-3, 2e-3, 1000).astype(np.float32),
+                        (ref[ok][:-1] + np.diff(ref[ok])) / 2,           # midpoints of neighbouring codes
+                        np.float32([448, -448, 463.9, 464, -464, 0.0, -0.0, 2 ** -10, 3 * 2 ** -10])]).astype(
+        np.float32)
+    v = v[np.isfinite(v) & (np.abs(v) <= 464)]
+    ours = oracle.f32_to_e4m3(v)
+    tref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(_e4m3_torch(ours), _e4m3_torch(tref))
+    # beyond the range the quantiser saturates
+    assert np.array_equal(oracle.f32_to_e4m3(np.float32([500, -1e6])), np.uint8([0x7E, 0xFE]))
+
+
+def pin_e2m1_values():
+    vals = oracle.e2m1_to_f32(np.arange(16, dtype=np.uint8))
+    assert np.array_equal(vals[:8], np.float32(E2M1_VALUES))
+    assert np.array_equal(vals[8:], -np.float32(E2M1_VALUES))
+
+
+def pin_fp8_quant_rules():
+    rng = np.random.default_rng(8)
+    v = rng.standard_normal(256).astype(np.float32)
+    q, sc = oracle.quant_row_fp8(v)
+    i = int(np.argmax(np.abs(v)))
+    assert _e4m3_torch(q[i:i + 1])[0] == np.float32(448.0) * np.sign(v[i])
+    assert np.float32(sc) == np.float32(np.float32(np.abs(v).max()) * np.float32(1.0 / 448.0))
+    # every code is the nearest E4M3 value to v * 448 / amax (torch rounds)
+    t = (v * np.float32(448.0)) * (np.float32(1.0) / np.float32(np.abs(v).max()))
+    assert np.array_equal(_e4m3_torch(q), torch.from_numpy(t.astype(np.float32)).to(torch.float8_e4m3fn).float().numpy())
+    # a power-of-two rescale leaves the codes and scales the row scale exactly
+    q4, sc4 = oracle.quant_row_fp8(v * np.float32(4.0))
+    assert np.array_equal(q4, q) and sc4 == sc * 4
+    # an all-zero row: zero codes, scale eps / 448
+    qz, scz = oracle.quant_row_fp8(np.zeros(64, np.float32), eps=1e-6)
+    assert not qz.any() and np.float32(scz) == np.float32(np.float32(1e-6) * np.float32(1.0 / 448.0))
+
+
+def pin_gemm_mx_exact():
+    # every product and partial sum here is exact in float64, so numpy's
+    # matmul of the decoded operands, rounded once to fp32, is the exact result
+    rng = np.random.default_rng(9)
+    M, N, K = 5, 24, 256
+    A = rng.integers(0, 256, (M, K), dtype=np.uint8)
+    A[(A & 0x7F) == 0x7F] = 0x3C                      # no NaN codes
+    B = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    S = rng.integers(120, 135, (N, K // 32), dtype=np.uint8)
+    a = _e4m3_torch(A).astype(np.float64)
+    nib = np.empty((N, K), np.uint8)
+    nib[:, 0::2], nib[:, 1::2] = B & 15, B >> 4        # element 2j in the low nibble
+    table = np.array(E2M1_VALUES + [-x for x in E2M1_VALUES])
+    b = table[nib] * np.repeat(2.0 ** (S.astype(np.float64) - 127), 32, axis=1)
+    ref = (a @ b.T).astype(np.float32)
+    assert np.array_equal(oracle.gemm_mx(A, B, S), ref)
+
+
+def pin_mx_block_scale_linearity():
+    # the up half's block scales + 1: h doubles, so the FP8 codes of h stay and
+    # its row scale, every z row and the output double exactly
+    spec = small_spec(T=7, H=128, I=64, E_g=4, K=2, I_s=64, weight_format="mxfp4", wseed=21)
+    c = synth.make_case(spec)
+    r = run(c, trace=True)
+    w1b = c.w1b.copy()
+    w1b[:, spec.I:] += 1
+    sw1b = c.sw1b.copy()
+    sw1b[spec.I_s:] += 1
+    r2 = run(_replace(c, w1b=w1b, sw1b=sw1b), trace=True)
+    rows = np.concatenate([np.arange(r["P"]), r["P"] + np.arange(r["T_act"])])
+    assert np.array_equal(r2["q_h"][rows], r["q_h"][rows]) and np.array_equal(r2["hs"][rows], r["hs"][rows] * 2)
+    assert np.array_equal(F32(r2["output"]), F32(r["output"]) * 2)
+    assert np.array_equal(F32(r2["share_output"]), F32(r["share_output"]) * 2)
+    # GEMM2's block scales + 1: its accumulators and outputs double
+    r3 = run(_replace(c, w2b=c.w2b + 1, sw2b=c.sw2b + 1), trace=True)
+    assert np.array_equal(r3["acc2"][rows], r["acc2"][rows] * 2)
+    assert np.array_equal(F32(r3["output"]), F32(r["output"]) * 2)
+
+
+def pin_mx_forward_stages():
+    # the traced stages of a whole FP4-weight block agree with the helpers
+    # pinned above, applied row by row in numpy
+    spec = small_spec(T=6, H=128, I=64, E_g=3, K=2, I_s=64, weight_format="mxfp4", smooth=True, wseed=22)
+    c = synth.make_case(spec)
+    r = run(c, trace=True)
+    e_row = np.repeat(np.arange(spec.E_loc), r["expert_token_nums"])
+    for row in range(r["P"]):
+        t = r["sorted_pair"][row] // spec.K
+        v = F32(c.x[t]) * c.smooth[e_row[row]]
+        q, sc = oracle.quant_row_fp8(v)
+        assert np.array_equal(r["q_x"][row], q) and np.float32(r["xs"][row]) == np.float32(sc)
+        acc = oracle.gemm_mx(q[None], c.w1[e_row[row]], c.w1b[e_row[row]])[0]
+        assert np.array_equal(r["acc1"][row, :2 * spec.I], acc)
+
+
 def pin_mask_and_ep_share():
     spec = small_spec(T=10, E_g=8, K=3, I_s=32, active=6, wseed=5)
     c = synth.make_case(spec)
@@ -429,7 +540,8 @@ PINS = [pin_route_bruteforce, pin_route_count_invariant, pin_quant_closed_forms,
         pin_quant_integer_rows, pin_quant_pow2_invariance, pin_gemm_exact, pin_swiglu_vs_torch,
         pin_dense_swiglu_ffn, pin_scale_linearity, pin_permutation_invariance, pin_combine,
         pin_mask_and_ep_share, pin_shared_matches_routed, pin_smooth_scales, pin_subset_and_empty,
-        pin_fused_route_scale]
+        pin_fused_route_scale, pin_e4m3_codes_vs_torch, pin_e2m1_values, pin_fp8_quant_rules, pin_gemm_mx_exact,
+        pin_mx_block_scale_linearity, pin_mx_forward_stages]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
