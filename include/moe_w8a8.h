@@ -89,9 +89,23 @@ typedef struct {
                             /*   weight is folded into the row's GEMM2 dequant scale */
                             /*   (fl(hs * w), "DeepSeek V4 Decode Optimization" sec. */
                             /*   2.3) and combine only sums; z rows then carry it    */
+    int32_t weight_format;  /* MOE_WEIGHT_INT8: the W8A8 block above.               */
+                            /*   MOE_WEIGHT_MXFP4: the FP8/FP4 variant of the expert */
+                            /*   GEMMs ("FIFO Pipeline Analysis ... Mega MoE": FP8   */
+                            /*   GEMMs, FP8 cast after SwiGLU, FP4 weights): x and h */
+                            /*   are quantised per row to FP8 E4M3 (scale = a'/448, */
+                            /*   q = e4m3((v*448)/a'), round to nearest even,        */
+                            /*   saturating), the weights are OCP E2M1 with one E8M0 */
+                            /*   scale per 32 k elements and keep their fp32         */
+                            /*   per-channel scales, the GEMMs accumulate in fp32.   */
+                            /*   Requires weight_layout == MOE_WEIGHT_PACKED (else   */
+                            /*   MOE_ERR_UNSUPPORTED) with every weight tensor       */
+                            /*   written by moe_w8a8_pack_weights_mx; the debug      */
+                            /*   acc1 / acc2 dumps then hold fp32 bit patterns       */
 } moe_w8a8_dims_t;
 
 enum { MOE_WEIGHT_ROW_MAJOR = 0, MOE_WEIGHT_PACKED = 1 };
+enum { MOE_WEIGHT_INT8 = 0, MOE_WEIGHT_MXFP4 = 1 };
 
 /* Optional intermediates for testing (every field may be NULL; all are device
  * buffers written in stream order). Rows are "grouped rows": rows [0, P) are
@@ -206,6 +220,30 @@ MOE_W8A8_API moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *dims,
 enum { MOE_PACK_GMM1 = 1, MOE_PACK_GMM2 = 2 };
 MOE_W8A8_API moe_status_t moe_w8a8_pack_weights(const int8_t *src, int8_t *dst, int64_t groups, int32_t n,
                                                 int32_t k, int32_t which, void *stream);
+
+/*
+ * FP4 weights for weight_format == MOE_WEIGHT_MXFP4, re-laid once at load time
+ * (OCP microscaling formats: E2M1 elements, E8M0 scale 2^(e-127) per block of
+ * 32 consecutive k elements of a weight row).
+ *
+ *  data         uint8 [groups, n, k/2]: element k' of row r in the low nibble
+ *               of byte k'/2 when k' is even, the high nibble when odd
+ *  block_scale  uint8 [groups, n, k/32] E8M0 exponents (255 = NaN: not allowed)
+ *  which        MOE_PACK_GMM1 / MOE_PACK_GMM2 as for moe_w8a8_pack_weights
+ *  dst          moe_w8a8_packed_mx_bytes(groups, n, k) bytes, 16-byte aligned:
+ *               first the element blocks, exactly as moe_w8a8_pack_weights lays
+ *               out a [groups, n, k/2] int8 tensor (one 1024-byte block per
+ *               16-row tile and 128-element k step), then the scales: for group
+ *               g, tile position p and k step s, the 64 bytes at
+ *               D + ((g*(n/16) + p)*(k/128) + s)*64, D = groups*n*k/2, hold at
+ *               byte l (l in [0,64)) block_scale[g][16j + l%16][4s + l/16], with
+ *               j the tile of position p as in moe_w8a8_pack_weights
+ *  n % 32 == 0, k % 128 == 0; no buffer may overlap dst. Stream-ordered.
+ */
+MOE_W8A8_API moe_status_t moe_w8a8_packed_mx_bytes(int64_t groups, int32_t n, int32_t k, size_t *bytes);
+MOE_W8A8_API moe_status_t moe_w8a8_pack_weights_mx(const uint8_t *data, const uint8_t *block_scale, uint8_t *dst,
+                                                   int64_t groups, int32_t n, int32_t k, int32_t which,
+                                                   void *stream);
 
 /* Static description of a status code. Never NULL. */
 MOE_W8A8_API const char *moe_w8a8_status_string(moe_status_t status);

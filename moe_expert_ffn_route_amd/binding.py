@@ -19,8 +19,10 @@ LIB_PATH = os.path.join(PKG, "libmoe_w8a8.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 
-EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_forward", "moe_w8a8_pack_weights", "moe_w8a8_status_string")
+EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_forward", "moe_w8a8_pack_weights", "moe_w8a8_packed_mx_bytes",
+           "moe_w8a8_pack_weights_mx", "moe_w8a8_status_string")
 MOE_WEIGHT_ROW_MAJOR, MOE_WEIGHT_PACKED = 0, 1
+MOE_WEIGHT_INT8, MOE_WEIGHT_MXFP4 = 0, 1
 MOE_PACK_GMM1, MOE_PACK_GMM2 = 1, 2
 
 
@@ -36,7 +38,7 @@ class Dims(ctypes.Structure):
                 ("share_inter", ctypes.c_int32), ("topk", ctypes.c_int32), ("moe_expert_num", ctypes.c_int32),
                 ("ep_rank_size", ctypes.c_int32), ("ep_rank_id", ctypes.c_int32), ("quant_mode", ctypes.c_int32),
                 ("amax_eps", ctypes.c_float), ("weight_layout", ctypes.c_int32),
-                ("fuse_route_scale", ctypes.c_int32)]
+                ("fuse_route_scale", ctypes.c_int32), ("weight_format", ctypes.c_int32)]
 
     @property
     def e_loc(self) -> int:
@@ -70,6 +72,12 @@ def library() -> ctypes.CDLL:
         L.moe_w8a8_forward.argtypes = ([ctypes.POINTER(Dims)] + [P] * 18 + [ctypes.c_size_t, ctypes.POINTER(Debug), P])
         L.moe_w8a8_pack_weights.restype = ctypes.c_int
         L.moe_w8a8_pack_weights.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
+        L.moe_w8a8_packed_mx_bytes.restype = ctypes.c_int
+        L.moe_w8a8_packed_mx_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_w8a8_pack_weights_mx.restype = ctypes.c_int
+        L.moe_w8a8_pack_weights_mx.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, P]
         L.moe_w8a8_status_string.restype = ctypes.c_char_p
         L.moe_w8a8_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -77,9 +85,10 @@ def library() -> ctypes.CDLL:
 
 
 def make_dims(num_tokens, hidden, inter, topk, moe_expert_num, share_inter=0, ep_rank_size=1, ep_rank_id=0,
-              quant_mode=1, amax_eps=1e-6, weight_layout=MOE_WEIGHT_ROW_MAJOR, fuse_route_scale=0) -> Dims:
+              quant_mode=1, amax_eps=1e-6, weight_layout=MOE_WEIGHT_ROW_MAJOR, fuse_route_scale=0,
+              weight_format=MOE_WEIGHT_INT8) -> Dims:
     return Dims(num_tokens, hidden, inter, share_inter, topk, moe_expert_num, ep_rank_size, ep_rank_id, quant_mode,
-                amax_eps, weight_layout, fuse_route_scale)
+                amax_eps, weight_layout, fuse_route_scale, weight_format)
 
 
 def moe_w8a8_status_string(code: int) -> str:
@@ -108,6 +117,35 @@ def moe_w8a8_pack_weights(src, which, dst=None, stream=None):
     rc = library().moe_w8a8_pack_weights(_ptr(src), _ptr(dst), shape[0], shape[1], shape[2], which, stream)
     if rc != MOE_OK:
         raise MoeError(rc, "moe_w8a8_pack_weights")
+    return dst
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else stream
+
+
+def moe_w8a8_packed_mx_bytes(groups: int, n: int, k: int) -> int:
+    b = ctypes.c_size_t(0)
+    rc = library().moe_w8a8_packed_mx_bytes(groups, n, k, ctypes.byref(b))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_w8a8_packed_mx_bytes")
+    return int(b.value)
+
+
+def moe_w8a8_pack_weights_mx(data, block_scale, which, dst=None, stream=None):
+    """Pack FP4 weights (uint8 E2M1 pairs [groups, n, k/2] or [n, k/2], E8M0
+    block scales [.., n, k/32], device tensors) into one buffer for
+    weight_format MOE_WEIGHT_MXFP4. Returns dst (uint8, allocated if None)."""
+    shape = data.shape if data.dim() == 3 else (1, *data.shape)
+    groups, n, k = shape[0], shape[1], 2 * shape[2]
+    if dst is None:
+        dst = torch.empty(moe_w8a8_packed_mx_bytes(groups, n, k), dtype=torch.uint8, device=data.device)
+    rc = library().moe_w8a8_pack_weights_mx(_ptr(data), _ptr(block_scale), _ptr(dst), groups, n, k, which,
+                                            _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_w8a8_pack_weights_mx")
     return dst
 
 
@@ -181,11 +219,24 @@ def upload(case, device="cuda", weights=None) -> dict:
              expert_ids=t(case.expert_ids), expert_scales=t(case.expert_scales),
              expert_smooth_scales=t(case.smooth), share_smooth_scales=t(case.share_smooth),
              x_active_mask=t(case.mask))
-    if weights is None:
+    if weights is None and case.w1b is None:
         weights = dict(gmm1_weight=t(case.w1), gmm1_weight_scale=t(case.w1s), gmm2_weight=t(case.w2),
                        gmm2_weight_scale=t(case.w2s), share_gmm1_weight=t(case.sw1),
                        share_gmm1_weight_scale=t(case.sw1s), share_gmm2_weight=t(case.sw2),
                        share_gmm2_weight_scale=t(case.sw2s))
+    if weights is None and case.w1b is not None:
+        # FP4 weights: element pairs and block scales packed into one buffer each
+        weights = {}
+        for name, data, bs in (("gmm1_weight", case.w1, case.w1b), ("gmm2_weight", case.w2, case.w2b),
+                               ("share_gmm1_weight", case.sw1, case.sw1b),
+                               ("share_gmm2_weight", case.sw2, case.sw2b)):
+            if data is not None:
+                weights[name] = moe_w8a8_pack_weights_mx(t(data), t(bs),
+                                                         MOE_PACK_GMM1 if "gmm1" in name else MOE_PACK_GMM2)
+        weights.update(gmm1_weight_scale=t(case.w1s), gmm2_weight_scale=t(case.w2s),
+                       share_gmm1_weight_scale=t(case.sw1s), share_gmm2_weight_scale=t(case.sw2s))
+        for k in ("share_gmm1_weight", "share_gmm2_weight"):
+            weights.setdefault(k, None)
     d.update(weights)
     return d
 

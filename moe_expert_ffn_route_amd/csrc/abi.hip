@@ -33,6 +33,8 @@ moe_status_t check_dims(const moe_w8a8_dims_t *d) {
     if (d->hidden > 16384 || d->inter > 16384 || d->share_inter > 16384) return MOE_ERR_UNSUPPORTED;
     if (d->weight_layout != MOE_WEIGHT_ROW_MAJOR && d->weight_layout != MOE_WEIGHT_PACKED) return MOE_ERR_INVALID_ARG;
     if (d->fuse_route_scale != 0 && d->fuse_route_scale != 1) return MOE_ERR_INVALID_ARG;
+    if (d->weight_format != MOE_WEIGHT_INT8 && d->weight_format != MOE_WEIGHT_MXFP4) return MOE_ERR_INVALID_ARG;
+    if (d->weight_format == MOE_WEIGHT_MXFP4 && d->weight_layout != MOE_WEIGHT_PACKED) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -45,10 +47,12 @@ Layout make_layout(const moe_w8a8_dims_t *d) {
     L.imax = d->inter > d->share_inter ? d->inter : d->share_inter;
     L.rows_max = static_cast<int>(TK + T);
     const size_t nonempty = E < TK ? E : TK;
-    // rows per GEMM work item: 16 for decode batches; 128 (tall items) when
-    // the routed experts average kTallMinRows rows or more; 32 otherwise
+    // rows per GEMM work item: 16 for decode batches; 256 (tall items) when
+    // the routed experts average kTallMinRows rows or more; 32 otherwise.
+    // FP4 weights run 16-row items at every batch size (gemm_mx.hip).
     const bool tall = T >= kTallMinRows && TK >= static_cast<size_t>(kTallMinRows) * E;
-    L.chunk_rows = T <= kChunkRowsSmall ? kChunkRowsSmall : tall ? kChunkRowsTall : kChunkRowsLarge;
+    const bool mx = d->weight_format == MOE_WEIGHT_MXFP4;
+    L.chunk_rows = mx || T <= kChunkRowsSmall ? kChunkRowsSmall : tall ? kChunkRowsTall : kChunkRowsLarge;
     const size_t cr = L.chunk_rows;
     L.max_chunks = static_cast<int>(nonempty + TK / cr + (shared ? (T + cr - 1) / cr : 0));
     const size_t R = L.rows_max;
@@ -94,6 +98,29 @@ extern "C" moe_status_t moe_w8a8_pack_weights(const int8_t *src, int8_t *dst, in
     if (bytes / 16 / 256 >= (1ull << 31)) return MOE_ERR_UNSUPPORTED;
     return launch_pack(src, dst, groups, n, k, which, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK
                                                                                                   : MOE_ERR_HIP;
+}
+
+extern "C" moe_status_t moe_w8a8_packed_mx_bytes(int64_t groups, int32_t n, int32_t k, size_t *bytes) {
+    if (!bytes || groups < 0 || n <= 0 || k <= 0 || n % 32 || k % 128) return MOE_ERR_INVALID_ARG;
+    *bytes = static_cast<size_t>(groups) * n * (k / 2 + k / 32);
+    return MOE_OK;
+}
+
+extern "C" moe_status_t moe_w8a8_pack_weights_mx(const uint8_t *data, const uint8_t *block_scale, uint8_t *dst,
+                                                 int64_t groups, int32_t n, int32_t k, int32_t which, void *stream) {
+    size_t bytes = 0;
+    if (!data || !block_scale || !dst || moe_w8a8_packed_mx_bytes(groups, n, k, &bytes) != MOE_OK)
+        return MOE_ERR_INVALID_ARG;
+    if (which != MOE_PACK_GMM1 && which != MOE_PACK_GMM2) return MOE_ERR_INVALID_ARG;
+    if (!aligned(data, 16) || !aligned(dst, 16)) return MOE_ERR_INVALID_ARG;
+    const uint64_t nd = static_cast<uint64_t>(groups) * n * (k / 2), ns = static_cast<uint64_t>(groups) * n * (k / 32);
+    const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst), a0 = reinterpret_cast<uintptr_t>(data),
+                    b0 = reinterpret_cast<uintptr_t>(block_scale);
+    if ((a0 < d0 + bytes && d0 < a0 + nd) || (b0 < d0 + bytes && d0 < b0 + ns)) return MOE_ERR_INVALID_ARG;
+    if (nd / 16 / 256 >= (1ull << 31)) return MOE_ERR_UNSUPPORTED;
+    return launch_pack_mx(data, block_scale, dst, groups, n, k, which, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
 }
 
 extern "C" const char *moe_w8a8_status_string(moe_status_t s) {
@@ -199,6 +226,8 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
     tq.share_smooth = T > 0 && shared ? share_smooth_scales : nullptr;
     tq.q_sm = reinterpret_cast<int8_t *>(ws + L.q_sm);
     tq.s_sm = reinterpret_cast<float *>(ws + L.s_sm);
+    const bool mx = d->weight_format == MOE_WEIGHT_MXFP4;
+    tq.fp8 = mx;
     if (launch_route_quant(ra, tq, s) != hipSuccess || !mark(1)) return MOE_ERR_HIP;
 
     // GEMM1's activation rows: per token (q_tok, index row_token) or per
@@ -234,9 +263,10 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g1.g_hi = E + 1;
         g1.packed = d->weight_layout == MOE_WEIGHT_PACKED;
         g1.mt = L.chunk_rows / kTileN;
-        // three kernels by chunk size: decode (gemm.hip), wide (gemm_wide.hip)
-        // and tall (gemm_tall.hip) work items
-        const bool tall = g1.mt == kTallTiles, wide = g1.mt == kWideTiles;
+        // three INT8 kernels by chunk size: decode (gemm.hip), wide
+        // (gemm_wide.hip) and tall (gemm_tall.hip) work items; FP4 weights:
+        // gemm_mx.hip (16-row items)
+        const bool tall = !mx && g1.mt == kTallTiles, wide = !mx && g1.mt == kWideTiles;
         const int nw = tall ? kTallPairs : wide ? wide_tile_pairs() : 1;  // tile pairs per work item
         g1.n_tiles = L.imax / kTileN / nw;
         g1.chunks = ra.chunks;
@@ -245,7 +275,8 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g1.row_token = ra.row_token;
         g1.h = reinterpret_cast<float *>(ws + L.h);
         g1.dbg_acc = D.acc1;
-        const hipError_t e1 = tall   ? launch_gemm1_tall(g1, L.max_chunks, s, kev(0), kev(1))
+        const hipError_t e1 = mx     ? launch_gemm1_mx(g1, L.max_chunks, s, kev(0), kev(1))
+                              : tall ? launch_gemm1_tall(g1, L.max_chunks, s, kev(0), kev(1))
                               : wide ? launch_gemm1_wide(g1, L.max_chunks, s, kev(0), kev(1))
                                      : launch_gemm1(g1, L.max_chunks, s, kev(0), kev(1));
         if (e1 != hipSuccess || !mark(2)) return MOE_ERR_HIP;
@@ -268,6 +299,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         rq.scale2 = fused ? reinterpret_cast<float *>(ws + L.hs2) : nullptr;
         rq.route_w = expert_scales;
         rq.sorted_pair = ra.sorted_pair;
+        rq.fp8 = mx;
         if (launch_requant(rq, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
 
         GemmArgs g2 = g1;
@@ -286,7 +318,8 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g2.dbg_z = D.z;
         // the contraction length of GEMM2 is the group's intermediate size
         auto gemm2 = [&](int k_dim, hipEvent_t e0, hipEvent_t e1) {
-            return tall   ? launch_gemm2_tall(g2, L.max_chunks, k_dim, s, e0, e1)
+            return mx     ? launch_gemm2_mx(g2, L.max_chunks, k_dim, s, e0, e1)
+                   : tall ? launch_gemm2_tall(g2, L.max_chunks, k_dim, s, e0, e1)
                    : wide ? launch_gemm2_wide(g2, L.max_chunks, k_dim, s, e0, e1)
                           : launch_gemm2(g2, L.max_chunks, k_dim, s, e0, e1);
         };

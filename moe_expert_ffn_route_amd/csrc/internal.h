@@ -89,6 +89,7 @@ struct TokQuantArgs {
     const float *share_smooth;  // [H] or null
     int8_t *q_sm;          // [T*K + T, H]
     float *s_sm;           // [T*K + T]
+    int fp8;               // quantise to FP8 E4M3 codes instead of INT8
 };
 
 struct RequantArgs {
@@ -105,6 +106,7 @@ struct RequantArgs {
     float *scale2;
     const float *route_w;        // [T*K]
     const int32_t *sorted_pair;  // [P]
+    int fp8;                     // FP8 E4M3 codes instead of INT8
 };
 
 struct GemmArgs {
@@ -169,8 +171,16 @@ int wide_tile_pairs();
 hipError_t launch_gemm1_tall(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_gemm2_tall(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
                              hipEvent_t ev_stop);
+// FP4-weight / FP8-activation GEMMs (gemm_mx.hip): 16-row work items as in
+// gemm.hip, weights from moe_w8a8_pack_weights_mx, A codes FP8 E4M3; k_dim %
+// 256 == 0. dbg_acc receives fp32 bit patterns.
+hipError_t launch_gemm1_mx(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_gemm2_mx(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
+                           hipEvent_t ev_stop);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_pack(const int8_t *src, int8_t *dst, int64_t groups, int n, int k, int which, hipStream_t s);
+hipError_t launch_pack_mx(const uint8_t *data, const uint8_t *bscale, uint8_t *dst, int64_t groups, int n, int k,
+                          int which, hipStream_t s);
 // debug only: the GEMM1 input rows of every grouped row (q_x / xs dump)
 hipError_t launch_dbg_gather(const GemmArgs &g1, const int32_t *row_group, const int32_t *meta, int has_shared,
                              int rows_max, int8_t *dst_q, float *dst_xs, hipStream_t s);
@@ -198,11 +208,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 //   dequant ("FusedDeepMoE Kernel 深度分析报告" sec. 6.1, 6.2):
 //     y = (float(acc) * w_scale[n]) * row_scale[r];
 //   SwiGLU (sec. 6.1): h = (y_g / (1 + exp(-y_g))) * y_u.
-__device__ __forceinline__ float dequant(int acc, float w_scale, float row_scale) {
+// The accumulator is int32 (INT8 GEMMs) or fp32 (FP4-weight GEMMs).
+template <typename Acc>
+__device__ __forceinline__ float dequant(Acc acc, float w_scale, float row_scale) {
     const float y = static_cast<float>(acc) * w_scale;
     return y * row_scale;
 }
-__device__ __forceinline__ float swiglu(int acc_g, int acc_u, float ws_g, float ws_u, float row_scale) {
+template <typename Acc>
+__device__ __forceinline__ float swiglu(Acc acc_g, Acc acc_u, float ws_g, float ws_u, float row_scale) {
     const float yg = dequant(acc_g, ws_g, row_scale);
     const float yu = dequant(acc_u, ws_u, row_scale);
     const float ex = expf(-yg);

@@ -1,4 +1,5 @@
-// Row quantisation kernels (the rule and its fp32 order are in rowquant.h):
+// Row quantisation kernels (the rule and its fp32 order are in rowquant.h;
+// FP8 instantiations quantise to E4M3 for the FP4-weight variant):
 //
 //   requant_wave_kernel / requant_kernel  the SwiGLU output h of every
 //                        grouped row ("FusedDeepMoE Kernel 深度分析报告"
@@ -15,13 +16,14 @@
 namespace moe {
 namespace {
 
+template <bool FP8>
 __global__ __launch_bounds__(kTPR) void requant_kernel(RequantArgs a) {
     __shared__ float s_part[kTPR / kWave];
     const int r = blockIdx.x;
     const int nrows = a.meta[kMetaP] + (a.has_shared ? a.meta[kMetaTAct] : 0);
     if (r >= nrows) return;
     const int n = a.row_group[r] < a.E_loc ? a.I : a.I_s;
-    quant_f32_row(a.h + static_cast<size_t>(r) * a.imax, n, a.eps, a.q + static_cast<size_t>(r) * a.imax,
+    quant_f32_row<FP8>(a.h + static_cast<size_t>(r) * a.imax, n, a.eps, a.q + static_cast<size_t>(r) * a.imax,
                   a.scale + r, true, 0, threadIdx.x, s_part);
     if (a.scale2 && threadIdx.x == 0) {  // the thread that wrote scale[r]
         const float hs = a.scale[r];
@@ -37,7 +39,7 @@ __device__ __forceinline__ int wave_row() {
 }
 
 // NCH 16-byte chunks of fp32 per lane: rows of up to NCH * 256 values.
-template <int NCH>
+template <int NCH, bool FP8>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void requant_wave_kernel(RequantArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const int r = wave_row();
@@ -73,10 +75,10 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void requant_wave_kernel(Req
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
         const int i = (lane + j * kWave) * 4;
-        if (i < n) *reinterpret_cast<uint32_t *>(dst + i) = quant4(v[j].x, v[j].y, v[j].z, v[j].w, inv);
+        if (i < n) *reinterpret_cast<uint32_t *>(dst + i) = quant4<FP8>(v[j].x, v[j].y, v[j].z, v[j].w, inv);
     }
     if (lane == 0) {
-        const float hs = ap * (1.0f / 127.0f);
+        const float hs = ap * (1.0f / kQMax<FP8>);
         a.scale[r] = hs;
         if (a.scale2) a.scale2[r] = r < P ? hs * a.route_w[a.sorted_pair[r]] : hs;
     }
@@ -99,18 +101,24 @@ __global__ __launch_bounds__(256) void dbg_gather_kernel(GemmArgs g, const int32
     if (dst_xs && threadIdx.x == 0) dst_xs[r] = (routed ? g.a_scale_r : g.a_scale_s)[src];
 }
 
+template <bool FP8>
+hipError_t launch_requant_fmt(const RequantArgs &a, dim3 wgrid, dim3 wblk, hipStream_t s) {
+    if (a.imax <= 8 * 256)
+        hipLaunchKernelGGL((requant_wave_kernel<8, FP8>), wgrid, wblk, 0, s, a);
+    else if (a.imax <= 16 * 256)
+        hipLaunchKernelGGL((requant_wave_kernel<16, FP8>), wgrid, wblk, 0, s, a);
+    else
+        hipLaunchKernelGGL(requant_kernel<FP8>, dim3(a.rows_max), dim3(kTPR), 0, s, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_requant(const RequantArgs &a, hipStream_t s) {
     if (a.rows_max <= 0) return hipSuccess;
     const dim3 wgrid((a.rows_max + kRowsPerBlock - 1) / kRowsPerBlock), wblk(kRowsPerBlock * kWave);
-    if (a.imax <= 8 * 256)
-        hipLaunchKernelGGL(requant_wave_kernel<8>, wgrid, wblk, 0, s, a);
-    else if (a.imax <= 16 * 256)
-        hipLaunchKernelGGL(requant_wave_kernel<16>, wgrid, wblk, 0, s, a);
-    else
-        hipLaunchKernelGGL(requant_kernel, dim3(a.rows_max), dim3(kTPR), 0, s, a);
-    return hipGetLastError();
+    if (a.fp8) return launch_requant_fmt<true>(a, wgrid, wblk, s);
+    return launch_requant_fmt<false>(a, wgrid, wblk, s);
 }
 
 hipError_t launch_dbg_gather(const GemmArgs &g1, const int32_t *row_group, const int32_t *meta, int has_shared,

@@ -250,6 +250,7 @@ constexpr int kTokQuantSlots = kRouteThreads / kTPR;  // rows quantised per bloc
 // some group reads plain per-token rows), then the (token, expert) pairs (when
 // expert smooth scales are given), then the tokens again (when the shared
 // expert has smooth scales).
+template <bool FP8>
 __device__ __forceinline__ void quant_unit(const TokQuantArgs &q, int u, int slot, int tr, float *s_part) {
     const int n_tok = q.q_tok ? q.T : 0;
     const int n_pair = q.smooth ? q.T * q.K : 0;
@@ -282,7 +283,7 @@ __device__ __forceinline__ void quant_unit(const TokQuantArgs &q, int u, int slo
         dst = q.q_sm + row * q.H;
         scale = q.s_sm + row;
     }
-    quant_bf16_row(src, sm, q.H, q.eps, dst, scale, active, slot, tr, s_part);
+    quant_bf16_row<FP8>(src, sm, q.H, q.eps, dst, scale, active, slot, tr, s_part);
 }
 
 __device__ __forceinline__ int quant_units(const TokQuantArgs &q) {
@@ -291,7 +292,9 @@ __device__ __forceinline__ int quant_units(const TokQuantArgs &q) {
 
 // Block 0 routes; blocks 1.. quantise rows of x (FusedDeepMoE sec. 4.1
 // quantises in dispatch). Neither job needs the other's result, so one launch
-// runs both side by side.
+// runs both side by side. FP8: rows are quantised to E4M3 (FP4-weight
+// variant) instead of INT8.
+template <bool FP8>
 __global__ __launch_bounds__(kRouteThreads) void route_quant_kernel(RouteArgs a, TokQuantArgs q) {
     if (blockIdx.x == 0) {
         route_block(a);
@@ -302,9 +305,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_quant_kernel(RouteArgs a,
     const int u = (blockIdx.x - 1) * kTokQuantSlots + slot;
     // units past the end take part in the block's barrier only
     if (u < quant_units(q)) {
-        quant_unit(q, u, slot, tr, s_part);
+        quant_unit<FP8>(q, u, slot, tr, s_part);
     } else {
-        quant_bf16_row(q.x, nullptr, q.H, q.eps, nullptr, nullptr, false, slot, tr, s_part);
+        quant_bf16_row<FP8>(q.x, nullptr, q.H, q.eps, nullptr, nullptr, false, slot, tr, s_part);
     }
 }
 
@@ -313,7 +316,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_quant_kernel(RouteArgs a,
 hipError_t launch_route_quant(const RouteArgs &a, const TokQuantArgs &q, hipStream_t s) {
     const int units = (q.q_tok ? q.T : 0) + (q.smooth ? q.T * q.K : 0) + (q.share_smooth ? q.T : 0);
     const int qblocks = (units + kTokQuantSlots - 1) / kTokQuantSlots;
-    hipLaunchKernelGGL(route_quant_kernel, dim3(1 + qblocks), dim3(kRouteThreads), 0, s, a, q);
+    if (q.fp8)
+        hipLaunchKernelGGL(route_quant_kernel<true>, dim3(1 + qblocks), dim3(kRouteThreads), 0, s, a, q);
+    else
+        hipLaunchKernelGGL(route_quant_kernel<false>, dim3(1 + qblocks), dim3(kRouteThreads), 0, s, a, q);
     return hipGetLastError();
 }
 

@@ -1,9 +1,12 @@
-// Per-row dynamic INT8 quantisation, as block-cooperative device functions.
+// Per-row dynamic INT8 (or FP8 E4M3) quantisation, as block-cooperative
+// device functions.
 //
 // The rule ("FusedDeepMoE Kernel 深度分析报告" sec. 7.2 BlockQuant, with the
 // eps floor of "DeepSeek V4 Decode Optimization" sec. 0):
 //   a' = max(max_i |v_i|, eps);  scale = a' * (1/127);
 //   q_i = rint((v_i * 127) * (1/a'))  (round to nearest even)
+// The FP8 form (FP4-weight variant) takes 448, the largest E4M3 value, for 127
+// and rounds to the E4M3 grid instead of to integers.
 // Every product is a separate IEEE fp32 operation (the library is built with
 // -ffp-contract=off) and 1/a' is a correctly rounded division, so the codes
 // are the exact function of the fp32 inputs that the rule defines.
@@ -39,10 +42,44 @@ __device__ __forceinline__ float row_amax(float m, int slot, int tr, float *s_pa
     return a;
 }
 
+// fp32 -> FP8 E4M3 code (OCP "e4m3fn": bias 7, 3 mantissa bits, largest
+// finite 448): round to nearest, ties to even, on the E4M3 grid (subnormal
+// step 2^-9); magnitudes that round above 448 saturate to 448; NaN -> 0x7F.
+__device__ __forceinline__ uint32_t e4m3_code(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return 0x7Fu;
+    const uint32_t sign = (u >> 24) & 0x80u;
+    if (a >= 0x43E00000u) return sign | 0x7Eu;   // |f| >= 448
+    if (a < 0x3C800000u) {                        // |f| < 2^-6: codes m * 2^-9 (m = 8 is 2^-6)
+        const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);
+        return sign | static_cast<uint32_t>(m);
+    }
+    int e = static_cast<int>(a >> 23) - 127;      // -6 .. 8
+    uint32_t q = (a >> 20) & 7u;                  // the 3 kept mantissa bits
+    const uint32_t rem = a & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
+    if (q == 8u) {
+        q = 0u;
+        ++e;
+    }
+    if (e > 8 || (e == 8 && q == 7u)) return sign | 0x7Eu;
+    return sign | (static_cast<uint32_t>(e + 7) << 3) | q;
+}
+
+// Largest code value of the format: 127 (int8) or 448 (FP8 E4M3).
+template <bool FP8>
+constexpr float kQMax = FP8 ? 448.0f : 127.0f;
+
+// Four values quantised with one row's inv = 1/a': int8 q = rint((v * 127) *
+// inv) in [-127, 127], or FP8 q = e4m3((v * 448) * inv); packed little end
+// first.
+template <bool FP8 = false>
 __device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float inv) {
-    auto q = [inv](float v) {
-        float t = v * 127.0f;
+    auto q = [inv](float v) -> uint32_t {
+        float t = v * kQMax<FP8>;
         t = t * inv;
+        if (FP8) return e4m3_code(t);
         float r = __builtin_rintf(t);
         r = fminf(fmaxf(r, -127.0f), 127.0f);
         return static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(static_cast<int>(r))));
@@ -53,6 +90,7 @@ __device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, f
 // Quantise a bf16 row of length n (multiple of 8), optionally times smooth
 // scales, into dst; lane tr of slot `slot`. `active` may be false for a
 // whole slot (its threads still take part in the barrier).
+template <bool FP8 = false>
 __device__ __forceinline__ void quant_bf16_row(const uint16_t *src, const float *smooth, int n, float eps,
                                                int8_t *dst, float *scale_out, bool active, int slot, int tr,
                                                float *s_part) {
@@ -88,15 +126,16 @@ __device__ __forceinline__ void quant_bf16_row(const uint16_t *src, const float 
     for (int j = 0; j < kBf16Chunks; ++j) {
         const int i = (tr + j * kTPR) * 8;
         if (i < n) {
-            const uint32_t lo = quant4(v[j][0], v[j][1], v[j][2], v[j][3], inv);
-            const uint32_t hi = quant4(v[j][4], v[j][5], v[j][6], v[j][7], inv);
+            const uint32_t lo = quant4<FP8>(v[j][0], v[j][1], v[j][2], v[j][3], inv);
+            const uint32_t hi = quant4<FP8>(v[j][4], v[j][5], v[j][6], v[j][7], inv);
             *reinterpret_cast<uint2 *>(dst + i) = make_uint2(lo, hi);
         }
     }
-    if (tr == 0) *scale_out = ap * (1.0f / 127.0f);
+    if (tr == 0) *scale_out = ap * (1.0f / kQMax<FP8>);
 }
 
 // Quantise an fp32 row of length n (multiple of 4) into dst.
+template <bool FP8 = false>
 __device__ __forceinline__ void quant_f32_row(const float *src, int n, float eps, int8_t *dst, float *scale_out,
                                               bool active, int slot, int tr, float *s_part) {
     float4 v[kF32Chunks];
@@ -115,9 +154,9 @@ __device__ __forceinline__ void quant_f32_row(const float *src, int n, float eps
 #pragma unroll
     for (int j = 0; j < kF32Chunks; ++j) {
         const int i = (tr + j * kTPR) * 4;
-        if (i < n) *reinterpret_cast<uint32_t *>(dst + i) = quant4(v[j].x, v[j].y, v[j].z, v[j].w, inv);
+        if (i < n) *reinterpret_cast<uint32_t *>(dst + i) = quant4<FP8>(v[j].x, v[j].y, v[j].z, v[j].w, inv);
     }
-    if (tr == 0) *scale_out = ap * (1.0f / 127.0f);
+    if (tr == 0) *scale_out = ap * (1.0f / kQMax<FP8>);
 }
 
 }  // namespace moe

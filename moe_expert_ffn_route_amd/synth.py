@@ -218,7 +218,9 @@ class Case:
         s = self.spec
         return dict(num_tokens=s.T, hidden=s.H, inter=s.I, share_inter=s.I_s, topk=s.K,
                     moe_expert_num=s.E_g, ep_rank_size=s.ep_size, ep_rank_id=s.ep_rank,
-                    quant_mode=1, amax_eps=s.eps, fuse_route_scale=int(s.fuse_route_scale))
+                    quant_mode=1, amax_eps=s.eps, fuse_route_scale=int(s.fuse_route_scale),
+                    weight_format=int(s.weight_format == "mxfp4"),
+                    weight_layout=int(s.weight_format == "mxfp4"))  # FP4 weights are always packed
 
 
 def _threads() -> int:
@@ -278,8 +280,18 @@ def make_case_mx(spec: Spec) -> Case:
     """A case with FP4 weights (weight_format "mxfp4")."""
     x, ids, esc, mask, smooth, ssm = make_activations(spec)
     E, H, I, Is = spec.E_loc, spec.H, spec.I, spec.I_s
-    parts = [expert_weights_mx(spec, spec.ep_rank * E + e) for e in range(E)]
-    w1, w1b, w1s, w2, w2b, w2s = (np.stack([p[i] for p in parts]) if E else None for i in range(6))
+    w1 = np.empty((E, 2 * I, H // 2), np.uint8)
+    w1b = np.empty((E, 2 * I, H // 32), np.uint8)
+    w1s = np.empty((E, 2 * I), np.float32)
+    w2 = np.empty((E, H, I // 2), np.uint8)
+    w2b = np.empty((E, H, I // 32), np.uint8)
+    w2s = np.empty((E, H), np.float32)
+
+    def fill(e):
+        w1[e], w1b[e], w1s[e], w2[e], w2b[e], w2s[e] = expert_weights_mx(spec, spec.ep_rank * E + e)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(E)))
     sw = [None] * 6
     if Is:
         s = spec.weight_seed

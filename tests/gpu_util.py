@@ -58,6 +58,18 @@ def run_gpu(case, tensors=None, dbg=True, stream=None, garbage_workspace=False, 
     return res
 
 
+def pack_reference(w, which):
+    """The packed order written out with numpy, from its definition: 1 KB
+    blocks per (tile, 64-byte step), lane l holding row l % 16, bytes
+    16 (l / 16)..+16; a GEMM1 weight's gate and up tiles alternate."""
+    G, n, k = w.shape
+    t = w.reshape(G, n // 16, 16, k // 64, 4, 16)          # g, tile, row-in-tile, step, lane-group, byte
+    t = t.transpose(0, 1, 3, 4, 2, 5)                      # g, tile, step, lane-group, row-in-tile, byte
+    if which == moe.MOE_PACK_GMM1:                         # (gate, up) halves -> gate j, up j, gate j + 1, ...
+        t = t.reshape(G, 2, n // 32, *t.shape[2:]).swapaxes(1, 2)
+    return np.ascontiguousarray(t).reshape(-1)
+
+
 def out_close(got_bits, ref_bits, what):
     g = F32(got_bits).astype(np.float64)
     r = F32(ref_bits).astype(np.float64)
@@ -71,10 +83,11 @@ def out_close(got_bits, ref_bits, what):
     return float(err.max(initial=0.0)), float((g == r).mean()) if r.size else 1.0
 
 
-def compare(case, gpu, ref, tokens=None):
-    """Stage-by-stage comparison. `ref` is oracle.forward(case, tokens, trace=True)."""
+def _routing_rows(case, gpu, ref, tokens):
+    """Check the routing outputs (bit-exact) and return (grouped rows the
+    oracle computed, tokens)."""
     s = case.spec
-    T, K, H = s.T, s.K, s.H
+    T, K = s.T, s.K
     # routing: always global
     P, Ta = ref["P"], ref["T_act"]
     nr = gpu["num_rows"]
@@ -93,7 +106,14 @@ def compare(case, gpu, ref, tokens=None):
         act = np.ones(T, bool) if case.mask is None else case.mask.astype(bool)
         rank = np.cumsum(act) - 1
         rows += [P + int(rank[t]) for t in toks if act[t]]
-    rows = np.array(sorted(rows), dtype=np.int64)
+    return np.array(sorted(rows), dtype=np.int64), toks
+
+
+def compare(case, gpu, ref, tokens=None):
+    """Stage-by-stage comparison. `ref` is oracle.forward(case, tokens, trace=True)."""
+    s = case.spec
+    P = ref["P"]
+    rows, toks = _routing_rows(case, gpu, ref, tokens)
     stats = {}
     if len(rows):
         inter = np.where(rows < P, s.I, s.I_s)
@@ -126,3 +146,98 @@ def check(case, tokens=None, tensors=None, **kw):
     gpu = run_gpu(case, tensors=tensors, **kw)
     ref = oracle.forward(case, tokens=tokens, trace=True)
     return compare(case, gpu, ref, tokens), gpu, ref
+
+
+# ---------------------------------------------------------------- FP4 weights
+#
+# The FP8 x FP4 MFMA accumulates in fp32 with its own rounding, so the GEMM
+# accumulators are not bit-exact; every later stage is checked bit-exactly
+# (up to expf) on the GPU's own inputs, which pins each kernel separately:
+#   - q_x, xs: bit-exact against the oracle (same fp32 operations);
+#   - acc1, acc2: |gpu - exact| <= ACC_REL * sum_k |term_k|, where the exact
+#     fp32-rounded sum and the magnitude sum come from oracle.gemm_mx on the
+#     GPU's input codes (for the magnitude: signs cleared). The hardware's
+#     own error is at most about 2^-13.5 of that sum per instruction (measured
+#     on random operands); the bound leaves a factor 5 above it; a wrong lane,
+#     block or scale mapping is off by O(1);
+#   - h: SwiGLU of (acc1 * w1s) * xs, relative 1e-5 (expf);
+#   - q_h, hs: bit-exact against the oracle's FP8 quantisation of the GPU's h;
+#   - z: bf16((acc2 * w2s) * row scale), bit-exact;
+#   - against the oracle's own trace: q_h codes within one E4M3 step;
+#   - output / share_output: the block's output tolerance (out_close).
+ACC_REL = 2.0 ** -11
+
+
+def _e4m3_step(c):
+    """Signed position of E4M3 codes on the grid (+0 and -0 both 0)."""
+    c = np.asarray(c).astype(np.int32)
+    m = c & 0x7F
+    return np.where(c & 0x80, -m, m)
+
+
+def _mx_acc_check(got, codes, data, bscale, what):
+    exact = oracle.gemm_mx(codes[None, :], data, bscale)[0]
+    mag = oracle.gemm_mx((codes & 0x7F)[None, :], data & 0x77, bscale)[0]
+    err = np.abs(got.astype(np.float64) - exact.astype(np.float64))
+    bound = ACC_REL * mag.astype(np.float64) + 1e-30
+    assert np.all(err <= bound), f"{what}: worst err/sum|terms| {np.max(err / (mag + 1e-30)):.3g}"
+    return float(np.max(err / (mag.astype(np.float64) + 1e-30)))
+
+
+def compare_mx(case, gpu, ref, tokens=None):
+    """compare() for weight_format "mxfp4"."""
+    s = case.spec
+    K, H, P = s.K, s.H, ref["P"]
+    rows, toks = _routing_rows(case, gpu, ref, tokens)
+    stats = {}
+    qx = gpu["q_x"].view(np.uint8)
+    qh = gpu["q_h"].view(np.uint8)
+    acc1 = gpu["acc1"].view(np.float32)
+    acc2 = gpu["acc2"].view(np.float32)
+    base = s.ep_rank * s.E_loc
+    worst = 0.0
+    flips = []
+    for r in rows:
+        if r < P:
+            p = int(gpu["sorted_pair"][r])
+            e = int(case.expert_ids[p // K, p % K]) - base
+            n = s.I
+            w1, w1b, w1s = case.w1[e], case.w1b[e], case.w1s[e]
+            w2, w2b, w2s = case.w2[e], case.w2b[e], case.w2s[e]
+            rw = case.expert_scales[p // K, p % K]
+        else:
+            n = s.I_s
+            w1, w1b, w1s, w2, w2b, w2s = case.sw1, case.sw1b, case.sw1s, case.sw2, case.sw2b, case.sw2s
+            rw = None
+        assert np.array_equal(qx[r], ref["q_x"][r]), f"q_x row {r}"
+        assert gpu["xs"][r] == ref["xs"][r], f"xs row {r}"
+        a1 = acc1[r, :2 * n]
+        worst = max(worst, _mx_acc_check(a1, qx[r], w1, w1b, f"acc1 row {r}"))
+        y = (a1 * w1s) * np.float32(gpu["xs"][r])
+        h_exp = oracle.swiglu(y.astype(np.float32))
+        hg = gpu["h"][r, :n]
+        assert np.all(np.abs(hg - h_exp) <= 1e-5 * np.abs(h_exp) + 1e-30), f"h row {r}"
+        q_exp, hs_exp = oracle.quant_row_fp8(hg, s.eps)
+        assert np.array_equal(qh[r, :n], q_exp), f"q_h row {r}"
+        assert gpu["hs"][r] == np.float32(hs_exp), f"hs row {r}"
+        d = np.abs(_e4m3_step(qh[r, :n]) - _e4m3_step(ref["q_h"][r, :n]))
+        assert d.max(initial=0) <= 1, f"q_h row {r} more than one E4M3 step from the oracle's"
+        flips.append(float((d > 0).mean()))
+        a2 = acc2[r, :H]
+        worst = max(worst, _mx_acc_check(a2, qh[r, :n], w2, w2b, f"acc2 row {r}"))
+        rs2 = np.float32(gpu["hs"][r])
+        if s.fuse_route_scale and rw is not None:
+            rs2 = np.float32(rs2 * np.float32(rw))
+        z_exp = synth.f32_to_bf16_bits((a2 * w2s) * rs2)
+        assert np.array_equal(gpu["z"][r], z_exp), f"z row {r}"
+    stats.update(rows=len(rows), acc_err_over_sum=worst, qh_step_frac=max(flips, default=0.0))
+    stats["output"] = out_close(gpu["output"][toks], ref["output"][toks], "output")
+    if s.I_s:
+        stats["share_output"] = out_close(gpu["share_output"][toks], ref["share_output"][toks], "share_output")
+    return stats
+
+
+def check_mx(case, tokens=None, tensors=None, **kw):
+    gpu = run_gpu(case, tensors=tensors, **kw)
+    ref = oracle.forward(case, tokens=tokens, trace=True)
+    return compare_mx(case, gpu, ref, tokens), gpu, ref

@@ -96,6 +96,8 @@ def test_workspace_size(lib):
     (dict(weight_layout=2), binding.MOE_ERR_INVALID_ARG),
     (dict(fuse_route_scale=2), binding.MOE_ERR_INVALID_ARG),
     (dict(fuse_route_scale=-1), binding.MOE_ERR_INVALID_ARG),
+    (dict(weight_format=2), binding.MOE_ERR_INVALID_ARG),
+    (dict(weight_format=1), binding.MOE_ERR_UNSUPPORTED),           # FP4 weights must be packed
 ])
 def test_bad_dims_rejected(lib, kw, code):
     n = ctypes.c_size_t(0)
@@ -156,6 +158,29 @@ def test_forward_rejects_bad_dims_and_shared_mismatch(lib):
     (FAKE, 2 * FAKE, 1, 32, 64, 3)])
 def test_pack_rejects_bad_arguments(lib, src, dst, g, n, k, which):
     assert lib.moe_w8a8_pack_weights(src, dst, g, n, k, which, None) == binding.MOE_ERR_INVALID_ARG
+
+
+def test_mx_workspace_and_packed_size(lib):
+    mx = moe.moe_w8a8_workspace_size(good_dims(weight_format=1, weight_layout=1))
+    assert mx > 0
+    # 16 * (n/16) tiles x k/128 steps x (1024 element bytes + 64 scale bytes)
+    assert moe.moe_w8a8_packed_mx_bytes(3, 64, 256) == 3 * 64 * (256 // 2 + 256 // 32)
+    assert moe.moe_w8a8_packed_mx_bytes(0, 32, 128) == 0
+    for g, n, k in ((1, 16, 128), (1, 32, 64), (-1, 32, 128), (1, 0, 128)):
+        b = ctypes.c_size_t(0)
+        assert lib.moe_w8a8_packed_mx_bytes(g, n, k, ctypes.byref(b)) == binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_w8a8_packed_mx_bytes(1, 32, 128, None) == binding.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("data,bs,dst,g,n,k,which", [
+    (None, FAKE, 4 * FAKE, 1, 32, 128, 1), (FAKE, None, 4 * FAKE, 1, 32, 128, 1),
+    (FAKE, 2 * FAKE, None, 1, 32, 128, 1), (FAKE, 2 * FAKE, 4 * FAKE, 1, 32, 64, 1),
+    (FAKE, 2 * FAKE, 4 * FAKE, 1, 48, 128, 2), (FAKE, 2 * FAKE, 4 * FAKE, 1, 32, 128, 0),
+    (FAKE + 8, 2 * FAKE, 4 * FAKE, 1, 32, 128, 1), (FAKE, 2 * FAKE, 4 * FAKE + 8, 1, 32, 128, 1),
+    (FAKE, 2 * FAKE, FAKE + 1024, 1, 32, 128, 2),        # dst overlaps the elements
+    (FAKE, 2 * FAKE, 2 * FAKE - 256, 1, 32, 128, 2)])    # dst overlaps the block scales
+def test_pack_mx_rejects_bad_arguments(lib, data, bs, dst, g, n, k, which):
+    assert lib.moe_w8a8_pack_weights_mx(data, bs, dst, g, n, k, which, None) == binding.MOE_ERR_INVALID_ARG
 
 
 def test_status_strings(lib):

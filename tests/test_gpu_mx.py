@@ -1,0 +1,129 @@
+"""GPU parity of the FP4-weight / FP8-activation variant (weight_format
+MOE_WEIGHT_MXFP4) against the CPU oracle's moe_oracle_forward_mx, stage by
+stage (tolerances in gpu_util.compare_mx: FP8 codes, scales and every
+epilogue bit-exact on the GPU's own inputs, the fp32 MFMA accumulators within
+a bound relative to the sum of the magnitudes of their terms, outputs within
+the block's output tolerance).
+
+The cases span every K split of the MX kernel (8, 4 and 2 waves; one batch
+per wave; 1- and 4-step batches over several passes), 16-row chunks with
+several chunks per expert (batches above 16 tokens), masks, smooth scales, an
+expert-parallel share, a shared expert whose intermediate differs (two GEMM2
+launches), the fused route scale, T = 0 and T = 1, and the decode workload's
+full shape with a sample of its tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_ffn_route_amd as moe
+from moe_expert_ffn_route_amd import synth
+from gpu_util import check_mx, pack_reference, say
+
+pytestmark = pytest.mark.gpu
+
+
+def spec(**kw):
+    base = dict(name="mx", T=8, H=512, I=256, E_g=8, K=2, seed=301, weight_format="mxfp4")
+    base.update(kw)
+    return synth.Spec(**base)
+
+
+CASES = {
+    # the tiny workload's shape (H / 128 = 4 steps: 4 waves x 1; I: 2 waves x 1)
+    "tiny_shape": (spec(), None),
+    # H 768 (6 steps: 2 waves x 3 passes), I 512 (4 waves), I_s 256: split GEMM2
+    "shared_mask_smooth_split": (spec(T=12, H=768, I=512, I_s=256, E_g=16, K=4, active=10, smooth=True,
+                                      share_smooth=True, seed=302), None),
+    # H 1024 (8 steps: 8 waves x 1), an expert-parallel share, fused route scale
+    "ep_share_fused": (spec(T=16, H=1024, I=256, E_g=32, K=6, ep_size=4, ep_rank=1, fuse_route_scale=True,
+                            seed=303), None),
+    # 40 tokens on 2 experts: three 16-row chunks per expert (the last ragged),
+    # 16 GEMM1 N tiles, so the chunks of one tile run 8 blocks apart
+    "t40_multichunk_shared": (spec(T=40, H=512, I=256, E_g=2, K=2, I_s=256, seed=304), None),
+    "t100_skewed_mask_fused": (spec(T=100, H=512, I=256, E_g=8, K=3, routing="zipf", zipf_s=1.5, active=90,
+                                    I_s=512, fuse_route_scale=True, seed=305), [0, 7, 50, 99]),
+    # K split beyond one batch per wave: H 9216 (72 steps: 8 waves x 9 passes
+    # of 1 step), I 12288 (96 steps: 8 waves x 3 passes of 4 steps)
+    "long_k_gemm1": (spec(T=3, H=9216, I=256, E_g=4, K=2, I_s=256, seed=306), None),
+    "long_k_gemm2": (spec(T=3, H=256, I=12288, E_g=4, K=2, I_s=512, seed=307), None),
+    "t1": (spec(T=1, H=512, I=256, E_g=4, K=2, I_s=512, seed=308), None),
+    "t0": (spec(T=0, I_s=256, seed=309), None),
+    "all_masked": (spec(T=6, I_s=256, active=0, seed=310), None),
+    # the decode workload's shape: T 8, H 4096, I 2048, 256 experts, top-8,
+    # shared expert 2048 (two tokens through the oracle)
+    "decode_full_shape": (spec(T=8, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1235), [2, 5]),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_mx_parity(name):
+    sp, tokens = CASES[name]
+    say(f"[mx] {name}: {sp}")
+    stats, _, _ = check_mx(synth.make_case(sp), tokens=tokens)
+    say(f"[mx] {name}: {stats}")
+    torch.cuda.empty_cache()
+
+
+def _random_specs(n, seed=4242):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E_g = int(rng.choice([2, 4, 8, 16]))
+        ep = int(rng.choice([d for d in (1, 2) if E_g % d == 0]))
+        T = int(rng.choice([1, 5, 8, 16, 17, 30]))
+        kw = dict(name=f"mxrandom{i}", T=T, H=int(rng.choice([256, 512, 768, 1024, 1280])),
+                  I=int(rng.choice([256, 512, 768])), E_g=E_g, K=int(rng.integers(1, min(E_g, 6) + 1)),
+                  I_s=int(rng.choice([0, 256, 512])), ep_size=ep, ep_rank=int(rng.integers(0, ep)),
+                  routing=str(rng.choice(["uniform", "zipf"])), seed=400 + i)
+        if rng.random() < 0.4:
+            kw["active"] = int(rng.integers(0, T + 1))
+        if rng.random() < 0.4:
+            kw["smooth"] = True
+        if kw["I_s"] and rng.random() < 0.4:
+            kw["share_smooth"] = True
+        if rng.random() < 0.3:
+            kw["fuse_route_scale"] = True
+        out.append(spec(**kw))
+    return out
+
+
+RANDOM = _random_specs(10)
+
+
+@pytest.mark.parametrize("i", range(len(RANDOM)))
+def test_mx_random_shapes(i):
+    say(f"[mx] random {i}: {RANDOM[i]}")
+    stats, _, _ = check_mx(synth.make_case(RANDOM[i]))
+    say(f"[mx] random {i}: {stats}")
+
+
+def _scale_reference(bs, which):
+    """The packed scale order from its definition: 64 bytes per (tile position,
+    128-element step), byte l the scale of row l % 16 for block l / 16."""
+    G, n, nb = bs.shape
+    t = bs.reshape(G, n // 16, 16, nb // 4, 4)            # g, tile, row-in-tile, step, block
+    t = t.transpose(0, 1, 3, 4, 2)                         # g, tile, step, block, row-in-tile
+    if which == moe.MOE_PACK_GMM1:
+        t = t.reshape(G, 2, n // 32, *t.shape[2:]).swapaxes(1, 2)
+    return np.ascontiguousarray(t).reshape(-1)
+
+
+@pytest.mark.parametrize("which", [1, 2], ids=["gmm1", "gmm2"])
+@pytest.mark.parametrize("shape", [(1, 32, 128), (3, 96, 384), (2, 512, 4096)])
+def test_pack_mx_layout(shape, which):
+    G, n, k = shape
+    rng = np.random.default_rng(11)
+    data = rng.integers(0, 256, (G, n, k // 2), dtype=np.uint8)
+    bs = rng.integers(0, 255, (G, n, k // 32), dtype=np.uint8)
+    d = moe.moe_w8a8_pack_weights_mx(torch.from_numpy(data).cuda(), torch.from_numpy(bs).cuda(), which)
+    torch.cuda.synchronize()
+    got = d.cpu().numpy()
+    assert got.size == moe.moe_w8a8_packed_mx_bytes(G, n, k)
+    nd = G * n * k // 2
+    assert np.array_equal(got[:nd], pack_reference(data.view(np.int8), which).view(np.uint8))
+    assert np.array_equal(got[nd:], _scale_reference(bs, which))
+    # spot checks from the header's definition: (g, tile position p, step s, byte l)
+    for g, p, s, l in [(0, 0, 0, 0), (G - 1, n // 16 - 1, k // 128 - 1, 63), (G // 2, 1, 0, 17)]:
+        j = p if which == 2 else (p // 2 if p % 2 == 0 else n // 32 + p // 2)
+        assert got[nd + ((g * (n // 16) + p) * (k // 128) + s) * 64 + l] == bs[g, 16 * j + l % 16, 4 * s + l // 16]

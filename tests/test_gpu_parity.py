@@ -18,7 +18,7 @@ import torch
 import moe_expert_ffn_route_amd as moe
 import oracle
 from moe_expert_ffn_route_amd import synth
-from gpu_util import check, compare, run_gpu, say
+from gpu_util import check, compare, pack_reference, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -136,18 +136,6 @@ def test_random_shapes_parity(i):
     say(f"[parity] random {i}: {stats}")
 
 
-def _pack_reference(w, which):
-    """The packed order written out with numpy, from its definition: 1 KB
-    blocks per (tile, 64-byte step), lane l holding row l % 16, bytes
-    16 (l / 16)..+16; a GEMM1 weight's gate and up tiles alternate."""
-    G, n, k = w.shape
-    t = w.reshape(G, n // 16, 16, k // 64, 4, 16)          # g, tile, row-in-tile, step, lane-group, byte
-    t = t.transpose(0, 1, 3, 4, 2, 5)                      # g, tile, step, lane-group, row-in-tile, byte
-    if which == moe.MOE_PACK_GMM1:                         # (gate, up) halves -> gate j, up j, gate j + 1, ...
-        t = t.reshape(G, 2, n // 32, *t.shape[2:]).swapaxes(1, 2)
-    return np.ascontiguousarray(t).reshape(-1)
-
-
 @pytest.mark.parametrize("which", [1, 2], ids=["gmm1", "gmm2"])
 @pytest.mark.parametrize("shape", [(1, 32, 64), (3, 96, 192), (2, 4096, 512), (1, 512, 2048)])
 def test_pack_layout(shape, which):
@@ -156,7 +144,7 @@ def test_pack_layout(shape, which):
     d = moe.moe_w8a8_pack_weights(torch.from_numpy(w).cuda(), which)
     torch.cuda.synchronize()
     got = d.cpu().numpy().reshape(-1)
-    assert np.array_equal(got, _pack_reference(w, which))
+    assert np.array_equal(got, pack_reference(w, which))
     # spot checks straight from the header's definition: block (g, p, s), lane l, byte b
     G, n, k = shape
     for g, p, s, l, b in [(0, 0, 0, 0, 0), (G - 1, n // 16 - 1, k // 64 - 1, 63, 15), (G // 2, 1, 0, 17, 3)]:
