@@ -15,11 +15,16 @@ Prints one JSON line: the metric (µs per MoE layer), the achieved HBM GB/s of
 the layer, the roofline of the dominant kernel (GEMM1) from HIP events bound
 to that kernel's launch (hipExtLaunchKernel) in every timed step, and the CPU
 oracle's time on this host as a baseline.
+
+`--weight-format mxfp4` times the FP4-weight / FP8-activation variant of the
+same workload instead (E2M1 weights with E8M0 block scales, 0.53 bytes per
+weight element); the default line is the INT8 block.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import json
 import os
 import sys
@@ -36,6 +41,7 @@ from moe_expert_ffn_route_amd import binding, synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix rate, published (no sparsity)
+MFMA_F8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix rate, published (an FP8 x FP4 product runs at it)
 MFMA_I8_OPS_PER_CLK_CU = 8192  # the per-CU rate at which 256 CUs at 2.4 GHz reach the published figure
 HIP_ATTR_CLOCK_RATE = 5  # hipDeviceAttributeClockRate (peak clock, kHz) in hip_runtime_api.h
 
@@ -98,23 +104,29 @@ class TimingEvent:
             _hip_rt.hipEventDestroy(self.cuda_event)
 
 
+def weight_bytes_per_element(spec) -> float:
+    """1 for INT8 weights; 1/2 + 1/32 for FP4 elements with one E8M0 scale per 32."""
+    return 0.5 + 1.0 / 32 if spec.weight_format == "mxfp4" else 1.0
+
+
 def algorithmic_bytes(case, counts):
     """Bytes the layer must move at least once: every touched expert's weights
     and scales, the shared expert's, the activations in and out."""
     s = case.spec
     H, I, Is, T, K = s.H, s.I, s.I_s, s.T, s.K
+    wb = weight_bytes_per_element(s)
     touched = int((counts > 0).sum())
-    per_expert = 3 * H * I + 4 * (2 * I + H)
-    shared = (3 * H * Is + 4 * (2 * Is + H)) if Is else 0
+    per_expert = int(3 * H * I * wb) + 4 * (2 * I + H)
+    shared = (int(3 * H * Is * wb) + 4 * (2 * Is + H)) if Is else 0
     act = 2 * T * H + 8 * T * K + 2 * T * H * (2 if Is else 1)
     if case.smooth is not None:
         act += 4 * s.E_loc * H
-    gemm1 = touched * (2 * I * H + 8 * I) + ((2 * Is * H + 8 * Is) if Is else 0)
+    gemm1 = touched * (int(2 * I * H * wb) + 8 * I) + ((int(2 * Is * H * wb) + 8 * Is) if Is else 0)
     routed_rows = int(counts.sum())
     t_act = T if case.mask is None else int(np.count_nonzero(case.mask))
     rows = routed_rows + (t_act if Is else 0)
     gemm1 += rows * (H + 4 + 4 * max(I, Is))  # q_x and xs read, h written
-    gemm2 = touched * (H * I + 4 * H) + ((H * Is + 4 * H) if Is else 0)
+    gemm2 = touched * (int(H * I * wb) + 4 * H) + ((int(H * Is * wb) + 4 * H) if Is else 0)
     gemm2 += routed_rows * (I + 4 + 2 * H) + ((t_act * (Is + 4 + 2 * H)) if Is else 0)  # q_h, hs in; z out
     return touched * per_expert + shared + act, gemm1, gemm2, touched, rows
 
@@ -187,15 +199,16 @@ def gemm1_traffic(workload):
     return None
 
 
-def cpu_baseline(case, budget_s=12.0, max_reps=40):
-    """The CPU oracle as it stands, single-threaded, on the same batch."""
+def cpu_baseline(case, budget_s=12.0, max_reps=40, tokens=None):
+    """The CPU oracle as it stands, single-threaded, on the same batch (or on
+    `tokens` of it)."""
     import oracle  # test infrastructure: only this leg of the benchmark uses it
     oracle.lib()
     times = []
     t_end = time.perf_counter() + budget_s
     while len(times) < max_reps and (not times or time.perf_counter() < t_end):
         t0 = time.perf_counter()
-        oracle.forward(case)
+        oracle.forward(case, tokens=tokens)
         times.append(time.perf_counter() - t0)
     return float(np.mean(times)) * 1e6, len(times)
 
@@ -218,6 +231,8 @@ def main():
                     help="capture one step per weight copy into HIP graphs and time their replays")
     ap.add_argument("--fuse-route-scale", action="store_true",
                     help="fold the routing weight into the GEMM2 row scale (combine only sums)")
+    ap.add_argument("--weight-format", choices=["int8", "mxfp4"], default="int8",
+                    help="mxfp4: FP4 weights with E8M0 block scales and FP8 activations (always packed)")
     ap.add_argument("--fenced-events", action="store_true",
                     help="time with default HIP events (each record adds a system-scope cache writeback) "
                          "instead of events created with hipEventDisableSystemFence")
@@ -246,12 +261,18 @@ def main():
     moe.library()  # fail loudly if the HIP library is missing
 
     spec = synth.WORKLOADS[args.config]
+    mx = args.weight_format == "mxfp4"
+    if mx:
+        if args.row_major:
+            print("--weight-format mxfp4 needs packed weights", file=sys.stderr)
+            sys.exit(2)
+        spec = dataclasses.replace(spec, name=spec.name + "_mxfp4", weight_format="mxfp4")
     log(f"[bench] workload {spec.name}: generating inputs")
     t0 = time.perf_counter()
-    case = synth.workload_case(args.config)
+    case = synth.make_case(spec)
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s; uploading")
-    dev = moe.upload(case)
-    if not args.row_major:
+    dev = moe.upload(case)  # FP4 weights are packed by upload (moe_w8a8_pack_weights_mx)
+    if not args.row_major and not mx:
         dev = moe.pack_weights(dev)  # one-time re-layout at load time (moe_w8a8_pack_weights)
         torch.cuda.synchronize()
     wkeys = [k for k in ("gmm1_weight", "gmm1_weight_scale", "gmm2_weight", "gmm2_weight_scale",
@@ -260,6 +281,7 @@ def main():
     layers = [dev] + [dict(dev, **{k: dev[k].clone() for k in wkeys}) for _ in range(max(0, args.layers - 1))]
     dims = moe.dims_of_case(case)
     dims.weight_layout = moe.MOE_WEIGHT_ROW_MAJOR if args.row_major else moe.MOE_WEIGHT_PACKED
+    dims.weight_format = moe.MOE_WEIGHT_MXFP4 if mx else moe.MOE_WEIGHT_INT8
     dims.fuse_route_scale = int(args.fuse_route_scale)
     runner = moe.Runner(dims)
     stream = torch.cuda.Stream()
@@ -363,10 +385,12 @@ def main():
     g1_ops, g2_ops = gemm_ops(case, counts)
     # the roofline that binds GEMM1: HBM below the ridge (peak ops / peak
     # bytes per second), the int8 MFMA rate above it
-    if g1_ops / gemm1_bytes > MFMA_I8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+    mfma_peak = MFMA_F8_PEAK_TFLOPS if mx else MFMA_I8_PEAK_TOPS
+    mfma_unit = "TFLOP/s (fp8 x fp4)" if mx else "TOP/s (int8)"
+    if g1_ops / gemm1_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
         g1_tops = g1_ops / (g1_us * 1e-6) / 1e12
         roofline = {"kernel": "gemm1_swiglu", "bound": "mfma", "achieved": round(g1_tops, 1),
-                    "peak": MFMA_I8_PEAK_TOPS, "unit": "TOP/s (int8)", "frac": round(g1_tops / MFMA_I8_PEAK_TOPS, 4),
+                    "peak": mfma_peak, "unit": mfma_unit, "frac": round(g1_tops / mfma_peak, 4),
                     "traffic": traffic, "algorithmic_ops": g1_ops, "algorithmic_bytes": gemm1_bytes,
                     "hbm_gbps": round(g1_gbs, 1), "avg_us": round(g1_us, 2), "timing": None}
     else:
@@ -384,19 +408,20 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "fp8e4m3 x fp4e2m1 (fp32 accumulate)" if mx else "int8",
         "data": "synthetic",
         "config": {"workload": spec.name, "tokens": spec.T, "hidden": spec.H, "inter": spec.I,
                    "experts": spec.E_g, "topk": spec.K, "share_inter": spec.I_s,
                    "touched_experts": touched, "grouped_rows": rows, "weight_copies": len(layers),
                    "weight_layout": "row_major" if args.row_major else "packed",
+                   "weight_format": args.weight_format,
                    "route_scale": "fused_gemm2" if args.fuse_route_scale else "combine",
                    "launch": "hip_graph" if graphs else "stream"},
         "hbm_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
         "tokens_per_s": round(spec.T / (us * 1e-6), 1),
         "step_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],  # one event per step boundary
         "tops": round(tops, 2),
-        "mfma_i8_frac": round(tops / MFMA_I8_PEAK_TOPS, 5),
+        "mfma_i8_frac": None if mx else round(tops / MFMA_I8_PEAK_TOPS, 5),
         "mfma_i8_peak_derived": mfma_peak_on_device(),
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},  # separate pass, every stage bracketed
         "roofline": dict(roofline, timing=timing),
@@ -408,9 +433,18 @@ def main():
         rec["cpu_baseline"] = None
     else:
         log("[bench] CPU oracle baseline")
-        cpu_us, reps = cpu_baseline(case)
+        if mx:
+            # the FP4 oracle is slower per product: two tokens, scaled to the batch
+            n_tok = min(2, spec.T)
+            cpu_us, reps = cpu_baseline(case, tokens=list(range(n_tok)))
+            cpu_us *= spec.T / max(1, n_tok)
+            sample = (f"tokens 0-{n_tok - 1} of this workload (routing of the whole batch), {reps} runs, "
+                      f"time scaled by {spec.T}/{n_tok} to the batch, single-threaded C oracle")
+        else:
+            cpu_us, reps = cpu_baseline(case)
+            sample = f"the full batch of this workload, {reps} runs, single-threaded C oracle"
         rec["cpu_baseline"] = {"value": round(cpu_us, 1), "unit": "us", "cores": 1, "kind": "oracle",
-                               "sample": f"the full batch of this workload, {reps} runs, single-threaded C oracle"}
+                               "sample": sample}
     print(json.dumps(rec), flush=True)
 
 

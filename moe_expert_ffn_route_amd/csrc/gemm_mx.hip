@@ -10,7 +10,7 @@
 //   GEMM2: acc over q_h and W2 likewise; z = bf16((acc * w2s[n]) * hs[r]).
 //
 // The work decomposition is gemm.hip's decode one (16-row chunks, a 16-channel
-// tile pair per workgroup, K split over the waves, partial tiles summed in
+// tile pair per workgroup, K split over 4 waves, partial tiles summed in
 // LDS, linear blockIdx so every XCD streams a share of every expert); only the
 // operands change:
 //   - a K step is 128 elements: the FP8 A operand of lane l (row l % 16,
@@ -240,36 +240,46 @@ hipError_t launch_one(const GemmArgs &a, dim3 grid, int k_dim, int n_pass, hipSt
     return hipGetLastError();
 }
 
-// K is split over 8 waves when its 128-element steps divide by 8, else over 4
-// or 2 (k_dim % 256 == 0, so the step count is even). With at most 8 steps
-// per wave a wave loads its whole slice in one batch; longer slices go in
-// batches of 4, 2 or 1 steps, software pipelined.
+// K is split over MOE_MX_WAVES waves when its 128-element steps divide by
+// that, else over 4 or 2 (k_dim % 256 == 0, so the step count is even). With
+// at most 8 steps per wave a wave loads its whole slice in one batch; longer
+// slices go in batches of 4, 2 or 1 steps, software pipelined. 4 waves (8
+// steps, 256 bytes per lane in flight at hidden 4096) beat 8 waves (4 steps)
+// on the decode workload: GEMM1 78 us against 83 us on MI355X.
+#ifndef MOE_MX_WAVES
+#define MOE_MX_WAVES 4
+#endif
+template <int KIND, int W>
+hipError_t launch_split(const GemmArgs &a, dim3 grid, int k_dim, int spw, hipStream_t s, hipEvent_t e0,
+                        hipEvent_t e1) {
+    switch (spw) {
+        case 1: return launch_one<KIND, W, 1, 1>(a, grid, k_dim, 1, s, e0, e1);
+        case 2: return launch_one<KIND, W, 2, 1>(a, grid, k_dim, 1, s, e0, e1);
+        case 3: return launch_one<KIND, W, 3, 1>(a, grid, k_dim, 1, s, e0, e1);
+        case 4: return launch_one<KIND, W, 4, 1>(a, grid, k_dim, 1, s, e0, e1);
+        case 5: return launch_one<KIND, W, 5, 1>(a, grid, k_dim, 1, s, e0, e1);
+        case 6: return launch_one<KIND, W, 6, 1>(a, grid, k_dim, 1, s, e0, e1);
+        case 7: return launch_one<KIND, W, 7, 1>(a, grid, k_dim, 1, s, e0, e1);
+        case 8: return launch_one<KIND, W, 8, 1>(a, grid, k_dim, 1, s, e0, e1);
+        default: break;
+    }
+    if (spw % 4 == 0) return launch_one<KIND, W, 4, 0>(a, grid, k_dim, spw / 4, s, e0, e1);
+    if (spw % 2 == 0) return launch_one<KIND, W, 2, 0>(a, grid, k_dim, spw / 2, s, e0, e1);
+    return launch_one<KIND, W, 1, 0>(a, grid, k_dim, spw, s, e0, e1);
+}
+
 template <int KIND>
 hipError_t launch_kind(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    static_assert(MOE_MX_WAVES == 8 || MOE_MX_WAVES == 4, "MOE_MX_WAVES is 8 or 4");
     if (a.mt != 1 || k_dim % 256) return hipErrorInvalidValue;
     const long blocks = static_cast<long>(max_chunks) * a.n_tiles;
     if (blocks <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(blocks));
     const int steps = k_dim / kStepK;
-    if (steps % 8) {
-        if (steps % 4 == 0) return launch_one<KIND, 4, 1, 0>(a, grid, k_dim, steps / 4, s, e0, e1);
-        return launch_one<KIND, 2, 1, 0>(a, grid, k_dim, steps / 2, s, e0, e1);
-    }
-    const int spw = steps / 8;
-    switch (spw) {
-        case 1: return launch_one<KIND, 8, 1, 1>(a, grid, k_dim, 1, s, e0, e1);
-        case 2: return launch_one<KIND, 8, 2, 1>(a, grid, k_dim, 1, s, e0, e1);
-        case 3: return launch_one<KIND, 8, 3, 1>(a, grid, k_dim, 1, s, e0, e1);
-        case 4: return launch_one<KIND, 8, 4, 1>(a, grid, k_dim, 1, s, e0, e1);
-        case 5: return launch_one<KIND, 8, 5, 1>(a, grid, k_dim, 1, s, e0, e1);
-        case 6: return launch_one<KIND, 8, 6, 1>(a, grid, k_dim, 1, s, e0, e1);
-        case 7: return launch_one<KIND, 8, 7, 1>(a, grid, k_dim, 1, s, e0, e1);
-        case 8: return launch_one<KIND, 8, 8, 1>(a, grid, k_dim, 1, s, e0, e1);
-        default: break;
-    }
-    if (spw % 4 == 0) return launch_one<KIND, 8, 4, 0>(a, grid, k_dim, spw / 4, s, e0, e1);
-    if (spw % 2 == 0) return launch_one<KIND, 8, 2, 0>(a, grid, k_dim, spw / 2, s, e0, e1);
-    return launch_one<KIND, 8, 1, 0>(a, grid, k_dim, spw, s, e0, e1);
+    if (steps % MOE_MX_WAVES == 0)
+        return launch_split<KIND, MOE_MX_WAVES>(a, grid, k_dim, steps / MOE_MX_WAVES, s, e0, e1);
+    if (steps % 4 == 0) return launch_one<KIND, 4, 1, 0>(a, grid, k_dim, steps / 4, s, e0, e1);
+    return launch_one<KIND, 2, 1, 0>(a, grid, k_dim, steps / 2, s, e0, e1);
 }
 
 }  // namespace

@@ -7,8 +7,8 @@
 //   dbg_gather_kernel    test support only: GEMM1's input rows in grouped-row
 //                        order (the q_x / xs dump).
 //
-// Rows of up to 4096 elements take one wavefront each, four to a workgroup,
-// with no workgroup barrier: the row sits in the wave's registers between its
+// Rows of up to 4096 elements take one wavefront each (in batches of more
+// than 256 grouped rows), four to a workgroup, with no workgroup barrier: the row sits in the wave's registers between its
 // amax and its quantisation. Longer rows take a workgroup of 256 threads each.
 // Either way each row is read once. (x is quantised in the routing launch.)
 #include "rowquant.h"
@@ -101,11 +101,25 @@ __global__ __launch_bounds__(256) void dbg_gather_kernel(GemmArgs g, const int32
     if (dst_xs && threadIdx.x == 0) dst_xs[r] = (routed ? g.a_scale_r : g.a_scale_s)[src];
 }
 
+// Rows of up to MOE_REQUANT_WAVE_MAX values take one wavefront each, longer
+// rows one 256-thread workgroup each. Batches of at most
+// MOE_REQUANT_BLOCK_ROWS grouped rows (decode) also take a workgroup per
+// row: with so few rows the chip is mostly idle, and four times the threads
+// per row shorten each row's chain of loads and conversions (measured on
+// MI355X at T = 8, 80 rows of 2048: 4.9 -> 4.6 us INT8, 5.5 -> 4.6 us FP8).
+#ifndef MOE_REQUANT_WAVE_MAX
+#define MOE_REQUANT_WAVE_MAX 4096
+#endif
+#ifndef MOE_REQUANT_BLOCK_ROWS
+#define MOE_REQUANT_BLOCK_ROWS 256
+#endif
+
 template <bool FP8>
 hipError_t launch_requant_fmt(const RequantArgs &a, dim3 wgrid, dim3 wblk, hipStream_t s) {
-    if (a.imax <= 8 * 256)
+    const bool wave = a.rows_max > MOE_REQUANT_BLOCK_ROWS;
+    if (wave && a.imax <= 8 * 256 && a.imax <= MOE_REQUANT_WAVE_MAX)
         hipLaunchKernelGGL((requant_wave_kernel<8, FP8>), wgrid, wblk, 0, s, a);
-    else if (a.imax <= 16 * 256)
+    else if (wave && a.imax <= 16 * 256 && a.imax <= MOE_REQUANT_WAVE_MAX)
         hipLaunchKernelGGL((requant_wave_kernel<16, FP8>), wgrid, wblk, 0, s, a);
     else
         hipLaunchKernelGGL(requant_kernel<FP8>, dim3(a.rows_max), dim3(kTPR), 0, s, a);

@@ -45,26 +45,18 @@ __device__ __forceinline__ float row_amax(float m, int slot, int tr, float *s_pa
 // fp32 -> FP8 E4M3 code (OCP "e4m3fn": bias 7, 3 mantissa bits, largest
 // finite 448): round to nearest, ties to even, on the E4M3 grid (subnormal
 // step 2^-9); magnitudes that round above 448 saturate to 448; NaN -> 0x7F.
-__device__ __forceinline__ uint32_t e4m3_code(float f) {
-    const uint32_t u = __float_as_uint(f);
+// Branch-free: normal values round the fp32 mantissa to 3 bits in integer
+// arithmetic (a carry moves into the exponent), then rebias the exponent
+// from 127 to 7; below 2^-6 the code is rint(|f| * 2^9).
+__host__ __device__ __forceinline__ uint32_t e4m3_code(float f) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, f);
     const uint32_t a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u) return 0x7Fu;
-    const uint32_t sign = (u >> 24) & 0x80u;
-    if (a >= 0x43E00000u) return sign | 0x7Eu;   // |f| >= 448
-    if (a < 0x3C800000u) {                        // |f| < 2^-6: codes m * 2^-9 (m = 8 is 2^-6)
-        const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);
-        return sign | static_cast<uint32_t>(m);
-    }
-    int e = static_cast<int>(a >> 23) - 127;      // -6 .. 8
-    uint32_t q = (a >> 20) & 7u;                  // the 3 kept mantissa bits
-    const uint32_t rem = a & 0xFFFFFu;
-    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
-    if (q == 8u) {
-        q = 0u;
-        ++e;
-    }
-    if (e > 8 || (e == 8 && q == 7u)) return sign | 0x7Eu;
-    return sign | (static_cast<uint32_t>(e + 7) << 3) | q;
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);   // RNE at mantissa bit 20
+    uint32_t nrm = (r >> 20) - (120u << 3);               // (e - 120) << 3 | m
+    nrm = nrm < 0x7Eu ? nrm : 0x7Eu;                      // saturate at 448
+    const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(__builtin_bit_cast(float, a) * 512.0f));
+    const uint32_t c = (a < 0x3C800000u ? sub : nrm) | ((u >> 24) & 0x80u);
+    return a > 0x7F800000u ? 0x7Fu : c;
 }
 
 // Largest code value of the format: 127 (int8) or 448 (FP8 E4M3).

@@ -5,8 +5,8 @@ epilogue bit-exact on the GPU's own inputs, the fp32 MFMA accumulators within
 a bound relative to the sum of the magnitudes of their terms, outputs within
 the block's output tolerance).
 
-The cases span every K split of the MX kernel (8, 4 and 2 waves; one batch
-per wave; 1- and 4-step batches over several passes), 16-row chunks with
+The cases span every K split of the MX kernel (4 and 2 waves; one batch per
+wave; 1-, 2- and 4-step batches over several passes), 16-row chunks with
 several chunks per expert (batches above 16 tokens), masks, smooth scales, an
 expert-parallel share, a shared expert whose intermediate differs (two GEMM2
 launches), the fused route scale, T = 0 and T = 1, and the decode workload's
@@ -35,7 +35,7 @@ CASES = {
     # H 768 (6 steps: 2 waves x 3 passes), I 512 (4 waves), I_s 256: split GEMM2
     "shared_mask_smooth_split": (spec(T=12, H=768, I=512, I_s=256, E_g=16, K=4, active=10, smooth=True,
                                       share_smooth=True, seed=302), None),
-    # H 1024 (8 steps: 8 waves x 1), an expert-parallel share, fused route scale
+    # H 1024 (8 steps: 4 waves x 2), an expert-parallel share, fused route scale
     "ep_share_fused": (spec(T=16, H=1024, I=256, E_g=32, K=6, ep_size=4, ep_rank=1, fuse_route_scale=True,
                             seed=303), None),
     # 40 tokens on 2 experts: three 16-row chunks per expert (the last ragged),
@@ -43,11 +43,13 @@ CASES = {
     "t40_multichunk_shared": (spec(T=40, H=512, I=256, E_g=2, K=2, I_s=256, seed=304), None),
     "t100_skewed_mask_fused": (spec(T=100, H=512, I=256, E_g=8, K=3, routing="zipf", zipf_s=1.5, active=90,
                                     I_s=512, fuse_route_scale=True, seed=305), [0, 7, 50, 99]),
-    # K split beyond one batch per wave: H 9216 (72 steps: 8 waves x 9 passes
-    # of 1 step), I 12288 (96 steps: 8 waves x 3 passes of 4 steps)
+    # K split beyond one batch per wave: H 9216 (72 steps: 4 waves x 9 passes
+    # of 2 steps), I 12288 (96 steps: 4 waves x 6 passes of 4 steps)
     "long_k_gemm1": (spec(T=3, H=9216, I=256, E_g=4, K=2, I_s=256, seed=306), None),
     "long_k_gemm2": (spec(T=3, H=256, I=12288, E_g=4, K=2, I_s=512, seed=307), None),
     "t1": (spec(T=1, H=512, I=256, E_g=4, K=2, I_s=512, seed=308), None),
+    # H 2048 (16 steps: 4 waves x 4), I 3072 (24 steps: 4 waves x 6)
+    "mid_k": (spec(T=9, H=2048, I=3072, E_g=4, K=2, I_s=1024, seed=312), None),
     "t0": (spec(T=0, I_s=256, seed=309), None),
     "all_masked": (spec(T=6, I_s=256, active=0, seed=310), None),
     # the decode workload's shape: T 8, H 4096, I 2048, 256 experts, top-8,
