@@ -172,7 +172,7 @@ def mfma_peak_on_device():
             "tops": round(cus * khz.value * 1e3 * MFMA_I8_OPS_PER_CLK_CU / 1e12, 1)}
 
 
-def gemm1_traffic(workload):
+def gemm1_traffic(workload, mx=False):
     """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary
     (FETCH_SIZE / WRITE_SIZE scaled by a plain copy's readings), or None when
     there is none for this workload or the GEMM sources changed since."""
@@ -188,13 +188,13 @@ def gemm1_traffic(workload):
     if rec is None:
         return None
     h = hashlib.sha256()
-    for name in ("gemm.hip", "internal.h", "abi.hip"):
+    for name in ("gemm_mx.hip" if mx else "gemm.hip", "internal.h", "abi.hip"):
         with open(os.path.join(ROOT, "moe_expert_ffn_route_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     if h.hexdigest() != rec.get("source_sha256"):
         return None
     for k, v in rec["kernels"].items():
-        if k.startswith("void gemm_kernel<1,"):
+        if k.startswith("void gemm_mx_kernel<1," if mx else "void gemm_kernel<1,"):
             return int(v["read_bytes"] + v["write_bytes"])
     return None
 
@@ -380,7 +380,7 @@ def main():
     layer_bytes, gemm1_bytes, gemm2_bytes, touched, rows = algorithmic_bytes(case, counts)
     us = ms_per_step * 1e3
     g1_gbs = gemm1_bytes / (g1_us * 1e-6) / 1e9
-    traffic = None if args.row_major else gemm1_traffic(spec.name)
+    traffic = None if args.row_major else gemm1_traffic(spec.name, mx)
     tops = layer_ops(case, counts) / (us * 1e-6) / 1e12
     g1_ops, g2_ops = gemm_ops(case, counts)
     # the roofline that binds GEMM1: HBM below the ridge (peak ops / peak
