@@ -49,10 +49,17 @@ Layout make_layout(const moe_w8a8_dims_t *d) {
     const size_t nonempty = E < TK ? E : TK;
     // rows per GEMM work item: 16 for decode batches; 256 (tall items) when
     // the routed experts average kTallMinRows rows or more; 32 otherwise.
-    // FP4 weights run 16-row items at every batch size (gemm_mx.hip).
+    // FP4 weights (gemm_mx.hip): 32 when the local experts can average 16 rows
+    // or more (T*K / ep_rank_size >= 16 * E_loc), else 16 (measured on MI355X:
+    // 32-row items take the T = 512 layer from 996 to 859 us but slow the
+    // skewed T = 64 layer from 305 to 328 us).
     const bool tall = T >= kTallMinRows && TK >= static_cast<size_t>(kTallMinRows) * E;
     const bool mx = d->weight_format == MOE_WEIGHT_MXFP4;
-    L.chunk_rows = mx || T <= kChunkRowsSmall ? kChunkRowsSmall : tall ? kChunkRowsTall : kChunkRowsLarge;
+    const bool mx_wide = T > kChunkRowsSmall && TK / d->ep_rank_size >= static_cast<size_t>(kTileN) * E;
+    L.chunk_rows = T <= kChunkRowsSmall ? kChunkRowsSmall
+                   : mx                 ? (mx_wide ? 2 * kTileN : kChunkRowsSmall)
+                   : tall               ? kChunkRowsTall
+                                        : kChunkRowsLarge;
     const size_t cr = L.chunk_rows;
     L.max_chunks = static_cast<int>(nonempty + TK / cr + (shared ? (T + cr - 1) / cr : 0));
     const size_t R = L.rows_max;

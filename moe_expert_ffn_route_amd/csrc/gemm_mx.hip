@@ -9,10 +9,10 @@
 //     h = (y_g / (1 + exp(-y_g))) * y_u.
 //   GEMM2: acc over q_h and W2 likewise; z = bf16((acc * w2s[n]) * hs[r]).
 //
-// The work decomposition is gemm.hip's decode one (16-row chunks, a 16-channel
-// tile pair per workgroup, K split over 4 waves, partial tiles summed in
-// LDS, linear blockIdx so every XCD streams a share of every expert); only the
-// operands change:
+// The work decomposition is gemm.hip's decode one (chunks of 16 rows, or of 32
+// rows above 16 tokens, a 16-channel tile pair per workgroup, K split over the
+// waves, partial tiles summed in LDS, linear blockIdx so every XCD streams a
+// share of every expert); only the operands change:
 //   - a K step is 128 elements: the FP8 A operand of lane l (row l % 16,
 //     g = l / 16) is 32 bytes, row bytes 16g .. +16 (register bytes 0..15)
 //     and 64 + 16g .. +16 (bytes 16..31) of the step; the FP4 B operand is 16
@@ -46,9 +46,14 @@ __device__ __forceinline__ v4i ld16_stream(const uint8_t *p) {
 }
 
 // KIND 1 = GEMM1 + SwiGLU, 2 = GEMM2 + bf16. KS = 128-element K steps a wave
-// loads per batch; NPASS = batches per wave (0: n_pass_rt at run time).
-template <int KIND, int WAVES, int KS, int NPASS>
-__global__ __launch_bounds__(WAVES * kWave) void gemm_mx_kernel(GemmArgs a, int k_dim, int n_pass_rt) {
+// loads per batch; NPASS = batches per wave (0: n_pass_rt at run time); MT =
+// 16-row tiles per chunk (each weight fragment feeds all of them, so a chunk
+// reads its weights once).
+// (Four-wave one-tile blocks ask for three resident blocks per CU: the
+// register budget of three waves per SIMD, which the 8-step batch fits.)
+template <int KIND, int WAVES, int KS, int NPASS, int MT>
+__global__ __launch_bounds__(WAVES * kWave, WAVES == 4 && MT == 1 ? 3 : 1) void gemm_mx_kernel(GemmArgs a, int k_dim,
+                                                                                                  int n_pass_rt) {
     constexpr int kThreads = WAVES * kWave;
     constexpr int kCols = KIND == 1 ? kTileN : 2 * kTileN;
     constexpr int kElems = kTileN * kCols;
@@ -110,8 +115,12 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_mx_kernel(GemmArgs a, int 
     const int32_t *tidx = KIND == 1 ? aidx : a.row_token;
     const uint8_t *Abase = reinterpret_cast<const uint8_t *>(KIND == 1 ? (routed ? a.A_r : a.A_s) : a.A);
     const float *Ascale = KIND == 1 ? (routed ? a.a_scale_r : a.a_scale_s) : a.a_scale;
-    const int lr = min(r16, rows - 1);
-    const int arow = KIND == 1 ? aidx[row0 + lr] : row0 + lr;
+    int arow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int lr = min(mt * kTileN + r16, rows - 1);
+        arow[mt] = KIND == 1 ? aidx[row0 + lr] : row0 + lr;
+    }
     const int jc = tid % kCols;
     const int col = (KIND == 1 ? nt * kTileN : nt * 2 * kTileN) + jc;
     const float wsc0 = Ws[col];
@@ -150,30 +159,50 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_mx_kernel(GemmArgs a, int 
     for (int e = 0; e < kEpt; ++e) rsc[e] = Ascale[KIND == 1 ? rtok[e] : rrow[e]];
     __builtin_amdgcn_sched_barrier(0);
 
-    const uint8_t *pa = Abase + static_cast<size_t>(arow) * a.a_stride + static_cast<size_t>(step0) * kStepK + kg * 16;
-    const bool av = r16 < rows;
-    v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint8_t *pa[MT];
+    v4f acc0[MT], acc1[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        pa[mt] = Abase + static_cast<size_t>(arow[mt]) * a.a_stride + static_cast<size_t>(step0) * kStepK + kg * 16;
+        acc0[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        acc1[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // One K batch: this batch's A rows, then (if any) the next weight batch,
+    // then the MFMAs. Row tiles past the chunk's rows are skipped (uniform).
     auto batch = [&](const v4i (&w)[2][KS], const int (&sc)[2][KS], v4i (&nw)[2][KS], int (&nsc)[2][KS], int pass,
                      bool has_next) {
-        v4i x0[KS], x1[KS];
-        const uint8_t *pam = pa + static_cast<size_t>(pass) * KS * kStepK;
+        v4i x0[MT][KS], x1[MT][KS];
 #pragma unroll
-        for (int i = 0; i < KS; ++i) {
-            x0[i] = ld16(pam + i * kStepK);
-            x1[i] = ld16(pam + i * kStepK + 64);
+        for (int mt = 0; mt < MT; ++mt) {
+            if (MT == 1 || mt * kTileN < rows) {
+                const uint8_t *pam = pa[mt] + static_cast<size_t>(pass) * KS * kStepK;
+#pragma unroll
+                for (int i = 0; i < KS; ++i) {
+                    x0[mt][i] = ld16(pam + i * kStepK);
+                    x1[mt][i] = ld16(pam + i * kStepK + 64);
+                }
+            }
         }
         if (has_next) ldw(nw, nsc, pass + 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < KS; ++i) {
-            const v4i lo = av ? x0[i] : v4i{0, 0, 0, 0};
-            const v4i hi = av ? x1[i] : v4i{0, 0, 0, 0};
-            const v8i xa = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            const v8i b0 = {w[0][i][0], w[0][i][1], w[0][i][2], w[0][i][3], 0, 0, 0, 0};
-            const v8i b1 = {w[1][i][0], w[1][i][1], w[1][i][2], w[1][i][3], 0, 0, 0, 0};
-            // cbsz 0: A is FP8 E4M3; blgp 4: B is FP4 E2M1 (4 registers)
-            acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xa, b0, acc0, 0, 4, 0, kUnitScale, 0, sc[0][i]);
-            acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xa, b1, acc1, 0, 4, 0, kUnitScale, 0, sc[1][i]);
+        for (int mt = 0; mt < MT; ++mt) {
+            if (MT == 1 || mt * kTileN < rows) {
+                const bool av = mt * kTileN + r16 < rows;
+#pragma unroll
+                for (int i = 0; i < KS; ++i) {
+                    const v4i lo = av ? x0[mt][i] : v4i{0, 0, 0, 0};
+                    const v4i hi = av ? x1[mt][i] : v4i{0, 0, 0, 0};
+                    const v8i xa = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    const v8i b0 = {w[0][i][0], w[0][i][1], w[0][i][2], w[0][i][3], 0, 0, 0, 0};
+                    const v8i b1 = {w[1][i][0], w[1][i][1], w[1][i][2], w[1][i][3], 0, 0, 0, 0};
+                    // cbsz 0: A is FP8 E4M3; blgp 4: B is FP4 E2M1 (4 registers)
+                    acc0[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xa, b0, acc0[mt], 0, 4, 0, kUnitScale,
+                                                                                0, sc[0][i]);
+                    acc1[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xa, b1, acc1[mt], 0, 4, 0, kUnitScale,
+                                                                                0, sc[1][i]);
+                }
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -190,17 +219,23 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_mx_kernel(GemmArgs a, int 
 
     __shared__ float red[WAVES][2][kTileN][kTileN];
 #pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+    if (mt * kTileN >= rows) break;  // uniform
+#pragma unroll
     for (int i = 0; i < 4; ++i) {
-        red[wave][0][4 * kg + i][r16] = acc0[i];
-        red[wave][1][4 * kg + i][r16] = acc1[i];
+        red[wave][0][4 * kg + i][r16] = acc0[mt][i];
+        red[wave][1][4 * kg + i][r16] = acc1[mt][i];
     }
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) {
         const int idx = tid + e * kThreads;
         const int m = idx / kCols;
-        if (idx < kElems && m < rows) {
-            const int r = row0 + m;
+        const int lr = mt * kTileN + m;
+        if (idx < kElems && lr < rows) {
+            const int r = row0 + lr;
+            // the first tile's row scales and tokens were fetched up front
+            const float rs = mt == 0 ? rsc[e] : Ascale[KIND == 1 ? aidx[r] : r];
             if (KIND == 1) {
                 float ag = 0.0f, au = 0.0f;
 #pragma unroll
@@ -208,7 +243,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_mx_kernel(GemmArgs a, int 
                     ag += red[w][0][m][jc];
                     au += red[w][1][m][jc];
                 }
-                a.h[static_cast<size_t>(r) * a.imax + col] = swiglu(ag, au, wsc0, wsc1, rsc[e]);
+                a.h[static_cast<size_t>(r) * a.imax + col] = swiglu(ag, au, wsc0, wsc1, rs);
                 if (a.dbg_acc) {
                     a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + col] = __float_as_int(ag);
                     a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + inter + col] = __float_as_int(au);
@@ -217,26 +252,31 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_mx_kernel(GemmArgs a, int 
                 float acc = 0.0f;
 #pragma unroll
                 for (int w = 0; w < WAVES; ++w) acc += red[w][jc / kTileN][m][jc % kTileN];
-                const uint16_t zb = f32_to_bf16(dequant(acc, wsc0, rsc[e]));
-                if (routed)
+                const uint16_t zb = f32_to_bf16(dequant(acc, wsc0, rs));
+                if (routed) {
                     a.z[static_cast<size_t>(r) * a.H + col] = zb;
-                else
-                    a.share_out[static_cast<size_t>(rtok[e]) * a.H + col] = zb;
+                } else {
+                    const int t = mt == 0 ? rtok[e] : a.row_token[r];
+                    a.share_out[static_cast<size_t>(t) * a.H + col] = zb;
+                }
                 if (a.dbg_acc) a.dbg_acc[static_cast<size_t>(r) * a.H + col] = __float_as_int(acc);
                 if (a.dbg_z) a.dbg_z[static_cast<size_t>(r) * a.H + col] = zb;
             }
         }
     }
+    __syncthreads();
+    }
 }
 
-template <int KIND, int WAVES, int KS, int NPASS>
+template <int KIND, int WAVES, int KS, int NPASS, int MT>
 hipError_t launch_one(const GemmArgs &a, dim3 grid, int k_dim, int n_pass, hipStream_t s, hipEvent_t e0,
                       hipEvent_t e1) {
     const dim3 blk(WAVES * kWave);
     if (e0 || e1)
-        hipExtLaunchKernelGGL((gemm_mx_kernel<KIND, WAVES, KS, NPASS>), grid, blk, 0, s, e0, e1, 0, a, k_dim, n_pass);
+        hipExtLaunchKernelGGL((gemm_mx_kernel<KIND, WAVES, KS, NPASS, MT>), grid, blk, 0, s, e0, e1, 0, a, k_dim,
+                              n_pass);
     else
-        hipLaunchKernelGGL((gemm_mx_kernel<KIND, WAVES, KS, NPASS>), grid, blk, 0, s, a, k_dim, n_pass);
+        hipLaunchKernelGGL((gemm_mx_kernel<KIND, WAVES, KS, NPASS, MT>), grid, blk, 0, s, a, k_dim, n_pass);
     return hipGetLastError();
 }
 
@@ -249,37 +289,45 @@ hipError_t launch_one(const GemmArgs &a, dim3 grid, int k_dim, int n_pass, hipSt
 #ifndef MOE_MX_WAVES
 #define MOE_MX_WAVES 4
 #endif
-template <int KIND, int W>
+template <int KIND, int W, int MT>
 hipError_t launch_split(const GemmArgs &a, dim3 grid, int k_dim, int spw, hipStream_t s, hipEvent_t e0,
                         hipEvent_t e1) {
     switch (spw) {
-        case 1: return launch_one<KIND, W, 1, 1>(a, grid, k_dim, 1, s, e0, e1);
-        case 2: return launch_one<KIND, W, 2, 1>(a, grid, k_dim, 1, s, e0, e1);
-        case 3: return launch_one<KIND, W, 3, 1>(a, grid, k_dim, 1, s, e0, e1);
-        case 4: return launch_one<KIND, W, 4, 1>(a, grid, k_dim, 1, s, e0, e1);
-        case 5: return launch_one<KIND, W, 5, 1>(a, grid, k_dim, 1, s, e0, e1);
-        case 6: return launch_one<KIND, W, 6, 1>(a, grid, k_dim, 1, s, e0, e1);
-        case 7: return launch_one<KIND, W, 7, 1>(a, grid, k_dim, 1, s, e0, e1);
-        case 8: return launch_one<KIND, W, 8, 1>(a, grid, k_dim, 1, s, e0, e1);
+        case 1: return launch_one<KIND, W, 1, 1, MT>(a, grid, k_dim, 1, s, e0, e1);
+        case 2: return launch_one<KIND, W, 2, 1, MT>(a, grid, k_dim, 1, s, e0, e1);
+        case 3: return launch_one<KIND, W, 3, 1, MT>(a, grid, k_dim, 1, s, e0, e1);
+        case 4: return launch_one<KIND, W, 4, 1, MT>(a, grid, k_dim, 1, s, e0, e1);
+        case 5: return launch_one<KIND, W, 5, 1, MT>(a, grid, k_dim, 1, s, e0, e1);
+        case 6: return launch_one<KIND, W, 6, 1, MT>(a, grid, k_dim, 1, s, e0, e1);
+        case 7: return launch_one<KIND, W, 7, 1, MT>(a, grid, k_dim, 1, s, e0, e1);
+        case 8: return launch_one<KIND, W, 8, 1, MT>(a, grid, k_dim, 1, s, e0, e1);
         default: break;
     }
-    if (spw % 4 == 0) return launch_one<KIND, W, 4, 0>(a, grid, k_dim, spw / 4, s, e0, e1);
-    if (spw % 2 == 0) return launch_one<KIND, W, 2, 0>(a, grid, k_dim, spw / 2, s, e0, e1);
-    return launch_one<KIND, W, 1, 0>(a, grid, k_dim, spw, s, e0, e1);
+    if (spw % 4 == 0) return launch_one<KIND, W, 4, 0, MT>(a, grid, k_dim, spw / 4, s, e0, e1);
+    if (spw % 2 == 0) return launch_one<KIND, W, 2, 0, MT>(a, grid, k_dim, spw / 2, s, e0, e1);
+    return launch_one<KIND, W, 1, 0, MT>(a, grid, k_dim, spw, s, e0, e1);
+}
+
+// One row tile per chunk (batches of at most 16 tokens) splits K over
+// MOE_MX_WAVES waves; two row tiles (32-row chunks, larger batches) over 8,
+// which keeps a wave's A and weight registers of a batch within budget.
+template <int KIND, int MT>
+hipError_t launch_mt(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    constexpr int W = MT == 1 ? MOE_MX_WAVES : 8;
+    const int steps = k_dim / kStepK;
+    if (steps % W == 0) return launch_split<KIND, W, MT>(a, grid, k_dim, steps / W, s, e0, e1);
+    if (steps % 4 == 0) return launch_one<KIND, 4, 1, 0, MT>(a, grid, k_dim, steps / 4, s, e0, e1);
+    return launch_one<KIND, 2, 1, 0, MT>(a, grid, k_dim, steps / 2, s, e0, e1);
 }
 
 template <int KIND>
 hipError_t launch_kind(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     static_assert(MOE_MX_WAVES == 8 || MOE_MX_WAVES == 4, "MOE_MX_WAVES is 8 or 4");
-    if (a.mt != 1 || k_dim % 256) return hipErrorInvalidValue;
+    if ((a.mt != 1 && a.mt != 2) || k_dim % 256) return hipErrorInvalidValue;
     const long blocks = static_cast<long>(max_chunks) * a.n_tiles;
     if (blocks <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(blocks));
-    const int steps = k_dim / kStepK;
-    if (steps % MOE_MX_WAVES == 0)
-        return launch_split<KIND, MOE_MX_WAVES>(a, grid, k_dim, steps / MOE_MX_WAVES, s, e0, e1);
-    if (steps % 4 == 0) return launch_one<KIND, 4, 1, 0>(a, grid, k_dim, steps / 4, s, e0, e1);
-    return launch_one<KIND, 2, 1, 0>(a, grid, k_dim, steps / 2, s, e0, e1);
+    return a.mt == 1 ? launch_mt<KIND, 1>(a, grid, k_dim, s, e0, e1) : launch_mt<KIND, 2>(a, grid, k_dim, s, e0, e1);
 }
 
 }  // namespace

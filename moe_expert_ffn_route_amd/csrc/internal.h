@@ -171,9 +171,9 @@ int wide_tile_pairs();
 hipError_t launch_gemm1_tall(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_gemm2_tall(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
                              hipEvent_t ev_stop);
-// FP4-weight / FP8-activation GEMMs (gemm_mx.hip): 16-row work items as in
-// gemm.hip, weights from moe_w8a8_pack_weights_mx, A codes FP8 E4M3; k_dim %
-// 256 == 0. dbg_acc receives fp32 bit patterns.
+// FP4-weight / FP8-activation GEMMs (gemm_mx.hip): work items of one or two
+// 16-row tiles (a.mt = 1 or 2), weights from moe_w8a8_pack_weights_mx, A codes
+// FP8 E4M3; k_dim % 256 == 0. dbg_acc receives fp32 bit patterns.
 hipError_t launch_gemm1_mx(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_gemm2_mx(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
                            hipEvent_t ev_stop);

@@ -5,9 +5,10 @@ epilogue bit-exact on the GPU's own inputs, the fp32 MFMA accumulators within
 a bound relative to the sum of the magnitudes of their terms, outputs within
 the block's output tolerance).
 
-The cases span every K split of the MX kernel (4 and 2 waves; one batch per
-wave; 1-, 2- and 4-step batches over several passes), 16-row chunks with
-several chunks per expert (batches above 16 tokens), masks, smooth scales, an
+The cases span every K split of the MX kernel (8, 4 and 2 waves; one batch
+per wave; 1-, 2- and 4-step batches over several passes), 16-row items
+(decode) and 32-row items with several chunks per expert (batches above 16
+tokens), masks, smooth scales, an
 expert-parallel share, a shared expert whose intermediate differs (two GEMM2
 launches), the fused route scale, T = 0 and T = 1, and the decode workload's
 full shape with a sample of its tokens.
@@ -38,8 +39,9 @@ CASES = {
     # H 1024 (8 steps: 4 waves x 2), an expert-parallel share, fused route scale
     "ep_share_fused": (spec(T=16, H=1024, I=256, E_g=32, K=6, ep_size=4, ep_rank=1, fuse_route_scale=True,
                             seed=303), None),
-    # 40 tokens on 2 experts: three 16-row chunks per expert (the last ragged),
-    # 16 GEMM1 N tiles, so the chunks of one tile run 8 blocks apart
+    # 40 tokens on 2 experts: two 32-row chunks per expert (the second with 8
+    # rows: its second row tile is skipped), 16 GEMM1 N tiles, so the chunks of
+    # one tile run 8 blocks apart
     "t40_multichunk_shared": (spec(T=40, H=512, I=256, E_g=2, K=2, I_s=256, seed=304), None),
     "t100_skewed_mask_fused": (spec(T=100, H=512, I=256, E_g=8, K=3, routing="zipf", zipf_s=1.5, active=90,
                                     I_s=512, fuse_route_scale=True, seed=305), [0, 7, 50, 99]),
@@ -47,6 +49,10 @@ CASES = {
     # of 2 steps), I 12288 (96 steps: 4 waves x 6 passes of 4 steps)
     "long_k_gemm1": (spec(T=3, H=9216, I=256, E_g=4, K=2, I_s=256, seed=306), None),
     "long_k_gemm2": (spec(T=3, H=256, I=12288, E_g=4, K=2, I_s=512, seed=307), None),
+    # 32-row items (T > 16) with long K: H 9216 (72 steps: 8 waves x 9
+    # passes of 1 step), I 3072 (24 steps: 8 waves x 3)
+    "t20_long_k_gemm1": (spec(T=20, H=9216, I=256, E_g=2, K=1, I_s=256, seed=313), None),
+    "t24_mid_k_gemm2": (spec(T=24, H=256, I=3072, E_g=2, K=2, I_s=512, seed=314), None),
     "t1": (spec(T=1, H=512, I=256, E_g=4, K=2, I_s=512, seed=308), None),
     # H 2048 (16 steps: 4 waves x 4), I 3072 (24 steps: 4 waves x 6)
     "mid_k": (spec(T=9, H=2048, I=3072, E_g=4, K=2, I_s=1024, seed=312), None),
@@ -129,3 +135,38 @@ def test_pack_mx_layout(shape, which):
     for g, p, s, l in [(0, 0, 0, 0), (G - 1, n // 16 - 1, k // 128 - 1, 63), (G // 2, 1, 0, 17)]:
         j = p if which == 2 else (p // 2 if p % 2 == 0 else n // 32 + p // 2)
         assert got[nd + ((g * (n // 16) + p) * (k // 128) + s) * 64 + l] == bs[g, 16 * j + l % 16, 4 * s + l // 16]
+
+
+@pytest.mark.parametrize("name", ["ep_share_fused", "t40_multichunk_shared"])
+def test_mx_hip_graph_capture_and_replay(name):
+    # the FP4 path launches kernels only, so a caller can capture it; every
+    # replay must match the eager result, with other eager work and
+    # synchronisations between the replays
+    sp, _ = CASES[name]
+    say(f"[mx graph] {name}: {sp}")
+    c = synth.make_case(sp)
+    t = moe.upload(c)
+    runner = moe.Runner(moe.dims_of_case(c))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        runner(t, stream=s)
+    torch.cuda.synchronize()
+    eager = [runner.output.clone(), runner.expert_token_nums.clone()]
+    if runner.share_output is not None:
+        eager.append(runner.share_output.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        runner(t, stream=s)
+    for i in range(4):
+        runner.output.fill_(3)
+        runner.expert_token_nums.fill_(-1)
+        if runner.share_output is not None:
+            runner.share_output.fill_(3)
+        runner.workspace.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(runner.output, eager[0]), i
+        assert torch.equal(runner.expert_token_nums, eager[1]), i
+        if runner.share_output is not None:
+            assert torch.equal(runner.share_output, eager[2]), i
