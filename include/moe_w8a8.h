@@ -79,7 +79,12 @@ typedef struct {
     int32_t ep_rank_size;   /* >= 1, divides E_g; E_loc = E_g / ep_rank_size <= 512  */
     int32_t ep_rank_id;     /* in [0, ep_rank_size): local experts are global ids    */
                             /*   [ep_rank_id*E_loc, (ep_rank_id+1)*E_loc)            */
-    int32_t quant_mode;     /* 1 = per-token dynamic INT8 (the only mode)            */
+    int32_t quant_mode;     /* 1 = per-token dynamic INT8; 2 = per token and group:  */
+                            /*   one amax / scale per row and group of quant_group   */
+                            /*   consecutive elements along the contraction, each    */
+                            /*   group's int32 partial dequantised by its own scale  */
+                            /*   and the groups summed in fp32 ("DeepSeek V4 Decode  */
+                            /*   Optimization" sec. 3.1); see quant_group            */
     float amax_eps;         /* > 0: row amax floor (e.g. 1e-6)                       */
     int32_t weight_layout;  /* MOE_WEIGHT_ROW_MAJOR: the layouts listed at           */
                             /*   moe_w8a8_forward; MOE_WEIGHT_PACKED: all four       */
@@ -102,6 +107,12 @@ typedef struct {
                             /*   MOE_ERR_UNSUPPORTED) with every weight tensor       */
                             /*   written by moe_w8a8_pack_weights_mx; the debug      */
                             /*   acc1 / acc2 dumps then hold fp32 bit patterns       */
+    int32_t quant_group;    /* quant_mode 2: elements per group, 64, 128 or 256,     */
+                            /*   dividing H, I and I_s; INT8 weights only, not with  */
+                            /*   fuse_route_scale (MOE_ERR_UNSUPPORTED). The debug   */
+                            /*   xs / hs dumps then hold H/G and max(I, I_s)/G       */
+                            /*   scales per row, acc1 / acc2 the fp32 bits of the    */
+                            /*   dequantised group sums. Ignored for quant_mode 1    */
 } moe_w8a8_dims_t;
 
 enum { MOE_WEIGHT_ROW_MAJOR = 0, MOE_WEIGHT_PACKED = 1 };

@@ -26,7 +26,7 @@ moe_status_t check_dims(const moe_w8a8_dims_t *d) {
         d->ep_rank_id >= d->ep_rank_size || d->moe_expert_num % d->ep_rank_size != 0)
         return MOE_ERR_INVALID_ARG;
     if (!(d->amax_eps > 0.0f) || !isfinite(d->amax_eps)) return MOE_ERR_INVALID_ARG;
-    if (d->quant_mode != 1) return MOE_ERR_UNSUPPORTED;
+    if (d->quant_mode != 1 && d->quant_mode != 2) return MOE_ERR_UNSUPPORTED;
     if (d->topk > kMaxTopK || d->num_tokens > kMaxTokens) return MOE_ERR_UNSUPPORTED;
     if (d->moe_expert_num / d->ep_rank_size > kMaxLocalExperts) return MOE_ERR_UNSUPPORTED;
     if (d->hidden % 256 || d->inter % 256 || d->share_inter % 256) return MOE_ERR_UNSUPPORTED;
@@ -35,6 +35,13 @@ moe_status_t check_dims(const moe_w8a8_dims_t *d) {
     if (d->fuse_route_scale != 0 && d->fuse_route_scale != 1) return MOE_ERR_INVALID_ARG;
     if (d->weight_format != MOE_WEIGHT_INT8 && d->weight_format != MOE_WEIGHT_MXFP4) return MOE_ERR_INVALID_ARG;
     if (d->weight_format == MOE_WEIGHT_MXFP4 && d->weight_layout != MOE_WEIGHT_PACKED) return MOE_ERR_UNSUPPORTED;
+    if (d->quant_mode == 2) {
+        const int g = d->quant_group;
+        if (g != 64 && g != 128 && g != 256) return MOE_ERR_UNSUPPORTED;
+        if (d->hidden % g || d->inter % g || d->share_inter % g) return MOE_ERR_UNSUPPORTED;
+        if (d->weight_format != MOE_WEIGHT_INT8 || d->fuse_route_scale) return MOE_ERR_UNSUPPORTED;
+        return MOE_ERR_UNSUPPORTED;  // kernels of the group-wise mode: not built yet
+    }
     return MOE_OK;
 }
 

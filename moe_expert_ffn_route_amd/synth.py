@@ -68,6 +68,7 @@ class Spec:
     eps: float = AMAX_EPS
     fuse_route_scale: bool = False  # routing weight folded into the GEMM2 row scale
     weight_format: str = "int8"     # "int8" | "mxfp4" (FP4 weights, FP8 activations)
+    quant_group: int = 0            # 0: one activation scale per row; G: per row and group of G
 
     @property
     def E_loc(self) -> int:
@@ -218,9 +219,10 @@ class Case:
         s = self.spec
         return dict(num_tokens=s.T, hidden=s.H, inter=s.I, share_inter=s.I_s, topk=s.K,
                     moe_expert_num=s.E_g, ep_rank_size=s.ep_size, ep_rank_id=s.ep_rank,
-                    quant_mode=1, amax_eps=s.eps, fuse_route_scale=int(s.fuse_route_scale),
+                    quant_mode=2 if s.quant_group else 1, amax_eps=s.eps, fuse_route_scale=int(s.fuse_route_scale),
                     weight_format=int(s.weight_format == "mxfp4"),
-                    weight_layout=int(s.weight_format == "mxfp4"))  # FP4 weights are always packed
+                    weight_layout=int(s.weight_format == "mxfp4"),  # FP4 weights are always packed
+                    quant_group=s.quant_group)
 
 
 def _threads() -> int:

@@ -36,7 +36,7 @@ class _Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("I_s", ctypes.c_int32), ("K", ctypes.c_int32), ("E_g", ctypes.c_int32),
                 ("ep_size", ctypes.c_int32), ("ep_rank", ctypes.c_int32), ("eps", ctypes.c_float),
-                ("fuse_route_scale", ctypes.c_int32)]
+                ("fuse_route_scale", ctypes.c_int32), ("quant_group", ctypes.c_int32)]
 
 
 class _Trace(ctypes.Structure):
@@ -78,6 +78,10 @@ def load(path: str):
     L.moe_oracle_quant_row_fp8.argtypes = [P, ctypes.c_int32, ctypes.c_float, P, P]
     L.moe_oracle_gemm_mx.restype = None
     L.moe_oracle_gemm_mx.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
+    L.moe_oracle_quant_row_groups.restype = None
+    L.moe_oracle_quant_row_groups.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P, P]
+    L.moe_oracle_gemm_i8_groups.restype = ctypes.c_int32
+    L.moe_oracle_gemm_i8_groups.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
     return L
 
 
@@ -115,13 +119,14 @@ def _c(a, dtype):
     return None if a is None else np.ascontiguousarray(a, dtype=dtype)
 
 
-def dims_of(T, H, I, K, E_g, I_s=0, ep_size=1, ep_rank=0, eps=1e-6, fuse_route_scale=False) -> _Dims:
-    return _Dims(T, H, I, I_s, K, E_g, ep_size, ep_rank, eps, int(bool(fuse_route_scale)))
+def dims_of(T, H, I, K, E_g, I_s=0, ep_size=1, ep_rank=0, eps=1e-6, fuse_route_scale=False,
+            quant_group=0) -> _Dims:
+    return _Dims(T, H, I, I_s, K, E_g, ep_size, ep_rank, eps, int(bool(fuse_route_scale)), int(quant_group))
 
 
 def _spec_dims(spec) -> _Dims:
     return dims_of(spec.T, spec.H, spec.I, spec.K, spec.E_g, spec.I_s, spec.ep_size, spec.ep_rank, spec.eps,
-                   spec.fuse_route_scale)
+                   spec.fuse_route_scale, getattr(spec, "quant_group", 0))
 
 
 def route(d: _Dims, expert_ids: np.ndarray, mask: Optional[np.ndarray] = None) -> dict:
@@ -169,6 +174,27 @@ def gemm_i8(A: np.ndarray, B: np.ndarray) -> np.ndarray:
     return C
 
 
+def quant_row_groups(v: np.ndarray, G: int, eps: float = 1e-6):
+    """Group-wise quantisation of one row: (codes, one scale per group of G)."""
+    v = _c(v, np.float32)
+    n = v.shape[-1]
+    q = np.zeros(n, np.int8)
+    s = np.zeros(n // G, np.float32)
+    lib().moe_oracle_quant_row_groups(_p(v), n, G, eps, _p(q), _p(s))
+    return q, s
+
+
+def gemm_i8_groups(a: np.ndarray, a_scales: np.ndarray, B: np.ndarray, wscale: np.ndarray, G: int) -> np.ndarray:
+    """One row through a GEMM with group-wise activation scales -> fp32 [N]."""
+    a, B = _c(a, np.int8), _c(B, np.int8)
+    a_scales, wscale = _c(a_scales, np.float32), _c(wscale, np.float32)
+    N, Kd = B.shape
+    y = np.zeros(N, np.float32)
+    if lib().moe_oracle_gemm_i8_groups(_p(a), _p(a_scales), _p(B), _p(wscale), N, Kd, G, _p(y)) != 0:
+        raise OverflowError("int32 partial overflow")
+    return y
+
+
 def swiglu(y: np.ndarray) -> np.ndarray:
     y = _c(y, np.float32)
     n = y.shape[-1] // 2
@@ -209,6 +235,11 @@ def forward(case, tokens: Optional[Sequence[int]] = None, trace: bool = False) -
         tr = _Trace(**{k: _p(v) for k, v in res.items()})
     sub = None if tokens is None else np.ascontiguousarray(tokens, np.int32)
     mx = getattr(s, "weight_format", "int8") == "mxfp4"
+    G = getattr(s, "quant_group", 0)
+    if trace and G:  # one scale per row and group; fp32 GEMM outputs in acc1 / acc2
+        res["xs"] = np.zeros((rows_max, H // G), np.float32)
+        res["hs"] = np.zeros((rows_max, Imax // G), np.float32)
+        tr = _Trace(**{k: _p(v) for k, v in res.items()})
     if mx:
         keep = [_c(case.x, np.uint16), _c(case.expert_ids, np.int32), _c(case.expert_scales, np.float32),
                 _c(case.w1, np.uint8), _c(case.w1b, np.uint8), _c(case.w1s, np.float32),
@@ -236,6 +267,7 @@ def forward(case, tokens: Optional[Sequence[int]] = None, trace: bool = False) -
         if mx:  # E4M3 codes and fp32 accumulators
             for k in ("q_x", "q_h"):
                 res[k] = res[k].view(np.uint8)
+        if mx or G:
             for k in ("acc1", "acc2"):
                 res[k] = res[k].view(np.float32)
     return res

@@ -7,7 +7,8 @@
  * quantisation -> grouped GEMM1 -> dequant/SwiGLU/quant -> grouped GEMM2 ->
  * combine; "FusedDeepMoE Kernel 深度分析报告" sec. 9.3) one stage at a time,
  * with the per-stage arithmetic of sec. 6.1, 6.2, 7.2 and 4.2 of that page and
- * the W8A8 contract of "DeepSeek V4 Decode Optimization" sec. 0.
+ * the W8A8 contract of "DeepSeek V4 Decode Optimization" sec. 0; the
+ * group-wise activation scales follow sec. 3.1 of the latter.
  */
 #include "moe_oracle.h"
 
@@ -110,6 +111,37 @@ void moe_oracle_quant_row(const float *v, int32_t n, float eps, int8_t *q, float
         if (r < -127.0f) r = -127.0f;
         q[i] = (int8_t)r;
     }
+}
+
+/* The narrowed amax of "DeepSeek V4 Decode Optimization" sec. 3.1: one amax,
+ * and so one scale, per row and group instead of per row; each group is
+ * quantised by the per-row rule above. */
+void moe_oracle_quant_row_groups(const float *v, int32_t n, int32_t G, float eps, int8_t *q, float *scales) {
+    for (int32_t g = 0; g < n / G; ++g) moe_oracle_quant_row(v + (size_t)g * G, G, eps, q + (size_t)g * G, &scales[g]);
+}
+
+/* Sec. 3.1 of the same page: each group's INT32 partial is dequantised by its
+ * own group scale (the per-row dequant order, FusedDeepMoE sec. 6.1 / 6.2,
+ * applied to the partial); the dequantised partials are added in fp32 from
+ * zero, group by group. */
+int32_t moe_oracle_gemm_i8_groups(const int8_t *a, const float *a_scales, const int8_t *B, const float *wscale,
+                                  int32_t N, int32_t Kd, int32_t G, float *y) {
+    int32_t rc = 0;
+    for (int32_t n = 0; n < N; ++n) {
+        const int8_t *b = B + (size_t)n * Kd;
+        float sum = 0.0f;
+        for (int32_t g = 0; g < Kd / G; ++g) {
+            int64_t s = 0;
+            for (int32_t k = g * G; k < (g + 1) * G; ++k) s += (int64_t)a[k] * (int64_t)b[k];
+            if (s > INT32_MAX || s < INT32_MIN) rc = -1;
+            float p = (float)(int32_t)s;
+            p = p * wscale[n];
+            p = p * a_scales[g];
+            sum = sum + p;
+        }
+        y[n] = sum;
+    }
+    return rc;
 }
 
 /* Grouped-GEMM contraction of one group (FusedDeepMoE sec. 3.3: int8 A,
@@ -263,10 +295,40 @@ static int32_t run_row(const moe_oracle_dims *d, const uint16_t *xrow, const exp
                        int fold, float route_w,
                        int32_t row, int32_t Imax, moe_oracle_trace *tr, uint16_t *zrow,
                        float *vbuf, int8_t *qx, int32_t *acc1, float *y, float *h,
-                       int8_t *qh, int32_t *acc2) {
+                       int8_t *qh, int32_t *acc2, float *gsc) {
     const int32_t H = d->H, I = ev->inter;
     int32_t rc = 0;
     float xs, hs;
+    const int32_t G = d->quant_group;
+    if (G > 0) {
+        /* group-wise activation scales (int8 weights only): x and h are
+         * quantised per group, each GEMM partial is dequantised by its own
+         * group scale; the fp32 GEMM outputs live in the int32 buffers */
+        float *xsg = gsc, *hsg = gsc + H / G;
+        float *y2 = (float *)(void *)acc2;
+        for (int32_t i = 0; i < H; ++i) {
+            float v = moe_oracle_bf16_to_f32(xrow[i]);
+            if (ev->smooth) v = v * ev->smooth[i];
+            vbuf[i] = v;
+        }
+        moe_oracle_quant_row_groups(vbuf, H, G, d->eps, qx, xsg);
+        rc |= moe_oracle_gemm_i8_groups(qx, xsg, (const int8_t *)ev->w1, ev->w1s, 2 * I, H, G, y);
+        moe_oracle_swiglu(y, I, h);
+        moe_oracle_quant_row_groups(h, I, G, d->eps, qh, hsg);
+        rc |= moe_oracle_gemm_i8_groups(qh, hsg, (const int8_t *)ev->w2, ev->w2s, H, I, G, y2);
+        for (int32_t n = 0; n < H; ++n) zrow[n] = moe_oracle_f32_to_bf16(y2[n]);
+        if (tr) {
+            if (tr->q_x) memcpy(tr->q_x + (size_t)row * H, qx, (size_t)H);
+            if (tr->xs) memcpy(tr->xs + (size_t)row * (H / G), xsg, sizeof(float) * (size_t)(H / G));
+            if (tr->acc1) memcpy(tr->acc1 + (size_t)row * 2 * Imax, y, sizeof(float) * 2 * (size_t)I);
+            if (tr->h) memcpy(tr->h + (size_t)row * Imax, h, sizeof(float) * (size_t)I);
+            if (tr->q_h) memcpy(tr->q_h + (size_t)row * Imax, qh, (size_t)I);
+            if (tr->hs) memcpy(tr->hs + (size_t)row * (Imax / G), hsg, sizeof(float) * (size_t)(I / G));
+            if (tr->acc2) memcpy(tr->acc2 + (size_t)row * H, y2, sizeof(float) * (size_t)H);
+            if (tr->z) memcpy(tr->z + (size_t)row * H, zrow, sizeof(uint16_t) * (size_t)H);
+        }
+        return rc;
+    }
     for (int32_t i = 0; i < H; ++i) {
         float v = moe_oracle_bf16_to_f32(xrow[i]);
         if (ev->smooth) v = v * ev->smooth[i];
@@ -330,6 +392,8 @@ static int32_t forward_impl(const moe_oracle_dims *d, const uint16_t *x,
     const int32_t E = d->E_g / d->ep_size;
     const int32_t Imax = Is > I ? Is : I;
     const int has_shared = Is > 0;
+    const int32_t G = d->quant_group;
+    if (G < 0 || (G > 0 && (H % G || I % G || Is % G || w1b || d->fuse_route_scale))) return -1;
     if (has_shared && (!sw1 || !sw1s || !sw2 || !sw2s || !share_output)) return -2;
 
     /* 1. dispatch grouping */
@@ -365,6 +429,7 @@ static int32_t forward_impl(const moe_oracle_dims *d, const uint16_t *x,
     int32_t *acc2 = (int32_t *)malloc(sizeof(int32_t) * (size_t)H);
     uint16_t *zk = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)H * (size_t)K);
     float *sum = (float *)malloc(sizeof(float) * (size_t)H);
+    float *gsc = (float *)malloc(sizeof(float) * (size_t)(H + Imax));
     int32_t rc = 0;
 
     const int32_t nt = token_subset ? n_subset : T;
@@ -385,7 +450,7 @@ static int32_t forward_impl(const moe_oracle_dims *d, const uint16_t *x,
                               mx ? w1b + (size_t)e * 2 * I * (H / 32) : NULL,
                               mx ? w2b + (size_t)e * H * (I / 32) : NULL};
             rc |= run_row(d, xrow, &ev, d->fuse_route_scale != 0, expert_scales[t * K + k], row, Imax,
-                          tr, zk + (size_t)k * H, vbuf, qx, acc1, y, h, qh, acc2);
+                          tr, zk + (size_t)k * H, vbuf, qx, acc1, y, h, qh, acc2, gsc);
         }
         /* 7. combine: fp32 sum from zero over kept pairs, k ascending, then
          * one bf16 cast (FusedDeepMoE sec. 4.2 LocalWindowCopy). Tokens with
@@ -414,12 +479,12 @@ static int32_t forward_impl(const moe_oracle_dims *d, const uint16_t *x,
             } else {
                 expert_view ev = {sw1, sw1s, sw2, sw2s, share_smooth, Is, sw1b, sw2b};
                 rc |= run_row(d, xrow, &ev, 0, 1.0f, shared_row[t], Imax, tr, so, vbuf, qx, acc1, y, h,
-                              qh, acc2);
+                              qh, acc2, gsc);
             }
         }
     }
     free(counts); free(offsets); free(sorted_pair); free(row_of_pair); free(shared_row);
-    free(vbuf); free(qx); free(acc1); free(y); free(h); free(qh); free(acc2); free(zk); free(sum);
+    free(vbuf); free(qx); free(acc1); free(y); free(h); free(qh); free(acc2); free(zk); free(sum); free(gsc);
     return rc;
 }
 

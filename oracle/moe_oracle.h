@@ -42,13 +42,20 @@ typedef struct {
     int32_t fuse_route_scale; /* 1: routing weight folded into the GEMM2
                                  row scale, combine only sums (DeepSeek V4
                                  Decode Optimization sec. 2.3)            */
+    int32_t quant_group;      /* 0: one activation scale per row; G > 0: one
+                                 per row and group of G consecutive elements
+                                 along the contraction (DeepSeek V4 Decode
+                                 Optimization sec. 3.1, the narrowed amax);
+                                 G divides H, I and I_s                   */
 } moe_oracle_dims;
 
 /* Optional intermediates, indexed by grouped row: routed rows [0, P) in
  * (local expert, token, k) order, then shared-expert rows [P, P + T_act) in
  * token order. Row strides: q_x/acc2/z: H; acc1: 2*max(I, I_s);
  * h/q_h: max(I, I_s). Any pointer may be NULL. Only rows of the tokens that
- * forward() computes are written. */
+ * forward() computes are written. With quant_group G > 0, xs holds H/G and hs
+ * max(I, I_s)/G scales per row, and acc1 / acc2 the bits of the fp32
+ * dequantised GEMM outputs (the group sums, before SwiGLU / the bf16 cast). */
 typedef struct {
     int32_t *sorted_pair;   /* [T*K] pair id t*K+k per routed row          */
     int32_t *row_of_pair;   /* [T*K] routed row of a pair, -1 if dropped    */
@@ -80,6 +87,18 @@ void moe_oracle_quant_row(const float *v, int32_t n, float eps, int8_t *q, float
 /* C[m][n] = sum_k A[m][k] * B[n][k], exact. Returns 0, or -1 if a sum leaves int32. */
 int32_t moe_oracle_gemm_i8(const int8_t *A, const int8_t *B, int32_t M, int32_t N,
                            int32_t Kd, int32_t *C);
+
+/* Group-wise form (quant_group G): the row quantiser applied to each group of
+ * G consecutive elements, one scale per group. */
+void moe_oracle_quant_row_groups(const float *v, int32_t n, int32_t G, float eps, int8_t *q, float *scales);
+
+/* One row through a GEMM with group-wise activation scales: for each output
+ * n, each group's exact int32 partial acc_g = sum_{k in g} a[k] * B[n][k] is
+ * dequantised by its own scale, p_g = fl(fl(float(acc_g) * wscale[n]) *
+ * a_scales[g]), and y[n] is the fp32 sum of the p_g from zero, g ascending.
+ * Returns 0, or -1 if a partial leaves int32. */
+int32_t moe_oracle_gemm_i8_groups(const int8_t *a, const float *a_scales, const int8_t *B, const float *wscale,
+                                  int32_t N, int32_t Kd, int32_t G, float *y);
 
 /* SwiGLU of one dequantised GEMM1 row: h[j] = silu(y[j]) * y[n_half + j]. */
 void moe_oracle_swiglu(const float *y, int32_t n_half, float *h);

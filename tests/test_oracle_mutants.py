@@ -46,6 +46,12 @@ MUTANTS = {
                                  "(k & 1) ? (uint8_t)(byte & 15) : (uint8_t)(byte >> 4)")],
     "mx_block_scale_bias": [("(int)sc[blk] - 127 - 10", "(int)sc[blk] - 128 - 10")],
     "fp8_quant_uses_127": [("float t = v[i] * 448.0f;", "float t = v[i] * 127.0f;")],
+    # group-wise activation scales
+    "group_scale_of_next_group": [("p = p * a_scales[g];", "p = p * a_scales[(g + 1) % (Kd / G)];")],
+    "group_partial_skips_weight_scale": [("p = p * wscale[n];", "p = p + 0.0f * wscale[n];")],
+    "group_sum_skips_first_group": [("for (int32_t g = 0; g < Kd / G; ++g) {", "for (int32_t g = 1; g < Kd / G; ++g) {")],
+    "group_quant_whole_row": [("moe_oracle_quant_row(v + (size_t)g * G, G, eps, q + (size_t)g * G, &scales[g]);",
+                               "{ float t_; moe_oracle_quant_row(v, n, eps, q, &t_); scales[g] = t_; }")],
 }
 
 

@@ -9,7 +9,8 @@ them against deliberately broken copies of the oracle.
 Sources: "FusedDeepMoE Kernel 深度分析报告" (sec. 1.2 signature, 4.1 dispatch,
 4.2 combine, 6.1/6.2 epilogues, 7.2 BlockQuant, 9.1 math correspondence) and
 "DeepSeek V4 Decode Optimization" sec. 0 (W8A8 contract; symmetric per-token
-int8 quantisation is invariant to a positive scalar).
+int8 quantisation is invariant to a positive scalar) and sec. 3.1 (group-wise
+amax).
 """
 import dataclasses
 
@@ -536,12 +537,103 @@ def pin_subset_and_empty():
     assert r["output"].shape == (0, c0.spec.H) and np.all(r["expert_token_nums"] == 0)
 
 
+# ------------------------------------------------ group-wise activation scales
+# "DeepSeek V4 Decode Optimization" sec. 3.1: the amax narrowed from per row to
+# per row and group, each group's INT32 partial dequantised by its own scale.
+
+
+def pin_group_quant_closed_forms():
+    rng = np.random.default_rng(31)
+    G = 64
+    v = rng.standard_normal(4 * G).astype(np.float32)
+    v[G + 5] = 40.0                      # an outlier in group 1
+    v[3 * G:] = 0.0                      # an all-zero group 3
+    q, s = oracle.quant_row_groups(v, G, eps=1e-6)
+    inv127 = np.float32(1.0) / np.float32(127.0)
+    for g in range(4):
+        vg, qg = v[g * G:(g + 1) * G], q[g * G:(g + 1) * G].astype(np.float64)
+        a = max(np.float32(np.abs(vg).max()), np.float32(1e-6))
+        assert s[g] == np.float32(a * inv127)                     # scale = a' * fl(1/127), per group
+        if g < 3:
+            assert abs(qg[int(np.argmax(np.abs(vg)))]) == 127     # the group max maps to +-127
+        assert np.all(np.abs(qg * a / 127.0 - vg) <= a / 254.0 * (1 + 1e-6))  # half a step of its own group
+    assert not q[3 * G:].any()
+    # the outlier coarsens only its own group: the other groups' codes and
+    # scales are those of the same row without it
+    w = v.copy()
+    w[G + 5] = 0.5
+    q2, s2 = oracle.quant_row_groups(w, G, eps=1e-6)
+    for g in (0, 2, 3):
+        assert s2[g] == s[g] and np.array_equal(q2[g * G:(g + 1) * G], q[g * G:(g + 1) * G])
+    assert s[1] > 5 * s2[1]
+
+
+def pin_group_gemm_vs_float64():
+    # each group's exact partial, dequantised by its own scale, summed: float64
+    # sums of numpy integer matmuls bound the fp32 result
+    rng = np.random.default_rng(32)
+    G, K, N = 64, 512, 40
+    a = rng.integers(-127, 128, K).astype(np.int8)
+    B = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    a_sc = rng.uniform(1e-3, 1e-1, K // G).astype(np.float32)   # very different scales per group
+    ws = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    y = oracle.gemm_i8_groups(a, a_sc, B, ws, G).astype(np.float64)
+    parts = np.stack([(B[:, g * G:(g + 1) * G].astype(np.int64) @ a[g * G:(g + 1) * G].astype(np.int64))
+                      for g in range(K // G)], axis=1).astype(np.float64)
+    terms = parts * ws[:, None].astype(np.float64) * a_sc[None, :].astype(np.float64)
+    ref = terms.sum(axis=1)
+    bound = 3 * (K // G) * 2.0 ** -24 * np.abs(terms).sum(axis=1)
+    assert np.all(np.abs(y - ref) <= bound)
+    # one group alone: exactly the per-row dequant of its partial
+    y1 = oracle.gemm_i8_groups(a[:G], a_sc[:1], B[:, :G].copy(), ws, G)
+    assert np.array_equal(y1, (parts[:, 0].astype(np.float32) * ws) * a_sc[0])
+
+
+def pin_group_single_group_is_row_mode():
+    # a group spanning the whole row is the per-row mode, bit for bit; the
+    # fp32 GEMM dumps then equal the per-row dequant of the int32 accumulators
+    spec = small_spec(T=6, H=128, I=128, E_g=4, K=2, I_s=128, smooth=True, active=5, wseed=23)
+    c = synth.make_case(spec)
+    r1 = run(c, trace=True)
+    r2 = run(_replace(c, spec=dataclasses.replace(spec, quant_group=128)), trace=True)
+    for k in ("output", "share_output", "expert_token_nums"):
+        assert np.array_equal(r2[k], r1[k]), k
+    rows = np.concatenate([np.arange(r1["P"]), r1["P"] + np.arange(r1["T_act"])])
+    for k in ("q_x", "q_h", "h", "z"):
+        assert np.array_equal(r2[k][rows], r1[k][rows]), k
+    assert np.array_equal(r2["xs"][rows, 0], r1["xs"][rows]) and np.array_equal(r2["hs"][rows, 0], r1["hs"][rows])
+    e_row = np.repeat(np.arange(spec.E_loc), r1["expert_token_nums"])
+    for row in range(r1["P"]):
+        y = (r1["acc1"][row, :2 * spec.I].astype(np.float32) * c.w1s[e_row[row]]) * r1["xs"][row]
+        assert np.array_equal(r2["acc1"][row, :2 * spec.I], y)
+
+
+def pin_group_outlier_resolution():
+    # one token with a large outlier: with 64-element groups only the outlier's
+    # group loses resolution, so GEMM1's dequantised output stays about
+    # sqrt(H / 64) = 4 times closer to the float64 product than with one scale
+    # per row (the quantisation error of x is all that differs)
+    spec = small_spec(T=1, H=1024, I=128, E_g=1, K=1, wseed=24)
+    c = synth.make_case(spec)
+    x = F32(c.x).copy()
+    x[0, 7] = 200.0
+    c = _replace(c, x=synth.f32_to_bf16_bits(x))
+    y = (c.w1[0].astype(np.float64) @ F32(c.x).astype(np.float64)[0]) * c.w1s[0]
+    r0 = run(c, trace=True)
+    y0 = (r0["acc1"][0, :2 * spec.I].astype(np.float32) * c.w1s[0]) * r0["xs"][0]
+    r1 = run(_replace(c, spec=dataclasses.replace(spec, quant_group=64)), trace=True)
+    y1 = r1["acc1"][0, :2 * spec.I]
+    e0, e1 = (np.linalg.norm(v.astype(np.float64) - y) / np.linalg.norm(y) for v in (y0, y1))
+    assert e1 < 0.03 and e0 > 3 * e1, (e0, e1)
+
+
 PINS = [pin_route_bruteforce, pin_route_count_invariant, pin_quant_closed_forms, pin_quant_ties_to_even, pin_quant_zero_and_eps,
         pin_quant_integer_rows, pin_quant_pow2_invariance, pin_gemm_exact, pin_swiglu_vs_torch,
         pin_dense_swiglu_ffn, pin_scale_linearity, pin_permutation_invariance, pin_combine,
         pin_mask_and_ep_share, pin_shared_matches_routed, pin_smooth_scales, pin_subset_and_empty,
         pin_fused_route_scale, pin_e4m3_codes_vs_torch, pin_e2m1_values, pin_fp8_quant_rules, pin_gemm_mx_exact,
-        pin_mx_block_scale_linearity, pin_mx_forward_stages]
+        pin_mx_block_scale_linearity, pin_mx_forward_stages, pin_group_quant_closed_forms, pin_group_gemm_vs_float64,
+        pin_group_single_group_is_row_mode, pin_group_outlier_resolution]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)

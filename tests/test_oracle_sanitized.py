@@ -37,6 +37,8 @@ CASES = {
     "k16_e512": spec(T=20, E_g=512, K=16, I_s=256),
     "fused_route_scale": spec(T=30, E_g=16, K=4, I_s=256, active=25, fuse_route_scale=True),
     "mxfp4_weights": spec(T=12, E_g=8, K=3, I_s=256, active=10, smooth=True, weight_format="mxfp4"),
+    "group_scales": spec(T=14, H=512, I=256, E_g=8, K=3, I_s=512, active=12, smooth=True, share_smooth=True,
+                         quant_group=64),
 }
 
 
