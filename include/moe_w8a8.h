@@ -107,9 +107,10 @@ typedef struct {
                             /*   MOE_ERR_UNSUPPORTED) with every weight tensor       */
                             /*   written by moe_w8a8_pack_weights_mx; the debug      */
                             /*   acc1 / acc2 dumps then hold fp32 bit patterns       */
-    int32_t quant_group;    /* quant_mode 2: elements per group, 64, 128 or 256,     */
-                            /*   dividing H, I and I_s; INT8 weights only, not with  */
-                            /*   fuse_route_scale (MOE_ERR_UNSUPPORTED). The debug   */
+    int32_t quant_group;    /* quant_mode 2: elements per group, 64, 128 or 256      */
+                            /*   (so it divides H, I and I_s); INT8 weights only,    */
+                            /*   not with fuse_route_scale (MOE_ERR_UNSUPPORTED      */
+                            /*   otherwise). The debug                               */
                             /*   xs / hs dumps then hold H/G and max(I, I_s)/G       */
                             /*   scales per row, acc1 / acc2 the fp32 bits of the    */
                             /*   dequantised group sums. Ignored for quant_mode 1    */

@@ -267,12 +267,16 @@ def debug_buffers(dims: Dims, device="cuda") -> tuple[Debug, dict]:
     T, K, H, E = dims.num_tokens, dims.topk, dims.hidden, dims.e_loc
     imax = max(dims.inter, dims.share_inter)
     R = T * K + T
+    G = dims.quant_group if dims.quant_mode == 2 else 0
+    ngx, ngh = (H // G, imax // G) if G else (1, 1)  # activation scales per row
     z = lambda *s, dt: torch.zeros(s, dtype=dt, device=device)
     bufs = dict(sorted_pair=z(max(1, T * K), dt=torch.int32), row_of_pair=z(max(1, T * K), dt=torch.int32),
                 group_offset=z(E + 1, dt=torch.int32), shared_token=z(max(1, T), dt=torch.int32),
-                num_rows=z(4, dt=torch.int32), q_x=z(max(1, R), H, dt=torch.int8), xs=z(max(1, R), dt=torch.float32),
+                num_rows=z(4, dt=torch.int32), q_x=z(max(1, R), H, dt=torch.int8),
+                xs=z(max(1, R), ngx, dt=torch.float32) if G else z(max(1, R), dt=torch.float32),
                 acc1=z(max(1, R), 2 * imax, dt=torch.int32), h=z(max(1, R), imax, dt=torch.float32),
-                q_h=z(max(1, R), imax, dt=torch.int8), hs=z(max(1, R), dt=torch.float32),
+                q_h=z(max(1, R), imax, dt=torch.int8),
+                hs=z(max(1, R), ngh, dt=torch.float32) if G else z(max(1, R), dt=torch.float32),
                 acc2=z(max(1, R), H, dt=torch.int32), z=z(max(1, R), H, dt=torch.int16))
     dbg = Debug(**{k: v.data_ptr() for k, v in bufs.items()})
     return dbg, bufs

@@ -37,12 +37,18 @@ moe_status_t check_dims(const moe_w8a8_dims_t *d) {
     if (d->weight_format == MOE_WEIGHT_MXFP4 && d->weight_layout != MOE_WEIGHT_PACKED) return MOE_ERR_UNSUPPORTED;
     if (d->quant_mode == 2) {
         const int g = d->quant_group;
-        if (g != 64 && g != 128 && g != 256) return MOE_ERR_UNSUPPORTED;
-        if (d->hidden % g || d->inter % g || d->share_inter % g) return MOE_ERR_UNSUPPORTED;
+        if (g != 64 && g != 128 && g != 256) return MOE_ERR_UNSUPPORTED;  // each divides H, I, I_s
         if (d->weight_format != MOE_WEIGHT_INT8 || d->fuse_route_scale) return MOE_ERR_UNSUPPORTED;
-        return MOE_ERR_UNSUPPORTED;  // kernels of the group-wise mode: not built yet
     }
     return MOE_OK;
+}
+
+// Activation scales per row of x (H / G) and of h (max(I, I_s) / G) with
+// group-wise scales (quant_mode 2), else 1.
+int groups_x(const moe_w8a8_dims_t *d) { return d->quant_mode == 2 ? d->hidden / d->quant_group : 1; }
+int groups_h(const moe_w8a8_dims_t *d) {
+    const int imax = d->inter > d->share_inter ? d->inter : d->share_inter;
+    return d->quant_mode == 2 ? imax / d->quant_group : 1;
 }
 
 Layout make_layout(const moe_w8a8_dims_t *d) {
@@ -56,6 +62,7 @@ Layout make_layout(const moe_w8a8_dims_t *d) {
     const size_t nonempty = E < TK ? E : TK;
     // rows per GEMM work item: 16 for decode batches; 256 (tall items) when
     // the routed experts average kTallMinRows rows or more; 32 otherwise.
+    // Group-wise scales: 16 at every batch size (gemm.hip).
     // FP4 weights (gemm_mx.hip): 32 when the local experts can average 16 rows
     // or more (T*K / ep_rank_size >= 16 * E_loc), else 16 (measured on MI355X:
     // 32-row items take the T = 512 layer from 996 to 859 us but slow the
@@ -63,10 +70,11 @@ Layout make_layout(const moe_w8a8_dims_t *d) {
     const bool tall = T >= kTallMinRows && TK >= static_cast<size_t>(kTallMinRows) * E;
     const bool mx = d->weight_format == MOE_WEIGHT_MXFP4;
     const bool mx_wide = T > kChunkRowsSmall && TK / d->ep_rank_size >= static_cast<size_t>(kTileN) * E;
-    L.chunk_rows = T <= kChunkRowsSmall ? kChunkRowsSmall
-                   : mx                 ? (mx_wide ? 2 * kTileN : kChunkRowsSmall)
-                   : tall               ? kChunkRowsTall
-                                        : kChunkRowsLarge;
+    const bool grp = d->quant_mode == 2;
+    L.chunk_rows = T <= kChunkRowsSmall || grp ? kChunkRowsSmall
+                   : mx                        ? (mx_wide ? 2 * kTileN : kChunkRowsSmall)
+                   : tall                      ? kChunkRowsTall
+                                               : kChunkRowsLarge;
     const size_t cr = L.chunk_rows;
     L.max_chunks = static_cast<int>(nonempty + TK / cr + (shared ? (T + cr - 1) / cr : 0));
     const size_t R = L.rows_max;
@@ -79,12 +87,13 @@ Layout make_layout(const moe_w8a8_dims_t *d) {
     L.row_group = o;   o = up256(o + sizeof(int32_t) * R);
     L.chunks = o;      o = up256(o + sizeof(int4) * L.max_chunks);
     L.q_tok = o;       o = up256(o + T * H);
-    L.xs_tok = o;      o = up256(o + sizeof(float) * T);
+    const size_t ngx = groups_x(d), ngh = groups_h(d);
+    L.xs_tok = o;      o = up256(o + sizeof(float) * T * ngx);
     L.q_sm = o;        o = up256(o + R * H);  // per-pair rows [0, T*K), per-token shared rows after
-    L.s_sm = o;        o = up256(o + sizeof(float) * R);
+    L.s_sm = o;        o = up256(o + sizeof(float) * R * ngx);
     L.h = o;           o = up256(o + sizeof(float) * R * L.imax);
     L.q_h = o;         o = up256(o + R * L.imax);
-    L.hs = o;          o = up256(o + sizeof(float) * R);
+    L.hs = o;          o = up256(o + sizeof(float) * R * ngh);
     L.hs2 = o;         o = up256(o + sizeof(float) * R);  // GEMM2 row scales with the routing weight folded in
     L.z = o;           o = up256(o + sizeof(uint16_t) * TK * H);
     L.total = o;
@@ -241,7 +250,11 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
     tq.q_sm = reinterpret_cast<int8_t *>(ws + L.q_sm);
     tq.s_sm = reinterpret_cast<float *>(ws + L.s_sm);
     const bool mx = d->weight_format == MOE_WEIGHT_MXFP4;
+    const bool grp = d->quant_mode == 2;
+    const int ngx = groups_x(d), ngh = groups_h(d);
     tq.fp8 = mx;
+    tq.ng = ngx;
+    tq.gl = grp ? d->quant_group / 8 : 0;
     if (launch_route_quant(ra, tq, s) != hipSuccess || !mark(1)) return MOE_ERR_HIP;
 
     // GEMM1's activation rows: per token (q_tok, index row_token) or per
@@ -259,7 +272,9 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g.a_scale_r = routed_tok ? tq.s_tok : tq.s_sm;
         g.idx_r = routed_tok ? ra.row_token : ra.sorted_pair;
         g.A_s = shared_tok ? tq.q_tok : tq.q_sm + sh_row0 * H;
-        g.a_scale_s = shared_tok ? tq.s_tok : tq.s_sm + sh_row0;
+        g.a_scale_s = shared_tok ? tq.s_tok : tq.s_sm + sh_row0 * ngx;
+        g.a_ng = ngx;
+        g.gsteps = grp ? d->quant_group / 64 : 0;
         return g;
     };
     if (T > 0) {
@@ -314,12 +329,15 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         rq.route_w = expert_scales;
         rq.sorted_pair = ra.sorted_pair;
         rq.fp8 = mx;
+        rq.ng = ngh;
+        rq.gl = grp ? d->quant_group / 4 : 0;
         if (launch_requant(rq, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
 
         GemmArgs g2 = g1;
         g2.A = rq.q;
         g2.a_stride = L.imax;
         g2.a_scale = fused ? rq.scale2 : rq.scale;
+        g2.a_ng = ngh;
         g2.W = gmm2_weight;
         g2.Ws = gmm2_weight_scale;
         g2.W_sh = share_gmm2_weight;
@@ -376,7 +394,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         {D.num_rows, L.meta, sizeof(int32_t) * kMetaWords},
         {D.h, L.h, sizeof(float) * R * L.imax},
         {D.q_h, L.q_h, R * L.imax},
-        {D.hs, L.hs, sizeof(float) * R},
+        {D.hs, L.hs, sizeof(float) * R * ngh},
     };
     if ((D.q_x || D.xs) &&
         launch_dbg_gather(gemm1_inputs(), I32(L.row_group), meta, shared, L.rows_max, D.q_x, D.xs, s) != hipSuccess)

@@ -51,8 +51,15 @@ __device__ __forceinline__ v4i ld16_stream(const int8_t *p) {
 
 // KIND 1 = GEMM1 + SwiGLU, 2 = GEMM2 + bf16. MT = 16-row MFMA tiles per
 // chunk. NPASS = K batches per wave (0: taken from n_pass_rt at run time).
-template <int KIND, int WAVES, int KSTEPS, bool PACKED, int MT, int NPASS>
+// GS > 0: group-wise activation scales ("DeepSeek V4 Decode Optimization"
+// sec. 3.1), one per GS 64-byte K steps of a row (a.a_ng per row): at the end
+// of each group the lane's int32 partials are dequantised,
+// p = (float(acc) * w_scale[n]) * group_scale[row], and added to its fp32
+// sums, which the epilogue adds over the waves in wave order (MT = 1; a
+// wave's K slice and each batch hold whole groups).
+template <int KIND, int WAVES, int KSTEPS, bool PACKED, int MT, int NPASS, int GS = 0>
 __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_dim, int n_pass_rt) {
+    static_assert(GS == 0 || (MT == 1 && KSTEPS % GS == 0), "group-wise scales: one row tile, whole groups per batch");
     constexpr int kThreads = WAVES * kWave;
     constexpr int kCols = KIND == 1 ? kTileN : 2 * kTileN;  // output columns of one work item
     constexpr int kElems = kTileN * kCols;                   // outputs of one 16-row tile
@@ -136,6 +143,19 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
     const int col = (KIND == 1 ? nt * kTileN : nt * 2 * kTileN) + jc;
     const float wsc0 = Ws[col];
     const float wsc1 = KIND == 1 ? Ws[inter + col] : 0.0f;
+    // group-wise scales: the lane's two output channels (one per weight tile)
+    // and the activation rows of its four accumulator rows 4 * (l / 16) + i
+    float wl0 = 0.0f, wl1 = 0.0f;
+    int srow[4] = {0, 0, 0, 0};
+    if constexpr (GS > 0) {
+        wl0 = Ws[rowA + r16];
+        wl1 = Ws[rowB + r16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int lr = min(4 * kg + i, rows - 1);
+            srow[i] = KIND == 1 ? aidx[row0 + lr] : row0 + lr;
+        }
+    }
     int rrow[kEpt], rtok[kEpt];  // epilogue rows of the first row tile
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) {
@@ -193,6 +213,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
         acc0[mt] = v4i{0, 0, 0, 0};
         acc1[mt] = v4i{0, 0, 0, 0};
     }
+    float f0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, f1[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // group-wise sums
     // One K batch: this batch's A rows, then (if any) the next weight batch,
     // then the MFMAs, which wait only for this batch's loads.
     auto batch = [&](const v4i (&w)[2][KSTEPS], v4i (&nxt)[2][KSTEPS], int pass, bool has_next) {
@@ -206,6 +227,16 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
                 for (int i = 0; i < KSTEPS; ++i) x[mt][i] = ld16(pam + i * 64);
             }
         }
+        // group-wise scales of this batch's groups, for the lane's four rows
+        constexpr int kGroups = GS > 0 ? KSTEPS / GS : 1;
+        float gsc[kGroups][4];
+        if constexpr (GS > 0) {
+            const int g0 = (step0 + pass * KSTEPS) / GS;
+#pragma unroll
+            for (int q = 0; q < kGroups; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gsc[q][i] = Ascale[static_cast<size_t>(srow[i]) * a.a_ng + g0 + q];
+        }
         if (has_next) ldw(nxt, pass + 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -217,6 +248,22 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
                     const v4i xi = av ? x[mt][i] : v4i{0, 0, 0, 0};
                     acc0[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xi, w[0][i], acc0[mt], 0, 0, 0);
                     acc1[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xi, w[1][i], acc1[mt], 0, 0, 0);
+                    if constexpr (GS > 0) {
+                        if ((i + 1) % GS == 0) {  // end of a group: dequantise its partials
+                            const int q = i / GS;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float p0 = static_cast<float>(acc0[0][e]) * wl0;
+                                p0 = p0 * gsc[q][e];
+                                f0[e] = f0[e] + p0;
+                                float p1 = static_cast<float>(acc1[0][e]) * wl1;
+                                p1 = p1 * gsc[q][e];
+                                f1[e] = f1[e] + p1;
+                            }
+                            acc0[0] = v4i{0, 0, 0, 0};
+                            acc1[0] = v4i{0, 0, 0, 0};
+                        }
+                    }
                 }
             }
         }
@@ -232,6 +279,49 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
         }
     }
 
+    if constexpr (GS > 0) {
+        // the waves' fp32 sums, added in wave order
+        __shared__ float redf[WAVES][2][kTileN][kTileN];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            redf[wave][0][4 * kg + i][r16] = f0[i];
+            redf[wave][1][4 * kg + i][r16] = f1[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e) {
+            const int idx = tid + e * kThreads;
+            const int m = idx / kCols;
+            if (idx < kElems && m < rows) {
+                const int r = row0 + m;
+                if (KIND == 1) {
+                    float yg = 0.0f, yu = 0.0f;
+#pragma unroll
+                    for (int w = 0; w < WAVES; ++w) {
+                        yg = yg + redf[w][0][m][jc];
+                        yu = yu + redf[w][1][m][jc];
+                    }
+                    a.h[static_cast<size_t>(r) * a.imax + col] = swiglu_y(yg, yu);
+                    if (a.dbg_acc) {
+                        a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + col] = __float_as_int(yg);
+                        a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + inter + col] = __float_as_int(yu);
+                    }
+                } else {
+                    float y = 0.0f;
+#pragma unroll
+                    for (int w = 0; w < WAVES; ++w) y = y + redf[w][jc / kTileN][m][jc % kTileN];
+                    const uint16_t zb = f32_to_bf16(y);
+                    if (routed)
+                        a.z[static_cast<size_t>(r) * a.H + col] = zb;
+                    else
+                        a.share_out[static_cast<size_t>(rtok[e]) * a.H + col] = zb;
+                    if (a.dbg_acc) a.dbg_acc[static_cast<size_t>(r) * a.H + col] = __float_as_int(y);
+                    if (a.dbg_z) a.dbg_z[static_cast<size_t>(r) * a.H + col] = zb;
+                }
+            }
+        }
+        return;
+    }
     __shared__ int red[WAVES][2][kTileN][kTileN];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -297,14 +387,15 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
 #ifndef MOE_GEMM2_KSTEPS
 #define MOE_GEMM2_KSTEPS 4
 #endif
-template <int KIND, int WAVES, int KSTEPS, bool PACKED, int MT, int NPASS>
+template <int KIND, int WAVES, int KSTEPS, bool PACKED, int MT, int NPASS, int GS = 0>
 void launch_one(const GemmArgs &a, dim3 grid, int k_dim, int n_pass, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const dim3 blk(WAVES * kWave);
     if (e0 || e1)
-        hipExtLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, NPASS>), grid, blk, 0, s, e0, e1, 0, a,
-                              k_dim, n_pass);
+        hipExtLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, NPASS, GS>), grid, blk, 0, s, e0, e1, 0,
+                              a, k_dim, n_pass);
     else
-        hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, NPASS>), grid, blk, 0, s, a, k_dim, n_pass);
+        hipLaunchKernelGGL((gemm_kernel<KIND, WAVES, KSTEPS, PACKED, MT, NPASS, GS>), grid, blk, 0, s, a, k_dim,
+                           n_pass);
 }
 
 template <int KIND, int WAVES, int KSTEPS, bool PACKED, int MT>
@@ -338,8 +429,59 @@ hipError_t launch_w(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s,
                     : launch_np<KIND, WAVES, 1, false, 1>(a, grid, k_dim, steps, s, e0, e1);
 }
 
+// Group-wise scales (a.gsteps = GS steps of 64 per group): every wave's K
+// slice must hold whole groups, so K is split over W = min(8, groups) waves
+// (groups = k_dim / (64 * GS), a power-of-two count is not required: W is the
+// largest of 8, 4, 2, 1 dividing it). A slice of up to 8 steps is one batch;
+// longer slices go in batches of one group.
+template <int KIND, bool PACKED, int GS, int W>
+hipError_t launch_grp_w(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    const int spw = k_dim / (64 * W);
+    switch (spw) {
+        case GS: launch_one<KIND, W, GS, PACKED, 1, 1, GS>(a, grid, k_dim, 1, s, e0, e1); break;
+        case 2 * GS: launch_one<KIND, W, 2 * GS, PACKED, 1, 1, GS>(a, grid, k_dim, 1, s, e0, e1); break;
+        case 4 * GS:
+            if constexpr (GS <= 2) launch_one<KIND, W, 4 * GS, PACKED, 1, 1, GS>(a, grid, k_dim, 1, s, e0, e1);
+            else launch_one<KIND, W, GS, PACKED, 1, 0, GS>(a, grid, k_dim, 4, s, e0, e1);
+            break;
+        case 8 * GS:
+            if constexpr (GS == 1) launch_one<KIND, W, 8, PACKED, 1, 1, GS>(a, grid, k_dim, 1, s, e0, e1);
+            else launch_one<KIND, W, GS, PACKED, 1, 0, GS>(a, grid, k_dim, 8, s, e0, e1);
+            break;
+        default: launch_one<KIND, W, GS, PACKED, 1, 0, GS>(a, grid, k_dim, spw / GS, s, e0, e1); break;
+    }
+    return hipGetLastError();
+}
+
+template <int KIND, bool PACKED, int GS>
+hipError_t launch_grp(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    const int groups = k_dim / (64 * GS);
+    if (groups % 8 == 0) return launch_grp_w<KIND, PACKED, GS, 8>(a, grid, k_dim, s, e0, e1);
+    if (groups % 4 == 0) return launch_grp_w<KIND, PACKED, GS, 4>(a, grid, k_dim, s, e0, e1);
+    if (groups % 2 == 0) return launch_grp_w<KIND, PACKED, GS, 2>(a, grid, k_dim, s, e0, e1);
+    return launch_grp_w<KIND, PACKED, GS, 1>(a, grid, k_dim, s, e0, e1);
+}
+
+template <int KIND, bool PACKED>
+hipError_t launch_grp_p(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    switch (a.gsteps) {
+        case 1: return launch_grp<KIND, PACKED, 1>(a, grid, k_dim, s, e0, e1);
+        case 2: return launch_grp<KIND, PACKED, 2>(a, grid, k_dim, s, e0, e1);
+        case 4: return launch_grp<KIND, PACKED, 4>(a, grid, k_dim, s, e0, e1);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int KIND>
 hipError_t launch_kind(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    if (a.gsteps > 0) {
+        if (a.mt != 1 || k_dim % (64 * a.gsteps)) return hipErrorInvalidValue;
+        const long blocks = static_cast<long>(max_chunks) * a.n_tiles;
+        if (blocks <= 0) return hipSuccess;
+        const dim3 grid(static_cast<unsigned>(blocks));
+        return a.packed ? launch_grp_p<KIND, true>(a, grid, k_dim, s, e0, e1)
+                        : launch_grp_p<KIND, false>(a, grid, k_dim, s, e0, e1);
+    }
     constexpr int W = KIND == 1 ? MOE_GEMM1_WAVES : MOE_GEMM2_WAVES;
     constexpr int KS = KIND == 1 ? MOE_GEMM1_KSTEPS : MOE_GEMM2_KSTEPS;
     if constexpr (W == 8) {

@@ -90,6 +90,8 @@ struct TokQuantArgs {
     int8_t *q_sm;          // [T*K + T, H]
     float *s_sm;           // [T*K + T]
     int fp8;               // quantise to FP8 E4M3 codes instead of INT8
+    int ng;                // scales per row: H / G with group-wise scales, else 1
+    int gl;                // group-wise scales: lanes per group (G / 8), else 0
 };
 
 struct RequantArgs {
@@ -107,6 +109,8 @@ struct RequantArgs {
     const float *route_w;        // [T*K]
     const int32_t *sorted_pair;  // [P]
     int fp8;                     // FP8 E4M3 codes instead of INT8
+    int ng;                      // scale stride per row: Imax / G with group-wise scales, else 1
+    int gl;                      // group-wise scales: lanes per group (G / 4), else 0
 };
 
 struct GemmArgs {
@@ -128,6 +132,8 @@ struct GemmArgs {
     int I, I_s, H, E_loc, imax;
     int g_lo, g_hi;   // only chunks of groups in [g_lo, g_hi)
     int packed;       // weights in moe_w8a8_pack_weights order
+    int gsteps;       // group-wise activation scales: 64-byte K steps per group (0: one scale per row)
+    int a_ng;         // activation scales per row (1 without group-wise scales)
     int mt;           // 16-row MFMA tiles per chunk
     int n_tiles;      // work items per chunk along N
     const int4 *chunks;
@@ -214,14 +220,15 @@ __device__ __forceinline__ float dequant(Acc acc, float w_scale, float row_scale
     const float y = static_cast<float>(acc) * w_scale;
     return y * row_scale;
 }
-template <typename Acc>
-__device__ __forceinline__ float swiglu(Acc acc_g, Acc acc_u, float ws_g, float ws_u, float row_scale) {
-    const float yg = dequant(acc_g, ws_g, row_scale);
-    const float yu = dequant(acc_u, ws_u, row_scale);
+__device__ __forceinline__ float swiglu_y(float yg, float yu) {
     const float ex = expf(-yg);
     const float den = 1.0f + ex;
     const float sg = yg / den;
     return sg * yu;
+}
+template <typename Acc>
+__device__ __forceinline__ float swiglu(Acc acc_g, Acc acc_u, float ws_g, float ws_u, float row_scale) {
+    return swiglu_y(dequant(acc_g, ws_g, row_scale), dequant(acc_u, ws_u, row_scale));
 }
 
 }  // namespace moe

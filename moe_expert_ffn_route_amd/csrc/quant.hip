@@ -8,23 +8,26 @@
 //                        order (the q_x / xs dump).
 //
 // Rows of up to 4096 elements take one wavefront each (in batches of more
-// than 256 grouped rows), four to a workgroup, with no workgroup barrier: the row sits in the wave's registers between its
-// amax and its quantisation. Longer rows take a workgroup of 256 threads each.
+// than 256 grouped rows), four to a workgroup, with no workgroup barrier: the
+// row sits in the wave's registers between its amax and its quantisation.
+// Longer rows take a workgroup of 256 threads each.
 // Either way each row is read once. (x is quantised in the routing launch.)
 #include "rowquant.h"
 
 namespace moe {
 namespace {
 
-template <bool FP8>
+// GL > 0: group-wise scales ("DeepSeek V4 Decode Optimization" sec. 3.1), one
+// per 4 * GL elements, a.ng of them per row.
+template <bool FP8, int GL>
 __global__ __launch_bounds__(kTPR) void requant_kernel(RequantArgs a) {
     __shared__ float s_part[kTPR / kWave];
     const int r = blockIdx.x;
     const int nrows = a.meta[kMetaP] + (a.has_shared ? a.meta[kMetaTAct] : 0);
     if (r >= nrows) return;
     const int n = a.row_group[r] < a.E_loc ? a.I : a.I_s;
-    quant_f32_row<FP8>(a.h + static_cast<size_t>(r) * a.imax, n, a.eps, a.q + static_cast<size_t>(r) * a.imax,
-                  a.scale + r, true, 0, threadIdx.x, s_part);
+    quant_f32_row<FP8, GL>(a.h + static_cast<size_t>(r) * a.imax, n, a.eps, a.q + static_cast<size_t>(r) * a.imax,
+                           a.scale + static_cast<size_t>(r) * a.ng, true, 0, threadIdx.x, s_part);
     if (a.scale2 && threadIdx.x == 0) {  // the thread that wrote scale[r]
         const float hs = a.scale[r];
         a.scale2[r] = r < a.meta[kMetaP] ? hs * a.route_w[a.sorted_pair[r]] : hs;
@@ -39,7 +42,7 @@ __device__ __forceinline__ int wave_row() {
 }
 
 // NCH 16-byte chunks of fp32 per lane: rows of up to NCH * 256 values.
-template <int NCH, bool FP8>
+template <int NCH, bool FP8, int GL>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void requant_wave_kernel(RequantArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const int r = wave_row();
@@ -63,6 +66,25 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void requant_wave_kernel(Req
     if (r >= nrows) return;
     if (!a.load_early) load();
     const int n = g < a.E_loc ? a.I : a.I_s;
+    int8_t *dst = a.q + static_cast<size_t>(r) * a.imax;
+    if constexpr (GL > 0) {
+        // one scale per group of 4 * GL elements, each in GL neighbouring lanes
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int i = (lane + j * kWave) * 4;
+            if (j * kWave * 4 >= n) break;  // uniform
+            const float mj = i < n ? fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w)))
+                                   : 0.0f;
+            const float ap = fmaxf(segment_max<GL>(mj), a.eps);
+            const float inv = 1.0f / ap;
+            if (i < n) {
+                *reinterpret_cast<uint32_t *>(dst + i) = quant4<FP8>(v[j].x, v[j].y, v[j].z, v[j].w, inv);
+                if ((lane & (GL - 1)) == 0)
+                    a.scale[static_cast<size_t>(r) * a.ng + i / (4 * GL)] = ap * (1.0f / kQMax<FP8>);
+            }
+        }
+        return;
+    }
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
@@ -71,7 +93,6 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void requant_wave_kernel(Req
     }
     const float ap = fmaxf(wave_max(m), a.eps);
     const float inv = 1.0f / ap;
-    int8_t *dst = a.q + static_cast<size_t>(r) * a.imax;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
         const int i = (lane + j * kWave) * 4;
@@ -98,7 +119,9 @@ __global__ __launch_bounds__(256) void dbg_gather_kernel(GemmArgs g, const int32
         for (int i = threadIdx.x * 16; i < g.H; i += 256 * 16)
             *reinterpret_cast<uint4 *>(dst_q + static_cast<size_t>(r) * g.H + i) =
                 *reinterpret_cast<const uint4 *>(qs + i);
-    if (dst_xs && threadIdx.x == 0) dst_xs[r] = (routed ? g.a_scale_r : g.a_scale_s)[src];
+    if (dst_xs && static_cast<int>(threadIdx.x) < g.a_ng)  // a_ng <= H / 64 <= 256 scales per row
+        dst_xs[static_cast<size_t>(r) * g.a_ng + threadIdx.x] =
+            (routed ? g.a_scale_r : g.a_scale_s)[src * g.a_ng + threadIdx.x];
 }
 
 // Rows of up to MOE_REQUANT_WAVE_MAX values take one wavefront each, longer
@@ -114,15 +137,15 @@ __global__ __launch_bounds__(256) void dbg_gather_kernel(GemmArgs g, const int32
 #define MOE_REQUANT_BLOCK_ROWS 256
 #endif
 
-template <bool FP8>
+template <bool FP8, int GL>
 hipError_t launch_requant_fmt(const RequantArgs &a, dim3 wgrid, dim3 wblk, hipStream_t s) {
     const bool wave = a.rows_max > MOE_REQUANT_BLOCK_ROWS;
     if (wave && a.imax <= 8 * 256 && a.imax <= MOE_REQUANT_WAVE_MAX)
-        hipLaunchKernelGGL((requant_wave_kernel<8, FP8>), wgrid, wblk, 0, s, a);
+        hipLaunchKernelGGL((requant_wave_kernel<8, FP8, GL>), wgrid, wblk, 0, s, a);
     else if (wave && a.imax <= 16 * 256 && a.imax <= MOE_REQUANT_WAVE_MAX)
-        hipLaunchKernelGGL((requant_wave_kernel<16, FP8>), wgrid, wblk, 0, s, a);
+        hipLaunchKernelGGL((requant_wave_kernel<16, FP8, GL>), wgrid, wblk, 0, s, a);
     else
-        hipLaunchKernelGGL(requant_kernel<FP8>, dim3(a.rows_max), dim3(kTPR), 0, s, a);
+        hipLaunchKernelGGL((requant_kernel<FP8, GL>), dim3(a.rows_max), dim3(kTPR), 0, s, a);
     return hipGetLastError();
 }
 
@@ -131,8 +154,13 @@ hipError_t launch_requant_fmt(const RequantArgs &a, dim3 wgrid, dim3 wblk, hipSt
 hipError_t launch_requant(const RequantArgs &a, hipStream_t s) {
     if (a.rows_max <= 0) return hipSuccess;
     const dim3 wgrid((a.rows_max + kRowsPerBlock - 1) / kRowsPerBlock), wblk(kRowsPerBlock * kWave);
-    if (a.fp8) return launch_requant_fmt<true>(a, wgrid, wblk, s);
-    return launch_requant_fmt<false>(a, wgrid, wblk, s);
+    if (a.fp8) return launch_requant_fmt<true, 0>(a, wgrid, wblk, s);
+    switch (a.gl) {
+        case 16: return launch_requant_fmt<false, 16>(a, wgrid, wblk, s);
+        case 32: return launch_requant_fmt<false, 32>(a, wgrid, wblk, s);
+        case 64: return launch_requant_fmt<false, 64>(a, wgrid, wblk, s);
+        default: return launch_requant_fmt<false, 0>(a, wgrid, wblk, s);
+    }
 }
 
 hipError_t launch_dbg_gather(const GemmArgs &g1, const int32_t *row_group, const int32_t *meta, int has_shared,

@@ -250,7 +250,7 @@ constexpr int kTokQuantSlots = kRouteThreads / kTPR;  // rows quantised per bloc
 // some group reads plain per-token rows), then the (token, expert) pairs (when
 // expert smooth scales are given), then the tokens again (when the shared
 // expert has smooth scales).
-template <bool FP8>
+template <bool FP8, int GL>
 __device__ __forceinline__ void quant_unit(const TokQuantArgs &q, int u, int slot, int tr, float *s_part) {
     const int n_tok = q.q_tok ? q.T : 0;
     const int n_pair = q.smooth ? q.T * q.K : 0;
@@ -263,7 +263,7 @@ __device__ __forceinline__ void quant_unit(const TokQuantArgs &q, int u, int slo
         active = !q.mask || q.mask[u];
         src += static_cast<size_t>(u) * q.H;
         dst = q.q_tok + static_cast<size_t>(u) * q.H;
-        scale = q.s_tok + u;
+        scale = q.s_tok + static_cast<size_t>(u) * q.ng;
     } else if (u < n_tok + n_pair) {
         const int p = u - n_tok, t = p / q.K;
         const int g = q.ids[p];
@@ -273,7 +273,7 @@ __device__ __forceinline__ void quant_unit(const TokQuantArgs &q, int u, int slo
         src += static_cast<size_t>(t) * q.H;
         sm = q.smooth + static_cast<size_t>(active ? e : 0) * q.H;
         dst = q.q_sm + static_cast<size_t>(p) * q.H;
-        scale = q.s_sm + p;
+        scale = q.s_sm + static_cast<size_t>(p) * q.ng;
     } else {
         const int t = u - n_tok - n_pair;
         active = t < q.T && (!q.mask || q.mask[t]);
@@ -281,9 +281,9 @@ __device__ __forceinline__ void quant_unit(const TokQuantArgs &q, int u, int slo
         sm = q.share_smooth;
         const size_t row = static_cast<size_t>(q.T) * q.K + (active ? t : 0);
         dst = q.q_sm + row * q.H;
-        scale = q.s_sm + row;
+        scale = q.s_sm + row * q.ng;
     }
-    quant_bf16_row<FP8>(src, sm, q.H, q.eps, dst, scale, active, slot, tr, s_part);
+    quant_bf16_row<FP8, GL>(src, sm, q.H, q.eps, dst, scale, active, slot, tr, s_part);
 }
 
 __device__ __forceinline__ int quant_units(const TokQuantArgs &q) {
@@ -293,8 +293,8 @@ __device__ __forceinline__ int quant_units(const TokQuantArgs &q) {
 // Block 0 routes; blocks 1.. quantise rows of x (FusedDeepMoE sec. 4.1
 // quantises in dispatch). Neither job needs the other's result, so one launch
 // runs both side by side. FP8: rows are quantised to E4M3 (FP4-weight
-// variant) instead of INT8.
-template <bool FP8>
+// variant) instead of INT8. GL > 0: group-wise scales, 8 * GL elements each.
+template <bool FP8, int GL>
 __global__ __launch_bounds__(kRouteThreads) void route_quant_kernel(RouteArgs a, TokQuantArgs q) {
     if (blockIdx.x == 0) {
         route_block(a);
@@ -305,9 +305,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_quant_kernel(RouteArgs a,
     const int u = (blockIdx.x - 1) * kTokQuantSlots + slot;
     // units past the end take part in the block's barrier only
     if (u < quant_units(q)) {
-        quant_unit<FP8>(q, u, slot, tr, s_part);
+        quant_unit<FP8, GL>(q, u, slot, tr, s_part);
     } else {
-        quant_bf16_row<FP8>(q.x, nullptr, q.H, q.eps, nullptr, nullptr, false, slot, tr, s_part);
+        quant_bf16_row<FP8, GL>(q.x, nullptr, q.H, q.eps, nullptr, nullptr, false, slot, tr, s_part);
     }
 }
 
@@ -316,10 +316,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_quant_kernel(RouteArgs a,
 hipError_t launch_route_quant(const RouteArgs &a, const TokQuantArgs &q, hipStream_t s) {
     const int units = (q.q_tok ? q.T : 0) + (q.smooth ? q.T * q.K : 0) + (q.share_smooth ? q.T : 0);
     const int qblocks = (units + kTokQuantSlots - 1) / kTokQuantSlots;
+    const dim3 grid(1 + qblocks), blk(kRouteThreads);
     if (q.fp8)
-        hipLaunchKernelGGL(route_quant_kernel<true>, dim3(1 + qblocks), dim3(kRouteThreads), 0, s, a, q);
+        hipLaunchKernelGGL((route_quant_kernel<true, 0>), grid, blk, 0, s, a, q);
+    else if (q.gl == 8)
+        hipLaunchKernelGGL((route_quant_kernel<false, 8>), grid, blk, 0, s, a, q);
+    else if (q.gl == 16)
+        hipLaunchKernelGGL((route_quant_kernel<false, 16>), grid, blk, 0, s, a, q);
+    else if (q.gl == 32)
+        hipLaunchKernelGGL((route_quant_kernel<false, 32>), grid, blk, 0, s, a, q);
     else
-        hipLaunchKernelGGL(route_quant_kernel<false>, dim3(1 + qblocks), dim3(kRouteThreads), 0, s, a, q);
+        hipLaunchKernelGGL((route_quant_kernel<false, 0>), grid, blk, 0, s, a, q);
     return hipGetLastError();
 }
 

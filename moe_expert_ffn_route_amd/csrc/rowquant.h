@@ -30,6 +30,15 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Max over aligned segments of GL consecutive lanes (GL a power of two <= 64):
+// the group amax when a group's values sit in GL neighbouring lanes.
+template <int GL>
+__device__ __forceinline__ float segment_max(float v) {
+#pragma unroll
+    for (int d = GL / 2; d > 0; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
+    return v;
+}
+
 // amax over the kTPR threads of row slot `slot` (tr = thread index in the row).
 // s_part holds kTPR / kWave floats per slot. Contains one __syncthreads().
 __device__ __forceinline__ float row_amax(float m, int slot, int tr, float *s_part) {
@@ -81,8 +90,11 @@ __device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, f
 
 // Quantise a bf16 row of length n (multiple of 8), optionally times smooth
 // scales, into dst; lane tr of slot `slot`. `active` may be false for a
-// whole slot (its threads still take part in the barrier).
-template <bool FP8 = false>
+// whole slot (its threads still take part in the barrier). GL > 0: group-wise
+// scales ("DeepSeek V4 Decode Optimization" sec. 3.1), one per group of 8 * GL
+// elements (the chunks of GL neighbouring lanes), written to scale_out[group];
+// no barrier then.
+template <bool FP8 = false, int GL = 0>
 __device__ __forceinline__ void quant_bf16_row(const uint16_t *src, const float *smooth, int n, float eps,
                                                int8_t *dst, float *scale_out, bool active, int slot, int tr,
                                                float *s_part) {
@@ -111,6 +123,28 @@ __device__ __forceinline__ void quant_bf16_row(const uint16_t *src, const float 
             for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[j][e]));
         }
     }
+    if constexpr (GL > 0) {
+        if (!active) return;  // whole slots, i.e. whole waves
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            const int i = (tr + j * kTPR) * 8;
+            if (j * kTPR * 8 >= n) break;  // uniform
+            float mj = 0.0f;
+            if (i < n) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) mj = fmaxf(mj, fabsf(v[j][e]));
+            }
+            const float ap = fmaxf(segment_max<GL>(mj), eps);  // a group never straddles n
+            const float inv = 1.0f / ap;
+            if (i < n) {
+                const uint32_t lo = quant4<FP8>(v[j][0], v[j][1], v[j][2], v[j][3], inv);
+                const uint32_t hi = quant4<FP8>(v[j][4], v[j][5], v[j][6], v[j][7], inv);
+                *reinterpret_cast<uint2 *>(dst + i) = make_uint2(lo, hi);
+                if ((tr & (GL - 1)) == 0) scale_out[i / (8 * GL)] = ap * (1.0f / kQMax<FP8>);
+            }
+        }
+        return;
+    }
     const float ap = fmaxf(row_amax(m, slot, tr, s_part), eps);
     if (!active) return;
     const float inv = 1.0f / ap;
@@ -126,8 +160,9 @@ __device__ __forceinline__ void quant_bf16_row(const uint16_t *src, const float 
     if (tr == 0) *scale_out = ap * (1.0f / kQMax<FP8>);
 }
 
-// Quantise an fp32 row of length n (multiple of 4) into dst.
-template <bool FP8 = false>
+// Quantise an fp32 row of length n (multiple of 4) into dst. GL > 0: one
+// scale per group of 4 * GL elements, as in quant_bf16_row.
+template <bool FP8 = false, int GL = 0>
 __device__ __forceinline__ void quant_f32_row(const float *src, int n, float eps, int8_t *dst, float *scale_out,
                                               bool active, int slot, int tr, float *s_part) {
     float4 v[kF32Chunks];
@@ -139,6 +174,23 @@ __device__ __forceinline__ void quant_f32_row(const float *src, int n, float eps
             v[j] = *reinterpret_cast<const float4 *>(src + i);
             m = fmaxf(m, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
         }
+    }
+    if constexpr (GL > 0) {
+        if (!active) return;
+#pragma unroll
+        for (int j = 0; j < kF32Chunks; ++j) {
+            const int i = (tr + j * kTPR) * 4;
+            if (j * kTPR * 4 >= n) break;  // uniform
+            const float mj = i < n ? fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w)))
+                                   : 0.0f;
+            const float ap = fmaxf(segment_max<GL>(mj), eps);
+            const float inv = 1.0f / ap;
+            if (i < n) {
+                *reinterpret_cast<uint32_t *>(dst + i) = quant4<FP8>(v[j].x, v[j].y, v[j].z, v[j].w, inv);
+                if ((tr & (GL - 1)) == 0) scale_out[i / (4 * GL)] = ap * (1.0f / kQMax<FP8>);
+            }
+        }
+        return;
     }
     const float ap = fmaxf(row_amax(m, slot, tr, s_part), eps);
     if (!active) return;

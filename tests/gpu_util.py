@@ -241,3 +241,77 @@ def check_mx(case, tokens=None, tensors=None, **kw):
     gpu = run_gpu(case, tensors=tensors, **kw)
     ref = oracle.forward(case, tokens=tokens, trace=True)
     return compare_mx(case, gpu, ref, tokens), gpu, ref
+
+
+# -------------------------------------------------- group-wise activation scales
+#
+# quant_mode 2: the GPU dequantises each group's int32 partial exactly as the
+# oracle does (p_g = (float(acc_g) * w_scale) * group_scale) but adds the p_g
+# per wave, then over the waves, where the oracle adds them left to right; so
+# the fp32 GEMM outputs are held to the bound of that reassociation,
+# |gpu - oracle| <= 2 * n_groups * 2^-24 * sum_g |p_g|, with the p_g taken
+# from numpy int64 products of the GPU's own codes. Every other stage is
+# checked bit-exactly on the GPU's own inputs, as for FP4 weights.
+
+
+def _group_terms(q, scales, W, ws, G):
+    """float64 p_g [N, n_groups] of one row: int64 partial x weight scale x group scale."""
+    n = len(scales)
+    parts = np.stack([W[:, g * G:(g + 1) * G].astype(np.int64) @ q[g * G:(g + 1) * G].astype(np.int64)
+                      for g in range(n)], axis=1).astype(np.float64)
+    return parts * ws[:, None].astype(np.float64) * scales[None, :].astype(np.float64)
+
+
+def _group_gemm_check(got, q, scales, W, ws, G, what):
+    exact = oracle.gemm_i8_groups(q, scales, W, ws, G).astype(np.float64)
+    terms = _group_terms(q, scales, W, ws, G)
+    bound = 2 * terms.shape[1] * 2.0 ** -24 * np.abs(terms).sum(axis=1) + 1e-30
+    err = np.abs(got.astype(np.float64) - exact)
+    assert np.all(err <= bound), f"{what}: worst err / bound {np.max(err / bound):.3g}"
+    return float(np.max(err / bound))
+
+
+def compare_group(case, gpu, ref, tokens=None):
+    """compare() for group-wise activation scales (quant_group > 0)."""
+    s = case.spec
+    K, H, P, G = s.K, s.H, ref["P"], s.quant_group
+    rows, toks = _routing_rows(case, gpu, ref, tokens)
+    acc1 = gpu["acc1"].view(np.float32)
+    acc2 = gpu["acc2"].view(np.float32)
+    base = s.ep_rank * s.E_loc
+    worst, flips = 0.0, []
+    for r in rows:
+        if r < P:
+            p = int(gpu["sorted_pair"][r])
+            e = int(case.expert_ids[p // K, p % K]) - base
+            n, w1, w1s, w2, w2s = s.I, case.w1[e], case.w1s[e], case.w2[e], case.w2s[e]
+        else:
+            n, w1, w1s, w2, w2s = s.I_s, case.sw1, case.sw1s, case.sw2, case.sw2s
+        assert np.array_equal(gpu["q_x"][r], ref["q_x"][r]), f"q_x row {r}"
+        assert np.array_equal(gpu["xs"][r], ref["xs"][r]), f"xs row {r}"
+        y1 = acc1[r, :2 * n]
+        worst = max(worst, _group_gemm_check(y1, gpu["q_x"][r], gpu["xs"][r], w1, w1s, G, f"acc1 row {r}"))
+        h_exp = oracle.swiglu(y1.astype(np.float32))
+        hg = gpu["h"][r, :n]
+        assert np.all(np.abs(hg - h_exp) <= 1e-5 * np.abs(h_exp) + 1e-30), f"h row {r}"
+        q_exp, hs_exp = oracle.quant_row_groups(hg, G, s.eps)
+        assert np.array_equal(gpu["q_h"][r, :n], q_exp), f"q_h row {r}"
+        assert np.array_equal(gpu["hs"][r, :n // G], hs_exp), f"hs row {r}"
+        d = np.abs(gpu["q_h"][r, :n].astype(int) - ref["q_h"][r, :n].astype(int))
+        assert d.max(initial=0) <= 1, f"q_h row {r} more than 1 from the oracle's"
+        flips.append(float((d > 0).mean()))
+        y2 = acc2[r, :H]
+        worst = max(worst, _group_gemm_check(y2, gpu["q_h"][r, :n], gpu["hs"][r, :n // G], w2, w2s, G,
+                                             f"acc2 row {r}"))
+        assert np.array_equal(gpu["z"][r], synth.f32_to_bf16_bits(y2)), f"z row {r}"
+    stats = dict(rows=len(rows), acc_err_over_bound=worst, qh_diff_frac=max(flips, default=0.0))
+    stats["output"] = out_close(gpu["output"][toks], ref["output"][toks], "output")
+    if s.I_s:
+        stats["share_output"] = out_close(gpu["share_output"][toks], ref["share_output"][toks], "share_output")
+    return stats
+
+
+def check_group(case, tokens=None, tensors=None, **kw):
+    gpu = run_gpu(case, tensors=tensors, **kw)
+    ref = oracle.forward(case, tokens=tokens, trace=True)
+    return compare_group(case, gpu, ref, tokens), gpu, ref

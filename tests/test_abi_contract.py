@@ -98,6 +98,16 @@ def test_workspace_size(lib):
     (dict(fuse_route_scale=-1), binding.MOE_ERR_INVALID_ARG),
     (dict(weight_format=2), binding.MOE_ERR_INVALID_ARG),
     (dict(weight_format=1), binding.MOE_ERR_UNSUPPORTED),           # FP4 weights must be packed
+    # group-wise activation scales: 64, 128 or 256 (H, I and I_s are
+    # multiples of 256, so every allowed size divides them); INT8 weights and
+    # the per-row route scale only
+    (dict(quant_mode=2, quant_group=32), binding.MOE_ERR_UNSUPPORTED),
+    (dict(quant_mode=2, quant_group=512), binding.MOE_ERR_UNSUPPORTED),
+    (dict(quant_mode=2, quant_group=0), binding.MOE_ERR_UNSUPPORTED),
+    (dict(quant_mode=2, quant_group=192), binding.MOE_ERR_UNSUPPORTED),
+    (dict(quant_mode=2, quant_group=128, fuse_route_scale=1), binding.MOE_ERR_UNSUPPORTED),
+    (dict(quant_mode=2, quant_group=128, weight_format=1, weight_layout=1), binding.MOE_ERR_UNSUPPORTED),
+    (dict(quant_mode=3), binding.MOE_ERR_UNSUPPORTED),
 ])
 def test_bad_dims_rejected(lib, kw, code):
     n = ctypes.c_size_t(0)
@@ -158,6 +168,14 @@ def test_forward_rejects_bad_dims_and_shared_mismatch(lib):
     (FAKE, 2 * FAKE, 1, 32, 64, 3)])
 def test_pack_rejects_bad_arguments(lib, src, dst, g, n, k, which):
     assert lib.moe_w8a8_pack_weights(src, dst, g, n, k, which, None) == binding.MOE_ERR_INVALID_ARG
+
+
+def test_group_mode_workspace(lib):
+    # the per-row scales become H / G and max(I, I_s) / G per row
+    d1 = good_dims(share_inter=512)
+    d2 = good_dims(share_inter=512, quant_mode=2, quant_group=64)
+    assert moe.moe_w8a8_workspace_size(d2) > moe.moe_w8a8_workspace_size(d1)
+    assert moe.moe_w8a8_workspace_size(good_dims(quant_mode=2, quant_group=256)) > 0
 
 
 def test_mx_workspace_and_packed_size(lib):

@@ -1,0 +1,93 @@
+"""GPU parity of group-wise activation scales (quant_mode 2, "DeepSeek V4
+Decode Optimization" sec. 3.1) against the CPU oracle's quant_group mode,
+stage by stage (gpu_util.compare_group: codes, group scales and epilogues
+bit-exact on the GPU's own inputs; the fp32 GEMM outputs within the bound of
+adding the same dequantised group partials in another order).
+
+The cases cover the three group sizes (64, 128, 256), every K split the
+group path takes (8, 4, 2 and 1 waves; a batch of whole groups, or one group
+per batch over several passes), 16-row items with several chunks per expert,
+masks, smooth scales, an EP share, a shared expert with a different
+intermediate (two GEMM2 launches), T = 0 / 1, and the decode workload's full
+shape on a sample of tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+from moe_expert_ffn_route_amd import synth
+from gpu_util import check_group, say
+
+pytestmark = pytest.mark.gpu
+
+
+def spec(**kw):
+    base = dict(name="grp", T=8, H=512, I=256, E_g=8, K=2, seed=501, quant_group=128)
+    base.update(kw)
+    return synth.Spec(**base)
+
+
+CASES = {
+    # the tiny workload's shape: H 512 = 4 groups of 128 (4 waves x 1 group),
+    # I 256 = 2 groups (2 waves)
+    "tiny_g128": (spec(), None),
+    # G 64: H 512 = 8 groups (8 waves x 1 step), I 256 = 4 groups (4 waves)
+    "tiny_g64_shared": (spec(quant_group=64, I_s=512, seed=502), None),
+    # G 256: I 256 is one group (one wave), H 1024 four (4 waves x 4 steps)
+    "g256_one_group": (spec(H=1024, quant_group=256, I_s=256, seed=503), None),
+    # H 768 = 6 groups of 128 (2 waves x 3 passes of 1 group), I 512, I_s 256
+    "mask_smooth_split_gemm2": (spec(T=12, H=768, I=512, I_s=256, E_g=16, K=4, active=10, smooth=True,
+                                     share_smooth=True, seed=504), None),
+    "ep_share": (spec(T=16, H=1024, I=512, E_g=32, K=6, ep_size=4, ep_rank=1, active=13, smooth=True, seed=505),
+                 None),
+    # 40 tokens on 2 experts: 16-row items, three chunks per expert, 16 N tiles
+    "t40_multichunk": (spec(T=40, H=512, I=256, E_g=2, K=2, I_s=256, seed=506), None),
+    # G 64 and H 9216: 144 groups, 8 waves x 18 passes of one group
+    "long_k_g64": (spec(T=3, H=9216, I=256, E_g=4, K=2, I_s=256, quant_group=64, seed=507), None),
+    "t1": (spec(T=1, I_s=512, seed=508), None),
+    "t0": (spec(T=0, I_s=256, seed=509), None),
+    # the decode workload's shape with 128-element groups (two tokens checked)
+    "decode_full_shape": (spec(T=8, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1235), [1, 6]),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_group_parity(name):
+    sp, tokens = CASES[name]
+    say(f"[grp] {name}: {sp}")
+    c = synth.make_case(sp)
+    stats, _, _ = check_group(c, tokens=tokens, packed=True)
+    say(f"[grp] {name}: {stats}")
+    if name == "tiny_g128":  # row-major weights too
+        stats, _, _ = check_group(c, tokens=tokens, packed=False)
+        say(f"[grp] {name} row-major: {stats}")
+    torch.cuda.empty_cache()
+
+
+def _random_specs(n, seed=6060):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.choice([64, 128, 256]))
+        E_g = int(rng.choice([2, 4, 8, 16]))
+        T = int(rng.choice([1, 5, 8, 16, 17, 30]))
+        kw = dict(name=f"grprandom{i}", T=T, H=int(rng.choice([1, 2, 3, 4])) * 256 * (2 if G == 256 else 1),
+                  I=int(rng.choice([256, 512])), E_g=E_g, K=int(rng.integers(1, min(E_g, 6) + 1)),
+                  I_s=int(rng.choice([0, 256, 512])), routing=str(rng.choice(["uniform", "zipf"])),
+                  quant_group=G, seed=600 + i)
+        if rng.random() < 0.4:
+            kw["active"] = int(rng.integers(0, T + 1))
+        if rng.random() < 0.4:
+            kw["smooth"] = True
+        out.append(spec(**kw))
+    return out
+
+
+RANDOM = _random_specs(8)
+
+
+@pytest.mark.parametrize("i", range(len(RANDOM)))
+def test_group_random_shapes(i):
+    say(f"[grp] random {i}: {RANDOM[i]}")
+    stats, _, _ = check_group(synth.make_case(RANDOM[i]), packed=bool(i % 2))
+    say(f"[grp] random {i}: {stats}")
