@@ -18,7 +18,9 @@ oracle's time on this host as a baseline.
 
 `--weight-format mxfp4` times the FP4-weight / FP8-activation variant of the
 same workload instead (E2M1 weights with E8M0 block scales, 0.53 bytes per
-weight element); the default line is the INT8 block.
+weight element), `--quant-group G` the variant with one activation scale per
+row and group of G elements; the default line is the INT8 block with one
+scale per row.
 """
 from __future__ import annotations
 
@@ -125,9 +127,11 @@ def algorithmic_bytes(case, counts):
     routed_rows = int(counts.sum())
     t_act = T if case.mask is None else int(np.count_nonzero(case.mask))
     rows = routed_rows + (t_act if Is else 0)
-    gemm1 += rows * (H + 4 + 4 * max(I, Is))  # q_x and xs read, h written
+    G = getattr(s, "quant_group", 0)
+    ngx, ngh = (H // G, max(I, Is) // G) if G else (1, 1)  # activation scales per row
+    gemm1 += rows * (H + 4 * ngx + 4 * max(I, Is))  # q_x and its scales read, h written
     gemm2 = touched * (int(H * I * wb) + 4 * H) + ((int(H * Is * wb) + 4 * H) if Is else 0)
-    gemm2 += routed_rows * (I + 4 + 2 * H) + ((t_act * (Is + 4 + 2 * H)) if Is else 0)  # q_h, hs in; z out
+    gemm2 += routed_rows * (I + 4 * ngh + 2 * H) + ((t_act * (Is + 4 * ngh + 2 * H)) if Is else 0)  # q_h, hs in; z out
     return touched * per_expert + shared + act, gemm1, gemm2, touched, rows
 
 
@@ -233,6 +237,8 @@ def main():
                     help="fold the routing weight into the GEMM2 row scale (combine only sums)")
     ap.add_argument("--weight-format", choices=["int8", "mxfp4"], default="int8",
                     help="mxfp4: FP4 weights with E8M0 block scales and FP8 activations (always packed)")
+    ap.add_argument("--quant-group", type=int, default=0, choices=[0, 64, 128, 256],
+                    help="group-wise activation scales (quant_mode 2) with groups of this many elements")
     ap.add_argument("--fenced-events", action="store_true",
                     help="time with default HIP events (each record adds a system-scope cache writeback) "
                          "instead of events created with hipEventDisableSystemFence")
@@ -267,9 +273,14 @@ def main():
             print("--weight-format mxfp4 needs packed weights", file=sys.stderr)
             sys.exit(2)
         spec = dataclasses.replace(spec, name=spec.name + "_mxfp4", weight_format="mxfp4")
+    if args.quant_group:
+        if mx:
+            print("--quant-group applies to INT8 weights", file=sys.stderr)
+            sys.exit(2)
+        spec = dataclasses.replace(spec, name=f"{spec.name}_g{args.quant_group}", quant_group=args.quant_group)
     log(f"[bench] workload {spec.name}: generating inputs")
     t0 = time.perf_counter()
-    case = synth.make_case(spec)
+    case = synth.make_case(spec) if (mx or args.quant_group) else synth.workload_case(args.config)
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s; uploading")
     dev = moe.upload(case)  # FP4 weights are packed by upload (moe_w8a8_pack_weights_mx)
     if not args.row_major and not mx:
@@ -415,6 +426,7 @@ def main():
                    "touched_experts": touched, "grouped_rows": rows, "weight_copies": len(layers),
                    "weight_layout": "row_major" if args.row_major else "packed",
                    "weight_format": args.weight_format,
+                   "activation_scales": f"per row and {args.quant_group} elements" if args.quant_group else "per row",
                    "route_scale": "fused_gemm2" if args.fuse_route_scale else "combine",
                    "launch": "hip_graph" if graphs else "stream"},
         "hbm_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),

@@ -232,10 +232,26 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
         float gsc[kGroups][4];
         if constexpr (GS > 0) {
             const int g0 = (step0 + pass * KSTEPS) / GS;
+            if (kGroups % 4 == 0 && (a.a_ng & 3) == 0) {  // uniform
+                // a row's scales of consecutive groups are contiguous and,
+                // with g0 a multiple of kGroups and a_ng of 4, 16-byte aligned
 #pragma unroll
-            for (int q = 0; q < kGroups; ++q)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) gsc[q][i] = Ascale[static_cast<size_t>(srow[i]) * a.a_ng + g0 + q];
+                    for (int q = 0; q + 3 < kGroups; q += 4) {
+                        const float4 v4 = *reinterpret_cast<const float4 *>(
+                            Ascale + static_cast<size_t>(srow[i]) * a.a_ng + g0 + q);
+                        gsc[q][i] = v4.x;
+                        gsc[q + 1][i] = v4.y;
+                        gsc[q + 2][i] = v4.z;
+                        gsc[q + 3][i] = v4.w;
+                    }
+            } else {
+#pragma unroll
+                for (int q = 0; q < kGroups; ++q)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) gsc[q][i] = Ascale[static_cast<size_t>(srow[i]) * a.a_ng + g0 + q];
+            }
         }
         if (has_next) ldw(nxt, pass + 1);
         __builtin_amdgcn_sched_barrier(0);

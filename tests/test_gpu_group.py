@@ -44,6 +44,11 @@ CASES = {
     "t40_multichunk": (spec(T=40, H=512, I=256, E_g=2, K=2, I_s=256, seed=506), None),
     # G 64 and H 9216: 144 groups, 8 waves x 18 passes of one group
     "long_k_g64": (spec(T=3, H=9216, I=256, E_g=4, K=2, I_s=256, quant_group=64, seed=507), None),
+    # I 4096 with I_s 4352 and G 128: a routed GEMM2 batch holds 4 groups
+    # (8 waves x 8 steps) but the h scale rows are 34 groups apart, so the
+    # scales are loaded one by one; the shared GEMM2 (34 groups) runs on 2
+    # waves x 17 passes of one group
+    "scale_stride_34": (spec(T=5, H=256, I=4096, I_s=4352, E_g=2, K=1, seed=510), None),
     "t1": (spec(T=1, I_s=512, seed=508), None),
     "t0": (spec(T=0, I_s=256, seed=509), None),
     # the decode workload's shape with 128-element groups (two tokens checked)
