@@ -255,30 +255,49 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
         }
         if (has_next) ldw(nxt, pass + 1);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (GS > 0) {
+            // Each group's first MFMA starts from zero; a finished group's
+            // partials are dequantised only after the next group's first
+            // MFMAs are issued, so the VALU work never waits right behind the
+            // MFMA that produced its operands (the batch's last group waits
+            // once, at the end).
+            const bool av = r16 < rows;
+            const v4i zero = {0, 0, 0, 0};
+            v4i pend0 = zero, pend1 = zero;
+            auto flush = [&](const v4i &s0, const v4i &s1, int q) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            if (MT == 1 || mt * kTileN < rows) {
-                const bool av = mt * kTileN + r16 < rows;
+                for (int e = 0; e < 4; ++e) {
+                    float p0 = static_cast<float>(s0[e]) * wl0;
+                    p0 = p0 * gsc[q][e];
+                    f0[e] = f0[e] + p0;
+                    float p1 = static_cast<float>(s1[e]) * wl1;
+                    p1 = p1 * gsc[q][e];
+                    f1[e] = f1[e] + p1;
+                }
+            };
 #pragma unroll
-                for (int i = 0; i < KSTEPS; ++i) {
-                    const v4i xi = av ? x[mt][i] : v4i{0, 0, 0, 0};
-                    acc0[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xi, w[0][i], acc0[mt], 0, 0, 0);
-                    acc1[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xi, w[1][i], acc1[mt], 0, 0, 0);
-                    if constexpr (GS > 0) {
-                        if ((i + 1) % GS == 0) {  // end of a group: dequantise its partials
-                            const int q = i / GS;
+            for (int i = 0; i < KSTEPS; ++i) {
+                const v4i xi = av ? x[0][i] : zero;
+                const bool first = i % GS == 0;
+                acc0[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xi, w[0][i], first ? zero : acc0[0], 0, 0, 0);
+                acc1[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xi, w[1][i], first ? zero : acc1[0], 0, 0, 0);
+                if (first && i > 0) flush(pend0, pend1, i / GS - 1);
+                if ((i + 1) % GS == 0) {
+                    pend0 = acc0[0];
+                    pend1 = acc1[0];
+                }
+            }
+            flush(pend0, pend1, kGroups - 1);
+        } else {
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                float p0 = static_cast<float>(acc0[0][e]) * wl0;
-                                p0 = p0 * gsc[q][e];
-                                f0[e] = f0[e] + p0;
-                                float p1 = static_cast<float>(acc1[0][e]) * wl1;
-                                p1 = p1 * gsc[q][e];
-                                f1[e] = f1[e] + p1;
-                            }
-                            acc0[0] = v4i{0, 0, 0, 0};
-                            acc1[0] = v4i{0, 0, 0, 0};
-                        }
+            for (int mt = 0; mt < MT; ++mt) {
+                if (MT == 1 || mt * kTileN < rows) {
+                    const bool av = mt * kTileN + r16 < rows;
+#pragma unroll
+                    for (int i = 0; i < KSTEPS; ++i) {
+                        const v4i xi = av ? x[mt][i] : v4i{0, 0, 0, 0};
+                        acc0[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xi, w[0][i], acc0[mt], 0, 0, 0);
+                        acc1[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xi, w[1][i], acc1[mt], 0, 0, 0);
                     }
                 }
             }
@@ -460,8 +479,8 @@ hipError_t launch_grp_w(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, 
             if constexpr (GS <= 2) launch_one<KIND, W, 4 * GS, PACKED, 1, 1, GS>(a, grid, k_dim, 1, s, e0, e1);
             else launch_one<KIND, W, GS, PACKED, 1, 0, GS>(a, grid, k_dim, 4, s, e0, e1);
             break;
-        case 8 * GS:
-            if constexpr (GS == 1) launch_one<KIND, W, 8, PACKED, 1, 1, GS>(a, grid, k_dim, 1, s, e0, e1);
+        case 8 * GS:  // 64-element groups: two batches of 4, which keeps 4 waves per SIMD
+            if constexpr (GS == 1) launch_one<KIND, W, 4, PACKED, 1, 2, GS>(a, grid, k_dim, 2, s, e0, e1);
             else launch_one<KIND, W, GS, PACKED, 1, 0, GS>(a, grid, k_dim, 8, s, e0, e1);
             break;
         default: launch_one<KIND, W, GS, PACKED, 1, 0, GS>(a, grid, k_dim, spw / GS, s, e0, e1); break;
