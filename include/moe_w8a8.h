@@ -11,6 +11,9 @@
  *   5. grouped INT8 GEMM2 (down) and dequantisation to bf16;
  *   6. routing-weighted top-k combine into `output`, and the optional shared
  *      expert on every active token into `share_output`.
+ * Options of the same call (moe_w8a8_dims_t): the routing weight folded into
+ * GEMM2's row scale (fuse_route_scale), group-wise activation scales
+ * (quant_mode 2), and FP4 weights with FP8 activations (weight_format).
  *
  * Passages that define the operation (pages, by title):
  *   "FusedDeepMoE Kernel 深度分析报告": sec. 1.2 (inputs, outputs, attributes),

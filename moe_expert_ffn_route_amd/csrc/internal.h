@@ -11,9 +11,11 @@ constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kMaxLocalExperts = 512;
 constexpr int kRouteThreads = 1024;  // the routing kernel runs as one workgroup
 constexpr int kRouteWaves = kRouteThreads / kWave;
-// Grouped rows per GEMM work item: one 16-row MFMA tile when T <= 16
-// (decode; gemm.hip), MOE_WIDE_MT tiles otherwise (gemm_wide.hip, which
-// shares each chunk's activations across the waves of a workgroup).
+// Grouped rows per GEMM work item (INT8 weights, one scale per row): one
+// 16-row MFMA tile when T <= 16 (decode; gemm.hip), MOE_WIDE_MT tiles
+// otherwise (gemm_wide.hip, which shares each chunk's activations across the
+// waves of a workgroup), or tall items (below). Group-wise scales run 16-row
+// items at every T; FP4 weights 16- or 32-row items (gemm_mx.hip).
 #ifndef MOE_WIDE_MT
 #define MOE_WIDE_MT 2
 #endif

@@ -78,7 +78,7 @@ def test_small_case_parity(name, packed):
 
 
 # The production tile shapes (hidden 4096, intermediate 2048: one K batch per
-# wave in GEMM1) at small T: 16-row chunks (T <= 16) and 64-row chunks
+# wave in GEMM1) at small T: 16-row chunks (T <= 16) and 32-row chunks
 # (T > 16), including an expert with more than one chunk.
 H4096 = {
     "h4096_t6_shared": spec(T=6, H=4096, I=2048, E_g=8, K=2, I_s=2048, seed=121),
