@@ -35,12 +35,23 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kTWaves = 16;                         // a grid of kTWM (rows) x kTWN (weight tiles)
+// Tuning: waves per workgroup, waves along N, tile pairs per wave (the rest
+// follows; the chunk is always 256 rows by 8 tile pairs).
+#ifndef MOE_TBIG_WAVES
+#define MOE_TBIG_WAVES 16
+#endif
+#ifndef MOE_TBIG_WN
+#define MOE_TBIG_WN 4
+#endif
+#ifndef MOE_TBIG_Q
+#define MOE_TBIG_Q 2
+#endif
+constexpr int kTWaves = MOE_TBIG_WAVES;             // a grid of kTWM (rows) x kTWN (weight tiles)
 constexpr int kTThreads = kTWaves * kWave;
-constexpr int kTWN = 4;
+constexpr int kTWN = MOE_TBIG_WN;
 constexpr int kTWM = kTWaves / kTWN;
 constexpr int kTMT = kChunkRowsTall / kTileN / kTWM;  // 16-row tiles per wave
-constexpr int kTQ = 2;                              // tile pairs per wave
+constexpr int kTQ = MOE_TBIG_Q;                     // tile pairs per wave
 constexpr int kTPairs = kTWN * kTQ;                 // tile pairs per block
 constexpr int kTSteps = 1;                          // 64-byte K steps per stage
 constexpr int kTRowTiles = kChunkRowsTall / kTileN;
