@@ -58,11 +58,12 @@ constexpr int kTRowTiles = kChunkRowsTall / kTileN;
 constexpr int kTAStage = kTRowTiles * kTSteps * 1024;
 constexpr int kTWStage = 2 * kTPairs * kTSteps * 1024;
 constexpr int kTStage = kTAStage + kTWStage;
-constexpr int kTLoads = kTAStage / 1024 / kTWaves;  // 1 KB blocks per operand, wave and stage
+constexpr int kTLoadsA = kTAStage / 1024 / kTWaves;  // 1 KB activation blocks per wave and stage
+constexpr int kTLoadsW = kTWStage / 1024 / kTWaves;  // 1 KB weight blocks per wave and stage
 static_assert(kTRowTiles == kTWM * kTMT, "a chunk is kTWM waves' rows");
 static_assert(kTPairs == kTallPairs, "the host sizes the grid with kTallPairs");
-static_assert(kTAStage == kTLoads * kTWaves * 1024 && kTWStage == kTLoads * kTWaves * 1024,
-              "a stage is kTLoads blocks per operand and wave");
+static_assert(kTAStage == kTLoadsA * kTWaves * 1024 && kTWStage == kTLoadsW * kTWaves * 1024,
+              "a stage is whole 1 KB blocks per wave");
 
 __device__ __forceinline__ v4i ld16(const int8_t *p) { return *reinterpret_cast<const v4i *>(p); }
 __device__ __forceinline__ v4i ld16_stream(const int8_t *p) {
@@ -116,7 +117,8 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
     auto row_b = [&](int q) { return KIND == 1 ? inter + row_a(q) : row_a(q) + kTileN; };
 
     // Global -> LDS copy of a stage: thread t copies the 16 bytes of lane
-    // t % 64 of 1 KB block j = kTWaves i + wave (i < kTLoads) of each operand.
+    // t % 64 of 1 KB block j = kTWaves i + wave (i < kTLoadsA, kTLoadsW) of
+    // each operand.
     // Activation block j is row tile j / kTSteps, K step j % kTSteps: lane l
     // reads row 16 (j / kTSteps) + l % 16 (rows past the chunk repeat its last
     // row; their outputs are never stored). Weight block j is tile pair
@@ -124,17 +126,21 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
     // contiguous in the packed layout.
     const int wstep = PACKED ? 1024 : 64;  // bytes between K steps of a tile
     const int wlane = PACKED ? lane * 16 : r16 * k_dim + kg * 16;
-    const int8_t *wsrc[kTLoads];
-    const int8_t *asrc[kTLoads];
+    const int8_t *wsrc[kTLoadsW];
+    const int8_t *asrc[kTLoadsA];
     const int32_t *aidx = KIND == 1 ? (routed ? a.idx_r : a.row_token) : nullptr;
     const int8_t *Abase = KIND == 1 ? (routed ? a.A_r : a.A_s) : a.A;
     const float *Ascale = KIND == 1 ? (routed ? a.a_scale_r : a.a_scale_s) : a.a_scale;
 #pragma unroll
-    for (int i = 0; i < kTLoads; ++i) {
+    for (int i = 0; i < kTLoadsW; ++i) {
         const int j = i * kTWaves + wave;
         const int wrow = ((j / kTSteps) & 1) ? row_b(j / (2 * kTSteps)) : row_a(j / (2 * kTSteps));
         const size_t wt = KIND == 1 && PACKED ? g1_tile_pos(wrow / kTileN, inter / kTileN) : wrow / kTileN;
         wsrc[i] = W + wt * tile_bytes + (j % kTSteps) * wstep + wlane;
+    }
+#pragma unroll
+    for (int i = 0; i < kTLoadsA; ++i) {
+        const int j = i * kTWaves + wave;
         const int lr = min((j / kTSteps) * kTileN + r16, rows - 1);
         const int ar = KIND == 1 ? aidx[row0 + lr] : row0 + lr;
         asrc[i] = Abase + static_cast<size_t>(ar) * a.a_stride + (j % kTSteps) * 64 + kg * 16;
@@ -142,23 +148,24 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
     // a stage's share of this thread, held in registers between its global
     // loads and its LDS stores
     struct Stage {
-        v4i a[kTLoads], w[kTLoads];
+        v4i a[kTLoadsA], w[kTLoadsW];
     };
     auto gload = [&](Stage &r, int s) {
 #pragma unroll
-        for (int i = 0; i < kTLoads; ++i) {
+        for (int i = 0; i < kTLoadsW; ++i) {
             const int8_t *pw = wsrc[i] + static_cast<size_t>(s) * kTSteps * wstep;
             r.w[i] = PACKED ? ld16_stream(pw) : ld16(pw);
-            r.a[i] = ld16(asrc[i] + s * kTSteps * 64);
         }
+#pragma unroll
+        for (int i = 0; i < kTLoadsA; ++i) r.a[i] = ld16(asrc[i] + s * kTSteps * 64);
     };
     auto lstore = [&](const Stage &r, int8_t *base) {
 #pragma unroll
-        for (int i = 0; i < kTLoads; ++i) {
-            const int j = i * kTWaves + wave;
-            *reinterpret_cast<v4i *>(base + j * 1024 + lane * 16) = r.a[i];
-            *reinterpret_cast<v4i *>(base + kTAStage + j * 1024 + lane * 16) = r.w[i];
-        }
+        for (int i = 0; i < kTLoadsA; ++i)
+            *reinterpret_cast<v4i *>(base + (i * kTWaves + wave) * 1024 + lane * 16) = r.a[i];
+#pragma unroll
+        for (int i = 0; i < kTLoadsW; ++i)
+            *reinterpret_cast<v4i *>(base + kTAStage + (i * kTWaves + wave) * 1024 + lane * 16) = r.w[i];
     };
 
     v4i acc0[kTMT][kTQ], acc1[kTMT][kTQ];

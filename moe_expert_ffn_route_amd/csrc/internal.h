@@ -31,7 +31,10 @@ constexpr int kChunkRowsLarge = 16 * MOE_WIDE_MT;
 #endif
 constexpr int kTallTiles = 16;
 constexpr int kChunkRowsTall = 16 * kTallTiles;
-constexpr int kTallPairs = 8;
+#ifndef MOE_TBIG_PAIRS
+#define MOE_TBIG_PAIRS 8
+#endif
+constexpr int kTallPairs = MOE_TBIG_PAIRS;
 constexpr int kTallMinRows = MOE_TALL_MIN_ROWS;
 constexpr int kTileN = 16;           // MFMA 16x16x64 output tile edge
 // A chunk entry's third word holds its row count (<= 256) in the low bits and
