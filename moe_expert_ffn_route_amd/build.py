@@ -1,4 +1,5 @@
-"""Build libmoe_w8a8.so (gfx950) in-tree with hipcc.
+"""Build libmoe_w8a8.so (gfx950) in-tree with hipcc (one compile per source,
+in parallel, then a link).
 
     python -m moe_expert_ffn_route_amd.build
 
@@ -26,11 +27,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}", "-ff
          "-fvisibility=hidden", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into the shared library (always rebuilds)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -39,7 +36,29 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{errs}")
     if errs.strip() and verbose:
         print(errs, file=sys.stderr)
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every HIP source into the shared library (always rebuilds):
+    one hipcc per source, in parallel, then one link. Every kernel is launched
+    from the source that defines it, so no relocatable device code is needed."""
+    import shutil
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    obj_dir = tempfile.mkdtemp(prefix="moe_w8a8_build_")
+    try:
+        cflags = [f for f in FLAGS if f != "-shared"]
+        objs = [os.path.join(obj_dir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[HIPCC, *cflags, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+        jobs = jobs or max(1, min(len(cmds), os.cpu_count() or 1, 16))
+        with ThreadPoolExecutor(jobs) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        tmp = LIB + f".tmp{os.getpid()}"
+        _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(obj_dir, ignore_errors=True)
     return LIB
 
 
