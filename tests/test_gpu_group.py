@@ -16,6 +16,7 @@ import pytest
 import torch
 
 from moe_expert_ffn_route_amd import synth
+import moe_expert_ffn_route_amd as moe
 from gpu_util import check_group, say
 
 pytestmark = pytest.mark.gpu
@@ -96,3 +97,30 @@ def test_group_random_shapes(i):
     say(f"[grp] random {i}: {RANDOM[i]}")
     stats, _, _ = check_group(synth.make_case(RANDOM[i]), packed=bool(i % 2))
     say(f"[grp] random {i}: {stats}")
+
+
+def test_group_hip_graph_capture_and_replay():
+    # group-wise scales launch kernels only: a captured forward replays to the
+    # eager result, with other eager work between the replays
+    c = synth.make_case(spec(T=20, H=768, I=512, E_g=4, K=2, I_s=256, active=18, smooth=True, seed=520))
+    t = moe.upload(c)
+    runner = moe.Runner(moe.dims_of_case(c))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        runner(t, stream=s)
+    torch.cuda.synchronize()
+    eager = (runner.output.clone(), runner.share_output.clone(), runner.expert_token_nums.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        runner(t, stream=s)
+    for i in range(4):
+        runner.output.fill_(3)
+        runner.share_output.fill_(3)
+        runner.expert_token_nums.fill_(-1)
+        runner.workspace.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(runner.output, eager[0]), i
+        assert torch.equal(runner.share_output, eager[1]), i
+        assert torch.equal(runner.expert_token_nums, eager[2]), i
