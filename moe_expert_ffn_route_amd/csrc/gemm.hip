@@ -30,7 +30,10 @@
 //   - the partial int32 tiles of the waves are summed in LDS (exact);
 //   - blockIdx maps linearly to (chunk, N tile), so the round-robin placement
 //     of blocks on the 8 XCDs gives each XCD an equal share of every expert;
-//   - the epilogue's scales are fetched before the weight stream starts.
+//   - the epilogue's scales are fetched before the weight stream starts;
+//   - with group-wise activation scales (GS > 0, "DeepSeek V4 Decode
+//     Optimization" sec. 3.1) each group's int32 partials are dequantised in
+//     the K loop and the epilogue sums fp32 values instead.
 // MFMA operand layout: lane l holds 16 bytes of row (l % 16) at byte offset
 // 16 * (l / 16) of a 64-byte K step, for A (token rows) and B (weight rows)
 // alike, so every product pairs equal K indices. Result lane l, register i
@@ -201,10 +204,11 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
     ldw(wbuf[0], 0);
     __builtin_amdgcn_sched_barrier(0);
 
-    // (3) loads that depend on (1): the first row tile's row scales
+    // (3) loads that depend on (1): the first row tile's row scales (none
+    //     with group-wise scales, which the K loop applies)
     float rsc[kEpt];
 #pragma unroll
-    for (int e = 0; e < kEpt; ++e) rsc[e] = Ascale[KIND == 1 ? rtok[e] : rrow[e]];
+    for (int e = 0; e < kEpt; ++e) rsc[e] = GS > 0 ? 0.0f : Ascale[KIND == 1 ? rtok[e] : rrow[e]];
     __builtin_amdgcn_sched_barrier(0);
 
     v4i acc0[MT], acc1[MT];
