@@ -62,19 +62,19 @@ Layout make_layout(const moe_w8a8_dims_t *d) {
     const size_t nonempty = E < TK ? E : TK;
     // rows per GEMM work item: 16 for decode batches; 256 (tall items) when
     // the routed experts average kTallMinRows rows or more; 32 otherwise.
-    // Group-wise scales: 16 at every batch size (gemm.hip).
-    // FP4 weights (gemm_mx.hip): 32 when the local experts can average 16 rows
-    // or more (T*K / ep_rank_size >= 16 * E_loc), else 16 (measured on MI355X:
-    // 32-row items take the T = 512 layer from 996 to 859 us but slow the
-    // skewed T = 64 layer from 305 to 328 us).
+    // FP4 weights (gemm_mx.hip) and group-wise scales (gemm.hip): 32 when the
+    // local experts can average 16 rows or more (T*K / ep_rank_size >=
+    // 16 * E_loc), else 16 (measured on MI355X with FP4 weights: 32-row items
+    // take the T = 512 layer from 996 to 859 us but slow the skewed T = 64
+    // layer from 305 to 328 us).
     const bool tall = T >= kTallMinRows && TK >= static_cast<size_t>(kTallMinRows) * E;
     const bool mx = d->weight_format == MOE_WEIGHT_MXFP4;
-    const bool mx_wide = T > kChunkRowsSmall && TK / d->ep_rank_size >= static_cast<size_t>(kTileN) * E;
     const bool grp = d->quant_mode == 2;
-    L.chunk_rows = T <= kChunkRowsSmall || grp ? kChunkRowsSmall
-                   : mx                        ? (mx_wide ? 2 * kTileN : kChunkRowsSmall)
-                   : tall                      ? kChunkRowsTall
-                                               : kChunkRowsLarge;
+    const bool two_tiles = T > kChunkRowsSmall && TK / d->ep_rank_size >= static_cast<size_t>(kTileN) * E;
+    L.chunk_rows = T <= kChunkRowsSmall ? kChunkRowsSmall
+                   : mx || grp          ? (two_tiles ? 2 * kTileN : kChunkRowsSmall)
+                   : tall               ? kChunkRowsTall
+                                        : kChunkRowsLarge;
     const size_t cr = L.chunk_rows;
     L.max_chunks = static_cast<int>(nonempty + TK / cr + (shared ? (T + cr - 1) / cr : 0));
     const size_t R = L.rows_max;
@@ -293,9 +293,9 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g1.packed = d->weight_layout == MOE_WEIGHT_PACKED;
         g1.mt = L.chunk_rows / kTileN;
         // three INT8 kernels by chunk size: decode (gemm.hip), wide
-        // (gemm_wide.hip) and tall (gemm_tall.hip) work items; FP4 weights:
-        // gemm_mx.hip (16-row items)
-        const bool tall = !mx && g1.mt == kTallTiles, wide = !mx && g1.mt == kWideTiles;
+        // (gemm_wide.hip) and tall (gemm_tall.hip) work items; group-wise
+        // scales: gemm.hip (16- or 32-row items); FP4 weights: gemm_mx.hip
+        const bool tall = !mx && !grp && g1.mt == kTallTiles, wide = !mx && !grp && g1.mt == kWideTiles;
         const int nw = tall ? kTallPairs : wide ? wide_tile_pairs() : 1;  // tile pairs per work item
         g1.n_tiles = L.imax / kTileN / nw;
         g1.chunks = ra.chunks;

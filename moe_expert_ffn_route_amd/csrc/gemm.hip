@@ -58,11 +58,11 @@ __device__ __forceinline__ v4i ld16_stream(const int8_t *p) {
 // sec. 3.1), one per GS 64-byte K steps of a row (a.a_ng per row): at the end
 // of each group the lane's int32 partials are dequantised,
 // p = (float(acc) * w_scale[n]) * group_scale[row], and added to its fp32
-// sums, which the epilogue adds over the waves in wave order (MT = 1; a
-// wave's K slice and each batch hold whole groups).
+// sums, which the epilogue adds over the waves in wave order (a wave's K
+// slice and each batch hold whole groups).
 template <int KIND, int WAVES, int KSTEPS, bool PACKED, int MT, int NPASS, int GS = 0>
 __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_dim, int n_pass_rt) {
-    static_assert(GS == 0 || (MT == 1 && KSTEPS % GS == 0), "group-wise scales: one row tile, whole groups per batch");
+    static_assert(GS == 0 || KSTEPS % GS == 0, "group-wise scales: whole groups per batch");
     constexpr int kThreads = WAVES * kWave;
     constexpr int kCols = KIND == 1 ? kTileN : 2 * kTileN;  // output columns of one work item
     constexpr int kElems = kTileN * kCols;                   // outputs of one 16-row tile
@@ -149,15 +149,17 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
     // group-wise scales: the lane's two output channels (one per weight tile)
     // and the activation rows of its four accumulator rows 4 * (l / 16) + i
     float wl0 = 0.0f, wl1 = 0.0f;
-    int srow[4] = {0, 0, 0, 0};
+    int srow[MT][4];
     if constexpr (GS > 0) {
         wl0 = Ws[rowA + r16];
         wl1 = Ws[rowB + r16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int lr = min(4 * kg + i, rows - 1);
-            srow[i] = KIND == 1 ? aidx[row0 + lr] : row0 + lr;
-        }
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int lr = min(mt * kTileN + 4 * kg + i, rows - 1);
+                srow[mt][i] = KIND == 1 ? aidx[row0 + lr] : row0 + lr;
+            }
     }
     int rrow[kEpt], rtok[kEpt];  // epilogue rows of the first row tile
 #pragma unroll
@@ -217,7 +219,14 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
         acc0[mt] = v4i{0, 0, 0, 0};
         acc1[mt] = v4i{0, 0, 0, 0};
     }
-    float f0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, f1[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // group-wise sums
+    float f0[MT][4], f1[MT][4];  // group-wise sums
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f0[mt][e] = 0.0f;
+            f1[mt][e] = 0.0f;
+        }
     // One K batch: this batch's A rows, then (if any) the next weight batch,
     // then the MFMAs, which wait only for this batch's loads.
     auto batch = [&](const v4i (&w)[2][KSTEPS], v4i (&nxt)[2][KSTEPS], int pass, bool has_next) {
@@ -232,29 +241,35 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
             }
         }
         // group-wise scales of this batch's groups, for the lane's four rows
+        // of each row tile
         constexpr int kGroups = GS > 0 ? KSTEPS / GS : 1;
-        float gsc[kGroups][4];
+        float gsc[MT][kGroups][4];
         if constexpr (GS > 0) {
             const int g0 = (step0 + pass * KSTEPS) / GS;
-            if (kGroups % 4 == 0 && (a.a_ng & 3) == 0) {  // uniform
-                // a row's scales of consecutive groups are contiguous and,
-                // with g0 a multiple of kGroups and a_ng of 4, 16-byte aligned
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+            for (int mt = 0; mt < MT; ++mt) {
+                if (!(MT == 1 || mt * kTileN < rows)) continue;  // uniform
+                if (kGroups % 4 == 0 && (a.a_ng & 3) == 0) {     // uniform
+                    // a row's scales of consecutive groups are contiguous and,
+                    // with g0 a multiple of kGroups and a_ng of 4, 16-byte aligned
 #pragma unroll
-                    for (int q = 0; q + 3 < kGroups; q += 4) {
-                        const float4 v4 = *reinterpret_cast<const float4 *>(
-                            Ascale + static_cast<size_t>(srow[i]) * a.a_ng + g0 + q);
-                        gsc[q][i] = v4.x;
-                        gsc[q + 1][i] = v4.y;
-                        gsc[q + 2][i] = v4.z;
-                        gsc[q + 3][i] = v4.w;
-                    }
-            } else {
+                    for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int q = 0; q < kGroups; ++q)
+                        for (int q = 0; q + 3 < kGroups; q += 4) {
+                            const float4 v4 = *reinterpret_cast<const float4 *>(
+                                Ascale + static_cast<size_t>(srow[mt][i]) * a.a_ng + g0 + q);
+                            gsc[mt][q][i] = v4.x;
+                            gsc[mt][q + 1][i] = v4.y;
+                            gsc[mt][q + 2][i] = v4.z;
+                            gsc[mt][q + 3][i] = v4.w;
+                        }
+                } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) gsc[q][i] = Ascale[static_cast<size_t>(srow[i]) * a.a_ng + g0 + q];
+                    for (int q = 0; q < kGroups; ++q)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            gsc[mt][q][i] = Ascale[static_cast<size_t>(srow[mt][i]) * a.a_ng + g0 + q];
+                }
             }
         }
         if (has_next) ldw(nxt, pass + 1);
@@ -265,33 +280,46 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
             // MFMAs are issued, so the VALU work never waits right behind the
             // MFMA that produced its operands (the batch's last group waits
             // once, at the end).
-            const bool av = r16 < rows;
             const v4i zero = {0, 0, 0, 0};
-            v4i pend0 = zero, pend1 = zero;
-            auto flush = [&](const v4i &s0, const v4i &s1, int q) {
+            v4i pend0[MT], pend1[MT];
+            auto flush = [&](int mt, int q) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float p0 = static_cast<float>(s0[e]) * wl0;
-                    p0 = p0 * gsc[q][e];
-                    f0[e] = f0[e] + p0;
-                    float p1 = static_cast<float>(s1[e]) * wl1;
-                    p1 = p1 * gsc[q][e];
-                    f1[e] = f1[e] + p1;
+                    float p0 = static_cast<float>(pend0[mt][e]) * wl0;
+                    p0 = p0 * gsc[mt][q][e];
+                    f0[mt][e] = f0[mt][e] + p0;
+                    float p1 = static_cast<float>(pend1[mt][e]) * wl1;
+                    p1 = p1 * gsc[mt][q][e];
+                    f1[mt][e] = f1[mt][e] + p1;
                 }
             };
 #pragma unroll
             for (int i = 0; i < KSTEPS; ++i) {
-                const v4i xi = av ? x[0][i] : zero;
                 const bool first = i % GS == 0;
-                acc0[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xi, w[0][i], first ? zero : acc0[0], 0, 0, 0);
-                acc1[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xi, w[1][i], first ? zero : acc1[0], 0, 0, 0);
-                if (first && i > 0) flush(pend0, pend1, i / GS - 1);
-                if ((i + 1) % GS == 0) {
-                    pend0 = acc0[0];
-                    pend1 = acc1[0];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    if (MT == 1 || mt * kTileN < rows) {  // uniform
+                        const v4i xi = mt * kTileN + r16 < rows ? x[mt][i] : zero;
+                        acc0[mt] =
+                            __builtin_amdgcn_mfma_i32_16x16x64_i8(xi, w[0][i], first ? zero : acc0[mt], 0, 0, 0);
+                        acc1[mt] =
+                            __builtin_amdgcn_mfma_i32_16x16x64_i8(xi, w[1][i], first ? zero : acc1[mt], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    if (MT == 1 || mt * kTileN < rows) {
+                        if (first && i > 0) flush(mt, i / GS - 1);
+                        if ((i + 1) % GS == 0) {
+                            pend0[mt] = acc0[mt];
+                            pend1[mt] = acc1[mt];
+                        }
+                    }
                 }
             }
-            flush(pend0, pend1, kGroups - 1);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                if (MT == 1 || mt * kTileN < rows) flush(mt, kGroups - 1);
         } else {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -319,20 +347,24 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
     }
 
     if constexpr (GS > 0) {
-        // the waves' fp32 sums, added in wave order
+        // the waves' fp32 sums, added in wave order, one row tile at a time
         __shared__ float redf[WAVES][2][kTileN][kTileN];
 #pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+        if (mt * kTileN >= rows) break;  // uniform
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
-            redf[wave][0][4 * kg + i][r16] = f0[i];
-            redf[wave][1][4 * kg + i][r16] = f1[i];
+            redf[wave][0][4 * kg + i][r16] = f0[mt][i];
+            redf[wave][1][4 * kg + i][r16] = f1[mt][i];
         }
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < kEpt; ++e) {
             const int idx = tid + e * kThreads;
             const int m = idx / kCols;
-            if (idx < kElems && m < rows) {
-                const int r = row0 + m;
+            const int lr = mt * kTileN + m;
+            if (idx < kElems && lr < rows) {
+                const int r = row0 + lr;
                 if (KIND == 1) {
                     float yg = 0.0f, yu = 0.0f;
 #pragma unroll
@@ -350,14 +382,18 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
 #pragma unroll
                     for (int w = 0; w < WAVES; ++w) y = y + redf[w][jc / kTileN][m][jc % kTileN];
                     const uint16_t zb = f32_to_bf16(y);
-                    if (routed)
+                    if (routed) {
                         a.z[static_cast<size_t>(r) * a.H + col] = zb;
-                    else
-                        a.share_out[static_cast<size_t>(rtok[e]) * a.H + col] = zb;
+                    } else {
+                        const int t = mt == 0 ? rtok[e] : a.row_token[r];
+                        a.share_out[static_cast<size_t>(t) * a.H + col] = zb;
+                    }
                     if (a.dbg_acc) a.dbg_acc[static_cast<size_t>(r) * a.H + col] = __float_as_int(y);
                     if (a.dbg_z) a.dbg_z[static_cast<size_t>(r) * a.H + col] = zb;
                 }
             }
+        }
+        __syncthreads();
         }
         return;
     }
@@ -471,11 +507,30 @@ hipError_t launch_w(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s,
 // Group-wise scales (a.gsteps = GS steps of 64 per group): every wave's K
 // slice must hold whole groups, so K is split over W = min(8, groups) waves
 // (groups = k_dim / (64 * GS), a power-of-two count is not required: W is the
-// largest of 8, 4, 2, 1 dividing it). A slice of up to 8 steps is one batch;
-// longer slices go in batches of one group.
-template <int KIND, bool PACKED, int GS, int W>
+// largest of 8, 4, 2, 1 dividing it). One row tile (MT = 1): a slice of up
+// to 8 steps is one batch, longer slices go in batches of one group. Two row
+// tiles (32-row items): batches of one group (MOE_GRP_WIDE_BATCH).
+// Two row tiles: batches of one group (0), or of 4 steps where they fit (4).
+// Measured on the T = 512 workload with 128-element groups: one group per
+// batch 1246 us per layer (GEMM1 774 us), 4-step batches 1438 us (GEMM1 979
+// us at 184 VGPRs, two waves per SIMD).
+#ifndef MOE_GRP_WIDE_BATCH
+#define MOE_GRP_WIDE_BATCH 0
+#endif
+template <int KIND, bool PACKED, int GS, int W, int MT>
 hipError_t launch_grp_w(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const int spw = k_dim / (64 * W);
+    if constexpr (MT == 2) {
+        if (MOE_GRP_WIDE_BATCH == 4 && spw % 4 == 0) {
+            const int np = spw / 4;
+            if (np == 1) launch_one<KIND, W, 4, PACKED, 2, 1, GS>(a, grid, k_dim, 1, s, e0, e1);
+            else if (np == 2) launch_one<KIND, W, 4, PACKED, 2, 2, GS>(a, grid, k_dim, 2, s, e0, e1);
+            else launch_one<KIND, W, 4, PACKED, 2, 0, GS>(a, grid, k_dim, np, s, e0, e1);
+        } else {
+            launch_one<KIND, W, GS, PACKED, 2, 0, GS>(a, grid, k_dim, spw / GS, s, e0, e1);
+        }
+        return hipGetLastError();
+    }
     switch (spw) {
         case GS: launch_one<KIND, W, GS, PACKED, 1, 1, GS>(a, grid, k_dim, 1, s, e0, e1); break;
         case 2 * GS: launch_one<KIND, W, 2 * GS, PACKED, 1, 1, GS>(a, grid, k_dim, 1, s, e0, e1); break;
@@ -492,21 +547,21 @@ hipError_t launch_grp_w(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, 
     return hipGetLastError();
 }
 
-template <int KIND, bool PACKED, int GS>
+template <int KIND, bool PACKED, int GS, int MT>
 hipError_t launch_grp(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const int groups = k_dim / (64 * GS);
-    if (groups % 8 == 0) return launch_grp_w<KIND, PACKED, GS, 8>(a, grid, k_dim, s, e0, e1);
-    if (groups % 4 == 0) return launch_grp_w<KIND, PACKED, GS, 4>(a, grid, k_dim, s, e0, e1);
-    if (groups % 2 == 0) return launch_grp_w<KIND, PACKED, GS, 2>(a, grid, k_dim, s, e0, e1);
-    return launch_grp_w<KIND, PACKED, GS, 1>(a, grid, k_dim, s, e0, e1);
+    if (groups % 8 == 0) return launch_grp_w<KIND, PACKED, GS, 8, MT>(a, grid, k_dim, s, e0, e1);
+    if (groups % 4 == 0) return launch_grp_w<KIND, PACKED, GS, 4, MT>(a, grid, k_dim, s, e0, e1);
+    if (groups % 2 == 0) return launch_grp_w<KIND, PACKED, GS, 2, MT>(a, grid, k_dim, s, e0, e1);
+    return launch_grp_w<KIND, PACKED, GS, 1, MT>(a, grid, k_dim, s, e0, e1);
 }
 
-template <int KIND, bool PACKED>
+template <int KIND, bool PACKED, int MT>
 hipError_t launch_grp_p(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     switch (a.gsteps) {
-        case 1: return launch_grp<KIND, PACKED, 1>(a, grid, k_dim, s, e0, e1);
-        case 2: return launch_grp<KIND, PACKED, 2>(a, grid, k_dim, s, e0, e1);
-        case 4: return launch_grp<KIND, PACKED, 4>(a, grid, k_dim, s, e0, e1);
+        case 1: return launch_grp<KIND, PACKED, 1, MT>(a, grid, k_dim, s, e0, e1);
+        case 2: return launch_grp<KIND, PACKED, 2, MT>(a, grid, k_dim, s, e0, e1);
+        case 4: return launch_grp<KIND, PACKED, 4, MT>(a, grid, k_dim, s, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
@@ -514,12 +569,15 @@ hipError_t launch_grp_p(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, 
 template <int KIND>
 hipError_t launch_kind(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     if (a.gsteps > 0) {
-        if (a.mt != 1 || k_dim % (64 * a.gsteps)) return hipErrorInvalidValue;
+        if ((a.mt != 1 && a.mt != 2) || k_dim % (64 * a.gsteps)) return hipErrorInvalidValue;
         const long blocks = static_cast<long>(max_chunks) * a.n_tiles;
         if (blocks <= 0) return hipSuccess;
         const dim3 grid(static_cast<unsigned>(blocks));
-        return a.packed ? launch_grp_p<KIND, true>(a, grid, k_dim, s, e0, e1)
-                        : launch_grp_p<KIND, false>(a, grid, k_dim, s, e0, e1);
+        if (a.mt == 2)
+            return a.packed ? launch_grp_p<KIND, true, 2>(a, grid, k_dim, s, e0, e1)
+                            : launch_grp_p<KIND, false, 2>(a, grid, k_dim, s, e0, e1);
+        return a.packed ? launch_grp_p<KIND, true, 1>(a, grid, k_dim, s, e0, e1)
+                        : launch_grp_p<KIND, false, 1>(a, grid, k_dim, s, e0, e1);
     }
     constexpr int W = KIND == 1 ? MOE_GEMM1_WAVES : MOE_GEMM2_WAVES;
     constexpr int KS = KIND == 1 ? MOE_GEMM1_KSTEPS : MOE_GEMM2_KSTEPS;

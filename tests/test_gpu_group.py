@@ -6,7 +6,8 @@ adding the same dequantised group partials in another order).
 
 The cases cover the three group sizes (64, 128, 256), every K split the
 group path takes (8, 4, 2 and 1 waves; a batch of whole groups, or one group
-per batch over several passes), 16-row items with several chunks per expert,
+per batch over several passes), 16- and 32-row items with several chunks per
+expert,
 masks, smooth scales, an EP share, a shared expert with a different
 intermediate (two GEMM2 launches), T = 0 / 1, and the decode workload's full
 shape on a sample of tokens.
@@ -41,8 +42,16 @@ CASES = {
                                      share_smooth=True, seed=504), None),
     "ep_share": (spec(T=16, H=1024, I=512, E_g=32, K=6, ep_size=4, ep_rank=1, active=13, smooth=True, seed=505),
                  None),
-    # 40 tokens on 2 experts: 16-row items, three chunks per expert, 16 N tiles
+    # 40 tokens on 2 experts: 32-row items (two row tiles; the second chunk of
+    # an expert has 8 rows, so its second tile is skipped), 16 N tiles
     "t40_multichunk": (spec(T=40, H=512, I=256, E_g=2, K=2, I_s=256, seed=506), None),
+    # two row tiles with H 4096 (8 waves x 2 batches of 4 steps) and I 256
+    # (2 waves x one 2-step group), and with H 768 (2 waves x 3 one-group
+    # batches), smooth scales
+    "t20_two_tiles_h4096": (spec(T=20, H=4096, I=256, E_g=1, K=1, I_s=256, seed=511), None),
+    "t40_two_tiles_h768": (spec(T=40, H=768, I=512, E_g=2, K=2, I_s=256, smooth=True, seed=512), None),
+    # many experts with few rows each at T > 16: 16-row items
+    "t24_few_rows_per_expert": (spec(T=24, H=512, I=256, E_g=16, K=2, I_s=256, seed=513), None),
     # G 64 and H 9216: 144 groups, 8 waves x 18 passes of one group
     "long_k_g64": (spec(T=3, H=9216, I=256, E_g=4, K=2, I_s=256, quant_group=64, seed=507), None),
     # I 4096 with I_s 4352 and G 128: a routed GEMM2 batch holds 4 groups
