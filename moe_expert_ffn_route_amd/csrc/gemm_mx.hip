@@ -311,10 +311,18 @@ hipError_t launch_split(const GemmArgs &a, dim3 grid, int k_dim, int spw, hipStr
 // One row tile per chunk (batches of at most 16 tokens) splits K over
 // MOE_MX_WAVES waves; two row tiles (32-row chunks, larger batches) over 8,
 // which keeps a wave's A and weight registers of a batch within budget.
+#ifndef MOE_MX_WIDE_KS
+#define MOE_MX_WIDE_KS 0  // two row tiles: steps per batch (0: the whole slice when it is at most 8 steps)
+#endif
 template <int KIND, int MT>
 hipError_t launch_mt(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     constexpr int W = MT == 1 ? MOE_MX_WAVES : 8;
     const int steps = k_dim / kStepK;
+    if constexpr (MT == 2 && MOE_MX_WIDE_KS > 0) {
+        if (steps % (W * MOE_MX_WIDE_KS) == 0)
+            return launch_one<KIND, W, MOE_MX_WIDE_KS, 0, MT>(a, grid, k_dim, steps / (W * MOE_MX_WIDE_KS), s, e0,
+                                                               e1);
+    }
     if (steps % W == 0) return launch_split<KIND, W, MT>(a, grid, k_dim, steps / W, s, e0, e1);
     if (steps % 4 == 0) return launch_one<KIND, 4, 1, 0, MT>(a, grid, k_dim, steps / 4, s, e0, e1);
     return launch_one<KIND, 2, 1, 0, MT>(a, grid, k_dim, steps / 2, s, e0, e1);
