@@ -203,6 +203,17 @@ def gemm1_traffic(workload, mx=False):
     return None
 
 
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, budget_s=12.0, max_reps=40, tokens=None):
     """The CPU oracle as it stands, single-threaded, on the same batch (or on
     `tokens` of it)."""
@@ -456,7 +467,8 @@ def main():
             cpu_us, reps = cpu_baseline(case)
             sample = f"the full batch of this workload, {reps} runs, single-threaded C oracle"
         rec["cpu_baseline"] = {"value": round(cpu_us, 1), "unit": "us", "cores": 1, "kind": "oracle",
-                               "sample": sample}
+                               "sample": sample, "host_cpu": host_cpu_model(),
+                               "host_threads_available": os.cpu_count()}
     print(json.dumps(rec), flush=True)
 
 
