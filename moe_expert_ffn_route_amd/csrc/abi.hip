@@ -345,6 +345,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         g2.n_tiles = H / (2 * kTileN) / nw;
         g2.h = nullptr;
         g2.z = reinterpret_cast<uint16_t *>(ws + L.z);
+        g2.zrow = ra.sorted_pair;  // routed z rows in pair order: combine reads row t*K + k
         g2.share_out = static_cast<uint16_t *>(share_output);
         g2.dbg_acc = D.acc2;
         g2.dbg_z = D.z;

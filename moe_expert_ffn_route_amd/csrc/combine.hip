@@ -9,8 +9,9 @@
 // so the result is deterministic.
 //
 // Grid = tokens x (H / 1024): each thread owns 8 consecutive channels and
-// issues the 16-byte loads of all K rows before it sums them, so a token
-// costs one memory round trip. It also clears the shared-expert rows of
+// issues the 16-byte loads of all K rows (z is in pair order) together with
+// the pairs' kept flags before it sums them, so a token costs one memory
+// round trip. It also clears the shared-expert rows of
 // inactive tokens, which GEMM2 never writes.
 #include "internal.h"
 
@@ -26,14 +27,15 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     if (c >= a.H) return;
     const int32_t *rop = a.row_of_pair + static_cast<size_t>(t) * a.K;
     const float *wt = a.scales + static_cast<size_t>(t) * a.K;
+    // z holds pair p = t*K + k at row p (written only for kept pairs): all K
+    // rows are loaded at once, alongside the row_of_pair entries that say
+    // which of them are kept (z has T*K rows, so every load is in bounds)
     uint4 raw[kMaxTopK];
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
         raw[k] = make_uint4(0, 0, 0, 0);
-        if (k < a.K) {
-            const int row = rop[k];
-            if (row >= 0) raw[k] = *reinterpret_cast<const uint4 *>(a.z + static_cast<size_t>(row) * a.H + c);
-        }
+        if (k < a.K)
+            raw[k] = *reinterpret_cast<const uint4 *>(a.z + (static_cast<size_t>(t) * a.K + k) * a.H + c);
     }
     float sum[8];
 #pragma unroll

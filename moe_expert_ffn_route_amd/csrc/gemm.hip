@@ -130,8 +130,9 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
     // that last row and are zeroed before the MFMA, so no load sits in a
     // divergent branch.
     const int32_t *aidx = KIND == 1 ? (routed ? a.idx_r : a.row_token) : nullptr;
-    const bool need_tok = KIND == 1 || !routed;
-    const int32_t *tidx = KIND == 1 ? aidx : a.row_token;  // epilogue rows: scale index / share_output row
+    // epilogue rows' index: GEMM1 the activation scale's row, GEMM2 the z row
+    // (the pair id) of a routed row or the share_output row of a shared one
+    const int32_t *tidx = KIND == 1 ? aidx : (routed ? a.zrow : a.row_token);
     const int8_t *Abase = KIND == 1 ? (routed ? a.A_r : a.A_s) : a.A;
     const float *Ascale = KIND == 1 ? (routed ? a.a_scale_r : a.a_scale_s) : a.a_scale;
     int arow[MT];
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) {
         rrow[e] = row0 + min(min(tid + e * kThreads, kElems - 1) / kCols, rows - 1);
-        rtok[e] = need_tok ? tidx[rrow[e]] : 0;
+        rtok[e] = tidx[rrow[e]];
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -382,12 +383,8 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
 #pragma unroll
                     for (int w = 0; w < WAVES; ++w) y = y + redf[w][jc / kTileN][m][jc % kTileN];
                     const uint16_t zb = f32_to_bf16(y);
-                    if (routed) {
-                        a.z[static_cast<size_t>(r) * a.H + col] = zb;
-                    } else {
-                        const int t = mt == 0 ? rtok[e] : a.row_token[r];
-                        a.share_out[static_cast<size_t>(t) * a.H + col] = zb;
-                    }
+                    const int t = mt == 0 ? rtok[e] : tidx[r];
+                    (routed ? a.z : a.share_out)[static_cast<size_t>(t) * a.H + col] = zb;
                     if (a.dbg_acc) a.dbg_acc[static_cast<size_t>(r) * a.H + col] = __float_as_int(y);
                     if (a.dbg_z) a.dbg_z[static_cast<size_t>(r) * a.H + col] = zb;
                 }
@@ -432,12 +429,8 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
 #pragma unroll
                     for (int w = 0; w < WAVES; ++w) acc += red[w][jc / kTileN][m][jc % kTileN];
                     const uint16_t zb = f32_to_bf16(dequant(acc, wsc0, rs));
-                    if (routed) {
-                        a.z[static_cast<size_t>(r) * a.H + col] = zb;
-                    } else {
-                        const int t = mt == 0 ? rtok[e] : a.row_token[r];
-                        a.share_out[static_cast<size_t>(t) * a.H + col] = zb;
-                    }
+                    const int t = mt == 0 ? rtok[e] : tidx[r];
+                    (routed ? a.z : a.share_out)[static_cast<size_t>(t) * a.H + col] = zb;
                     if (a.dbg_acc) a.dbg_acc[static_cast<size_t>(r) * a.H + col] = acc;
                     if (a.dbg_z) a.dbg_z[static_cast<size_t>(r) * a.H + col] = zb;
                 }

@@ -111,8 +111,9 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES == 4 && MT == 1 ? 3 : 1) void 
     // (1) independent small loads (activation row index, epilogue rows,
     //     channel scales) ahead of the weight stream
     const int32_t *aidx = KIND == 1 ? (routed ? a.idx_r : a.row_token) : nullptr;
-    const bool need_tok = KIND == 1 || !routed;
-    const int32_t *tidx = KIND == 1 ? aidx : a.row_token;
+    // epilogue rows' index: GEMM1 the activation scale's row, GEMM2 the z row
+    // (pair id) of a routed row or the share_output row of a shared one
+    const int32_t *tidx = KIND == 1 ? aidx : (routed ? a.zrow : a.row_token);
     const uint8_t *Abase = reinterpret_cast<const uint8_t *>(KIND == 1 ? (routed ? a.A_r : a.A_s) : a.A);
     const float *Ascale = KIND == 1 ? (routed ? a.a_scale_r : a.a_scale_s) : a.a_scale;
     int arow[MT];
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES == 4 && MT == 1 ? 3 : 1) void 
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) {
         rrow[e] = row0 + min(min(tid + e * kThreads, kElems - 1) / kCols, rows - 1);
-        rtok[e] = need_tok ? tidx[rrow[e]] : 0;
+        rtok[e] = tidx[rrow[e]];
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -253,12 +254,8 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES == 4 && MT == 1 ? 3 : 1) void 
 #pragma unroll
                 for (int w = 0; w < WAVES; ++w) acc += red[w][jc / kTileN][m][jc % kTileN];
                 const uint16_t zb = f32_to_bf16(dequant(acc, wsc0, rs));
-                if (routed) {
-                    a.z[static_cast<size_t>(r) * a.H + col] = zb;
-                } else {
-                    const int t = mt == 0 ? rtok[e] : a.row_token[r];
-                    a.share_out[static_cast<size_t>(t) * a.H + col] = zb;
-                }
+                const int t = mt == 0 ? rtok[e] : tidx[r];
+                (routed ? a.z : a.share_out)[static_cast<size_t>(t) * a.H + col] = zb;
                 if (a.dbg_acc) a.dbg_acc[static_cast<size_t>(r) * a.H + col] = __float_as_int(acc);
                 if (a.dbg_z) a.dbg_z[static_cast<size_t>(r) * a.H + col] = zb;
             }

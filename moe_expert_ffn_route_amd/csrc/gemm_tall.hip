@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
 
     // Epilogue: lane l holds rows 4 (l / 16) + i of each of the wave's row
     // tiles, at channel l % 16 of each weight tile.
-    const int32_t *tidx = KIND == 1 ? aidx : (routed ? nullptr : a.row_token);
+    const int32_t *tidx = KIND == 1 ? aidx : (routed ? a.zrow : a.row_token);
 #pragma unroll
     for (int mt = 0; mt < kTMT; ++mt) {
         int otok[4];
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int lr = min(wm * kTMT * kTileN + mt * kTileN + 4 * kg + i, rows - 1);
-            otok[i] = tidx ? tidx[row0 + lr] : 0;
+            otok[i] = tidx[row0 + lr];
             rsc[i] = Ascale[KIND == 1 ? otok[i] : row0 + lr];
         }
 #pragma unroll
@@ -274,8 +274,7 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
                     const int wcol = even ? rowA + r16 : rowB + r16 - 1;
                     if (lr < rows) {
                         const int r = row0 + lr;
-                        uint16_t *dst = routed ? a.z + static_cast<size_t>(r) * a.H
-                                               : a.share_out + static_cast<size_t>(otok[i]) * a.H;
+                        uint16_t *dst = (routed ? a.z : a.share_out) + static_cast<size_t>(otok[i]) * a.H;
                         *reinterpret_cast<uint32_t *>(dst + wcol) = word;
                         if (a.dbg_acc) {
                             a.dbg_acc[static_cast<size_t>(r) * a.H + rowA + r16] = acc0[mt][q][i];

@@ -49,7 +49,7 @@ struct WideItem {
     int jcol;                 // channels from one tile pair to the next
     int row0, rows, S, inter;
     const int32_t *aidx;        // GEMM1: where row r's activations are (null: row r)
-    const int32_t *tidx;        // epilogue rows' scale index / share_output row (null: none)
+    const int32_t *tidx;        // epilogue rows' scale index (GEMM1) / z or share_output row (GEMM2)
     bool routed;
 };
 
@@ -247,8 +247,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
                     const int wcol = even ? rowA + r16 : rowB + r16 - 1;
                     if (lr < rows) {
                         const int r = row0 + lr;
-                        uint16_t *dst = it.routed ? a.z + static_cast<size_t>(r) * a.H
-                                                  : a.share_out + static_cast<size_t>(otok[mt][i]) * a.H;
+                        uint16_t *dst = (it.routed ? a.z : a.share_out) + static_cast<size_t>(otok[mt][i]) * a.H;
                         *reinterpret_cast<uint32_t *>(dst + wcol) = word;
                         if (a.dbg_acc) {
                             a.dbg_acc[static_cast<size_t>(r) * a.H + rowA + r16] = acc0[mt][j][i];
@@ -335,7 +334,7 @@ __device__ __forceinline__ bool decode_item(const GemmArgs &a, const int4 *chunk
     // token's or the (token, expert) pair's quantised row; shared rows: the
     // token's); GEMM2 row r reads row r
     it.aidx = KIND == 1 ? (it.routed ? a.idx_r : a.row_token) : nullptr;
-    it.tidx = KIND == 1 ? it.aidx : (it.routed ? nullptr : a.row_token);
+    it.tidx = KIND == 1 ? it.aidx : (it.routed ? a.zrow : a.row_token);
     it.Abase = KIND == 1 ? (it.routed ? a.A_r : a.A_s) : a.A;
     it.Ascale = KIND == 1 ? (it.routed ? a.a_scale_r : a.a_scale_s) : a.a_scale;
     return true;

@@ -147,7 +147,8 @@ struct GemmArgs {
     const int32_t *row_token;
     // outputs
     float *h;              // GEMM1: [rows_max, imax]
-    uint16_t *z;           // GEMM2 routed rows: [rows_max, H] bf16
+    uint16_t *z;           // GEMM2 routed rows: [T*K, H] bf16, routed row r at row zrow[r] (its pair id)
+    const int32_t *zrow;   // [P] pair id of routed row r (sorted_pair)
     uint16_t *share_out;   // GEMM2 shared rows: [T, H] bf16 indexed by token
     int32_t *dbg_acc;      // optional [rows_max, 2*imax] (GEMM1) / [rows_max, H] (GEMM2)
     uint16_t *dbg_z;       // optional [rows_max, H]
