@@ -321,6 +321,7 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         rq.has_shared = shared;
         rq.rows_max = L.rows_max;
         rq.load_early = d->ep_rank_size == 1;  // then nearly every grouped row is in use
+        rq.rows_expected = static_cast<int>(static_cast<size_t>(T) * K / d->ep_rank_size) + (shared ? T : 0);
         rq.eps = d->amax_eps;
         rq.q = reinterpret_cast<int8_t *>(ws + L.q_h);
         rq.scale = reinterpret_cast<float *>(ws + L.hs);

@@ -105,6 +105,7 @@ struct RequantArgs {
     const int32_t *meta;
     int E_loc, I, I_s, imax, has_shared, rows_max;
     int load_early;  // read each h row before the row count is known (all pairs local)
+    int rows_expected;  // grouped rows the batch can use: T*K / ep_rank_size (+ T with a shared expert)
     float eps;
     int8_t *q;     // [rows_max, imax]
     float *scale;  // [rows_max]

@@ -125,11 +125,12 @@ __global__ __launch_bounds__(256) void dbg_gather_kernel(GemmArgs g, const int32
 }
 
 // Rows of up to MOE_REQUANT_WAVE_MAX values take one wavefront each, longer
-// rows one 256-thread workgroup each. Batches of at most
-// MOE_REQUANT_BLOCK_ROWS grouped rows (decode) also take a workgroup per
-// row: with so few rows the chip is mostly idle, and four times the threads
-// per row shorten each row's chain of loads and conversions (measured on
-// MI355X at T = 8, 80 rows of 2048: 4.9 -> 4.6 us INT8, 5.5 -> 4.6 us FP8).
+// rows one 256-thread workgroup each. Batches expected to use at most
+// MOE_REQUANT_BLOCK_ROWS grouped rows (decode, or an expert-parallel share of
+// a larger batch) also take a workgroup per row: with so few rows the chip is
+// mostly idle, and four times the threads per row shorten each row's chain of
+// loads and conversions (measured on MI355X at T = 8, 80 rows of 2048: 4.9 ->
+// 4.6 us INT8, 5.5 -> 4.6 us FP8).
 #ifndef MOE_REQUANT_WAVE_MAX
 #define MOE_REQUANT_WAVE_MAX 4096
 #endif
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(256) void dbg_gather_kernel(GemmArgs g, const int32
 
 template <bool FP8, int GL>
 hipError_t launch_requant_fmt(const RequantArgs &a, dim3 wgrid, dim3 wblk, hipStream_t s) {
-    const bool wave = a.rows_max > MOE_REQUANT_BLOCK_ROWS;
+    const bool wave = a.rows_expected > MOE_REQUANT_BLOCK_ROWS;
     if (wave && a.imax <= 8 * 256 && a.imax <= MOE_REQUANT_WAVE_MAX)
         hipLaunchKernelGGL((requant_wave_kernel<8, FP8, GL>), wgrid, wblk, 0, s, a);
     else if (wave && a.imax <= 16 * 256 && a.imax <= MOE_REQUANT_WAVE_MAX)
