@@ -63,6 +63,8 @@ CASES = {
     "t0": (spec(T=0, I_s=256, seed=509), None),
     # the decode workload's shape with 128-element groups (two tokens checked)
     "decode_full_shape": (spec(T=8, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1235), [1, 6]),
+    # the large-batch workload's shape (two-tile items; two tokens checked)
+    "t512_full_shape": (spec(T=512, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1238, wseed=1235), [7, 300]),
 }
 
 

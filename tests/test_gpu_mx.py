@@ -61,6 +61,8 @@ CASES = {
     # the decode workload's shape: T 8, H 4096, I 2048, 256 experts, top-8,
     # shared expert 2048 (two tokens through the oracle)
     "decode_full_shape": (spec(T=8, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1235), [2, 5]),
+    # the large-batch workload's shape (two-tile items; two tokens checked)
+    "t512_full_shape": (spec(T=512, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1238, wseed=1235), [3, 400]),
 }
 
 
