@@ -7,10 +7,9 @@ adding the same dequantised group partials in another order).
 The cases cover the three group sizes (64, 128, 256), every K split the
 group path takes (8, 4, 2 and 1 waves; a batch of whole groups, or one group
 per batch over several passes), 16- and 32-row items with several chunks per
-expert,
-masks, smooth scales, an EP share, a shared expert with a different
-intermediate (two GEMM2 launches), T = 0 / 1, and the decode workload's full
-shape on a sample of tokens.
+expert, masks, smooth scales, an EP share, a shared expert with a different
+intermediate (two GEMM2 launches), T = 0 / 1, and the full shapes of the
+decode and T = 512 workloads on samples of their tokens.
 """
 import numpy as np
 import pytest

@@ -8,10 +8,10 @@ the block's output tolerance).
 The cases span every K split of the MX kernel (8, 4 and 2 waves; one batch
 per wave; 1-, 2- and 4-step batches over several passes), 16-row items
 (decode) and 32-row items with several chunks per expert (batches above 16
-tokens), masks, smooth scales, an
-expert-parallel share, a shared expert whose intermediate differs (two GEMM2
-launches), the fused route scale, T = 0 and T = 1, and the decode workload's
-full shape with a sample of its tokens.
+tokens), masks, smooth scales, an expert-parallel share, a shared expert
+whose intermediate differs (two GEMM2 launches), the fused route scale,
+T = 0 and T = 1, and the full shapes of the decode and T = 512 workloads on
+samples of their tokens.
 """
 import numpy as np
 import pytest
