@@ -260,7 +260,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(expert parallelism across GPUs is not part of this build)", file=sys.stderr)
+              "(expert parallelism across GPUs is not part of this library)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

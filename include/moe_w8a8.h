@@ -63,7 +63,7 @@ extern "C" {
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = -1, /* NULL / misaligned pointer, inconsistent sizes */
-    MOE_ERR_UNSUPPORTED = -2, /* legal for the operator, outside what this build runs */
+    MOE_ERR_UNSUPPORTED = -2, /* legal for the operator, outside what this library runs */
     MOE_ERR_WORKSPACE = -3,   /* workspace pointer NULL or workspace_bytes too small */
     MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
 } moe_status_t;

@@ -14,13 +14,10 @@
 // channels). Its 16 waves form a 4 x 4 grid: wave (wm, wn) multiplies rows
 // [64 wm, 64 wm + 64) by the 2 tile pairs [2 wn, 2 wn + 2), so it holds
 // 4 x 4 MFMA tiles of int32 sums and four waves share a SIMD. Both operands
-// go through LDS one 64-byte K step (a stage) at a time, double buffered,
-// with the global loads two stages ahead: each stage, a thread issues its
-// 16-byte shares of stage s + 2 into registers, the waves run the stage's
-// MFMAs from LDS, and the thread writes its (already loaded) shares of stage
-// s + 1 to the other buffer; one workgroup barrier per stage publishes it.
-// Every activation fragment read from LDS feeds 4 MFMAs and every weight
-// fragment 4.
+// go through LDS one 64-byte K step (a stage, 32 KB) at a time, in four
+// buffers filled by direct global-to-LDS copies three stages ahead (no
+// staging registers), with one workgroup barrier per stage. Every activation
+// fragment read from LDS feeds 4 MFMAs and every weight fragment 4.
 //
 // LDS stage layout, all in MFMA lane order (1 KB blocks, lane l at byte
 // 16 l: row l % 16, bytes 16 (l / 16) .. +16 of the K step): the chunk's 16
@@ -65,15 +62,12 @@ static_assert(kTPairs == kTallPairs, "the host sizes the grid with kTallPairs");
 static_assert(kTAStage == kTLoadsA * kTWaves * 1024 && kTWStage == kTLoadsW * kTWaves * 1024,
               "a stage is whole 1 KB blocks per wave");
 
-__device__ __forceinline__ v4i ld16(const int8_t *p) { return *reinterpret_cast<const v4i *>(p); }
-__device__ __forceinline__ v4i ld16_stream(const int8_t *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
-}
-
 template <int KIND, bool PACKED>
 __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int k_dim) {
-    __shared__ __attribute__((aligned(16))) int8_t s_b0[kTStage];
-    __shared__ __attribute__((aligned(16))) int8_t s_b1[kTStage];
+    __shared__ __attribute__((aligned(16))) int8_t s_d0[kTStage];
+    __shared__ __attribute__((aligned(16))) int8_t s_d1[kTStage];
+    __shared__ __attribute__((aligned(16))) int8_t s_d2[kTStage];
+    __shared__ __attribute__((aligned(16))) int8_t s_d3[kTStage];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -118,7 +112,8 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
 
     // Global -> LDS copy of a stage: thread t copies the 16 bytes of lane
     // t % 64 of 1 KB block j = kTWaves i + wave (i < kTLoadsA, kTLoadsW) of
-    // each operand.
+    // each operand (a copy instruction puts lane l's 16 bytes at byte 16 l of
+    // the wave's block).
     // Activation block j is row tile j / kTSteps, K step j % kTSteps: lane l
     // reads row 16 (j / kTSteps) + l % 16 (rows past the chunk repeat its last
     // row; their outputs are never stored). Weight block j is tile pair
@@ -145,29 +140,6 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
         const int ar = KIND == 1 ? aidx[row0 + lr] : row0 + lr;
         asrc[i] = Abase + static_cast<size_t>(ar) * a.a_stride + (j % kTSteps) * 64 + kg * 16;
     }
-    // a stage's share of this thread, held in registers between its global
-    // loads and its LDS stores
-    struct Stage {
-        v4i a[kTLoadsA], w[kTLoadsW];
-    };
-    auto gload = [&](Stage &r, int s) {
-#pragma unroll
-        for (int i = 0; i < kTLoadsW; ++i) {
-            const int8_t *pw = wsrc[i] + static_cast<size_t>(s) * kTSteps * wstep;
-            r.w[i] = PACKED ? ld16_stream(pw) : ld16(pw);
-        }
-#pragma unroll
-        for (int i = 0; i < kTLoadsA; ++i) r.a[i] = ld16(asrc[i] + s * kTSteps * 64);
-    };
-    auto lstore = [&](const Stage &r, int8_t *base) {
-#pragma unroll
-        for (int i = 0; i < kTLoadsA; ++i)
-            *reinterpret_cast<v4i *>(base + (i * kTWaves + wave) * 1024 + lane * 16) = r.a[i];
-#pragma unroll
-        for (int i = 0; i < kTLoadsW; ++i)
-            *reinterpret_cast<v4i *>(base + kTAStage + (i * kTWaves + wave) * 1024 + lane * 16) = r.w[i];
-    };
-
     v4i acc0[kTMT][kTQ], acc1[kTMT][kTQ];
 #pragma unroll
     for (int mt = 0; mt < kTMT; ++mt)
@@ -199,31 +171,44 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
                 }
         }
     };
-    const int n_stages = k_dim / (kTSteps * 64);  // even: k_dim is a multiple of 256
-    // Stage s: the loads of stage s + 2 go out into the register set that
-    // stage s filled, then the MFMAs of stage s run from LDS, then stage
-    // s + 1 (loaded during stage s - 1) goes from registers to the other LDS
-    // buffer, and a workgroup barrier publishes it. Two register sets and two
-    // LDS buffers alternate, so the loop runs two stages per turn. The loads
-    // and stores run unconditionally (the last stages reload the last stage,
-    // which nobody reads), so that the compiler can count the loads in flight
-    // exactly and wait only for the ones a store needs.
-    Stage r0, r1;
-    auto stage = [&](int s, Stage &mine, const Stage &next, const int8_t *cur, int8_t *other) {
-        gload(mine, min(s + 2, n_stages - 1));
-        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-        compute(cur);
-        lstore(next, other);
-        __syncthreads();
+    const int n_stages = k_dim / (kTSteps * 64);  // a multiple of 4: k_dim is a multiple of 256
+    // Four LDS buffers, stage t in buffer t % 4, filled by direct
+    // global-to-LDS copies (lane l's 16 bytes land at byte 16 l of the 1 KB
+    // block, the MFMA lane order) three stages ahead: at stage s a thread
+    // issues its copies of stage s + 3 into the buffer stage s - 1 used
+    // (every wave finished reading it before the last barrier), runs stage
+    // s's MFMAs, waits until its copies of stage s + 1 have landed (the four
+    // copies of stages s + 2 and s + 3 may still be in flight) and passes a
+    // barrier. Copies past the last stage reload it into a free buffer; all
+    // copies have landed before the waves leave.
+    typedef __attribute__((address_space(3))) void lds_void;
+    typedef __attribute__((address_space(1))) void glb_void;
+    static_assert(kTLoadsA == 1 && kTLoadsW == 1 && kTSteps == 1, "two copies per thread and stage");
+    auto dma = [&](int s, int8_t *buf) {
+        __builtin_amdgcn_global_load_lds((glb_void *)(asrc[0] + s * 64), (lds_void *)(buf + wave * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((glb_void *)(wsrc[0] + static_cast<size_t>(s) * wstep),
+                                         (lds_void *)(buf + kTAStage + wave * 1024), 16, 0, PACKED ? 2 : 0);  // 2: nt
     };
-    gload(r0, 0);
-    gload(r1, 1);  // n_stages >= 4
-    lstore(r0, s_b0);
-    __syncthreads();
-    for (int s = 0; s < n_stages; s += 2) {
-        stage(s, r0, r1, s_b0, s_b1);
-        stage(s + 1, r1, r0, s_b1, s_b0);
+    auto step = [&](int s, const int8_t *cur, int8_t *freebuf) {
+        dma(min(s + 3, n_stages - 1), freebuf);
+        __builtin_amdgcn_sched_barrier(0);  // issue the copies before the stage's LDS reads
+        compute(cur);
+        // s_waitcnt fields: vmcnt bits 3:0, expcnt 6:4 (7: no wait), lgkmcnt 11:8
+        __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+    };
+    dma(0, s_d0);
+    dma(1, s_d1);
+    dma(2, s_d2);
+    __builtin_amdgcn_s_waitcnt(0x0074);
+    __builtin_amdgcn_s_barrier();
+    for (int s = 0; s < n_stages; s += 4) {  // n_stages is a multiple of 4
+        step(s, s_d0, s_d3);
+        step(s + 1, s_d1, s_d0);
+        step(s + 2, s_d2, s_d1);
+        step(s + 3, s_d3, s_d2);
     }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): the reloads past the last stage have landed
 
     // Epilogue: lane l holds rows 4 (l / 16) + i of each of the wave's row
     // tiles, at channel l % 16 of each weight tile.
@@ -291,7 +276,7 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
 
 template <int KIND>
 hipError_t launch_tall(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    if (k_dim % (2 * kTSteps * 64) != 0) return hipErrorInvalidValue;  // whole pairs of stages
+    if (k_dim % (4 * kTSteps * 64) != 0) return hipErrorInvalidValue;  // the loop runs 4 stages per turn
     const long blocks = static_cast<long>(max_chunks) * a.n_tiles;
     if (blocks <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(blocks)), blk(kTThreads);
