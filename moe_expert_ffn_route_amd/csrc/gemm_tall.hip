@@ -177,30 +177,40 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
     // block, the MFMA lane order) three stages ahead: at stage s a thread
     // issues its copies of stage s + 3 into the buffer stage s - 1 used
     // (every wave finished reading it before the last barrier), runs stage
-    // s's MFMAs, waits until its copies of stage s + 1 have landed (the four
+    // s's MFMAs, waits until its copies of stage s + 1 have landed (the
     // copies of stages s + 2 and s + 3 may still be in flight) and passes a
     // barrier. Copies past the last stage reload it into a free buffer; all
     // copies have landed before the waves leave.
     typedef __attribute__((address_space(3))) void lds_void;
     typedef __attribute__((address_space(1))) void glb_void;
-    static_assert(kTLoadsA == 1 && kTLoadsW == 1 && kTSteps == 1, "two copies per thread and stage");
+    static_assert(kTSteps == 1, "one K step per stage");
+    // s_waitcnt immediate: vmcnt(n) (bits 3:0 and 15:14), expcnt 7 (no wait,
+    // bits 6:4), lgkmcnt(0) (bits 11:8)
+    constexpr int kCopies = kTLoadsA + kTLoadsW;  // per thread and stage
+    static_assert(2 * kCopies <= 63, "vmcnt range");
+    constexpr int kWaitNext = (2 * kCopies & 15) | ((2 * kCopies >> 4) << 14) | (7 << 4);
     auto dma = [&](int s, int8_t *buf) {
-        __builtin_amdgcn_global_load_lds((glb_void *)(asrc[0] + s * 64), (lds_void *)(buf + wave * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((glb_void *)(wsrc[0] + static_cast<size_t>(s) * wstep),
-                                         (lds_void *)(buf + kTAStage + wave * 1024), 16, 0, PACKED ? 2 : 0);  // 2: nt
+#pragma unroll
+        for (int i = 0; i < kTLoadsA; ++i)
+            __builtin_amdgcn_global_load_lds((glb_void *)(asrc[i] + s * 64),
+                                             (lds_void *)(buf + (i * kTWaves + wave) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kTLoadsW; ++i)
+            __builtin_amdgcn_global_load_lds((glb_void *)(wsrc[i] + static_cast<size_t>(s) * wstep),
+                                             (lds_void *)(buf + kTAStage + (i * kTWaves + wave) * 1024), 16, 0,
+                                             PACKED ? 2 : 0);  // 2: nt
     };
     auto step = [&](int s, const int8_t *cur, int8_t *freebuf) {
         dma(min(s + 3, n_stages - 1), freebuf);
         __builtin_amdgcn_sched_barrier(0);  // issue the copies before the stage's LDS reads
         compute(cur);
-        // s_waitcnt fields: vmcnt bits 3:0, expcnt 6:4 (7: no wait), lgkmcnt 11:8
-        __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(kWaitNext);  // stage s + 1's copies have landed, and this wave's LDS reads
         __builtin_amdgcn_s_barrier();
     };
     dma(0, s_d0);
     dma(1, s_d1);
     dma(2, s_d2);
-    __builtin_amdgcn_s_waitcnt(0x0074);
+    __builtin_amdgcn_s_waitcnt(kWaitNext);
     __builtin_amdgcn_s_barrier();
     for (int s = 0; s < n_stages; s += 4) {  // n_stages is a multiple of 4
         step(s, s_d0, s_d3);
