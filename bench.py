@@ -176,10 +176,12 @@ def mfma_peak_on_device():
             "tops": round(cus * khz.value * 1e3 * MFMA_I8_OPS_PER_CLK_CU / 1e12, 1)}
 
 
-def gemm1_traffic(workload, mx=False):
-    """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE / WRITE_SIZE scaled by a plain copy's readings), or None when
-    there is none for this workload or the GEMM sources changed since."""
+def gemm_traffic(workload, kernel_prefix):
+    """HBM bytes per launch of the kernel whose name starts with
+    `kernel_prefix`, from the committed rocprofv3 counter summary of this
+    workload (read requests counted by size, 32 / 64 / 128 bytes; write
+    bytes from WRITE_SIZE), or None when there is none or when a source file
+    it lists has changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"gemm_hbm_traffic__{workload}.md")
     if not os.path.exists(path):
@@ -192,15 +194,27 @@ def gemm1_traffic(workload, mx=False):
     if rec is None:
         return None
     h = hashlib.sha256()
-    for name in ("gemm_mx.hip" if mx else "gemm.hip", "internal.h", "abi.hip"):
+    for name in rec.get("sources", []):
         with open(os.path.join(ROOT, "moe_expert_ffn_route_amd", "csrc", name), "rb") as f:
             h.update(f.read())
-    if h.hexdigest() != rec.get("source_sha256"):
+    if not rec.get("sources") or h.hexdigest() != rec.get("source_sha256"):
         return None
     for k, v in rec["kernels"].items():
-        if k.startswith("void gemm_mx_kernel<1," if mx else "void gemm_kernel<1,"):
+        if k.startswith(kernel_prefix):
             return int(v["read_bytes"] + v["write_bytes"])
     return None
+
+
+def gemm1_kernel_prefix(case, mx):
+    """Name prefix of the GEMM1 kernel the library picks for this batch."""
+    if mx:
+        return "void gemm_mx_kernel<1,"
+    s = case.spec
+    if s.T <= 16 or getattr(s, "quant_group", 0):
+        return "void gemm_kernel<1,"
+    if s.T >= 256 and s.T * s.K // s.ep_size >= 256 * s.E_loc:
+        return "void gemm_tall_kernel<1,"
+    return "void gemm_wide_kernel<1,"
 
 
 def host_cpu_model() -> str:
@@ -214,18 +228,157 @@ def host_cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(case, budget_s=12.0, max_reps=40, tokens=None):
-    """The CPU oracle as it stands, single-threaded, on the same batch (or on
-    `tokens` of it)."""
+def cpu_baseline(case, budget_s=12.0, max_reps=40, tokens=None, threads=1):
+    """The CPU oracle as it stands, on the same batch (or on `tokens` of it):
+    single-threaded, or with the tokens split over `threads` host threads
+    (each running the unchanged single-threaded C forward on its subset).
+    Returns (mean µs per run, runs, output of the last run)."""
     import oracle  # test infrastructure: only this leg of the benchmark uses it
     oracle.lib()
     times = []
+    out = None
     t_end = time.perf_counter() + budget_s
     while len(times) < max_reps and (not times or time.perf_counter() < t_end):
         t0 = time.perf_counter()
-        oracle.forward(case, tokens=tokens)
+        out = oracle.forward(case, tokens=tokens, threads=threads)
         times.append(time.perf_counter() - t0)
-    return float(np.mean(times)) * 1e6, len(times)
+    return float(np.mean(times)) * 1e6, len(times), out
+
+
+class Leg:
+    """Resident inputs of one workload: weight copies (shared with another leg
+    where the model is the same), activations, and a Runner."""
+
+    def __init__(self, case, layers, dims):
+        self.case, self.layers, self.dims = case, layers, dims
+        self.runner = moe.Runner(dims)
+
+
+def measure(leg, steps, warmup, stream, fence_free, kernel_events=True, graphs=None):
+    """Time `steps` forwards of one leg (step i on weight copy i % copies).
+    Returns µs per step, GEMM1 / GEMM2 kernel durations from events bound to
+    their launches, per-stage times (marker events, separate pass) and the
+    per-step distribution (one marker per step boundary, separate pass)."""
+    runner, layers = leg.runner, leg.layers
+    n_ev = len(binding.STAGES) + 1
+    events = [[TimingEvent(fence_free) for _ in range(n_ev)] for _ in range(steps)]
+    kevents = [[TimingEvent(fence_free) for _ in range(4)] for _ in range(steps)]
+    for evs in events + kevents:
+        for e in evs:
+            e.record(stream)  # materialise the HIP event handles
+    torch.cuda.synchronize()
+    # timed region: the library binds two events to the GEMM1 launch itself
+    # (its start and end); the per-stage pass below records a marker event
+    # between every two stages and binds GEMM2's pair (GEMM1 only in the timed
+    # region: each bound event costs a few µs of the step)
+    k_arrays = [(ctypes.c_void_p * 4)(evs[0].cuda_event, evs[1].cuda_event, None, None) for evs in kevents]
+    k2_arrays = [(ctypes.c_void_p * 4)(None, None, evs[2].cuda_event, evs[3].cuda_event) for evs in kevents]
+    all_arrays = [(ctypes.c_void_p * n_ev)(*[e.cuda_event for e in evs]) for evs in events]
+    k_dbg = [binding.Debug(kernel_events=ctypes.cast(p, ctypes.c_void_p).value) for p in k_arrays]
+    all_dbg = [binding.Debug(stage_events=ctypes.cast(p, ctypes.c_void_p).value,
+                             kernel_events=ctypes.cast(q, ctypes.c_void_p).value)
+               for p, q in zip(all_arrays, k2_arrays)]
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            runner(layers[i % len(layers)], stream=stream)
+    torch.cuda.synchronize()
+    if graphs:
+        for i in range(warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+
+    t_start = TimingEvent(fence_free)
+    t_stop = TimingEvent(fence_free)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        t_start.record(stream)
+        for i in range(steps):
+            if graphs:
+                graphs[i % len(graphs)].replay()
+            else:
+                runner(layers[i % len(layers)], dbg=k_dbg[i] if kernel_events else None, stream=stream)
+        t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_stop) / steps
+    g1_us = None
+    if kernel_events and not graphs:
+        g1_us = float(np.mean([kevents[i][0].elapsed_time(kevents[i][1]) for i in range(steps)])) * 1e3
+
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            runner(layers[i % len(layers)], dbg=all_dbg[i], stream=stream)
+    torch.cuda.synchronize()
+    stage_us = {name: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(steps)]) * 1e3)
+                for j, name in enumerate(binding.STAGES)}
+    g2_us = float(np.mean([kevents[i][2].elapsed_time(kevents[i][3]) for i in range(steps)])) * 1e3
+    timing = "kernel-bound HIP events in the timed steps"
+    if g1_us is None:
+        g1_us = stage_us["gemm1"]
+        timing = "marker HIP events between stages (per-stage pass)"
+    timing += ", hipEventDisableSystemFence" if fence_free else ", default event flags"
+
+    bounds = [TimingEvent(fence_free) for _ in range(steps + 1)]
+    with torch.cuda.stream(stream):
+        bounds[0].record(stream)
+        for i in range(steps):
+            if graphs:
+                graphs[i % len(graphs)].replay()
+            else:
+                runner(layers[i % len(layers)], stream=stream)
+            bounds[i + 1].record(stream)
+    torch.cuda.synchronize()
+    step_samples = [bounds[i].elapsed_time(bounds[i + 1]) * 1e3 for i in range(steps)]
+    p10, p50, p90 = (float(v) for v in np.percentile(step_samples, [10, 50, 90]))
+    out = runner.output.float()
+    if not torch.isfinite(out).all():
+        raise RuntimeError("non-finite output")
+    return dict(us=ms_per_step * 1e3, ms_per_step=ms_per_step, g1_us=g1_us, g2_us=g2_us, stage_us=stage_us,
+                p=(p10, p50, p90), timing=timing, counts=runner.expert_token_nums.cpu().numpy())
+
+
+def large_batch_record(base_case, layers, wkeys, weight_layout, steps, warmup, stream, fence_free):
+    """The T = 512 half of the metric: the large-batch workload (same model as
+    the decode workload, so the resident weight copies are reused; only the
+    512 tokens' activations are generated), timed like the decode step.
+    Returns the record's fields: µs per layer, int8 TOP/s over the layer and
+    its fraction of the MFMA peak, the layer's algorithmic GB/s, and each
+    GEMM's kernel-bound duration with its algorithmic HBM bandwidth."""
+    spec4 = synth.WORKLOADS[4]
+    s1 = base_case.spec
+    assert (spec4.weight_seed, spec4.H, spec4.I, spec4.E_g, spec4.I_s) == (s1.weight_seed, s1.H, s1.I, s1.E_g, s1.I_s)
+    case4 = synth.make_case(spec4, weights=(base_case.w1, base_case.w1s, base_case.w2, base_case.w2s))
+    act = moe.upload(case4, weights={k: layers[0][k] for k in wkeys})
+    legs = [dict(act, **{k: lay[k] for k in wkeys}) for lay in layers]
+    dims4 = moe.dims_of_case(case4)
+    dims4.weight_layout = weight_layout
+    leg = Leg(case4, legs, dims4)
+    m = measure(leg, steps, warmup, stream, fence_free)
+    counts = m["counts"]
+    layer_bytes, g1_bytes, g2_bytes, touched, rows = algorithmic_bytes(case4, counts)
+    g1_ops, g2_ops = gemm_ops(case4, counts)
+    us = m["us"]
+    tops = layer_ops(case4, counts) / (us * 1e-6) / 1e12
+    return {
+        "workload": spec4.name, "tokens": spec4.T, "touched_experts": touched, "grouped_rows": rows,
+        "us_per_layer": round(us, 2),
+        "step_us_p10_p50_p90": [round(v, 2) for v in m["p"]],
+        "tops": round(tops, 1), "mfma_i8_frac": round(tops / MFMA_I8_PEAK_TOPS, 4),
+        "hbm_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
+        "hbm_frac": round(layer_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "gemm1": {"avg_us": round(m["g1_us"], 2), "algorithmic_bytes": g1_bytes,
+                  "achieved_gbps": round(g1_bytes / (m["g1_us"] * 1e-6) / 1e9, 1),
+                  "hbm_frac": round(g1_bytes / (m["g1_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                  "tops": round(g1_ops / (m["g1_us"] * 1e-6) / 1e12, 1),
+                  "traffic": gemm_traffic(spec4.name, gemm1_kernel_prefix(case4, False))},
+        "gemm2": {"avg_us": round(m["g2_us"], 2), "algorithmic_bytes": g2_bytes,
+                  "achieved_gbps": round(g2_bytes / (m["g2_us"] * 1e-6) / 1e9, 1),
+                  "hbm_frac": round(g2_bytes / (m["g2_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                  "tops": round(g2_ops / (m["g2_us"] * 1e-6) / 1e12, 1)},
+        "stage_us": {k: round(v, 2) for k, v in m["stage_us"].items()},
+        "timing": m["timing"],
+        "bound": "hbm (about 36 int8 operations per weight byte, far below the MFMA ridge of about 625)",
+    }
 
 
 def main():
@@ -253,6 +406,8 @@ def main():
     ap.add_argument("--fenced-events", action="store_true",
                     help="time with default HIP events (each record adds a system-scope cache writeback) "
                          "instead of events created with hipEventDisableSystemFence")
+    ap.add_argument("--no-large-batch", action="store_true",
+                    help="skip the T = 512 leg (large_batch_t512) of the default decode line")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the GEMM kernel events (GEMM times then come from the "
                          "per-stage pass)")
@@ -305,104 +460,37 @@ def main():
     dims.weight_layout = moe.MOE_WEIGHT_ROW_MAJOR if args.row_major else moe.MOE_WEIGHT_PACKED
     dims.weight_format = moe.MOE_WEIGHT_MXFP4 if mx else moe.MOE_WEIGHT_INT8
     dims.fuse_route_scale = int(args.fuse_route_scale)
-    runner = moe.Runner(dims)
+    leg = Leg(case, layers, dims)
+    runner = leg.runner
     stream = torch.cuda.Stream()
     fence_free = not args.fenced_events
-    n_ev = len(binding.STAGES) + 1
-    events = [[TimingEvent(fence_free) for _ in range(n_ev)] for _ in range(args.steps)]
-    kevents = [[TimingEvent(fence_free) for _ in range(4)] for _ in range(args.steps)]
-    for evs in events + kevents:
-        for e in evs:
-            e.record(stream)  # materialise the HIP event handles
-    torch.cuda.synchronize()
-    # timed region: the library binds two events to the GEMM1 launch itself
-    # (its start and end); the per-stage pass below records a marker event
-    # between every two stages and binds GEMM2's pair
-    # (GEMM1 only: each bound event costs a few µs of the step)
-    k_arrays = [(ctypes.c_void_p * 4)(evs[0].cuda_event, evs[1].cuda_event, None, None) for evs in kevents]
-    k2_arrays = [(ctypes.c_void_p * 4)(None, None, evs[2].cuda_event, evs[3].cuda_event) for evs in kevents]
-    all_arrays = [(ctypes.c_void_p * n_ev)(*[e.cuda_event for e in evs]) for evs in events]
-    k_dbg = [binding.Debug(kernel_events=ctypes.cast(p, ctypes.c_void_p).value) for p in k_arrays]
-    all_dbg = [binding.Debug(stage_events=ctypes.cast(p, ctypes.c_void_p).value,
-                             kernel_events=ctypes.cast(q, ctypes.c_void_p).value)
-               for p, q in zip(all_arrays, k2_arrays)]
-
-    log(f"[bench] warmup {args.warmup} steps")
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            runner(layers[i % len(layers)], stream=stream)
-    torch.cuda.synchronize()
-    counts = runner.expert_token_nums.cpu().numpy()
 
     graphs = []
     if args.graph:
         # one graph per weight copy; the GEMM1 events of the timed region are
         # not recorded inside graphs (stage times come from the per-stage pass)
+        with torch.cuda.stream(stream):
+            runner(layers[0], stream=stream)
+        torch.cuda.synchronize()
         for li in range(len(layers)):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
                 runner(layers[li], stream=stream)
             graphs.append(g)
         torch.cuda.synchronize()
-        for i in range(args.warmup):
-            graphs[i % len(graphs)].replay()
-        torch.cuda.synchronize()
 
-    log(f"[bench] timing {args.steps} steps")
-    t_start = TimingEvent(fence_free)
-    t_stop = TimingEvent(fence_free)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        t_start.record(stream)
-        for i in range(args.steps):
-            if graphs:
-                graphs[i % len(graphs)].replay()
-            else:
-                runner(layers[i % len(layers)], dbg=None if args.no_kernel_events else k_dbg[i], stream=stream)
-        t_stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_stop)
-    ms_per_step = total_ms / args.steps
-    g1_us = g2_us = None
-    if not args.no_kernel_events and not graphs:
-        g1_us = float(np.mean([kevents[i][0].elapsed_time(kevents[i][1]) for i in range(args.steps)])) * 1e3
-
-    log("[bench] per-stage pass")
-    with torch.cuda.stream(stream):
-        for i in range(args.steps):
-            runner(layers[i % len(layers)], dbg=all_dbg[i], stream=stream)
-    torch.cuda.synchronize()
-    stage_us = {name: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]) * 1e3)
-                for j, name in enumerate(binding.STAGES)}
-    g2_us = float(np.mean([kevents[i][2].elapsed_time(kevents[i][3]) for i in range(args.steps)])) * 1e3
-    timing = "kernel-bound HIP events in the timed steps"
-    if g1_us is None:
-        g1_us = stage_us["gemm1"]
-        timing = "marker HIP events between stages (per-stage pass)"
-    timing += ", default event flags" if args.fenced_events else ", hipEventDisableSystemFence"
-
-    log("[bench] per-step distribution pass")
-    bounds = [TimingEvent(fence_free) for _ in range(args.steps + 1)]
-    with torch.cuda.stream(stream):
-        bounds[0].record(stream)
-        for i in range(args.steps):
-            if graphs:
-                graphs[i % len(graphs)].replay()
-            else:
-                runner(layers[i % len(layers)], stream=stream)
-            bounds[i + 1].record(stream)
-    torch.cuda.synchronize()
-    step_samples = [bounds[i].elapsed_time(bounds[i + 1]) * 1e3 for i in range(args.steps)]
-    p10, p50, p90 = (float(v) for v in np.percentile(step_samples, [10, 50, 90]))
-
-    out = runner.output.float()
-    if not torch.isfinite(out).all():
-        raise RuntimeError("non-finite output")
+    log(f"[bench] warmup {args.warmup} steps, timing {args.steps} steps (three passes)")
+    m = measure(leg, args.steps, args.warmup, stream, fence_free, kernel_events=not args.no_kernel_events,
+                graphs=graphs)
+    counts = m["counts"]
+    g1_us, g2_us, stage_us, timing = m["g1_us"], m["g2_us"], m["stage_us"], m["timing"]
+    p10, p50, p90 = m["p"]
+    ms_per_step = m["ms_per_step"]
 
     layer_bytes, gemm1_bytes, gemm2_bytes, touched, rows = algorithmic_bytes(case, counts)
     us = ms_per_step * 1e3
     g1_gbs = gemm1_bytes / (g1_us * 1e-6) / 1e9
-    traffic = None if args.row_major else gemm1_traffic(spec.name, mx)
+    traffic = None if args.row_major else gemm_traffic(spec.name, gemm1_kernel_prefix(case, mx))
     tops = layer_ops(case, counts) / (us * 1e-6) / 1e12
     g1_ops, g2_ops = gemm_ops(case, counts)
     # the roofline that binds GEMM1: HBM below the ridge (peak ops / peak
@@ -414,13 +502,15 @@ def main():
         roofline = {"kernel": "gemm1_swiglu", "bound": "mfma", "achieved": round(g1_tops, 1),
                     "peak": mfma_peak, "unit": mfma_unit, "frac": round(g1_tops / mfma_peak, 4),
                     "traffic": traffic, "algorithmic_ops": g1_ops, "algorithmic_bytes": gemm1_bytes,
-                    "hbm_gbps": round(g1_gbs, 1), "avg_us": round(g1_us, 2), "timing": None}
+                    "hbm_gbps": round(g1_gbs, 1), "avg_us": round(g1_us, 2), "timing": timing}
     else:
         roofline = {"kernel": "gemm1_swiglu", "bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "algorithmic_bytes": gemm1_bytes, "avg_us": round(g1_us, 2), "timing": None}
+                    "algorithmic_bytes": gemm1_bytes, "avg_us": round(g1_us, 2), "timing": timing}
+    headline = args.config == 1 and not mx and not args.quant_group
     rec = {
-        "metric": "µs per MoE layer (T=8 decode); achieved HBM GB/s in hbm_gbps",
+        "metric": ("µs per MoE layer (T=8 decode); achieved HBM GB/s in hbm_gbps; INT8 TOP/s at T=512 in "
+                   "large_batch_t512.tops") if headline else "µs per MoE layer; achieved HBM GB/s in hbm_gbps",
         "value": round(us, 2),
         "unit": "us",
         "n_gpus": 1,
@@ -447,11 +537,15 @@ def main():
         "mfma_i8_frac": None if mx else round(tops / MFMA_I8_PEAK_TOPS, 5),
         "mfma_i8_peak_derived": mfma_peak_on_device(),
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},  # separate pass, every stage bracketed
-        "roofline": dict(roofline, timing=timing),
+        "roofline": roofline,
         "gemm2": {"achieved": round(gemm2_bytes / (g2_us * 1e-6) / 1e9, 1), "unit": "GB/s",
                   "algorithmic_bytes": gemm2_bytes, "avg_us": round(g2_us, 2),
                   "tops": round(g2_ops / (g2_us * 1e-6) / 1e12, 1)},
     }
+    if headline and not args.no_large_batch and not graphs:
+        log("[bench] large-batch leg (T = 512, same resident weights)")
+        rec["large_batch_t512"] = large_batch_record(case, layers, wkeys, dims.weight_layout, args.steps,
+                                                     args.warmup, stream, fence_free)
     if args.no_cpu_baseline:
         rec["cpu_baseline"] = None
     else:
@@ -459,16 +553,32 @@ def main():
         if mx:
             # the FP4 oracle is slower per product: two tokens, scaled to the batch
             n_tok = min(2, spec.T)
-            cpu_us, reps = cpu_baseline(case, tokens=list(range(n_tok)))
+            cpu_us, reps, _ = cpu_baseline(case, tokens=list(range(n_tok)))
             cpu_us *= spec.T / max(1, n_tok)
             sample = (f"tokens 0-{n_tok - 1} of this workload (routing of the whole batch), {reps} runs, "
                       f"time scaled by {spec.T}/{n_tok} to the batch, single-threaded C oracle")
         else:
-            cpu_us, reps = cpu_baseline(case)
+            cpu_us, reps, ref1 = cpu_baseline(case)
             sample = f"the full batch of this workload, {reps} runs, single-threaded C oracle"
         rec["cpu_baseline"] = {"value": round(cpu_us, 1), "unit": "us", "cores": 1, "kind": "oracle",
                                "sample": sample, "host_cpu": host_cpu_model(),
                                "host_threads_available": os.cpu_count()}
+        if not mx:
+            # the same oracle on every host thread: tokens split over threads
+            # (one token per thread at most, so a batch of T tokens uses at
+            # most T threads); bit-identical to the single-threaded run
+            n_thr = max(1, min(os.cpu_count() or 1, spec.T))
+            cpu_all, reps_all, ref_all = cpu_baseline(case, budget_s=6.0, threads=n_thr)
+            for k in ("output", "share_output", "expert_token_nums"):
+                a, b = ref1[k], ref_all[k]
+                if (a is None) != (b is None) or (a is not None and not np.array_equal(a, b)):
+                    raise RuntimeError(f"threaded oracle differs from the single-threaded run in {k}")
+            rec["cpu_baseline_all_cores"] = {
+                "value": round(cpu_all, 1), "unit": "us", "cores": n_thr, "kind": "oracle",
+                "sample": (f"the full batch of this workload, {reps_all} runs, tokens split over {n_thr} host "
+                           "threads, each running the single-threaded C oracle; output bit-identical to the "
+                           "single-threaded run"),
+                "host_cpu": host_cpu_model(), "host_threads_available": os.cpu_count()}
     print(json.dumps(rec), flush=True)
 
 

@@ -67,7 +67,9 @@ Layout make_layout(const moe_w8a8_dims_t *d) {
     // 16 * E_loc), else 16 (measured on MI355X with FP4 weights: 32-row items
     // take the T = 512 layer from 996 to 859 us but slow the skewed T = 64
     // layer from 305 to 328 us).
-    const bool tall = T >= kTallMinRows && TK >= static_cast<size_t>(kTallMinRows) * E;
+    // (the routed rows this rank can expect are T*K / ep_rank_size, as for
+    // the other item-size rules)
+    const bool tall = T >= kTallMinRows && TK / d->ep_rank_size >= static_cast<size_t>(kTallMinRows) * E;
     const bool mx = d->weight_format == MOE_WEIGHT_MXFP4;
     const bool grp = d->quant_mode == 2;
     const bool two_tiles = T > kChunkRowsSmall && TK / d->ep_rank_size >= static_cast<size_t>(kTileN) * E;

@@ -22,8 +22,8 @@ constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kWideTiles = MOE_WIDE_MT;
 constexpr int kChunkRowsSmall = 16;
 constexpr int kChunkRowsLarge = 16 * MOE_WIDE_MT;
-// When the routed experts average at least kTallMinRows rows (T * K >=
-// kTallMinRows * E_loc), every group is cut into chunks of kChunkRowsTall rows
+// When the routed experts can average at least kTallMinRows rows (T * K /
+// ep_rank_size >= kTallMinRows * E_loc), every group is cut into chunks of kChunkRowsTall rows
 // instead: tall work items (gemm_tall.hip), each covering kTallPairs pairs of
 // 16-row weight tiles with both operands staged through LDS.
 #ifndef MOE_TALL_MIN_ROWS
@@ -70,7 +70,7 @@ struct RouteArgs {
     int32_t *row_of_pair;  // [T*K]
     int32_t *row_token;    // [rows_max]
     int32_t *row_group;    // [rows_max]
-    int4 *chunks;          // [max_chunks] (group, first row, rows | count << 8, index)
+    int4 *chunks;          // [max_chunks] (group, first row, rows | count << kChunkCountShift, index)
     int32_t *meta;         // [kMetaWords]
     int32_t *dbg_shared_token;  // [T] or null
 };

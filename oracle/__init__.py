@@ -211,8 +211,21 @@ def f32_to_bf16(f: float) -> int:
     return lib().moe_oracle_f32_to_bf16(f)
 
 
-def forward(case, tokens: Optional[Sequence[int]] = None, trace: bool = False) -> dict:
-    """Run the oracle on a synth.Case. tokens=None computes every output row."""
+def default_threads() -> int:
+    """Host threads for token-split oracle runs (at most 16)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def forward(case, tokens: Optional[Sequence[int]] = None, trace: bool = False, threads: int = 1) -> dict:
+    """Run the oracle on a synth.Case. tokens=None computes every output row.
+
+    threads > 1 splits the tokens over that many host threads, each running
+    the unchanged single-threaded C forward on its own token subset (ctypes
+    releases the GIL). The C forward writes only the output and trace rows of
+    the tokens it is given, so the threads share the per-row buffers (they
+    write disjoint rows) and each gets its own routing outputs, which are
+    identical and taken from the first thread. The result equals the
+    single-threaded run bit for bit."""
     s = case.spec
     d = _spec_dims(s)
     T, H, K, E = s.T, s.H, s.K, s.E_loc
@@ -220,26 +233,24 @@ def forward(case, tokens: Optional[Sequence[int]] = None, trace: bool = False) -
     rows_max = T * K + T
     out = np.zeros((T, H), np.uint16)
     sout = np.zeros((T, H), np.uint16) if s.I_s else None
-    etn = np.zeros(E, np.int32)
-    tr = None
-    res = {}
-    if trace:
-        res = dict(sorted_pair=np.full(max(1, T * K), -1, np.int32),
-                   row_of_pair=np.full(max(1, T * K), -1, np.int32),
-                   offsets=np.zeros(E + 1, np.int32), shared_token=np.full(max(1, T), -1, np.int32),
-                   num_rows=np.zeros(3, np.int32),
-                   q_x=np.zeros((rows_max, H), np.int8), xs=np.zeros(rows_max, np.float32),
-                   acc1=np.zeros((rows_max, 2 * Imax), np.int32), h=np.zeros((rows_max, Imax), np.float32),
-                   q_h=np.zeros((rows_max, Imax), np.int8), hs=np.zeros(rows_max, np.float32),
-                   acc2=np.zeros((rows_max, H), np.int32), z=np.zeros((rows_max, H), np.uint16))
-        tr = _Trace(**{k: _p(v) for k, v in res.items()})
-    sub = None if tokens is None else np.ascontiguousarray(tokens, np.int32)
     mx = getattr(s, "weight_format", "int8") == "mxfp4"
     G = getattr(s, "quant_group", 0)
-    if trace and G:  # one scale per row and group; fp32 GEMM outputs in acc1 / acc2
-        res["xs"] = np.zeros((rows_max, H // G), np.float32)
-        res["hs"] = np.zeros((rows_max, Imax // G), np.float32)
-        tr = _Trace(**{k: _p(v) for k, v in res.items()})
+    routing_keys = ("sorted_pair", "row_of_pair", "offsets", "shared_token", "num_rows")
+
+    def routing_bufs():
+        return dict(sorted_pair=np.full(max(1, T * K), -1, np.int32),
+                    row_of_pair=np.full(max(1, T * K), -1, np.int32),
+                    offsets=np.zeros(E + 1, np.int32), shared_token=np.full(max(1, T), -1, np.int32),
+                    num_rows=np.zeros(3, np.int32))
+
+    rows = {}
+    if trace:
+        rows = dict(q_x=np.zeros((rows_max, H), np.int8),
+                    xs=np.zeros((rows_max, H // G), np.float32) if G else np.zeros(rows_max, np.float32),
+                    acc1=np.zeros((rows_max, 2 * Imax), np.int32), h=np.zeros((rows_max, Imax), np.float32),
+                    q_h=np.zeros((rows_max, Imax), np.int8),
+                    hs=np.zeros((rows_max, Imax // G), np.float32) if G else np.zeros(rows_max, np.float32),
+                    acc2=np.zeros((rows_max, H), np.int32), z=np.zeros((rows_max, H), np.uint16))
     if mx:
         keep = [_c(case.x, np.uint16), _c(case.expert_ids, np.int32), _c(case.expert_scales, np.float32),
                 _c(case.w1, np.uint8), _c(case.w1b, np.uint8), _c(case.w1s, np.float32),
@@ -254,10 +265,31 @@ def forward(case, tokens: Optional[Sequence[int]] = None, trace: bool = False) -
                 _c(case.sw1, np.int8), _c(case.sw1s, np.float32), _c(case.sw2, np.int8), _c(case.sw2s, np.float32),
                 _c(case.smooth, np.float32), _c(case.share_smooth, np.float32), _c(case.mask, np.uint8)]
         fwd = lib().moe_oracle_forward
-    rc = fwd(ctypes.byref(d), *[_p(a) for a in keep], _p(sub), 0 if sub is None else len(sub), _p(out), _p(sout),
-             _p(etn), ctypes.byref(tr) if tr is not None else None)
-    if rc != 0:
-        raise RuntimeError(f"oracle forward failed: {rc}")
+
+    def run(sub):
+        """One C forward over the token subset `sub` (None = all tokens)."""
+        etn = np.zeros(E, np.int32)
+        rb = routing_bufs() if trace else {}
+        tr = _Trace(**{k: _p(v) for k, v in {**rb, **rows}.items()}) if trace else None
+        rc = fwd(ctypes.byref(d), *[_p(a) for a in keep], _p(sub), 0 if sub is None else len(sub), _p(out),
+                 _p(sout), _p(etn), ctypes.byref(tr) if tr is not None else None)
+        if rc != 0:
+            raise RuntimeError(f"oracle forward failed: {rc}")
+        return etn, rb
+
+    sub = None if tokens is None else np.ascontiguousarray(tokens, np.int32)
+    toks = np.arange(T, dtype=np.int32) if sub is None else sub
+    n_thr = max(1, min(int(threads), len(toks)))
+    if n_thr == 1:
+        etn, rb = run(sub)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        parts = [np.ascontiguousarray(toks[i::n_thr]) for i in range(n_thr)]  # every token has K pairs
+        with ThreadPoolExecutor(n_thr) as ex:
+            results = list(ex.map(run, parts))
+        etn, rb = results[0]
+    res = dict(rb)
+    res.update(rows)
     res.update(output=out, share_output=sout, expert_token_nums=etn)
     if trace:
         P, Ta = int(res["num_rows"][0]), int(res["num_rows"][1])

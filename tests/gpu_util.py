@@ -7,9 +7,12 @@ Tolerances (checked in compare()):
   - acc1 (GEMM1 int32): bit-exact
   - h (SwiGLU, fp32): relative 1e-5 (the GPU's expf may differ from the host
     libm's in the last place)
-  - q_h: differs by at most 1 on at most 0.1 % of elements; hs relative 1e-5
-  - acc2 (GEMM2 int32) and z (bf16): bit-exact on every row whose q_h and hs
-    equal the oracle's
+  - q_h, hs: bit-exact against the oracle's quantisation of the GPU's own h;
+    against the oracle's own trace q_h differs by at most 1 on at most 0.1 %
+    of elements and hs by relative 1e-5
+  - acc2 (GEMM2 int32) and z (bf16): bit-exact on every row, from the GPU's
+    own q_h and hs (and against the oracle's trace on every row whose q_h
+    and hs equal the oracle's)
   - output / share_output: max |gpu - ref| <= 2e-2 * max |ref| and
     sum |gpu - ref| / sum |ref| <= 5e-3
 """
@@ -109,8 +112,61 @@ def _routing_rows(case, gpu, ref, tokens):
     return np.array(sorted(rows), dtype=np.int64), toks
 
 
+def _row_experts(case, gpu, rows, P):
+    """Group index of each grouped row: the local expert of a routed row (from
+    the GPU's own sorted_pair, which is checked bit-exactly first), E_loc for a
+    shared row."""
+    s = case.spec
+    base = s.ep_rank * s.E_loc
+    sp = gpu["sorted_pair"]
+    ids = case.expert_ids.reshape(-1)
+    return np.array([int(ids[sp[r]]) - base if r < P else s.E_loc for r in rows], dtype=np.int64)
+
+
+def _gemm2_own_inputs(case, gpu, rows, P):
+    """GEMM2 of every grouped row on the GPU's own requantised input: acc2 must
+    equal the exact product of the GPU's q_h row and W2 (float64 sums of int8
+    products are exact: |acc| <= I * 127^2 < 2^53), and z must equal
+    bf16((float(acc2) * w2s) * row scale) with the GPU's hs (times the pair's
+    routing weight, rounded once, with the fused route scale). Returns the
+    number of rows checked."""
+    s = case.spec
+    groups = _row_experts(case, gpu, rows, P)
+    qh, hs = gpu["q_h"], gpu["hs"].astype(np.float32)
+    w_pair = case.expert_scales.reshape(-1).astype(np.float32)
+    for g in np.unique(groups):
+        rg = rows[groups == g]
+        if g < s.E_loc:
+            n, W, ws = s.I, case.w2[g], case.w2s[g]
+        else:
+            n, W, ws = s.I_s, case.sw2, case.sw2s
+        exact = qh[rg, :n].astype(np.float64) @ W.astype(np.float64).T
+        assert np.abs(exact).max(initial=0) < 2 ** 31
+        exact = exact.astype(np.int64)
+        got = gpu["acc2"][rg].astype(np.int64)
+        bad = np.nonzero(~np.all(got == exact, axis=1))[0]
+        assert bad.size == 0, f"acc2 row {int(rg[bad[0]])} (group {g}) differs from q_h x W2"
+        rs = hs[rg]
+        if s.fuse_route_scale and g < s.E_loc:
+            rs = (rs * w_pair[gpu["sorted_pair"][rg]]).astype(np.float32)
+        y = exact.astype(np.int32).astype(np.float32) * ws.astype(np.float32)[None, :]
+        y = (y * rs[:, None]).astype(np.float32)
+        zexp = synth.f32_to_bf16_bits(y)
+        bad = np.nonzero(~np.all(gpu["z"][rg] == zexp, axis=1))[0]
+        assert bad.size == 0, f"z row {int(rg[bad[0]])} (group {g}) is not bf16((acc2 * w2s) * hs)"
+    return len(rows)
+
+
 def compare(case, gpu, ref, tokens=None):
-    """Stage-by-stage comparison. `ref` is oracle.forward(case, tokens, trace=True)."""
+    """Stage-by-stage comparison. `ref` is oracle.forward(case, tokens, trace=True).
+
+    Every grouped row of the computed tokens is checked at every stage: q_x,
+    xs, acc1 against the oracle bit for bit; h against the oracle to
+    relative 1e-5; q_h / hs bit for bit against the oracle's quantisation of
+    the GPU's own h, and within 1 LSB of the oracle's trace; acc2 and z bit
+    for bit from the GPU's own q_h / hs (where those equal the oracle's, also
+    against the oracle's own acc2 and z); outputs within the block's
+    tolerance."""
     s = case.spec
     P = ref["P"]
     rows, toks = _routing_rows(case, gpu, ref, tokens)
@@ -125,26 +181,37 @@ def compare(case, gpu, ref, tokens=None):
         hmask = np.arange(Imax)[None, :] < inter[:, None]
         hg, hr = gpu["h"][rows][hmask], ref["h"][rows][hmask]
         assert np.all(np.abs(hg - hr) <= 1e-5 * np.abs(hr) + 1e-30), "h"
+        # requantisation on the GPU's own h: the oracle's quantiser, bit for bit
+        for r, n in zip(rows, inter):
+            q_exp, hs_exp = oracle.quant_row(gpu["h"][r, :n], s.eps)
+            assert np.array_equal(gpu["q_h"][r, :n], q_exp), f"q_h row {r} is not the quantisation of its h"
+            assert gpu["hs"][r] == hs_exp, f"hs row {r} is not the scale of its h"
         dq = np.abs(gpu["q_h"][rows].astype(int) - ref["q_h"][rows].astype(int))[hmask]
         assert dq.max(initial=0) <= 1, "q_h off by more than 1"
         frac = (dq > 0).mean() if dq.size else 0.0
         assert frac <= 1e-3, f"q_h differs on {frac:.2%}"
         assert np.all(np.abs(gpu["hs"][rows] - ref["hs"][rows]) <= 1e-5 * ref["hs"][rows])
+        checked = _gemm2_own_inputs(case, gpu, rows, P)
         same = [r for r, n in zip(rows, inter)
                 if np.array_equal(gpu["q_h"][r, :n], ref["q_h"][r, :n]) and gpu["hs"][r] == ref["hs"][r]]
         for r in same:
             assert np.array_equal(gpu["acc2"][r], ref["acc2"][r]), f"acc2 row {r}"
             assert np.array_equal(gpu["z"][r], ref["z"][r]), f"z row {r}"
-        stats.update(rows=len(rows), rows_exact_qh=len(same), qh_diff_frac=float(frac))
+        stats.update(rows=len(rows), rows_gemm2_checked=checked, rows_exact_qh=len(same),
+                     qh_diff_frac=float(frac))
     stats["output"] = out_close(gpu["output"][toks], ref["output"][toks], "output")
     if s.I_s:
         stats["share_output"] = out_close(gpu["share_output"][toks], ref["share_output"][toks], "share_output")
     return stats
 
 
-def check(case, tokens=None, tensors=None, **kw):
+def check(case, tokens=None, tensors=None, ref=None, **kw):
+    """Run the GPU path and compare it with the oracle (computed here on the
+    host's threads unless `ref` passes an earlier oracle run of the same
+    case and tokens)."""
     gpu = run_gpu(case, tensors=tensors, **kw)
-    ref = oracle.forward(case, tokens=tokens, trace=True)
+    if ref is None:
+        ref = oracle.forward(case, tokens=tokens, trace=True, threads=oracle.default_threads())
     return compare(case, gpu, ref, tokens), gpu, ref
 
 
@@ -175,6 +242,15 @@ def _e4m3_step(c):
     return np.where(c & 0x80, -m, m)
 
 
+def _map_rows(fn, rows):
+    """fn over every grouped row on the host's threads (the oracle's routines
+    and numpy's kernels release the GIL); the first failing row's assertion
+    propagates."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(oracle.default_threads()) as ex:
+        return list(ex.map(fn, [int(r) for r in rows]))
+
+
 def _mx_acc_check(got, codes, data, bscale, what):
     exact = oracle.gemm_mx(codes[None, :], data, bscale)[0]
     mag = oracle.gemm_mx((codes & 0x7F)[None, :], data & 0x77, bscale)[0]
@@ -195,9 +271,9 @@ def compare_mx(case, gpu, ref, tokens=None):
     acc1 = gpu["acc1"].view(np.float32)
     acc2 = gpu["acc2"].view(np.float32)
     base = s.ep_rank * s.E_loc
-    worst = 0.0
-    flips = []
-    for r in rows:
+
+    def row_check(r):
+        worst = 0.0
         if r < P:
             p = int(gpu["sorted_pair"][r])
             e = int(case.expert_ids[p // K, p % K]) - base
@@ -222,7 +298,6 @@ def compare_mx(case, gpu, ref, tokens=None):
         assert gpu["hs"][r] == np.float32(hs_exp), f"hs row {r}"
         d = np.abs(_e4m3_step(qh[r, :n]) - _e4m3_step(ref["q_h"][r, :n]))
         assert d.max(initial=0) <= 1, f"q_h row {r} more than one E4M3 step from the oracle's"
-        flips.append(float((d > 0).mean()))
         a2 = acc2[r, :H]
         worst = max(worst, _mx_acc_check(a2, qh[r, :n], w2, w2b, f"acc2 row {r}"))
         rs2 = np.float32(gpu["hs"][r])
@@ -230,6 +305,11 @@ def compare_mx(case, gpu, ref, tokens=None):
             rs2 = np.float32(rs2 * np.float32(rw))
         z_exp = synth.f32_to_bf16_bits((a2 * w2s) * rs2)
         assert np.array_equal(gpu["z"][r], z_exp), f"z row {r}"
+        return worst, float((d > 0).mean())
+
+    res = _map_rows(row_check, rows)
+    worst = max((w for w, _ in res), default=0.0)
+    flips = [f for _, f in res]
     stats.update(rows=len(rows), acc_err_over_sum=worst, qh_step_frac=max(flips, default=0.0))
     stats["output"] = out_close(gpu["output"][toks], ref["output"][toks], "output")
     if s.I_s:
@@ -239,7 +319,7 @@ def compare_mx(case, gpu, ref, tokens=None):
 
 def check_mx(case, tokens=None, tensors=None, **kw):
     gpu = run_gpu(case, tensors=tensors, **kw)
-    ref = oracle.forward(case, tokens=tokens, trace=True)
+    ref = oracle.forward(case, tokens=tokens, trace=True, threads=oracle.default_threads())
     return compare_mx(case, gpu, ref, tokens), gpu, ref
 
 
@@ -279,8 +359,9 @@ def compare_group(case, gpu, ref, tokens=None):
     acc1 = gpu["acc1"].view(np.float32)
     acc2 = gpu["acc2"].view(np.float32)
     base = s.ep_rank * s.E_loc
-    worst, flips = 0.0, []
-    for r in rows:
+
+    def row_check(r):
+        worst = 0.0
         if r < P:
             p = int(gpu["sorted_pair"][r])
             e = int(case.expert_ids[p // K, p % K]) - base
@@ -299,11 +380,15 @@ def compare_group(case, gpu, ref, tokens=None):
         assert np.array_equal(gpu["hs"][r, :n // G], hs_exp), f"hs row {r}"
         d = np.abs(gpu["q_h"][r, :n].astype(int) - ref["q_h"][r, :n].astype(int))
         assert d.max(initial=0) <= 1, f"q_h row {r} more than 1 from the oracle's"
-        flips.append(float((d > 0).mean()))
         y2 = acc2[r, :H]
         worst = max(worst, _group_gemm_check(y2, gpu["q_h"][r, :n], gpu["hs"][r, :n // G], w2, w2s, G,
                                              f"acc2 row {r}"))
         assert np.array_equal(gpu["z"][r], synth.f32_to_bf16_bits(y2)), f"z row {r}"
+        return worst, float((d > 0).mean())
+
+    res = _map_rows(row_check, rows)
+    worst = max((w for w, _ in res), default=0.0)
+    flips = [f for _, f in res]
     stats = dict(rows=len(rows), acc_err_over_bound=worst, qh_diff_frac=max(flips, default=0.0))
     stats["output"] = out_close(gpu["output"][toks], ref["output"][toks], "output")
     if s.I_s:
@@ -313,5 +398,5 @@ def compare_group(case, gpu, ref, tokens=None):
 
 def check_group(case, tokens=None, tensors=None, **kw):
     gpu = run_gpu(case, tensors=tensors, **kw)
-    ref = oracle.forward(case, tokens=tokens, trace=True)
+    ref = oracle.forward(case, tokens=tokens, trace=True, threads=oracle.default_threads())
     return compare_group(case, gpu, ref, tokens), gpu, ref

@@ -9,7 +9,8 @@ group path takes (8, 4, 2 and 1 waves; a batch of whole groups, or one group
 per batch over several passes), 16- and 32-row items with several chunks per
 expert, masks, smooth scales, an EP share, a shared expert with a different
 intermediate (two GEMM2 launches), T = 0 / 1, and the full shapes of the
-decode and T = 512 workloads on samples of their tokens.
+decode workload (every token) and of the T = 512 workload (every other
+token).
 """
 import numpy as np
 import pytest
@@ -60,10 +61,12 @@ CASES = {
     "scale_stride_34": (spec(T=5, H=256, I=4096, I_s=4352, E_g=2, K=1, seed=510), None),
     "t1": (spec(T=1, I_s=512, seed=508), None),
     "t0": (spec(T=0, I_s=256, seed=509), None),
-    # the decode workload's shape with 128-element groups (two tokens checked)
-    "decode_full_shape": (spec(T=8, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1235), [1, 6]),
-    # the large-batch workload's shape (two-tile items; two tokens checked)
-    "t512_full_shape": (spec(T=512, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1238, wseed=1235), [7, 300]),
+    # the decode workload's shape with 128-element groups (every token)
+    "decode_full_shape": (spec(T=8, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1235), None),
+    # the large-batch workload's shape (two-tile items): every other token,
+    # 2304 grouped rows
+    "t512_full_shape": (spec(T=512, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1238, wseed=1235),
+                        list(range(1, 512, 2))),
 }
 
 

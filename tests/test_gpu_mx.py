@@ -10,8 +10,8 @@ per wave; 1-, 2- and 4-step batches over several passes), 16-row items
 (decode) and 32-row items with several chunks per expert (batches above 16
 tokens), masks, smooth scales, an expert-parallel share, a shared expert
 whose intermediate differs (two GEMM2 launches), the fused route scale,
-T = 0 and T = 1, and the full shapes of the decode and T = 512 workloads on
-samples of their tokens.
+T = 0 and T = 1, and the full shapes of the decode workload (every token) and
+of the T = 512 workload (32 tokens spread over the batch).
 """
 import numpy as np
 import pytest
@@ -59,10 +59,13 @@ CASES = {
     "t0": (spec(T=0, I_s=256, seed=309), None),
     "all_masked": (spec(T=6, I_s=256, active=0, seed=310), None),
     # the decode workload's shape: T 8, H 4096, I 2048, 256 experts, top-8,
-    # shared expert 2048 (two tokens through the oracle)
-    "decode_full_shape": (spec(T=8, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1235), [2, 5]),
-    # the large-batch workload's shape (two-tile items; two tokens checked)
-    "t512_full_shape": (spec(T=512, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1238, wseed=1235), [3, 400]),
+    # shared expert 2048 (every token through the oracle)
+    "decode_full_shape": (spec(T=8, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1235), None),
+    # the large-batch workload's shape (two-tile items): 32 tokens spread over
+    # the batch through the oracle (the FP4 oracle decodes every code per
+    # product, about 0.8 s per grouped row on one host thread)
+    "t512_full_shape": (spec(T=512, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1238, wseed=1235),
+                        list(range(3, 512, 16))),
 }
 
 

@@ -5,9 +5,9 @@ Small cases run the whole oracle; they span several MFMA row tiles, several
 64-row chunks per expert, ragged tails, masks, expert-parallel shares, smooth
 scales, a shared expert whose intermediate differs from the routed one, and
 the degenerate cases (T = 0, T = 1, every token masked, ids out of range).
-The five named workloads run at full size; the oracle then computes a sample
-of tokens (all of them where it finishes in seconds) and the routing outputs
-in full.
+The five named workloads (and the compute-bound probe) run at full size with
+every token through the oracle, whose tokens are split over the host's
+threads.
 """
 import dataclasses
 
@@ -58,6 +58,12 @@ SMALL = {
                                          share_smooth=True, seed=115),
     "tall_skewed": spec(T=600, H=256, I=256, E_g=2, K=1, routing="zipf", zipf_s=2.0, I_s=256, seed=116),
     "tall_tail_two_tiles": spec(T=280, H=512, I=256, E_g=1, K=1, I_s=256, seed=117),
+    # expert-parallel shares of a large batch: the item size follows the rows
+    # this rank can expect (T*K / ep_rank_size), so 512 tokens over 8 experts
+    # on 4 ranks take 32-row items, and 600 tokens on 1 of 2 experts tall ones
+    "ep_share_t512_wide_items": spec(T=512, H=256, I=256, E_g=8, K=2, ep_size=4, ep_rank=3, I_s=256, seed=143),
+    "ep_share_t600_tall_items": spec(T=600, H=256, I=256, E_g=2, K=2, ep_size=2, ep_rank=0, active=580,
+                                     seed=144),
     # the routing weight folded into the GEMM2 row scale (combine only sums),
     # on each item size, with masks, an EP share, smooth scales and a split
     # GEMM2 (I_s != I)
@@ -154,13 +160,13 @@ def test_pack_layout(shape, which):
 
 
 # Size limits of the C ABI: 512 local experts, top-16, hidden and intermediate
-# 16384, and many routing rounds (32768 pairs); the oracle computes a sample of
-# tokens where the full batch would take long, the routing always in full.
+# 16384, and many routing rounds (32768 pairs); every token goes through the
+# oracle.
 LIMITS = {
     "e512_k16": (spec(T=64, H=256, I=256, E_g=512, K=16, I_s=256, seed=131), None),
     "hidden_16384": (spec(T=3, H=16384, I=256, E_g=4, K=2, I_s=256, seed=132), None),
     "inter_16384": (spec(T=3, H=256, I=16384, E_g=4, K=2, I_s=512, seed=133), None),
-    "pairs_32768": (spec(T=2048, H=256, I=256, E_g=64, K=16, active=1900, seed=134), [0, 5, 777, 2047]),
+    "pairs_32768": (spec(T=2048, H=256, I=256, E_g=64, K=16, active=1900, seed=134), None),
     "t24_hidden_16384": (spec(T=24, H=16384, I=256, E_g=4, K=2, I_s=256, seed=135), None),
     "t24_inter_16384": (spec(T=24, H=256, I=16384, E_g=4, K=2, I_s=512, seed=136), None),
 }
@@ -340,24 +346,25 @@ def weights_for(s):
     return _WEIGHTS[key]
 
 
-# tokens sampled by the oracle (None = all); 1, 3 and 4 share one set of weights
-FULL = {1: None, 3: 24, 4: 12, 2: None, 5: 6}
+# Every token of every workload goes through the oracle (split over the
+# host's threads); 1, 3 and 4 share one set of weights. Configs 1 and 4 run
+# both weight layouts against one oracle run.
+FULL = (1, 2, 3, 4, 5)
 
 
-@pytest.mark.parametrize("cfg", list(FULL))
+@pytest.mark.parametrize("cfg", FULL)
 def test_full_size_workload(cfg):
     s = synth.WORKLOADS[cfg]
-    say(f"[parity] config {cfg} {s.name}")
+    say(f"[parity] config {cfg} {s.name}: all {s.T} tokens")
     case = synth.workload_case(cfg, weights=weights_for(s))
-    n = FULL[cfg]
-    tokens = None
-    if n is not None:
-        rng = np.random.default_rng(cfg)
-        tokens = np.sort(rng.choice(s.T, n, replace=False))
-    stats, gpu, ref = check(case, tokens=tokens, packed=True)
+    ref = oracle.forward(case, trace=True, threads=oracle.default_threads())
+    say(f"[parity] config {cfg}: oracle done ({ref['P']} routed rows)")
+    stats, gpu, _ = check(case, ref=ref, packed=True)
     say(f"[parity] config {cfg} packed: {stats}")
     if cfg in (1, 4):
-        stats, gpu, ref = check(case, tokens=tokens, packed=False)
+        del gpu
+        stats, gpu, _ = check(case, ref=ref, packed=False)
         say(f"[parity] config {cfg} row-major: {stats}")
+    assert stats["rows"] == ref["P"] + (ref["T_act"] if s.I_s else 0)
     del gpu, ref
     torch.cuda.empty_cache()
