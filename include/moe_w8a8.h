@@ -65,7 +65,9 @@ typedef enum {
     MOE_ERR_INVALID_ARG = -1, /* NULL / misaligned pointer, inconsistent sizes */
     MOE_ERR_UNSUPPORTED = -2, /* legal for the operator, outside what this library runs */
     MOE_ERR_WORKSPACE = -3,   /* workspace pointer NULL or workspace_bytes too small */
-    MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+    MOE_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+    MOE_ERR_SCRATCH_LIMIT = -5 /* moe_w8a8_forward_noalloc: the call needs more
+                                  than MOE_W8A8_NOALLOC_SCRATCH_BYTES of workspace */
 } moe_status_t;
 
 /* Sizes and attributes of one call (FusedDeepMoE sec. 1.2 attributes and the
@@ -210,6 +212,50 @@ MOE_W8A8_API moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *dims,
                               int32_t *expert_token_nums,
                               void *workspace,
                               size_t workspace_bytes,
+                              const moe_w8a8_debug_t *dbg,
+                              void *stream);
+
+/*
+ * moe_w8a8_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Every other argument, the result and the
+ * errors are those of moe_w8a8_forward; the call allocates nothing (no
+ * hipMalloc, no hipFree, no allocating library routine).
+ *
+ * The workspace is a device array built into the library,
+ * MOE_W8A8_NOALLOC_SCRATCH_BYTES bytes on each GPU the library runs on, held
+ * from module load until the process ends. Its device address is looked up
+ * on the first call on each device (the device that is current at the call,
+ * which must be the stream's device). Calls whose workspace (see
+ * moe_w8a8_workspace_size) would exceed it return MOE_ERR_SCRATCH_LIMIT and
+ * launch nothing: at hidden 4096, intermediate 2048, top-8 with a shared
+ * expert, batches of up to about 128 tokens fit.
+ *
+ * All calls on one GPU share that GPU's array, so two calls that may overlap
+ * on one GPU (different streams, or different host threads without ordering)
+ * race: order them on one stream, or use moe_w8a8_forward with a workspace
+ * each. The array keeps the last call's contents; nothing needs to start at
+ * zero (every index and counter the block uses is rebuilt by each call).
+ */
+#define MOE_W8A8_NOALLOC_SCRATCH_BYTES (32u << 20)
+MOE_W8A8_API moe_status_t moe_w8a8_forward_noalloc(const moe_w8a8_dims_t *dims,
+                              const void *x,
+                              const int32_t *expert_ids,
+                              const float *expert_scales,
+                              const int8_t *gmm1_weight,
+                              const float *gmm1_weight_scale,
+                              const int8_t *gmm2_weight,
+                              const float *gmm2_weight_scale,
+                              const int8_t *share_gmm1_weight,
+                              const float *share_gmm1_weight_scale,
+                              const int8_t *share_gmm2_weight,
+                              const float *share_gmm2_weight_scale,
+                              const float *expert_smooth_scales,
+                              const float *share_smooth_scales,
+                              const uint8_t *x_active_mask,
+                              void *output,
+                              void *share_output,
+                              int32_t *expert_token_nums,
                               const moe_w8a8_debug_t *dbg,
                               void *stream);
 

@@ -18,9 +18,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_w8a8.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ERR_SCRATCH_LIMIT = -5
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MOE_W8A8_NOALLOC_SCRATCH_BYTES
 
-EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_forward", "moe_w8a8_pack_weights", "moe_w8a8_packed_mx_bytes",
-           "moe_w8a8_pack_weights_mx", "moe_w8a8_status_string")
+EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_forward", "moe_w8a8_forward_noalloc", "moe_w8a8_pack_weights",
+           "moe_w8a8_packed_mx_bytes", "moe_w8a8_pack_weights_mx", "moe_w8a8_status_string")
 MOE_WEIGHT_ROW_MAJOR, MOE_WEIGHT_PACKED = 0, 1
 MOE_WEIGHT_INT8, MOE_WEIGHT_MXFP4 = 0, 1
 MOE_PACK_GMM1, MOE_PACK_GMM2 = 1, 2
@@ -71,6 +73,8 @@ def library() -> ctypes.CDLL:
         L.moe_w8a8_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_size_t)]
         L.moe_w8a8_forward.restype = ctypes.c_int
         L.moe_w8a8_forward.argtypes = ([ctypes.POINTER(Dims)] + [P] * 18 + [ctypes.c_size_t, ctypes.POINTER(Debug), P])
+        L.moe_w8a8_forward_noalloc.restype = ctypes.c_int
+        L.moe_w8a8_forward_noalloc.argtypes = [ctypes.POINTER(Dims)] + [P] * 17 + [ctypes.POINTER(Debug), P]
         L.moe_w8a8_pack_weights.restype = ctypes.c_int
         L.moe_w8a8_pack_weights.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
         L.moe_w8a8_packed_mx_bytes.restype = ctypes.c_int
@@ -193,6 +197,25 @@ def moe_w8a8_forward(dims: Dims, x, expert_ids, expert_scales, gmm1_weight, gmm1
                                     ctypes.byref(dbg) if dbg is not None else None, stream)
     if check and rc != MOE_OK:
         raise MoeError(rc, "moe_w8a8_forward")
+    return rc
+
+
+def moe_w8a8_forward_noalloc(dims: Dims, x, expert_ids, expert_scales, gmm1_weight, gmm1_weight_scale,
+                             gmm2_weight, gmm2_weight_scale, share_gmm1_weight=None, share_gmm1_weight_scale=None,
+                             share_gmm2_weight=None, share_gmm2_weight_scale=None, expert_smooth_scales=None,
+                             share_smooth_scales=None, x_active_mask=None, output=None, share_output=None,
+                             expert_token_nums=None, dbg: Optional[Debug] = None, stream=None,
+                             check: bool = True) -> int:
+    """Call the entry point that takes no workspace (the library's built-in
+    per-device scratch array). Returns the status code; raises MoeError on
+    failure when check=True."""
+    args = [x, expert_ids, expert_scales, gmm1_weight, gmm1_weight_scale, gmm2_weight, gmm2_weight_scale,
+            share_gmm1_weight, share_gmm1_weight_scale, share_gmm2_weight, share_gmm2_weight_scale,
+            expert_smooth_scales, share_smooth_scales, x_active_mask, output, share_output, expert_token_nums]
+    rc = library().moe_w8a8_forward_noalloc(ctypes.byref(dims), *[_ptr(a) for a in args],
+                                            ctypes.byref(dbg) if dbg is not None else None, _stream(stream))
+    if check and rc != MOE_OK:
+        raise MoeError(rc, "moe_w8a8_forward_noalloc")
     return rc
 
 

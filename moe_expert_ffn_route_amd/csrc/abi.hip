@@ -8,6 +8,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe_w8a8.h"
 #include "internal.h"
 
@@ -155,21 +157,23 @@ extern "C" const char *moe_w8a8_status_string(moe_status_t s) {
         case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
         case MOE_ERR_WORKSPACE: return "workspace missing or too small";
         case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_SCRATCH_LIMIT:
+            return "the call needs more scratch than moe_w8a8_forward_noalloc's built-in buffer holds "
+                   "(use moe_w8a8_forward with a workspace)";
     }
     return "unknown status";
 }
 
-extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x, const int32_t *expert_ids,
-                                         const float *expert_scales, const int8_t *gmm1_weight,
-                                         const float *gmm1_weight_scale, const int8_t *gmm2_weight,
-                                         const float *gmm2_weight_scale, const int8_t *share_gmm1_weight,
-                                         const float *share_gmm1_weight_scale, const int8_t *share_gmm2_weight,
-                                         const float *share_gmm2_weight_scale, const float *expert_smooth_scales,
-                                         const float *share_smooth_scales, const uint8_t *x_active_mask,
-                                         void *output, void *share_output, int32_t *expert_token_nums,
-                                         void *workspace, size_t workspace_bytes, const moe_w8a8_debug_t *dbg,
-                                         void *stream) {
-    moe_status_t st = check_dims(d);
+// Host-side checks of a forward call's sizes and pointers (not the
+// workspace): nothing is launched unless this returns MOE_OK.
+static moe_status_t check_call(const moe_w8a8_dims_t *d, const void *x, const int32_t *expert_ids,
+                               const float *expert_scales, const int8_t *gmm1_weight, const float *gmm1_weight_scale,
+                               const int8_t *gmm2_weight, const float *gmm2_weight_scale,
+                               const int8_t *share_gmm1_weight, const float *share_gmm1_weight_scale,
+                               const int8_t *share_gmm2_weight, const float *share_gmm2_weight_scale,
+                               const float *expert_smooth_scales, const float *share_smooth_scales, void *output,
+                               void *share_output, int32_t *expert_token_nums) {
+    const moe_status_t st = check_dims(d);
     if (st != MOE_OK) return st;
     const bool shared = d->share_inter > 0;
     const int n_share_ptrs = (share_gmm1_weight != nullptr) + (share_gmm1_weight_scale != nullptr) +
@@ -188,7 +192,25 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
                         share_gmm1_weight_scale, share_gmm2_weight_scale, expert_token_nums};
     for (const void *p : a4)
         if (p && !aligned(p, 4)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
 
+// The block on a caller-given workspace (both forward entry points).
+static moe_status_t forward_impl(const moe_w8a8_dims_t *d, const void *x, const int32_t *expert_ids,
+                                 const float *expert_scales, const int8_t *gmm1_weight, const float *gmm1_weight_scale,
+                                 const int8_t *gmm2_weight, const float *gmm2_weight_scale,
+                                 const int8_t *share_gmm1_weight, const float *share_gmm1_weight_scale,
+                                 const int8_t *share_gmm2_weight, const float *share_gmm2_weight_scale,
+                                 const float *expert_smooth_scales, const float *share_smooth_scales,
+                                 const uint8_t *x_active_mask, void *output, void *share_output,
+                                 int32_t *expert_token_nums, void *workspace, size_t workspace_bytes,
+                                 const moe_w8a8_debug_t *dbg, void *stream) {
+    const moe_status_t st = check_call(d, x, expert_ids, expert_scales, gmm1_weight, gmm1_weight_scale, gmm2_weight,
+                                       gmm2_weight_scale, share_gmm1_weight, share_gmm1_weight_scale,
+                                       share_gmm2_weight, share_gmm2_weight_scale, expert_smooth_scales,
+                                       share_smooth_scales, output, share_output, expert_token_nums);
+    if (st != MOE_OK) return st;
+    const bool shared = d->share_inter > 0;
     const Layout L = make_layout(d);
     if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARG;
@@ -407,4 +429,72 @@ extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x
         if (c.dst && c.bytes && hipMemcpyAsync(c.dst, ws + c.off, c.bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
             return MOE_ERR_HIP;
     return MOE_OK;
+}
+
+extern "C" moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *d, const void *x, const int32_t *expert_ids,
+                                         const float *expert_scales, const int8_t *gmm1_weight,
+                                         const float *gmm1_weight_scale, const int8_t *gmm2_weight,
+                                         const float *gmm2_weight_scale, const int8_t *share_gmm1_weight,
+                                         const float *share_gmm1_weight_scale, const int8_t *share_gmm2_weight,
+                                         const float *share_gmm2_weight_scale, const float *expert_smooth_scales,
+                                         const float *share_smooth_scales, const uint8_t *x_active_mask,
+                                         void *output, void *share_output, int32_t *expert_token_nums,
+                                         void *workspace, size_t workspace_bytes, const moe_w8a8_debug_t *dbg,
+                                         void *stream) {
+    return forward_impl(d, x, expert_ids, expert_scales, gmm1_weight, gmm1_weight_scale, gmm2_weight,
+                        gmm2_weight_scale, share_gmm1_weight, share_gmm1_weight_scale, share_gmm2_weight,
+                        share_gmm2_weight_scale, expert_smooth_scales, share_smooth_scales, x_active_mask, output,
+                        share_output, expert_token_nums, workspace, workspace_bytes, dbg, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing: the workspace is a device-resident
+// array of this library. Each GPU the library runs on holds its own copy from
+// module load until the process ends. In host code `scratch` names only a
+// host-side stand-in for the symbol, never device memory: the array's device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is ever handed to kernels or copies.
+static __device__ __align__(256) unsigned char scratch[MOE_W8A8_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's `scratch` array (null on failure).
+void *scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        if (reinterpret_cast<uintptr_t>(p) % 256) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_w8a8_forward_noalloc(
+    const moe_w8a8_dims_t *d, const void *x, const int32_t *expert_ids, const float *expert_scales,
+    const int8_t *gmm1_weight, const float *gmm1_weight_scale, const int8_t *gmm2_weight,
+    const float *gmm2_weight_scale, const int8_t *share_gmm1_weight, const float *share_gmm1_weight_scale,
+    const int8_t *share_gmm2_weight, const float *share_gmm2_weight_scale, const float *expert_smooth_scales,
+    const float *share_smooth_scales, const uint8_t *x_active_mask, void *output, void *share_output,
+    int32_t *expert_token_nums, const moe_w8a8_debug_t *dbg, void *stream) {
+    const moe_status_t st = check_call(d, x, expert_ids, expert_scales, gmm1_weight, gmm1_weight_scale, gmm2_weight,
+                                       gmm2_weight_scale, share_gmm1_weight, share_gmm1_weight_scale,
+                                       share_gmm2_weight, share_gmm2_weight_scale, expert_smooth_scales,
+                                       share_smooth_scales, output, share_output, expert_token_nums);
+    if (st != MOE_OK) return st;
+    if (make_layout(d).total > static_cast<size_t>(MOE_W8A8_NOALLOC_SCRATCH_BYTES)) return MOE_ERR_SCRATCH_LIMIT;
+    void *ws = scratch_on_current_device();
+    if (!ws) return MOE_ERR_HIP;
+    return forward_impl(d, x, expert_ids, expert_scales, gmm1_weight, gmm1_weight_scale, gmm2_weight,
+                        gmm2_weight_scale, share_gmm1_weight, share_gmm1_weight_scale, share_gmm2_weight,
+                        share_gmm2_weight_scale, expert_smooth_scales, share_smooth_scales, x_active_mask, output,
+                        share_output, expert_token_nums, ws, MOE_W8A8_NOALLOC_SCRATCH_BYTES, dbg, stream);
 }

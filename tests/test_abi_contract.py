@@ -202,6 +202,54 @@ def test_pack_mx_rejects_bad_arguments(lib, data, bs, dst, g, n, k, which):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -99):
+    for code in (0, -1, -2, -3, -4, -5, -99):
         s = moe.moe_w8a8_status_string(code)
         assert isinstance(s, str) and s
+
+
+def call_noalloc(lib, dims, **over):
+    args = dict(x=FAKE, expert_ids=FAKE, expert_scales=FAKE, gmm1_weight=FAKE, gmm1_weight_scale=FAKE,
+                gmm2_weight=FAKE, gmm2_weight_scale=FAKE, share_gmm1_weight=None, share_gmm1_weight_scale=None,
+                share_gmm2_weight=None, share_gmm2_weight_scale=None, expert_smooth_scales=None,
+                share_smooth_scales=None, x_active_mask=None, output=FAKE, share_output=None,
+                expert_token_nums=FAKE)
+    args.update(over)
+    order = ["x", "expert_ids", "expert_scales", "gmm1_weight", "gmm1_weight_scale", "gmm2_weight",
+             "gmm2_weight_scale", "share_gmm1_weight", "share_gmm1_weight_scale", "share_gmm2_weight",
+             "share_gmm2_weight_scale", "expert_smooth_scales", "share_smooth_scales", "x_active_mask", "output",
+             "share_output", "expert_token_nums"]
+    d = ctypes.byref(dims) if dims is not None else None
+    return lib.moe_w8a8_forward_noalloc(d, *[args[k] for k in order], None, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x=None), binding.MOE_ERR_INVALID_ARG),
+    (dict(output=None), binding.MOE_ERR_INVALID_ARG),
+    (dict(gmm1_weight=FAKE + 4), binding.MOE_ERR_INVALID_ARG),
+    (dict(share_gmm1_weight=FAKE), binding.MOE_ERR_INVALID_ARG),
+])
+def test_noalloc_rejects_bad_arguments_before_any_hip_call(lib, over, code):
+    # argument checks come before the library touches the device
+    assert call_noalloc(lib, good_dims(), **over) == code
+    assert call_noalloc(lib, None) == binding.MOE_ERR_INVALID_ARG
+    assert call_noalloc(lib, good_dims(quant_mode=0)) == binding.MOE_ERR_UNSUPPORTED
+
+
+def test_noalloc_scratch_limit(lib):
+    # calls whose workspace exceeds the built-in array are rejected up front
+    # with their own status; the decode and 128-token EP-share shapes fit
+    big = good_dims(num_tokens=512, hidden=4096, inter=2048, topk=8, moe_expert_num=256, share_inter=2048)
+    assert moe.moe_w8a8_workspace_size(big) > binding.NOALLOC_SCRATCH_BYTES
+    share = dict(share_gmm1_weight=FAKE, share_gmm1_weight_scale=FAKE, share_gmm2_weight=FAKE,
+                 share_gmm2_weight_scale=FAKE, share_output=FAKE)
+    assert call_noalloc(lib, big, **share) == binding.MOE_ERR_SCRATCH_LIMIT
+    assert "scratch" in moe.moe_w8a8_status_string(binding.MOE_ERR_SCRATCH_LIMIT)
+    for T in (8, 128):
+        d = good_dims(num_tokens=T, hidden=4096, inter=2048, topk=8, moe_expert_num=256, share_inter=2048)
+        assert moe.moe_w8a8_workspace_size(d) <= binding.NOALLOC_SCRATCH_BYTES, T
+
+
+def test_noalloc_scratch_size_matches_header():
+    with open(HEADER) as f:
+        m = re.search(r"#define MOE_W8A8_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.NOALLOC_SCRATCH_BYTES
