@@ -399,6 +399,9 @@ def main():
                     help="capture one step per weight copy into HIP graphs and time their replays")
     ap.add_argument("--fuse-route-scale", action="store_true",
                     help="fold the routing weight into the GEMM2 row scale (combine only sums)")
+    ap.add_argument("--requant-in-epilogue", type=int, choices=[0, 1], default=0,
+                    help="1: requantise h in GEMM1's epilogue (last-arriving workgroup per chunk) instead of a "
+                         "launch of its own (decode batches)")
     ap.add_argument("--weight-format", choices=["int8", "mxfp4"], default="int8",
                     help="mxfp4: FP4 weights with E8M0 block scales and FP8 activations (always packed)")
     ap.add_argument("--quant-group", type=int, default=0, choices=[0, 64, 128, 256],
@@ -460,6 +463,7 @@ def main():
     dims.weight_layout = moe.MOE_WEIGHT_ROW_MAJOR if args.row_major else moe.MOE_WEIGHT_PACKED
     dims.weight_format = moe.MOE_WEIGHT_MXFP4 if mx else moe.MOE_WEIGHT_INT8
     dims.fuse_route_scale = int(args.fuse_route_scale)
+    dims.requant_in_epilogue = args.requant_in_epilogue
     leg = Leg(case, layers, dims)
     runner = leg.runner
     stream = torch.cuda.Stream()
@@ -529,6 +533,7 @@ def main():
                    "weight_format": args.weight_format,
                    "activation_scales": f"per row and {args.quant_group} elements" if args.quant_group else "per row",
                    "route_scale": "fused_gemm2" if args.fuse_route_scale else "combine",
+                   "requant": "gemm1_epilogue" if args.requant_in_epilogue and spec.T <= 16 else "own_launch",
                    "launch": "hip_graph" if graphs else "stream"},
         "hbm_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
         "tokens_per_s": round(spec.T / (us * 1e-6), 1),

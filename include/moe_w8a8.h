@@ -119,6 +119,17 @@ typedef struct {
                             /*   xs / hs dumps then hold H/G and max(I, I_s)/G       */
                             /*   scales per row, acc1 / acc2 the fp32 bits of the    */
                             /*   dequantised group sums. Ignored for quant_mode 1    */
+    int32_t requant_in_epilogue; /* 0: h is requantised by a launch of its own.     */
+                            /*   1: inside GEMM1's epilogue where the batch runs the */
+                            /*   decode GEMM (T <= 16, INT8 weights, quant_mode 1):  */
+                            /*   the last of a chunk's GEMM1 workgroups to finish    */
+                            /*   quantises the chunk's rows, found by an arrival     */
+                            /*   count per chunk that the same call's routing resets */
+                            /*   ("FIFO Pipeline Analysis ... Mega MoE": the first   */
+                            /*   GEMM's epilogue ends in the cast after SwiGLU, with */
+                            /*   arrival counts; "FusedDeepMoE Kernel 深度分析报告"  */
+                            /*   sec. 7: SwiGLU and quantisation fused). Results are */
+                            /*   identical either way; other batches ignore it       */
 } moe_w8a8_dims_t;
 
 enum { MOE_WEIGHT_ROW_MAJOR = 0, MOE_WEIGHT_PACKED = 1 };

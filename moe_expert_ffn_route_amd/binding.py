@@ -41,7 +41,7 @@ class Dims(ctypes.Structure):
                 ("ep_rank_size", ctypes.c_int32), ("ep_rank_id", ctypes.c_int32), ("quant_mode", ctypes.c_int32),
                 ("amax_eps", ctypes.c_float), ("weight_layout", ctypes.c_int32),
                 ("fuse_route_scale", ctypes.c_int32), ("weight_format", ctypes.c_int32),
-                ("quant_group", ctypes.c_int32)]
+                ("quant_group", ctypes.c_int32), ("requant_in_epilogue", ctypes.c_int32)]
 
     @property
     def e_loc(self) -> int:
@@ -91,9 +91,9 @@ def library() -> ctypes.CDLL:
 
 def make_dims(num_tokens, hidden, inter, topk, moe_expert_num, share_inter=0, ep_rank_size=1, ep_rank_id=0,
               quant_mode=1, amax_eps=1e-6, weight_layout=MOE_WEIGHT_ROW_MAJOR, fuse_route_scale=0,
-              weight_format=MOE_WEIGHT_INT8, quant_group=0) -> Dims:
+              weight_format=MOE_WEIGHT_INT8, quant_group=0, requant_in_epilogue=0) -> Dims:
     return Dims(num_tokens, hidden, inter, share_inter, topk, moe_expert_num, ep_rank_size, ep_rank_id, quant_mode,
-                amax_eps, weight_layout, fuse_route_scale, weight_format, quant_group)
+                amax_eps, weight_layout, fuse_route_scale, weight_format, quant_group, requant_in_epilogue)
 
 
 def moe_w8a8_status_string(code: int) -> str:

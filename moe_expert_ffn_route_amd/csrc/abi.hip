@@ -35,6 +35,7 @@ moe_status_t check_dims(const moe_w8a8_dims_t *d) {
     if (d->hidden > 16384 || d->inter > 16384 || d->share_inter > 16384) return MOE_ERR_UNSUPPORTED;
     if (d->weight_layout != MOE_WEIGHT_ROW_MAJOR && d->weight_layout != MOE_WEIGHT_PACKED) return MOE_ERR_INVALID_ARG;
     if (d->fuse_route_scale != 0 && d->fuse_route_scale != 1) return MOE_ERR_INVALID_ARG;
+    if (d->requant_in_epilogue != 0 && d->requant_in_epilogue != 1) return MOE_ERR_INVALID_ARG;
     if (d->weight_format != MOE_WEIGHT_INT8 && d->weight_format != MOE_WEIGHT_MXFP4) return MOE_ERR_INVALID_ARG;
     if (d->weight_format == MOE_WEIGHT_MXFP4 && d->weight_layout != MOE_WEIGHT_PACKED) return MOE_ERR_UNSUPPORTED;
     if (d->quant_mode == 2) {
@@ -100,6 +101,7 @@ Layout make_layout(const moe_w8a8_dims_t *d) {
     L.hs = o;          o = up256(o + sizeof(float) * R * ngh);
     L.hs2 = o;         o = up256(o + sizeof(float) * R);  // GEMM2 row scales with the routing weight folded in
     L.z = o;           o = up256(o + sizeof(uint16_t) * TK * H);
+    L.fin_count = o;   o = up256(o + sizeof(int32_t) * L.max_chunks);  // GEMM1 arrivals per chunk
     L.total = o;
     return L;
 }
@@ -256,6 +258,12 @@ static moe_status_t forward_impl(const moe_w8a8_dims_t *d, const void *x, const 
     ra.chunks = reinterpret_cast<int4 *>(ws + L.chunks);
     ra.meta = meta;
     ra.dbg_shared_token = D.shared_token;
+    // requantisation in GEMM1's epilogue: where the decode GEMM runs (16-row
+    // work items, INT8 weights, one scale per row)
+    const bool fin = d->requant_in_epilogue && d->weight_format == MOE_WEIGHT_INT8 && d->quant_mode == 1 &&
+                     L.chunk_rows == kChunkRowsSmall;
+    ra.zero_words = fin ? I32(L.fin_count) : nullptr;
+    ra.n_zero = fin ? L.max_chunks : 0;
     TokQuantArgs tq;
     tq.x = static_cast<const uint16_t *>(x);
     tq.mask = x_active_mask;
@@ -328,6 +336,16 @@ static moe_status_t forward_impl(const moe_w8a8_dims_t *d, const void *x, const 
         g1.row_token = ra.row_token;
         g1.h = reinterpret_cast<float *>(ws + L.h);
         g1.dbg_acc = D.acc1;
+        const bool fused = d->fuse_route_scale != 0;
+        if (fin) {
+            g1.fin_count = I32(L.fin_count);
+            g1.fin_q = reinterpret_cast<int8_t *>(ws + L.q_h);
+            g1.fin_scale = reinterpret_cast<float *>(ws + L.hs);
+            g1.fin_scale2 = fused ? reinterpret_cast<float *>(ws + L.hs2) : nullptr;
+            g1.fin_route_w = expert_scales;
+            g1.fin_sorted_pair = ra.sorted_pair;
+            g1.fin_eps = d->amax_eps;
+        }
         const hipError_t e1 = mx     ? launch_gemm1_mx(g1, L.max_chunks, s, kev(0), kev(1))
                               : tall ? launch_gemm1_tall(g1, L.max_chunks, s, kev(0), kev(1))
                               : wide ? launch_gemm1_wide(g1, L.max_chunks, s, kev(0), kev(1))
@@ -349,14 +367,13 @@ static moe_status_t forward_impl(const moe_w8a8_dims_t *d, const void *x, const 
         rq.eps = d->amax_eps;
         rq.q = reinterpret_cast<int8_t *>(ws + L.q_h);
         rq.scale = reinterpret_cast<float *>(ws + L.hs);
-        const bool fused = d->fuse_route_scale != 0;
         rq.scale2 = fused ? reinterpret_cast<float *>(ws + L.hs2) : nullptr;
         rq.route_w = expert_scales;
         rq.sorted_pair = ra.sorted_pair;
         rq.fp8 = mx;
         rq.ng = ngh;
         rq.gl = grp ? d->quant_group / 4 : 0;
-        if (launch_requant(rq, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
+        if ((!fin && launch_requant(rq, s) != hipSuccess) || !mark(3)) return MOE_ERR_HIP;
 
         GemmArgs g2 = g1;
         g2.A = rq.q;
@@ -369,6 +386,7 @@ static moe_status_t forward_impl(const moe_w8a8_dims_t *d, const void *x, const 
         g2.Ws_sh = share_gmm2_weight_scale;
         g2.n_tiles = H / (2 * kTileN) / nw;
         g2.h = nullptr;
+        g2.fin_count = nullptr;
         g2.z = reinterpret_cast<uint16_t *>(ws + L.z);
         g2.zrow = ra.sorted_pair;  // routed z rows in pair order: combine reads row t*K + k
         g2.share_out = static_cast<uint16_t *>(share_output);

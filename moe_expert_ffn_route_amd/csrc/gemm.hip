@@ -39,6 +39,7 @@
 // alike, so every product pairs equal K indices. Result lane l, register i
 // holds D[4 * (l / 16) + i][l % 16].
 #include "internal.h"
+#include "rowquant.h"
 
 #include <hip/hip_ext.h>
 
@@ -50,6 +51,78 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ v4i ld16(const int8_t *p) { return *reinterpret_cast<const v4i *>(p); }
 __device__ __forceinline__ v4i ld16_stream(const int8_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+}
+
+// Agent-coherent fp32 store / load (global_store / global_load with the
+// agent-scope coherence bit): a value stored this way by a block on one XCD is
+// read by a block on another XCD through these loads once the store has
+// completed, without writing back or invalidating any XCD's L2.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 load4_coherent(const float *p) {
+    return make_float4(load_coherent(p), load_coherent(p + 1), load_coherent(p + 2), load_coherent(p + 3));
+}
+
+// Requantisation of one chunk's h rows by the last of its N-tile blocks to
+// arrive ("FusedDeepMoE Kernel 深度分析报告" sec. 7.2 BlockQuant, with the eps
+// floor of "DeepSeek V4 Decode Optimization" sec. 0): per row, a' = max(max
+// |h|, eps), hs = a' * (1/127), q = rint((h * 127) * (1/a')), the fp32
+// operations of the requant kernel in the same order. One wave per row (wave
+// max, no barrier); rows of up to kFinRegs * 256 values stay in registers,
+// longer rows are read twice.
+constexpr int kFinRegs = 8;
+template <int WAVES>
+__device__ __forceinline__ void finalize_requant(const GemmArgs &a, int row0, int rows, int n, int wave, int lane) {
+    const int P = a.meta[kMetaP];
+    for (int lr = wave; lr < rows; lr += WAVES) {  // uniform per wave
+        const int r = row0 + lr;
+        const float *src = a.h + static_cast<size_t>(r) * a.imax;
+        int8_t *dst = a.fin_q + static_cast<size_t>(r) * a.imax;
+        float m = 0.0f;
+        float ap, inv;
+        if (n <= kFinRegs * kWave * 4) {
+            // every load is issued (lanes past the row re-read its start), so
+            // the loads of the whole row are in flight together
+            float4 v[kFinRegs];
+#pragma unroll
+            for (int j = 0; j < kFinRegs; ++j) {
+                const int i = (lane + j * kWave) * 4;
+                v[j] = load4_coherent(src + (i < n ? i : 0));
+            }
+#pragma unroll
+            for (int j = 0; j < kFinRegs; ++j) {
+                const int i = (lane + j * kWave) * 4;
+                if (i < n) m = fmaxf(m, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+            }
+            ap = fmaxf(wave_max(m), a.fin_eps);
+            inv = 1.0f / ap;
+#pragma unroll
+            for (int j = 0; j < kFinRegs; ++j) {
+                const int i = (lane + j * kWave) * 4;
+                if (i < n) *reinterpret_cast<uint32_t *>(dst + i) = quant4<false>(v[j].x, v[j].y, v[j].z, v[j].w, inv);
+            }
+        } else {
+            for (int i = lane * 4; i < n; i += kWave * 4) {
+                const float4 v = load4_coherent(src + i);
+                m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
+            ap = fmaxf(wave_max(m), a.fin_eps);
+            inv = 1.0f / ap;
+            for (int i = lane * 4; i < n; i += kWave * 4) {
+                const float4 v = load4_coherent(src + i);
+                *reinterpret_cast<uint32_t *>(dst + i) = quant4<false>(v.x, v.y, v.z, v.w, inv);
+            }
+        }
+        if (lane == 0) {
+            const float hs = ap * (1.0f / kQMax<false>);
+            a.fin_scale[r] = hs;
+            if (a.fin_scale2) a.fin_scale2[r] = r < P ? hs * a.fin_route_w[a.fin_sorted_pair[r]] : hs;
+        }
+    }
 }
 
 // KIND 1 = GEMM1 + SwiGLU, 2 = GEMM2 + bf16. MT = 16-row MFMA tiles per
@@ -419,7 +492,9 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
                         ag += red[w][0][m][jc];
                         au += red[w][1][m][jc];
                     }
-                    a.h[static_cast<size_t>(r) * a.imax + col] = swiglu(ag, au, wsc0, wsc1, rs);
+                    const float hv = swiglu(ag, au, wsc0, wsc1, rs);
+                    if (a.fin_count) store_coherent(a.h + static_cast<size_t>(r) * a.imax + col, hv);
+                    else a.h[static_cast<size_t>(r) * a.imax + col] = hv;
                     if (a.dbg_acc) {
                         a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + col] = ag;
                         a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + inter + col] = au;
@@ -437,6 +512,22 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_kernel(GemmArgs a, int k_d
             }
         }
         __syncthreads();
+    }
+    if (KIND == 1 && a.fin_count) {
+        // Arrival count of this chunk: every thread waits until its h stores
+        // (agent-coherent) have completed, the barrier gathers the block, and
+        // one thread counts the block in. The block that brings the count to
+        // the chunk's number of N tiles is the last: every other block's h
+        // values are then visible to its coherent loads, and it quantises the
+        // chunk's rows. Nothing waits on another block.
+        __shared__ int s_last;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0)
+            s_last = __hip_atomic_fetch_add(a.fin_count + c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     inter / kTileN - 1;
+        __syncthreads();
+        if (s_last) finalize_requant<WAVES>(a, row0, rows, inter, wave, lane);
     }
 }
 

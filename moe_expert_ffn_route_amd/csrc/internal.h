@@ -56,7 +56,7 @@ struct Layout {
     int chunk_rows;  // rows per GEMM work item
     int imax;        // max(I, I_s)
     size_t meta, offsets, sorted_pair, row_of_pair, row_token, row_group, chunks;
-    size_t q_tok, xs_tok, q_sm, s_sm, h, q_h, hs, hs2, z, total;
+    size_t q_tok, xs_tok, q_sm, s_sm, h, q_h, hs, hs2, z, fin_count, total;
 };
 
 struct RouteArgs {
@@ -73,6 +73,8 @@ struct RouteArgs {
     int4 *chunks;          // [max_chunks] (group, first row, rows | count << kChunkCountShift, index)
     int32_t *meta;         // [kMetaWords]
     int32_t *dbg_shared_token;  // [T] or null
+    int32_t *zero_words;   // [n_zero] counters of later launches of this call, cleared here (or null)
+    int n_zero;
 };
 
 // Quantisation of x in the routing launch, which needs no routing result:
@@ -153,6 +155,18 @@ struct GemmArgs {
     uint16_t *share_out;   // GEMM2 shared rows: [T, H] bf16 indexed by token
     int32_t *dbg_acc;      // optional [rows_max, 2*imax] (GEMM1) / [rows_max, H] (GEMM2)
     uint16_t *dbg_z;       // optional [rows_max, H]
+    // Requantisation in GEMM1's epilogue (decode kernel, INT8, one scale per
+    // row): every N-tile block of a chunk publishes its h values with
+    // agent-coherent stores and counts itself in fin_count[chunk]; the last
+    // block to arrive quantises the chunk's rows (q_h, hs) as the requant
+    // kernel would. No block waits for another. null: separate requant launch.
+    int32_t *fin_count;           // [max_chunks], zeroed by the routing launch of the same call
+    int8_t *fin_q;                // q_h [rows_max, imax]
+    float *fin_scale;             // hs [rows_max]
+    float *fin_scale2;            // fused route scale: hs * route weight (routed rows), else null
+    const float *fin_route_w;     // [T*K]
+    const int32_t *fin_sorted_pair;  // [P]
+    float fin_eps;
 };
 
 struct CombineArgs {

@@ -104,6 +104,9 @@ __device__ void route_block(const RouteArgs &a) {
     }
     const bool tok_act0 = tid < a.T && (!a.mask || a.mask[tid]);
 
+    // per-call reset of the arrival counters a later launch of this call
+    // counts in (the workspace is never assumed to be zero)
+    for (int i = tid; i < a.n_zero; i += kRouteThreads) a.zero_words[i] = 0;
     for (int i = tid; i < E; i += kRouteThreads) {
         s_count[i] = 0;
         s_run[i] = 0;

@@ -69,6 +69,7 @@ class Spec:
     fuse_route_scale: bool = False  # routing weight folded into the GEMM2 row scale
     weight_format: str = "int8"     # "int8" | "mxfp4" (FP4 weights, FP8 activations)
     quant_group: int = 0            # 0: one activation scale per row; G: per row and group of G
+    requant_in_epilogue: bool = False  # requantise h in GEMM1's epilogue (decode GEMM) instead of its own launch
 
     @property
     def E_loc(self) -> int:
@@ -222,7 +223,7 @@ class Case:
                     quant_mode=2 if s.quant_group else 1, amax_eps=s.eps, fuse_route_scale=int(s.fuse_route_scale),
                     weight_format=int(s.weight_format == "mxfp4"),
                     weight_layout=int(s.weight_format == "mxfp4"),  # FP4 weights are always packed
-                    quant_group=s.quant_group)
+                    quant_group=s.quant_group, requant_in_epilogue=int(s.requant_in_epilogue))
 
 
 def _threads() -> int:

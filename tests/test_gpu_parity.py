@@ -83,6 +83,49 @@ def test_small_case_parity(name, packed):
     say(f"[parity] {name}: {stats}")
 
 
+# Requantisation in GEMM1's epilogue (requant_in_epilogue, decode GEMM): the
+# last of a chunk's N-tile workgroups to arrive quantises the chunk's h rows.
+# Cases: one chunk per expert with many N tiles, a shared expert whose
+# intermediate differs (fewer arrivals for its chunk than the grid's N extent),
+# masks, smooth scales, an EP share, the fused route scale, rows longer than
+# the finaliser keeps in registers (I 4096 and 16384), T = 1, every token
+# masked; a batch above 16 tokens (option ignored: the separate launch runs).
+FIN = {
+    "fin_decode_shared_mask_smooth": spec(T=12, H=512, I=512, E_g=8, K=3, I_s=256, active=10, smooth=True,
+                                          share_smooth=True, requant_in_epilogue=True, seed=161),
+    "fin_split_shared_larger": spec(T=16, H=768, I=256, E_g=4, K=2, I_s=768, requant_in_epilogue=True, seed=162),
+    "fin_ep_share_fused": spec(T=9, H=512, I=256, E_g=32, K=6, ep_size=4, ep_rank=2, fuse_route_scale=True,
+                               requant_in_epilogue=True, seed=163),
+    "fin_long_rows_4096": spec(T=6, H=256, I=4096, E_g=4, K=2, I_s=2304, requant_in_epilogue=True, seed=164),
+    "fin_long_rows_16384": spec(T=3, H=256, I=16384, E_g=2, K=1, I_s=512, requant_in_epilogue=True, seed=165),
+    "fin_t1": spec(T=1, H=1024, I=512, E_g=4, K=2, I_s=512, requant_in_epilogue=True, seed=166),
+    "fin_all_masked": spec(T=7, I_s=256, active=0, requant_in_epilogue=True, seed=167),
+    "fin_ignored_above_16_tokens": spec(T=40, H=512, I=256, E_g=4, K=2, I_s=512, requant_in_epilogue=True,
+                                        seed=168),
+    "fin_decode_h4096": spec(T=8, H=4096, I=2048, E_g=16, K=4, I_s=2048, requant_in_epilogue=True, seed=169),
+}
+
+
+@pytest.mark.parametrize("packed", [True, False], ids=["packed", "rowmajor"])
+@pytest.mark.parametrize("name", list(FIN))
+def test_requant_in_epilogue_parity(name, packed):
+    say(f"[parity] {name} packed={packed}: {FIN[name]}")
+    case = synth.make_case(FIN[name])
+    stats, gpu, ref = check(case, packed=packed)
+    say(f"[parity] {name}: {stats}")
+    # identical to the separate requantisation launch, bit for bit
+    plain = run_gpu(dataclasses.replace(case, spec=dataclasses.replace(case.spec, requant_in_epilogue=False)),
+                    packed=packed)
+    for k in ("output", "share_output"):
+        if gpu.get(k) is not None:
+            assert np.array_equal(gpu[k], plain[k]), k
+    P, Ta = int(gpu["num_rows"][0]), int(gpu["num_rows"][1])
+    for r in range(P + (Ta if case.spec.I_s else 0)):  # rows in use
+        n = case.spec.I if r < P else case.spec.I_s
+        assert np.array_equal(gpu["q_h"][r, :n], plain["q_h"][r, :n]), f"q_h row {r}"
+        assert gpu["hs"][r] == plain["hs"][r], f"hs row {r}"
+
+
 # The production tile shapes (hidden 4096, intermediate 2048: one K batch per
 # wave in GEMM1) at small T: 16-row chunks (T <= 16) and 32-row chunks
 # (T > 16), including an expert with more than one chunk.
@@ -128,6 +171,10 @@ def _random_specs(n, seed=2024):
         if rng.random() < 0.3:
             kw["fuse_route_scale"] = True
         out.append((synth.Spec(**kw), bool(i % 2)))
+    # the same draws again with requantisation in GEMM1's epilogue (where it
+    # applies: batches of at most 16 tokens)
+    out += [(dataclasses.replace(sp, name=sp.name + "_fin", requant_in_epilogue=True), pk)
+            for sp, pk in out if sp.T <= 16]
     return out
 
 
@@ -232,6 +279,8 @@ def test_deterministic_dirty_workspace_and_side_stream():
 
 GRAPH_CASES = {
     "decode": spec(T=12, H=512, I=256, E_g=8, K=2, I_s=256, active=10, seed=116),
+    "decode_requant_in_epilogue": spec(T=12, H=512, I=256, E_g=8, K=2, I_s=512, active=10,
+                                       requant_in_epilogue=True, seed=120),
     "wide": spec(T=40, H=512, I=256, E_g=8, K=2, I_s=512, active=37, seed=118),
     "tall": spec(T=300, H=512, I=256, E_g=2, K=2, I_s=256, seed=119),
 }
@@ -365,6 +414,11 @@ def test_full_size_workload(cfg):
         del gpu
         stats, gpu, _ = check(case, ref=ref, packed=False)
         say(f"[parity] config {cfg} row-major: {stats}")
+    if cfg == 1:  # requantisation in GEMM1's epilogue
+        del gpu
+        fin = dataclasses.replace(case, spec=dataclasses.replace(case.spec, requant_in_epilogue=True))
+        stats, gpu, _ = check(fin, ref=ref, packed=True)
+        say(f"[parity] config {cfg} requant in GEMM1's epilogue: {stats}")
     assert stats["rows"] == ref["P"] + (ref["T_act"] if s.I_s else 0)
     del gpu, ref
     torch.cuda.empty_cache()
