@@ -72,6 +72,7 @@ def hip_runtime() -> ctypes.CDLL:
         _hip_rt.hipEventRecord.argtypes = [P, P]
         _hip_rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
         _hip_rt.hipEventDestroy.argtypes = [P]
+        _hip_rt.hipStreamWaitEvent.argtypes = [P, P, ctypes.c_uint]
     return _hip_rt
 
 
@@ -254,12 +255,15 @@ class Leg:
         self.runner = moe.Runner(dims)
 
 
-def measure(leg, steps, warmup, stream, fence_free, kernel_events=True, graphs=None):
+def measure(leg, steps, warmup, stream, fence_free, kernel_events=True, graphs=None, after_step=None):
     """Time `steps` forwards of one leg (step i on weight copy i % copies).
     Returns µs per step, GEMM1 / GEMM2 kernel durations from events bound to
     their launches, per-stage times (marker events, separate pass) and the
-    per-step distribution (one marker per step boundary, separate pass)."""
+    per-step distribution (one marker per step boundary, separate pass).
+    after_step(i), if given, is called after step i is enqueued (in every
+    pass)."""
     runner, layers = leg.runner, leg.layers
+    hook = after_step or (lambda i: None)
     n_ev = len(binding.STAGES) + 1
     events = [[TimingEvent(fence_free) for _ in range(n_ev)] for _ in range(steps)]
     kevents = [[TimingEvent(fence_free) for _ in range(4)] for _ in range(steps)]
@@ -282,6 +286,7 @@ def measure(leg, steps, warmup, stream, fence_free, kernel_events=True, graphs=N
     with torch.cuda.stream(stream):
         for i in range(warmup):
             runner(layers[i % len(layers)], stream=stream)
+            hook(i)
     torch.cuda.synchronize()
     if graphs:
         for i in range(warmup):
@@ -298,6 +303,7 @@ def measure(leg, steps, warmup, stream, fence_free, kernel_events=True, graphs=N
                 graphs[i % len(graphs)].replay()
             else:
                 runner(layers[i % len(layers)], dbg=k_dbg[i] if kernel_events else None, stream=stream)
+            hook(i)
         t_stop.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_stop) / steps
@@ -308,6 +314,7 @@ def measure(leg, steps, warmup, stream, fence_free, kernel_events=True, graphs=N
     with torch.cuda.stream(stream):
         for i in range(steps):
             runner(layers[i % len(layers)], dbg=all_dbg[i], stream=stream)
+            hook(i)
     torch.cuda.synchronize()
     stage_us = {name: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(steps)]) * 1e3)
                 for j, name in enumerate(binding.STAGES)}
@@ -326,6 +333,7 @@ def measure(leg, steps, warmup, stream, fence_free, kernel_events=True, graphs=N
                 graphs[i % len(graphs)].replay()
             else:
                 runner(layers[i % len(layers)], stream=stream)
+            hook(i)
             bounds[i + 1].record(stream)
     torch.cuda.synchronize()
     step_samples = [bounds[i].elapsed_time(bounds[i + 1]) * 1e3 for i in range(steps)]
@@ -409,6 +417,9 @@ def main():
     ap.add_argument("--fenced-events", action="store_true",
                     help="time with default HIP events (each record adds a system-scope cache writeback) "
                          "instead of events created with hipEventDisableSystemFence")
+    ap.add_argument("--warm-next-shared", action="store_true",
+                    help="after each layer, warm the next layer's shared-expert GEMM1 weights on a second stream "
+                         "(moe_w8a8_warm), overlapping that layer's routing launch")
     ap.add_argument("--no-large-batch", action="store_true",
                     help="skip the T = 512 leg (large_batch_t512) of the default decode line")
     ap.add_argument("--no-kernel-events", action="store_true",
@@ -483,9 +494,31 @@ def main():
             graphs.append(g)
         torch.cuda.synchronize()
 
+    after_step = None
+    if args.warm_next_shared:
+        if not spec.I_s or graphs:
+            print("--warm-next-shared needs a shared expert and stream launches", file=sys.stderr)
+            sys.exit(2)
+        # after layer i is enqueued, a second stream waits for it and warms
+        # layer i + 1's shared-expert GEMM1 weights and scales, which then
+        # overlap layer i + 1's routing launch (HBM otherwise idle)
+        # (fence-free events: the warm only reads weights, so the wait orders
+        # launches and needs no cache writeback; a default event's record
+        # would add one per step)
+        side = torch.cuda.Stream()
+        marks = [TimingEvent(fence_free) for _ in range(len(layers))]
+
+        def after_step(i):
+            nxt = layers[(i + 1) % len(layers)]
+            ev = marks[i % len(layers)]
+            ev.record(stream)
+            if hip_runtime().hipStreamWaitEvent(side.cuda_stream, ev.cuda_event, 0) != 0:
+                raise RuntimeError("hipStreamWaitEvent failed")
+            moe.moe_w8a8_warm(nxt["share_gmm1_weight"], stream=side)
+            moe.moe_w8a8_warm(nxt["share_gmm1_weight_scale"], stream=side)
     log(f"[bench] warmup {args.warmup} steps, timing {args.steps} steps (three passes)")
     m = measure(leg, args.steps, args.warmup, stream, fence_free, kernel_events=not args.no_kernel_events,
-                graphs=graphs)
+                graphs=graphs, after_step=after_step)
     counts = m["counts"]
     g1_us, g2_us, stage_us, timing = m["g1_us"], m["g2_us"], m["stage_us"], m["timing"]
     p10, p50, p90 = m["p"]
@@ -534,7 +567,8 @@ def main():
                    "activation_scales": f"per row and {args.quant_group} elements" if args.quant_group else "per row",
                    "route_scale": "fused_gemm2" if args.fuse_route_scale else "combine",
                    "requant": "gemm1_epilogue" if args.requant_in_epilogue and spec.T <= 16 else "own_launch",
-                   "launch": "hip_graph" if graphs else "stream"},
+                   "launch": "hip_graph" if graphs else "stream",
+                   "warm_next_shared": bool(args.warm_next_shared)},
         "hbm_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
         "tokens_per_s": round(spec.T / (us * 1e-6), 1),
         "step_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],  # one event per step boundary

@@ -317,6 +317,20 @@ MOE_W8A8_API moe_status_t moe_w8a8_pack_weights_mx(const uint8_t *data, const ui
                                                    int64_t groups, int32_t n, int32_t k, int32_t which,
                                                    void *stream);
 
+/*
+ * Cache warm ("DeepSeek V4 Decode Optimization" sec. 4.5, inter-layer
+ * eviction): read the device range [ptr, ptr + bytes) once on `stream` and
+ * discard it, so that its lines sit in the 256 MB memory-side cache (and an
+ * XCD's L2) when a later kernel reads them. A hint with no destination: no
+ * value anywhere changes, and dropping the call changes no result. Meant for
+ * the next layer's weights that every call touches (the shared expert's),
+ * issued on a second stream while the current layer runs its latency-bound
+ * launches; a range larger than the cache evicts itself. ptr 16-byte aligned,
+ * bytes a multiple of 16 (MOE_ERR_INVALID_ARG otherwise); bytes == 0 is a
+ * no-op. Stream-ordered, no allocation.
+ */
+MOE_W8A8_API moe_status_t moe_w8a8_warm(const void *ptr, size_t bytes, void *stream);
+
 /* Static description of a status code. Never NULL. */
 MOE_W8A8_API const char *moe_w8a8_status_string(moe_status_t status);
 

@@ -22,7 +22,7 @@ MOE_ERR_SCRATCH_LIMIT = -5
 NOALLOC_SCRATCH_BYTES = 32 << 20  # MOE_W8A8_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_forward", "moe_w8a8_forward_noalloc", "moe_w8a8_pack_weights",
-           "moe_w8a8_packed_mx_bytes", "moe_w8a8_pack_weights_mx", "moe_w8a8_status_string")
+           "moe_w8a8_packed_mx_bytes", "moe_w8a8_pack_weights_mx", "moe_w8a8_warm", "moe_w8a8_status_string")
 MOE_WEIGHT_ROW_MAJOR, MOE_WEIGHT_PACKED = 0, 1
 MOE_WEIGHT_INT8, MOE_WEIGHT_MXFP4 = 0, 1
 MOE_PACK_GMM1, MOE_PACK_GMM2 = 1, 2
@@ -83,6 +83,8 @@ def library() -> ctypes.CDLL:
         L.moe_w8a8_pack_weights_mx.restype = ctypes.c_int
         L.moe_w8a8_pack_weights_mx.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int32, P]
+        L.moe_w8a8_warm.restype = ctypes.c_int
+        L.moe_w8a8_warm.argtypes = [P, ctypes.c_size_t, P]
         L.moe_w8a8_status_string.restype = ctypes.c_char_p
         L.moe_w8a8_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -129,6 +131,14 @@ def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
     return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else stream
+
+
+def moe_w8a8_warm(t, nbytes: Optional[int] = None, stream=None) -> None:
+    """Warm the caches with a device tensor's bytes (or its first nbytes)."""
+    n = t.numel() * t.element_size() if nbytes is None else nbytes
+    rc = library().moe_w8a8_warm(_ptr(t), n, _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_w8a8_warm")
 
 
 def moe_w8a8_packed_mx_bytes(groups: int, n: int, k: int) -> int:

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_w8a8.so")
 SOURCES = ["abi.hip", "route.hip", "quant.hip", "gemm.hip", "gemm_wide.hip", "gemm_tall.hip", "gemm_mx.hip", "combine.hip",
-           "pack.hip"]
+           "pack.hip", "warm.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -253,3 +253,11 @@ def test_noalloc_scratch_size_matches_header():
     with open(HEADER) as f:
         m = re.search(r"#define MOE_W8A8_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
     assert m and int(m.group(1)) << int(m.group(2)) == binding.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("ptr,nbytes,code", [
+    (None, 16, binding.MOE_ERR_INVALID_ARG), (FAKE + 8, 16, binding.MOE_ERR_INVALID_ARG),
+    (FAKE, 24, binding.MOE_ERR_INVALID_ARG), (None, 0, binding.MOE_OK), (FAKE, 0, binding.MOE_OK)])
+def test_warm_rejects_bad_arguments(lib, ptr, nbytes, code):
+    # zero bytes is a no-op that launches nothing, whatever the pointer
+    assert lib.moe_w8a8_warm(ptr, nbytes, None) == code

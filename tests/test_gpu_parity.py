@@ -422,3 +422,33 @@ def test_full_size_workload(cfg):
     assert stats["rows"] == ref["P"] + (ref["T_act"] if s.I_s else 0)
     del gpu, ref
     torch.cuda.empty_cache()
+
+
+def test_cache_warm_changes_no_result():
+    # the warm is a cache hint: warming the next layer's shared expert on a
+    # second stream while this layer runs leaves every output bit unchanged,
+    # and so does warming the weights this call is about to read
+    c = synth.make_case(spec(T=8, H=1024, I=512, E_g=16, K=4, I_s=512, seed=171))
+    t = moe.pack_weights(moe.upload(c))
+    nxt = {k: v.clone() for k, v in t.items() if k.startswith("share_gmm") and v is not None}
+    dims = moe.dims_of_case(c)
+    dims.weight_layout = moe.MOE_WEIGHT_PACKED
+    runner = moe.Runner(dims)
+    runner(t)
+    torch.cuda.synchronize()
+    ref = (runner.output.clone(), runner.share_output.clone())
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    for i in range(3):
+        runner.output.fill_(1)
+        runner.share_output.fill_(1)
+        ev = torch.cuda.Event()
+        ev.record(main)
+        side.wait_event(ev)
+        moe.moe_w8a8_warm(nxt["share_gmm1_weight"], stream=side)
+        moe.moe_w8a8_warm(t["gmm1_weight"], stream=side)
+        runner(t, stream=main)
+        torch.cuda.synchronize()
+        assert torch.equal(runner.output, ref[0]) and torch.equal(runner.share_output, ref[1]), i
+    # the warmed tensors themselves are untouched
+    for k, v in nxt.items():
+        assert torch.equal(v, t[k])
