@@ -334,7 +334,9 @@ static moe_status_t forward_impl(const moe_w8a8_dims_t *d, const void *x, const 
         // (gemm_wide.hip) and tall (gemm_tall.hip) work items; group-wise
         // scales: gemm.hip (16- or 32-row items); FP4 weights: gemm_mx.hip
         const bool tall = !mx && !grp && g1.mt == kTallTiles, wide = !mx && !grp && g1.mt == kWideTiles;
-        const int nw = tall ? kTallPairs : wide ? wide_tile_pairs() : 1;  // tile pairs per work item
+        // tile pairs per work item
+        const int nw = tall ? kTallPairs : wide ? wide_tile_pairs() : (mx && g1.mt == 2) ? mx_wide_tile_pairs(1) : 1;
+        const int nw2 = mx && g1.mt == 2 ? mx_wide_tile_pairs(2) : nw;
         g1.n_tiles = L.imax / kTileN / nw;
         g1.chunks = ra.chunks;
         g1.count_word = kMetaChunks;
@@ -390,7 +392,7 @@ static moe_status_t forward_impl(const moe_w8a8_dims_t *d, const void *x, const 
         g2.Ws = gmm2_weight_scale;
         g2.W_sh = share_gmm2_weight;
         g2.Ws_sh = share_gmm2_weight_scale;
-        g2.n_tiles = H / (2 * kTileN) / nw;
+        g2.n_tiles = H / (2 * kTileN) / nw2;
         g2.h = nullptr;
         g2.fin_count = nullptr;
         g2.z = reinterpret_cast<uint16_t *>(ws + L.z);

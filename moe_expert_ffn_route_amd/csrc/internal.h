@@ -204,6 +204,9 @@ hipError_t launch_gemm2_tall(const GemmArgs &a, int max_chunks, int k_dim, hipSt
 hipError_t launch_gemm1_mx(const GemmArgs &a, int max_chunks, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_gemm2_mx(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t ev_start,
                            hipEvent_t ev_stop);
+// Tile pairs per work item of the two-tile (32-row) FP4-weight kernel, for
+// GEMM1 (kind 1) or GEMM2 (kind 2).
+int mx_wide_tile_pairs(int kind);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 // Reads [ptr, ptr + bytes) once and discards it (a cache warm); bytes % 16 == 0.
 hipError_t launch_warm(const void *ptr, size_t bytes, hipStream_t s);

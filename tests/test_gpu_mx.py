@@ -53,6 +53,11 @@ CASES = {
     # passes of 1 step), I 3072 (24 steps: 8 waves x 3)
     "t20_long_k_gemm1": (spec(T=20, H=9216, I=256, E_g=2, K=1, I_s=256, seed=313), None),
     "t24_mid_k_gemm2": (spec(T=24, H=256, I=3072, E_g=2, K=2, I_s=512, seed=314), None),
+    # two-tile items on every weight-ring length of that kernel: H 768 (6
+    # steps: a 2-step ring), I 512 (4 steps: a 4-step ring), I_s 256 (2
+    # steps), and I 2048 (16 steps: an 8-step ring in two turns)
+    "t40_rings_2_and_4": (spec(T=40, H=768, I=512, E_g=2, K=2, I_s=256, seed=315), None),
+    "t36_ring_8_two_turns": (spec(T=36, H=1024, I=2048, E_g=2, K=2, I_s=1024, active=33, seed=316), None),
     "t1": (spec(T=1, H=512, I=256, E_g=4, K=2, I_s=512, seed=308), None),
     # H 2048 (16 steps: 4 waves x 4), I 3072 (24 steps: 4 waves x 6)
     "mid_k": (spec(T=9, H=2048, I=3072, E_g=4, K=2, I_s=1024, seed=312), None),
