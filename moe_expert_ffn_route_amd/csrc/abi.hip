@@ -65,7 +65,7 @@ Layout make_layout(const moe_w8a8_dims_t *d) {
     const size_t nonempty = E < TK ? E : TK;
     // rows per GEMM work item: 16 for decode batches; 256 (tall items) when
     // the routed experts average kTallMinRows rows or more; 32 otherwise.
-    // FP4 weights (gemm_mx.hip) and group-wise scales (gemm.hip): 32 when the
+    // FP4 weights (gemm_mx.hip) and group-wise scales (gemm.hip, gemm_wide.hip): 32 when the
     // local experts can average 16 rows or more (T*K / ep_rank_size >=
     // 16 * E_loc), else 16 (measured on MI355X with FP4 weights: 32-row items
     // take the T = 512 layer from 996 to 859 us but slow the skewed T = 64
@@ -332,8 +332,9 @@ static moe_status_t forward_impl(const moe_w8a8_dims_t *d, const void *x, const 
         g1.mt = L.chunk_rows / kTileN;
         // three INT8 kernels by chunk size: decode (gemm.hip), wide
         // (gemm_wide.hip) and tall (gemm_tall.hip) work items; group-wise
-        // scales: gemm.hip (16- or 32-row items); FP4 weights: gemm_mx.hip
-        const bool tall = !mx && !grp && g1.mt == kTallTiles, wide = !mx && !grp && g1.mt == kWideTiles;
+        // scales: gemm.hip (16-row items) or gemm_wide.hip (32-row items);
+        // FP4 weights: gemm_mx.hip
+        const bool tall = !mx && !grp && g1.mt == kTallTiles, wide = !mx && g1.mt == kWideTiles;
         // tile pairs per work item
         const int nw = tall ? kTallPairs : wide ? wide_tile_pairs() : (mx && g1.mt == 2) ? mx_wide_tile_pairs(1) : 1;
         const int nw2 = mx && g1.mt == 2 ? mx_wide_tile_pairs(2) : nw;

@@ -20,7 +20,10 @@
 //     slab s, write it to LDS at the end of the slab and meet at one
 //     workgroup barrier per slab;
 //   - with no K split there is no cross-wave reduction: each lane holds the
-//     finished int32 sums of its (row, channel) outputs.
+//     finished int32 sums of its (row, channel) outputs;
+//   - with group-wise activation scales each group's int32 sums are
+//     dequantised by the group's scale at the group's end and added to fp32
+//     sums in group order, which is the order the oracle adds them in.
 // LDS layout: the slab's rows, each padded by 16 bytes (see wide_body).
 #include "internal.h"
 
@@ -56,8 +59,15 @@ struct WideItem {
 // The K loop and epilogue for MTA active row tiles (the chunk's rows, rounded
 // up to whole tiles) and NT pairs of weight tiles per wave. Runs the same
 // sequence in every wave of the block.
-template <int KIND, int NW, int NT, int MTA, int SLAB, int RING, bool PACKED>
-__device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it, v4i *s_a) {
+// GS > 0: group-wise activation scales ("DeepSeek V4 Decode Optimization"
+// sec. 3.1), one per GS 64-byte K steps of a row (a.a_ng per row). At the end
+// of each group the lane's int32 sums are dequantised, p = (float(acc) *
+// w_scale[n]) * group_scale[row], and added to fp32 sums in group order (a
+// wave walks the whole K, so the order is the groups' own); each group's
+// first MFMA starts from zero. The groups' scales of a slab travel with its
+// activation rows through LDS (s_g).
+template <int KIND, int NW, int NT, int MTA, int SLAB, int RING, bool PACKED, int GS = 0>
+__device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it, v4i *s_a, float *s_g) {
     // Activation slab layout in LDS: the chunk's 16 * MTA rows, each holding
     // the slab's SLAB * 64 bytes plus 16 bytes of padding. A load instruction
     // reads kRpi whole row segments (contiguous, so every 128-byte line it
@@ -72,6 +82,10 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
     constexpr int kUpw = (kUnits + NW - 1) / NW;   // of them, per wave
     constexpr int kSlabsPerRing = RING / SLAB;
     static_assert(kWave % kLpr == 0, "a load instruction covers whole row segments");
+    static_assert(GS == 0 || SLAB % GS == 0, "group-wise scales: whole groups per slab");
+    constexpr int kGps = GS > 0 ? SLAB / GS : 1;    // groups per slab
+    constexpr int kGvals = kTileN * MTA * kGps;    // group scales of a slab
+    static_assert(kGvals <= NW * kWave, "one thread stages each group scale of a slab");
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int r16 = lane & 15, kg = lane >> 4;
@@ -88,6 +102,15 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
         const int lr = min(u * kRpi + lane / kLpr, rows - 1);  // rows past the chunk repeat its last row
         const int ar = it.aidx ? it.aidx[row0 + lr] : row0 + lr;
         asrc[j] = it.Abase + static_cast<size_t>(ar) * a.a_stride + seg * 16;
+    }
+    // group-wise scales: thread t < kGvals stages the scale of row t / kGps,
+    // group t % kGps of each slab
+    const float *gsrc = nullptr;
+    if constexpr (GS > 0) {
+        const int t = threadIdx.x;
+        const int lr = min(min(t, kGvals - 1) / kGps, rows - 1);
+        const int srow = it.aidx ? it.aidx[row0 + lr] : row0 + lr;
+        gsrc = it.Ascale + static_cast<size_t>(srow) * a.a_ng + min(t, kGvals - 1) % kGps;
     }
     // a token indexes the row scale of per-token rows and the share_output
     // row of the shared expert's GEMM2
@@ -107,7 +130,8 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
         for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                rsc[mt][i] = it.Ascale[it.aidx ? otok[mt][i] : row0 + min(mt * kTileN + 4 * kg + i, rows - 1)];
+                rsc[mt][i] = GS > 0 ? 0.0f
+                                    : it.Ascale[it.aidx ? otok[mt][i] : row0 + min(mt * kTileN + 4 * kg + i, rows - 1)];
     };
     load_tokens();
     float ws0[NT], ws1[NT];
@@ -124,16 +148,23 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
         return PACKED ? ld16_stream(p) : ld16(p);
     };
     v4i stage[kUpw];
+    float gstage = 0.0f;
     auto load_slab = [&](int s) {
 #pragma unroll
         for (int j = 0; j < kUpw; ++j)
             if (kUnits % NW == 0 || wave + j * NW < kUnits) stage[j] = ld16(asrc[j] + s * SLAB * 64);
+        if constexpr (GS > 0) {
+            if (static_cast<int>(threadIdx.x) < kGvals) gstage = gsrc[s * kGps];
+        }
     };
     auto store_slab = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < kUpw; ++j)
             if (kUnits % NW == 0 || wave + j * NW < kUnits)
                 s_a[buf * kBuf + ((wave + j * NW) * kRpi + lane / kLpr) * kStr + seg] = stage[j];
+        if constexpr (GS > 0) {
+            if (static_cast<int>(threadIdx.x) < kGvals) s_g[buf * kGvals + threadIdx.x] = gstage;
+        }
     };
     load_slab(0);
     __builtin_amdgcn_sched_barrier(0);
@@ -155,13 +186,38 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
     __syncthreads();
 
     v4i acc0[MTA][NT], acc1[MTA][NT];
+    float f0[MTA][NT][4], f1[MTA][NT][4];  // group-wise: dequantised sums
 #pragma unroll
     for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             acc0[mt][j] = v4i{0, 0, 0, 0};
             acc1[mt][j] = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f0[mt][j][i] = 0.0f;
+                f1[mt][j][i] = 0.0f;
+            }
         }
+    // group-wise: dequantise the finished group q of slab buffer `cur` into
+    // the fp32 sums, in group order
+    auto flush = [&](int cur, int q) {
+#pragma unroll
+        for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float gsc = s_g[cur * kGvals + (mt * kTileN + 4 * kg + i) * kGps + q];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    float p0 = static_cast<float>(acc0[mt][j][i]) * ws0[j];
+                    p0 = p0 * gsc;
+                    f0[mt][j][i] = f0[mt][j][i] + p0;
+                    float p1 = static_cast<float>(acc1[mt][j][i]) * ws1[j];
+                    p1 = p1 * gsc;
+                    f1[mt][j][i] = f1[mt][j][i] + p1;
+                }
+            }
+    };
     // One slab of SLAB K steps at ring position h: the next slab's activation
     // loads, then for each step the MFMAs of all row tiles followed by the
     // weight loads that refill the step's ring slot (RING steps ahead); at the
@@ -175,15 +231,20 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
 #pragma unroll
         for (int i = 0; i < SLAB; ++i) {
             const int slot = h * SLAB + i;
+            const bool first = GS > 0 && i % (GS > 0 ? GS : 1) == 0;  // a group's first step
+            const v4i zero = {0, 0, 0, 0};
 #pragma unroll
             for (int mt = 0; mt < MTA; ++mt) {
                 const v4i x = s_a[cur * kBuf + (mt * kTileN + r16) * kStr + i * 4 + kg];
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
-                    acc0[mt][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x, w0[slot][j], acc0[mt][j], 0, 0, 0);
-                    acc1[mt][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x, w1[slot][j], acc1[mt][j], 0, 0, 0);
+                    acc0[mt][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x, w0[slot][j], first ? zero : acc0[mt][j],
+                                                                        0, 0, 0);
+                    acc1[mt][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x, w1[slot][j], first ? zero : acc1[mt][j],
+                                                                        0, 0, 0);
                 }
             }
+            if (GS > 0 && (i + 1) % (GS > 0 ? GS : 1) == 0) flush(cur, i / (GS > 0 ? GS : 1));
             if (more_w) {
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
@@ -223,10 +284,13 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
                     if (lr < rows) {
                         const int r = row0 + lr;
                         a.h[static_cast<size_t>(r) * a.imax + col] =
-                            swiglu(acc0[mt][j][i], acc1[mt][j][i], ws0[j], ws1[j], rsc[mt][i]);
+                            GS > 0 ? swiglu_y(f0[mt][j][i], f1[mt][j][i])
+                                   : swiglu(acc0[mt][j][i], acc1[mt][j][i], ws0[j], ws1[j], rsc[mt][i]);
                         if (a.dbg_acc) {
-                            a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + col] = acc0[mt][j][i];
-                            a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + it.inter + col] = acc1[mt][j][i];
+                            a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + col] =
+                                GS > 0 ? __float_as_int(f0[mt][j][i]) : acc0[mt][j][i];
+                            a.dbg_acc[static_cast<size_t>(r) * 2 * a.imax + it.inter + col] =
+                                GS > 0 ? __float_as_int(f1[mt][j][i]) : acc1[mt][j][i];
                         }
                     }
                 }
@@ -234,8 +298,10 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int lr = mt * kTileN + 4 * kg + i;
-                    const uint32_t b0 = f32_to_bf16(dequant(acc0[mt][j][i], ws0[j], rsc[mt][i]));
-                    const uint32_t b1 = f32_to_bf16(dequant(acc1[mt][j][i], ws1[j], rsc[mt][i]));
+                    const uint32_t b0 =
+                        f32_to_bf16(GS > 0 ? f0[mt][j][i] : dequant(acc0[mt][j][i], ws0[j], rsc[mt][i]));
+                    const uint32_t b1 =
+                        f32_to_bf16(GS > 0 ? f1[mt][j][i] : dequant(acc1[mt][j][i], ws1[j], rsc[mt][i]));
                     // pair up neighbouring channels for 4-byte stores: even
                     // lanes take channels (c, c + 1) of tile A, odd lanes
                     // (c - 1, c) of tile B, so 16 lanes store 64 contiguous
@@ -250,8 +316,10 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WideItem &it,
                         uint16_t *dst = (it.routed ? a.z : a.share_out) + static_cast<size_t>(otok[mt][i]) * a.H;
                         *reinterpret_cast<uint32_t *>(dst + wcol) = word;
                         if (a.dbg_acc) {
-                            a.dbg_acc[static_cast<size_t>(r) * a.H + rowA + r16] = acc0[mt][j][i];
-                            a.dbg_acc[static_cast<size_t>(r) * a.H + rowB + r16] = acc1[mt][j][i];
+                            a.dbg_acc[static_cast<size_t>(r) * a.H + rowA + r16] =
+                                GS > 0 ? __float_as_int(f0[mt][j][i]) : acc0[mt][j][i];
+                            a.dbg_acc[static_cast<size_t>(r) * a.H + rowB + r16] =
+                                GS > 0 ? __float_as_int(f1[mt][j][i]) : acc1[mt][j][i];
                         }
                         if (a.dbg_z)
                             *reinterpret_cast<uint32_t *>(a.dbg_z + static_cast<size_t>(r) * a.H + wcol) = word;
@@ -350,48 +418,70 @@ __device__ __forceinline__ bool decode_item(const GemmArgs &a, const int4 *chunk
 #endif
 constexpr int kWideWaves = MOE_WIDE_WAVES, kWideSlab = MOE_WIDE_SLAB;
 
-template <int KIND, int NW, int NT, int MT, int SLAB, int RING, bool PACKED>
+template <int KIND, int NW, int NT, int MT, int SLAB, int RING, bool PACKED, int GS>
 __global__ __launch_bounds__(NW * kWave, 2) void gemm_wide_kernel(GemmArgs a, int k_dim) {
     __shared__ v4i s_a[2 * kTileN * MT * (4 * SLAB + 1)];
+    __shared__ float s_g[GS > 0 ? 2 * kTileN * MT * (SLAB / (GS > 0 ? GS : 1)) : 1];
     WideItem it;
     if (!decode_item<KIND, NW, NT, PACKED>(a, a.chunks, a.count_word, a.n_tiles, blockIdx.x, k_dim, it)) return;
     // run the body for the row tiles the chunk actually fills
     static_assert(MT <= 2, "items of one or two row tiles");
     const int tiles = (it.rows + kTileN - 1) / kTileN;
     if constexpr (MT > 1) {
-        if (tiles > 1) return wide_body<KIND, NW, NT, 2, SLAB, RING, PACKED>(a, it, s_a);
+        if (tiles > 1) return wide_body<KIND, NW, NT, 2, SLAB, RING, PACKED, GS>(a, it, s_a, s_g);
     }
-    wide_body<KIND, NW, NT, 1, SLAB, RING, PACKED>(a, it, s_a);
+    wide_body<KIND, NW, NT, 1, SLAB, RING, PACKED, GS>(a, it, s_a, s_g);
 }
 
-template <int KIND, int NW, int NT, int MT, int SLAB, int RING>
+template <int KIND, int NW, int NT, int MT, int SLAB, int RING, int GS>
 hipError_t launch_t(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const long blocks = static_cast<long>(max_chunks) * a.n_tiles;
     if (blocks <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(blocks)), blk(NW * kWave);
     if (a.packed) {
         if (e0 || e1)
-            hipExtLaunchKernelGGL((gemm_wide_kernel<KIND, NW, NT, MT, SLAB, RING, true>), grid, blk, 0, s, e0, e1, 0,
-                                  a, k_dim);
-        else
-            hipLaunchKernelGGL((gemm_wide_kernel<KIND, NW, NT, MT, SLAB, RING, true>), grid, blk, 0, s, a, k_dim);
-    } else {
-        if (e0 || e1)
-            hipExtLaunchKernelGGL((gemm_wide_kernel<KIND, NW, NT, MT, SLAB, RING, false>), grid, blk, 0, s, e0, e1,
+            hipExtLaunchKernelGGL((gemm_wide_kernel<KIND, NW, NT, MT, SLAB, RING, true, GS>), grid, blk, 0, s, e0, e1,
                                   0, a, k_dim);
         else
-            hipLaunchKernelGGL((gemm_wide_kernel<KIND, NW, NT, MT, SLAB, RING, false>), grid, blk, 0, s, a, k_dim);
+            hipLaunchKernelGGL((gemm_wide_kernel<KIND, NW, NT, MT, SLAB, RING, true, GS>), grid, blk, 0, s, a, k_dim);
+    } else {
+        if (e0 || e1)
+            hipExtLaunchKernelGGL((gemm_wide_kernel<KIND, NW, NT, MT, SLAB, RING, false, GS>), grid, blk, 0, s, e0,
+                                  e1, 0, a, k_dim);
+        else
+            hipLaunchKernelGGL((gemm_wide_kernel<KIND, NW, NT, MT, SLAB, RING, false, GS>), grid, blk, 0, s, a, k_dim);
     }
     return hipGetLastError();
 }
 
-// k_dim is a multiple of 256, so rings of 4 steps always divide it
+// Longest weight ring with group-wise scales of 128 elements (the per-group
+// dequantisation holds extra registers: with 64-element groups an 8-step
+// ring spills, so those take 4). Measured at T = 512, 128-element groups:
+// 8-step ring 1073 us per layer (234 VGPRs), 4-step 1088 us (153 VGPRs).
+#ifndef MOE_WIDE_GRP_RING
+#define MOE_WIDE_GRP_RING 8
+#endif
+template <int KIND, int GS>
+hipError_t launch_rings(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    constexpr int kMaxRing = GS == 1 ? 4 : GS == 2 ? MOE_WIDE_GRP_RING : 8;
+    if (kMaxRing == 8 && (k_dim / 64) % 8 == 0)
+        return launch_t<KIND, kWideWaves, 1, kWideTiles, kWideSlab, 8, GS>(a, max_chunks, k_dim, s, e0, e1);
+    return launch_t<KIND, kWideWaves, 1, kWideTiles, kWideSlab, 4, GS>(a, max_chunks, k_dim, s, e0, e1);
+}
+
+// k_dim is a multiple of 256, so rings of 4 steps always divide it; a group
+// (gsteps = 1, 2 or 4 steps) never straddles a slab of 4 steps
 template <int KIND>
 hipError_t launch_items(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     if (a.mt != kWideTiles) return hipErrorInvalidValue;
-    if ((k_dim / 64) % 8 == 0)
-        return launch_t<KIND, kWideWaves, 1, kWideTiles, kWideSlab, 8>(a, max_chunks, k_dim, s, e0, e1);
-    return launch_t<KIND, kWideWaves, 1, kWideTiles, kWideSlab, 4>(a, max_chunks, k_dim, s, e0, e1);
+    static_assert(kWideSlab % 4 == 0, "slabs hold whole groups of up to 4 steps");
+    switch (a.gsteps) {
+        case 0: return launch_rings<KIND, 0>(a, max_chunks, k_dim, s, e0, e1);
+        case 1: return launch_rings<KIND, 1>(a, max_chunks, k_dim, s, e0, e1);
+        case 2: return launch_rings<KIND, 2>(a, max_chunks, k_dim, s, e0, e1);
+        case 4: return launch_rings<KIND, 4>(a, max_chunks, k_dim, s, e0, e1);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
