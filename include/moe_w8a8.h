@@ -169,8 +169,14 @@ typedef struct {
 } moe_w8a8_debug_t;
 
 /* Workspace bytes that moe_w8a8_forward needs for these dims. The size depends
- * only on T, H, I, I_s, K and E_loc. Returns MOE_ERR_INVALID_ARG for NULL
- * arguments and the same size errors as moe_w8a8_forward. */
+ * only on T, H, I, I_s, K, E_loc and the options. The workspace holds every
+ * intermediate the launches of one call hand to each other, as FusedDeepMoE
+ * sec. 2.2 (workspace layout) does: the grouped rows' quantised GEMM1 input and
+ * its scales, the SwiGLU output, the quantised GEMM2 input and its scales, the
+ * GEMM2 output rows before combine, and the per-expert counts, prefix sum and
+ * row order; here also the GEMM work-item list and per-call counters. Returns
+ * MOE_ERR_INVALID_ARG for NULL arguments and the same size errors as
+ * moe_w8a8_forward. */
 MOE_W8A8_API moe_status_t moe_w8a8_workspace_size(const moe_w8a8_dims_t *dims, size_t *bytes);
 
 /*
