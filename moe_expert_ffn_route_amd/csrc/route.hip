@@ -247,6 +247,133 @@ __device__ void route_block(const RouteArgs &a) {
     }
 }
 
+// Exclusive prefix sum over the 64 lanes of a wave; *total gets the sum.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int *total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += o;
+    }
+    *total = __shfl(inc, kWave - 1, kWave);
+    return inc - v;
+}
+
+// Orders one wave's LDS accesses for the compiler; the hardware performs a
+// wave's LDS operations in issue order, so no barrier is needed between
+// lanes of one wave.
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+constexpr int kWaveExperts = (kMaxLocalExperts + kWave - 1) / kWave;  // local experts per lane
+
+// The same routing for batches of at most 64 pairs (decode), by one wave with
+// no workgroup barrier: lane p holds pair p; its rank among the pairs of its
+// expert comes from ballots on the expert id's bits, the per-expert counts go
+// to LDS through the first lane of each expert, and the exclusive prefixes
+// over experts (row offsets, chunk indices) are wave scans over blocks of
+// consecutive experts per lane. Same outputs as route_block.
+__device__ void route_wave(const RouteArgs &a) {
+    __shared__ int w_count[kMaxLocalExperts];
+    __shared__ int w_off[kMaxLocalExperts];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int E = a.E_loc, TK = a.T * a.K;
+    const int p = lane;
+    const int e = p < TK ? classify_pair(a, p) : kPairDropped;
+    const bool act_tok = lane < a.T && (!a.mask || a.mask[lane]);
+    for (int i = lane; i < a.n_zero; i += kWave) a.zero_words[i] = 0;
+    const bool valid = e >= 0;
+    unsigned long long peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 10; ++b) {  // expert ids < 1024
+        const bool bit = valid && ((e >> b) & 1);
+        const unsigned long long m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    const unsigned long long lower = peers & lanes_below(lane);
+    const int rank = __popcll(lower);
+    const int n_bad = __popcll(__ballot(e == kPairBad));
+    for (int x = lane; x < E; x += kWave) w_count[x] = 0;
+    wave_lds_fence();
+    if (valid && lower == 0ull) w_count[e] = __popcll(peers);
+    wave_lds_fence();
+
+    // exclusive prefix of the counts (row offsets) and of the chunks per
+    // expert: lane l covers experts [l * per, (l + 1) * per)
+    const int per = (E + kWave - 1) / kWave;
+    int cnt[kWaveExperts];
+    int rsum = 0, csum = 0;
+#pragma unroll
+    for (int j = 0; j < kWaveExperts; ++j) {
+        const int x = lane * per + j;
+        cnt[j] = j < per && x < E ? w_count[x] : 0;
+        rsum += cnt[j];
+        csum += (cnt[j] + a.chunk_rows - 1) / a.chunk_rows;
+    }
+    int P, n_routed_chunks;
+    int roff = wave_exclusive_scan(rsum, &P);
+    int coff = wave_exclusive_scan(csum, &n_routed_chunks);
+#pragma unroll
+    for (int j = 0; j < kWaveExperts; ++j) {
+        const int x = lane * per + j;
+        if (j < per && x < E) {
+            w_off[x] = roff;
+            a.counts_out[x] = cnt[j];
+            a.offsets[x] = roff;
+            const int nch = (cnt[j] + a.chunk_rows - 1) / a.chunk_rows;
+            for (int i = 0; i < nch; ++i) {
+                const int r = i * a.chunk_rows;
+                a.chunks[coff + i] =
+                    make_int4(x, roff + r, min(a.chunk_rows, cnt[j] - r) | (nch << kChunkCountShift), i);
+            }
+            roff += cnt[j];
+            coff += nch;
+        }
+    }
+    wave_lds_fence();
+
+    // rows of the kept pairs
+    if (p < TK) {
+        if (valid) {
+            const int pos = w_off[e] + rank;
+            a.row_of_pair[p] = pos;
+            a.sorted_pair[pos] = p;
+            a.row_token[pos] = p / a.K;
+            a.row_group[pos] = e;
+        } else {
+            a.row_of_pair[p] = -1;
+        }
+    }
+    // shared-expert rows: active tokens in token order, after the routed rows
+    int t_act;
+    const int ti = wave_exclusive_scan(act_tok ? 1 : 0, &t_act);
+    if (act_tok) {
+        if (a.has_shared) {
+            a.row_token[P + ti] = lane;
+            a.row_group[P + ti] = E;
+        }
+        if (a.dbg_shared_token) a.dbg_shared_token[ti] = lane;
+    }
+    int n_chunks = n_routed_chunks;
+    if (a.has_shared) {
+        const int nch = (t_act + a.chunk_rows - 1) / a.chunk_rows;
+        for (int i = lane; i < nch; i += kWave) {
+            const int r = i * a.chunk_rows;
+            a.chunks[n_routed_chunks + i] =
+                make_int4(E, P + r, min(a.chunk_rows, t_act - r) | (nch << kChunkCountShift), i);
+        }
+        n_chunks += nch;
+    }
+    if (lane == 0) {
+        a.offsets[E] = P;
+        a.offsets[E + 1] = P + t_act;
+        a.meta[kMetaP] = P;
+        a.meta[kMetaTAct] = t_act;
+        a.meta[kMetaBad] = n_bad;
+        a.meta[kMetaChunks] = n_chunks;
+    }
+}
+
 constexpr int kTokQuantSlots = kRouteThreads / kTPR;  // rows quantised per block
 
 // Rows the quantisation blocks of the routing launch work on: the tokens (when
@@ -300,7 +427,12 @@ __device__ __forceinline__ int quant_units(const TokQuantArgs &q) {
 template <bool FP8, int GL>
 __global__ __launch_bounds__(kRouteThreads) void route_quant_kernel(RouteArgs a, TokQuantArgs q) {
     if (blockIdx.x == 0) {
-        route_block(a);
+        // up to 64 pairs: one wave routes, the block's other waves leave
+        if (a.T * a.K <= kWave) {
+            if (threadIdx.x < kWave) route_wave(a);
+        } else {
+            route_block(a);
+        }
         return;
     }
     __shared__ float s_part[kTokQuantSlots * (kTPR / kWave)];

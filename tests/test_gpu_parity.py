@@ -72,6 +72,14 @@ SMALL = {
     "fused_wide_ep_smooth": spec(T=60, H=512, I=256, E_g=16, K=4, ep_size=2, ep_rank=1, active=50, smooth=True,
                                  fuse_route_scale=True, seed=152),
     "fused_tall_split_gemm2": spec(T=300, H=512, I=256, E_g=2, K=2, I_s=512, fuse_route_scale=True, seed=153),
+    # batches of at most 64 (token, k) pairs are routed by one wave: the
+    # largest expert count (512 local experts, 8 per lane), 64 tokens of top-1
+    # (32-row items, a shared expert of 64 rows in two chunks), masks, bad ids
+    # and an EP share
+    "wave_routing_e512_k16": spec(T=4, H=256, I=256, E_g=512, K=16, I_s=256, seed=181),
+    "wave_routing_t64_k1_shared": spec(T=64, H=256, I=256, E_g=8, K=1, I_s=256, active=60, seed=182),
+    "wave_routing_ep_share_mask": spec(T=21, H=512, I=256, E_g=64, K=3, ep_size=4, ep_rank=1, active=17,
+                                       smooth=True, seed=183),
 }
 
 
