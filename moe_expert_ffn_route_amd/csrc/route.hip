@@ -374,6 +374,176 @@ __device__ void route_wave(const RouteArgs &a) {
     }
 }
 
+// Exclusive scan of four values at once over the 1024 threads of the block
+// (one barrier); *total gets the block sums. s_tmp holds kRouteWaves int4.
+__device__ int4 block_exclusive_scan4(int4 v, int4 *s_tmp, int4 *total) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    int4 inc = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int ox = __shfl_up(inc.x, d, kWave), oy = __shfl_up(inc.y, d, kWave);
+        const int oz = __shfl_up(inc.z, d, kWave), ow = __shfl_up(inc.w, d, kWave);
+        if (lane >= d) {
+            inc.x += ox;
+            inc.y += oy;
+            inc.z += oz;
+            inc.w += ow;
+        }
+    }
+    if (lane == kWave - 1) s_tmp[wave] = inc;
+    __syncthreads();
+    int4 before = make_int4(0, 0, 0, 0), all = make_int4(0, 0, 0, 0);
+    for (int w = 0; w < kRouteWaves; ++w) {
+        const int4 c = s_tmp[w];
+        if (w < wave) {
+            before.x += c.x;
+            before.y += c.y;
+            before.z += c.z;
+            before.w += c.w;
+        }
+        all.x += c.x;
+        all.y += c.y;
+        all.z += c.z;
+        all.w += c.w;
+    }
+    *total = all;
+    return make_int4(before.x + inc.x - v.x, before.y + inc.y - v.y, before.z + inc.z - v.z, before.w + inc.w - v.w);
+}
+
+constexpr int kFastRounds = 4;  // 64-pair rounds per wave: up to 4096 pairs
+
+// The routing for 64 < T*K <= 4096 pairs and T <= 1024 tokens with four
+// workgroup barriers. Wave w takes the consecutive pairs [w L, (w + 1) L)
+// (L a multiple of 64), so the stable (expert, pair) order is: the pairs of
+// lower waves, then this wave's earlier rounds, then the lower lanes of this
+// round. Each wave keeps its running per-expert counts in a row of LDS of its
+// own (a wave's LDS operations complete in issue order, so no barrier is
+// needed within a wave); one pass per expert then turns the rows into
+// per-wave prefixes, and one block scan of four values gives the experts' row
+// offsets and chunk indices, the shared rows' positions and the count of ids
+// out of range. Same outputs as route_block.
+__device__ void route_block_fast(const RouteArgs &a) {
+    __shared__ int f_tbl[kRouteWaves][kMaxLocalExperts];
+    __shared__ int f_off[kMaxLocalExperts];
+    __shared__ int4 f_tmp[kRouteWaves];
+    __shared__ uint32_t f_stage[kRouteStage];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const int E = a.E_loc, TK = a.T * a.K;
+    const int L = (TK + kRouteThreads - 1) / kRouteThreads * kWave;  // pairs per wave
+    const int rounds = L / kWave;
+
+    int e_r[kFastRounds];
+#pragma unroll
+    for (int j = 0; j < kFastRounds; ++j) {
+        const int p = wave * L + j * kWave + lane;
+        e_r[j] = j < rounds && p < TK ? classify_pair(a, p) : kPairDropped;
+    }
+    const bool tok_act = tid < a.T && (!a.mask || a.mask[tid]);
+    for (int i = tid; i < a.n_zero; i += kRouteThreads) a.zero_words[i] = 0;
+
+    // 1. this wave's pairs: position among its own pairs of the same expert
+    for (int x = lane; x < E; x += kWave) f_tbl[wave][x] = 0;
+    wave_lds_fence();
+    int pos_w[kFastRounds];
+    int n_bad = 0;
+#pragma unroll
+    for (int j = 0; j < kFastRounds; ++j) {
+        pos_w[j] = 0;
+        if (j >= rounds) continue;  // uniform
+        const int e = e_r[j];
+        const bool valid = e >= 0;
+        n_bad += e == kPairBad;
+        unsigned long long peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 10; ++b) {
+            const bool bit = valid && ((e >> b) & 1);
+            const unsigned long long m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        const unsigned long long lower = peers & lanes_below(lane);
+        const int base = valid ? f_tbl[wave][e] : 0;
+        wave_lds_fence();
+        pos_w[j] = base + __popcll(lower);
+        if (valid && lower == 0ull) f_tbl[wave][e] = base + __popcll(peers);
+        wave_lds_fence();
+    }
+    __syncthreads();
+
+    // 2. per expert (thread x): prefix over the waves in place, and the total
+    int cnt = 0;
+    if (tid < E) {
+        for (int w = 0; w < kRouteWaves; ++w) {
+            const int v = f_tbl[w][tid];
+            f_tbl[w][tid] = cnt;
+            cnt += v;
+        }
+    }
+    const int nch = (cnt + a.chunk_rows - 1) / a.chunk_rows;
+    // 3. row offsets and chunk indices of the experts, shared rows, bad ids
+    int4 tot;
+    const int4 ex = block_exclusive_scan4(make_int4(cnt, nch, tok_act ? 1 : 0, n_bad), f_tmp, &tot);
+    const int P = tot.x, t_act = tot.z;
+    if (tid < E) f_off[tid] = ex.x;
+    __syncthreads();
+
+    // 4. rows of the kept pairs, collected in LDS in row order
+#pragma unroll
+    for (int j = 0; j < kFastRounds; ++j) {
+        const int p = wave * L + j * kWave + lane;
+        if (j < rounds && p < TK) {
+            const int e = e_r[j];
+            if (e >= 0) {
+                const int pos = f_off[e] + f_tbl[wave][e] + pos_w[j];
+                a.row_of_pair[p] = pos;
+                f_stage[pos] = (static_cast<uint32_t>(e) << kStagePairBits) | static_cast<uint32_t>(p);
+            } else {
+                a.row_of_pair[p] = -1;
+            }
+        }
+    }
+    if (tid < E) {
+        a.counts_out[tid] = cnt;
+        a.offsets[tid] = ex.x;
+        for (int i = 0; i < nch; ++i) {
+            const int r = i * a.chunk_rows;
+            a.chunks[ex.y + i] = make_int4(tid, ex.x + r, min(a.chunk_rows, cnt - r) | (nch << kChunkCountShift), i);
+        }
+    }
+    if (tok_act) {
+        if (a.has_shared) {
+            a.row_token[P + ex.z] = tid;
+            a.row_group[P + ex.z] = E;
+        }
+        if (a.dbg_shared_token) a.dbg_shared_token[ex.z] = tid;
+    }
+    int n_chunks = tot.y;
+    if (a.has_shared) {
+        const int sch = (t_act + a.chunk_rows - 1) / a.chunk_rows;
+        for (int i = tid; i < sch; i += kRouteThreads) {
+            const int r = i * a.chunk_rows;
+            a.chunks[tot.y + i] = make_int4(E, P + r, min(a.chunk_rows, t_act - r) | (sch << kChunkCountShift), i);
+        }
+        n_chunks += sch;
+    }
+    if (tid == 0) {
+        a.offsets[E] = P;
+        a.offsets[E + 1] = P + t_act;
+        a.meta[kMetaP] = P;
+        a.meta[kMetaTAct] = t_act;
+        a.meta[kMetaBad] = tot.w;
+        a.meta[kMetaChunks] = n_chunks;
+    }
+    __syncthreads();
+    for (int r = tid; r < P; r += kRouteThreads) {
+        const uint32_t v = f_stage[r];
+        const int p = static_cast<int>(v & ((1u << kStagePairBits) - 1u));
+        a.sorted_pair[r] = p;
+        a.row_token[r] = p / a.K;
+        a.row_group[r] = static_cast<int>(v >> kStagePairBits);
+    }
+}
+
 constexpr int kTokQuantSlots = kRouteThreads / kTPR;  // rows quantised per block
 
 // Rows the quantisation blocks of the routing launch work on: the tokens (when
@@ -430,6 +600,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_quant_kernel(RouteArgs a,
         // up to 64 pairs: one wave routes, the block's other waves leave
         if (a.T * a.K <= kWave) {
             if (threadIdx.x < kWave) route_wave(a);
+        } else if (a.T * a.K <= kFastRounds * kRouteThreads && a.T <= kRouteThreads) {
+            route_block_fast(a);
         } else {
             route_block(a);
         }
