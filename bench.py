@@ -207,13 +207,22 @@ def gemm_traffic(workload, kernel_prefix):
 
 
 def gemm1_kernel_prefix(case, mx):
-    """Name prefix of the GEMM1 kernel the library picks for this batch."""
-    if mx:
-        return "void gemm_mx_kernel<1,"
+    """Name prefix of the GEMM1 kernel the library picks for this batch (the
+    work-item rules of the C ABI: 16-row items up to 16 tokens; FP4 weights
+    and group-wise scales 32-row items when the local experts can average 16
+    rows, on the two-tile kernels; otherwise 256-row tall items when they can
+    average 256 rows, else 32-row wide items)."""
     s = case.spec
-    if s.T <= 16 or getattr(s, "quant_group", 0):
-        return "void gemm_kernel<1,"
-    if s.T >= 256 and s.T * s.K // s.ep_size >= 256 * s.E_loc:
+    grp = getattr(s, "quant_group", 0)
+    rows_per_expert = s.T * s.K // s.ep_size
+    if s.T <= 16:
+        return "void gemm_mx_kernel<1," if mx else "void gemm_kernel<1,"
+    if mx or grp:
+        two_tiles = rows_per_expert >= 16 * s.E_loc
+        if mx:
+            return "void gemm_mx_wide_kernel<1," if two_tiles else "void gemm_mx_kernel<1,"
+        return "void gemm_wide_kernel<1," if two_tiles else "void gemm_kernel<1,"
+    if s.T >= 256 and rows_per_expert >= 256 * s.E_loc:
         return "void gemm_tall_kernel<1,"
     return "void gemm_wide_kernel<1,"
 
