@@ -61,6 +61,14 @@ CASES = {
     "scale_stride_34": (spec(T=5, H=256, I=4096, I_s=4352, E_g=2, K=1, seed=510), None),
     "t1": (spec(T=1, I_s=512, seed=508), None),
     "t0": (spec(T=0, I_s=256, seed=509), None),
+    # 32-row items on the wide kernel with each group size (64: a 4-step
+    # weight ring; 128 and 256: 8 steps), an EP share, masks and smooth
+    # scales, a shared expert whose intermediate differs
+    "wide_g64_ep_mask": (spec(T=48, H=1024, I=512, E_g=8, K=4, ep_size=2, ep_rank=1, active=44, smooth=True,
+                              I_s=768, quant_group=64, seed=514), None),
+    "wide_g128_shared_smooth": (spec(T=40, H=2048, I=1024, E_g=2, K=2, I_s=512, share_smooth=True,
+                                     quant_group=128, seed=515), None),
+    "wide_g256_long_k": (spec(T=36, H=4096, I=768, E_g=2, K=1, I_s=256, quant_group=256, seed=516), None),
     # the decode workload's shape with 128-element groups (every token)
     "decode_full_shape": (spec(T=8, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1235), None),
     # the large-batch workload's shape (two-tile items): every other token,
@@ -89,11 +97,12 @@ def _random_specs(n, seed=6060):
     for i in range(n):
         G = int(rng.choice([64, 128, 256]))
         E_g = int(rng.choice([2, 4, 8, 16]))
-        T = int(rng.choice([1, 5, 8, 16, 17, 30]))
+        T = int(rng.choice([1, 5, 8, 16, 17, 30, 40, 64]))
+        ep = int(rng.choice([d for d in (1, 2) if E_g % d == 0]))
         kw = dict(name=f"grprandom{i}", T=T, H=int(rng.choice([1, 2, 3, 4])) * 256 * (2 if G == 256 else 1),
                   I=int(rng.choice([256, 512])), E_g=E_g, K=int(rng.integers(1, min(E_g, 6) + 1)),
                   I_s=int(rng.choice([0, 256, 512])), routing=str(rng.choice(["uniform", "zipf"])),
-                  quant_group=G, seed=600 + i)
+                  ep_size=ep, ep_rank=int(rng.integers(0, ep)), quant_group=G, seed=600 + i)
         if rng.random() < 0.4:
             kw["active"] = int(rng.integers(0, T + 1))
         if rng.random() < 0.4:
@@ -102,7 +111,7 @@ def _random_specs(n, seed=6060):
     return out
 
 
-RANDOM = _random_specs(8)
+RANDOM = _random_specs(14)
 
 
 @pytest.mark.parametrize("i", range(len(RANDOM)))
