@@ -43,6 +43,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 #ifndef MOE_TBIG_Q
 #define MOE_TBIG_Q 2
 #endif
+#ifndef MOE_TALL_XCD
+#define MOE_TALL_XCD 1
+#endif
 constexpr int kTWaves = MOE_TBIG_WAVES;             // a grid of kTWM (rows) x kTWN (weight tiles)
 constexpr int kTThreads = kTWaves * kWave;
 constexpr int kTWN = MOE_TBIG_WN;
@@ -74,17 +77,28 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tall_kernel(GemmArgs a, int
     const int wm = wave % kTWM, wn = wave / kTWM;
     const int r16 = lane & 15, kg = lane >> 4;
 
-    // Work item = (chunk, group of 8 tile pairs), linear in blockIdx; a
-    // group of several chunks puts the chunks of one N group 8 blocks apart
-    // (same XCD, in flight together: the weights come from HBM once).
-    int c = blockIdx.x / a.n_tiles;
-    int nt = blockIdx.x % a.n_tiles;
-    int4 ch = a.chunks[c];  // c < max_chunks: inside the chunk list even when unused
-    if (c >= a.meta[a.count_word]) return;
+    // Work item = (chunk, group of 8 tile pairs), chunk-major; within a group
+    // of several chunks the items are ordered by 8 N groups, then chunk, so
+    // the chunks of one N group are 8 items apart and in flight together.
+    const int n_chunks = a.meta[a.count_word];
+    int b = blockIdx.x;
+#if MOE_TALL_XCD
+    // XCD-aware order: the dispatcher hands block b to XCD b % 8, so the first
+    // n8 = (items & ~7) blocks are renumbered to give XCD x the consecutive
+    // items [x n8 / 8, (x + 1) n8 / 8): an expert's chunks and all their N
+    // groups run on one XCD, whose L2 then serves both the weight tiles (read
+    // by every chunk) and the activation chunks (read by every N group).
+    const int n8 = (n_chunks * a.n_tiles) & ~7;
+    if (b < n8) b = (b & 7) * (n8 >> 3) + (b >> 3);
+#endif
+    int c = b / a.n_tiles;
+    int nt = b % a.n_tiles;
+    if (c >= n_chunks) return;
+    int4 ch = a.chunks[c];
     const int nch = ch.z >> kChunkCountShift;
     if (nch > 1 && (a.n_tiles & 7) == 0) {
         const int c0 = c - ch.w;
-        const int i = blockIdx.x - c0 * a.n_tiles;
+        const int i = b - c0 * a.n_tiles;
         const int q = i / (8 * nch), rem = i - q * 8 * nch;
         c = c0 + rem / 8;
         nt = q * 8 + rem % 8;
