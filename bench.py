@@ -46,6 +46,24 @@ MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix rate, published (no spars
 MFMA_F8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix rate, published (an FP8 x FP4 product runs at it)
 MFMA_I8_OPS_PER_CLK_CU = 8192  # the per-CU rate at which 256 CUs at 2.4 GHz reach the published figure
 HIP_ATTR_CLOCK_RATE = 5  # hipDeviceAttributeClockRate (peak clock, kHz) in hip_runtime_api.h
+START_GATE_CYCLES = 2_000_000  # about 1 ms of a one-thread sleep kernel (see start_gate)
+
+
+def start_gate(stream, enabled=True):
+    """Enqueue a bounded one-thread sleep kernel (torch.cuda._sleep, about
+    1 ms) on `stream` ahead of a timed region's start event. The GPU is idle
+    after the synchronisation that opens the region, so without it the start
+    event would fire at once and the region would also time the host's
+    latency to enqueue the first step; with it the host has enqueued the
+    first steps by the time the start event fires, and the region times the
+    device running the K steps back to back. Returns whether it gated (False
+    when disabled or when this torch build has no sleep kernel)."""
+    sleep = getattr(torch.cuda, "_sleep", None)
+    if not enabled or sleep is None:
+        return False
+    with torch.cuda.stream(stream):
+        sleep(START_GATE_CYCLES)
+    return True
 
 
 def log(*a):
@@ -264,13 +282,13 @@ class Leg:
         self.runner = moe.Runner(dims)
 
 
-def measure(leg, steps, warmup, stream, fence_free, kernel_events=True, graphs=None, after_step=None):
+def measure(leg, steps, warmup, stream, fence_free, kernel_events=True, graphs=None, after_step=None, gate=True):
     """Time `steps` forwards of one leg (step i on weight copy i % copies).
     Returns µs per step, GEMM1 / GEMM2 kernel durations from events bound to
     their launches, per-stage times (marker events, separate pass) and the
     per-step distribution (one marker per step boundary, separate pass).
     after_step(i), if given, is called after step i is enqueued (in every
-    pass)."""
+    pass). gate: open the timed region and the per-step pass with start_gate."""
     runner, layers = leg.runner, leg.layers
     hook = after_step or (lambda i: None)
     n_ev = len(binding.STAGES) + 1
@@ -305,6 +323,7 @@ def measure(leg, steps, warmup, stream, fence_free, kernel_events=True, graphs=N
     t_start = TimingEvent(fence_free)
     t_stop = TimingEvent(fence_free)
     torch.cuda.synchronize()
+    gated = start_gate(stream, gate)
     with torch.cuda.stream(stream):
         t_start.record(stream)
         for i in range(steps):
@@ -333,8 +352,11 @@ def measure(leg, steps, warmup, stream, fence_free, kernel_events=True, graphs=N
         g1_us = stage_us["gemm1"]
         timing = "marker HIP events between stages (per-stage pass)"
     timing += ", hipEventDisableSystemFence" if fence_free else ", default event flags"
+    timing += ", region opened behind a 1 ms sleep kernel" if gated else ", region opened on an idle GPU"
 
     bounds = [TimingEvent(fence_free) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    start_gate(stream, gate)
     with torch.cuda.stream(stream):
         bounds[0].record(stream)
         for i in range(steps):
@@ -354,7 +376,7 @@ def measure(leg, steps, warmup, stream, fence_free, kernel_events=True, graphs=N
                 p=(p10, p50, p90), timing=timing, counts=runner.expert_token_nums.cpu().numpy())
 
 
-def large_batch_record(base_case, layers, wkeys, weight_layout, steps, warmup, stream, fence_free):
+def large_batch_record(base_case, layers, wkeys, weight_layout, steps, warmup, stream, fence_free, gate=True):
     """The T = 512 half of the metric: the large-batch workload (same model as
     the decode workload, so the resident weight copies are reused; only the
     512 tokens' activations are generated), timed like the decode step.
@@ -370,7 +392,7 @@ def large_batch_record(base_case, layers, wkeys, weight_layout, steps, warmup, s
     dims4 = moe.dims_of_case(case4)
     dims4.weight_layout = weight_layout
     leg = Leg(case4, legs, dims4)
-    m = measure(leg, steps, warmup, stream, fence_free)
+    m = measure(leg, steps, warmup, stream, fence_free, gate=gate)
     counts = m["counts"]
     layer_bytes, g1_bytes, g2_bytes, touched, rows = algorithmic_bytes(case4, counts)
     g1_ops, g2_ops = gemm_ops(case4, counts)
@@ -431,6 +453,9 @@ def main():
                          "(moe_w8a8_warm), overlapping that layer's routing launch")
     ap.add_argument("--no-large-batch", action="store_true",
                     help="skip the T = 512 leg (large_batch_t512) of the default decode line")
+    ap.add_argument("--no-start-gate", action="store_true",
+                    help="start the timed region on an idle GPU (the region then also times the host's latency "
+                         "to enqueue the first step) instead of behind a 1 ms sleep kernel")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the GEMM kernel events (GEMM times then come from the "
                          "per-stage pass)")
@@ -527,7 +552,7 @@ def main():
             moe.moe_w8a8_warm(nxt["share_gmm1_weight_scale"], stream=side)
     log(f"[bench] warmup {args.warmup} steps, timing {args.steps} steps (three passes)")
     m = measure(leg, args.steps, args.warmup, stream, fence_free, kernel_events=not args.no_kernel_events,
-                graphs=graphs, after_step=after_step)
+                graphs=graphs, after_step=after_step, gate=not args.no_start_gate)
     counts = m["counts"]
     g1_us, g2_us, stage_us, timing = m["g1_us"], m["g2_us"], m["stage_us"], m["timing"]
     p10, p50, p90 = m["p"]
@@ -593,7 +618,8 @@ def main():
     if headline and not args.no_large_batch and not graphs:
         log("[bench] large-batch leg (T = 512, same resident weights)")
         rec["large_batch_t512"] = large_batch_record(case, layers, wkeys, dims.weight_layout, args.steps,
-                                                     args.warmup, stream, fence_free)
+                                                     args.warmup, stream, fence_free,
+                                                     gate=not args.no_start_gate)
     if args.no_cpu_baseline:
         rec["cpu_baseline"] = None
     else:

@@ -54,6 +54,11 @@ SMALL = {
     # weight tiles, so the two chunks of a group run 8 blocks apart
     "tall_two_chunks_grouped": spec(T=512, H=256, I=1024, E_g=1, K=1, I_s=256, seed=141),
     "tall_three_chunks_ragged": spec(T=700, H=512, I=256, E_g=1, K=1, seed=142),
+    # XCD-ordered tall items: 4 experts of one or two ragged chunks (262, 279,
+    # 244, 255 rows) and a shared expert of 3 chunks with I_s != I (a split
+    # GEMM2): 36 GEMM1 items, so the first 32 are renumbered over the 8 XCDs
+    # and the last 4 keep their order
+    "tall_xcd_order_ragged_split": spec(T=520, H=1024, I=512, E_g=4, K=2, I_s=256, seed=145),
     "tall_mask_smooth_split_gemm2": spec(T=290, H=768, I=256, E_g=2, K=2, I_s=512, active=270, smooth=True,
                                          share_smooth=True, seed=115),
     "tall_skewed": spec(T=600, H=256, I=256, E_g=2, K=1, routing="zipf", zipf_s=2.0, I_s=256, seed=116),
