@@ -195,6 +195,30 @@ def mfma_peak_on_device():
             "tops": round(cus * khz.value * 1e3 * MFMA_I8_OPS_PER_CLK_CU / 1e12, 1)}
 
 
+READ_PROBE_BYTES = 2 << 30  # 8x the 256 MB memory-side cache
+
+
+def hbm_read_probe(stream, fence_free, reps=5):
+    """The HBM read rate this device reaches: moe_w8a8_read_probe (the GEMMs'
+    weight-stream access pattern, nothing else) over a 2 GiB range, one
+    untimed pass, then `reps` timed passes (HIP events on the launch stream).
+    Returns the median GB/s and the passes' figures."""
+    buf = torch.empty(READ_PROBE_BYTES, dtype=torch.uint8, device="cuda")  # contents are never used
+    evs = [TimingEvent(fence_free) for _ in range(reps + 1)]
+    with torch.cuda.stream(stream):
+        moe.moe_w8a8_read_probe(buf, stream=stream)
+        for i in range(reps):
+            evs[i].record(stream)
+            moe.moe_w8a8_read_probe(buf, stream=stream)
+        evs[reps].record(stream)
+    torch.cuda.synchronize()
+    gbs = [READ_PROBE_BYTES / (evs[i].elapsed_time(evs[i + 1]) * 1e-3) / 1e9 for i in range(reps)]
+    del buf
+    return {"gbps": round(float(np.median(gbs)), 1), "passes_gbps": [round(g, 1) for g in gbs],
+            "bytes": READ_PROBE_BYTES, "entry_point": "moe_w8a8_read_probe",
+            "pattern": "1 KB contiguous per wave load, non-temporal, 8 loads in flight per wave, whole chip"}
+
+
 def gemm_traffic(workload, kernel_prefix):
     """HBM bytes per launch of the kernel whose name starts with
     `kernel_prefix`, from the committed rocprofv3 counter summary of this
@@ -578,6 +602,11 @@ def main():
         roofline = {"kernel": "gemm1_swiglu", "bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "algorithmic_bytes": gemm1_bytes, "avg_us": round(g1_us, 2), "timing": timing}
+    log("[bench] HBM read probe")
+    read_probe = hbm_read_probe(stream, fence_free)
+    if roofline["bound"] == "hbm":
+        roofline["measured_peak"] = read_probe["gbps"]
+        roofline["frac_of_measured_peak"] = round(g1_gbs / read_probe["gbps"], 4)
     headline = args.config == 1 and not mx and not args.quant_group
     rec = {
         "metric": ("µs per MoE layer (T=8 decode); achieved HBM GB/s in hbm_gbps; INT8 TOP/s at T=512 in "
@@ -609,6 +638,7 @@ def main():
         "tops": round(tops, 2),
         "mfma_i8_frac": None if mx else round(tops / MFMA_I8_PEAK_TOPS, 5),
         "mfma_i8_peak_derived": mfma_peak_on_device(),
+        "hbm_read_probe": read_probe,
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},  # separate pass, every stage bracketed
         "roofline": roofline,
         "gemm2": {"achieved": round(gemm2_bytes / (g2_us * 1e-6) / 1e9, 1), "unit": "GB/s",
@@ -620,6 +650,9 @@ def main():
         rec["large_batch_t512"] = large_batch_record(case, layers, wkeys, dims.weight_layout, args.steps,
                                                      args.warmup, stream, fence_free,
                                                      gate=not args.no_start_gate)
+        for g in ("gemm1", "gemm2"):
+            lb = rec["large_batch_t512"][g]
+            lb["frac_of_measured_peak"] = round(lb["achieved_gbps"] / read_probe["gbps"], 4)
     if args.no_cpu_baseline:
         rec["cpu_baseline"] = None
     else:

@@ -337,6 +337,20 @@ MOE_W8A8_API moe_status_t moe_w8a8_pack_weights_mx(const uint8_t *data, const ui
  */
 MOE_W8A8_API moe_status_t moe_w8a8_warm(const void *ptr, size_t bytes, void *stream);
 
+/*
+ * Read-bandwidth probe, for measurement only: read the device range
+ * [ptr, ptr + bytes) once on `stream` over the whole chip, with the access
+ * pattern of the GEMMs' weight stream (each wave loads 1 KB contiguous per
+ * instruction, non-temporal, eight loads in flight), and discard the data.
+ * Timing it over a range larger than the 256 MB memory-side cache gives the
+ * HBM read rate this device reaches, the measured counterpart of the
+ * published peak that a memory-bound kernel's roofline fraction is set
+ * against. No value anywhere changes. ptr 16-byte aligned, bytes a multiple
+ * of 16 (MOE_ERR_INVALID_ARG otherwise); bytes == 0 is a no-op.
+ * Stream-ordered, no allocation.
+ */
+MOE_W8A8_API moe_status_t moe_w8a8_read_probe(const void *ptr, size_t bytes, void *stream);
+
 /* Static description of a status code. Never NULL. */
 MOE_W8A8_API const char *moe_w8a8_status_string(moe_status_t status);
 

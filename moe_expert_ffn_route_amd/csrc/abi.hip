@@ -158,6 +158,12 @@ extern "C" moe_status_t moe_w8a8_warm(const void *ptr, size_t bytes, void *strea
     return launch_warm(ptr, bytes, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+extern "C" moe_status_t moe_w8a8_read_probe(const void *ptr, size_t bytes, void *stream) {
+    if (bytes == 0) return MOE_OK;
+    if (!ptr || !aligned(ptr, 16) || bytes % 16) return MOE_ERR_INVALID_ARG;
+    return launch_read_probe(ptr, bytes, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 extern "C" const char *moe_w8a8_status_string(moe_status_t s) {
     switch (s) {
         case MOE_OK: return "ok";

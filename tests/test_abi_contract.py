@@ -258,6 +258,7 @@ def test_noalloc_scratch_size_matches_header():
 @pytest.mark.parametrize("ptr,nbytes,code", [
     (None, 16, binding.MOE_ERR_INVALID_ARG), (FAKE + 8, 16, binding.MOE_ERR_INVALID_ARG),
     (FAKE, 24, binding.MOE_ERR_INVALID_ARG), (None, 0, binding.MOE_OK), (FAKE, 0, binding.MOE_OK)])
-def test_warm_rejects_bad_arguments(lib, ptr, nbytes, code):
+@pytest.mark.parametrize("entry", ["moe_w8a8_warm", "moe_w8a8_read_probe"])
+def test_warm_and_read_probe_reject_bad_arguments(lib, entry, ptr, nbytes, code):
     # zero bytes is a no-op that launches nothing, whatever the pointer
-    assert lib.moe_w8a8_warm(ptr, nbytes, None) == code
+    assert getattr(lib, entry)(ptr, nbytes, None) == code

@@ -465,3 +465,15 @@ def test_cache_warm_changes_no_result():
     # the warmed tensors themselves are untouched
     for k, v in nxt.items():
         assert torch.equal(v, t[k])
+
+
+@pytest.mark.parametrize("nbytes", [16, 1024, 4096 + 48, 8 << 20, (64 << 20) + 16 * 37])
+def test_read_probe_reads_and_changes_nothing(nbytes):
+    # the bandwidth probe only reads: its range, and a guard band written
+    # after it, keep every byte, for whole and ragged last wave passes
+    buf = torch.randint(0, 256, (nbytes + 4096,), dtype=torch.uint8, device="cuda")
+    ref = buf.clone()
+    for _ in range(2):
+        moe.moe_w8a8_read_probe(buf, nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref)
