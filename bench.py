@@ -195,12 +195,12 @@ def mfma_peak_on_device():
             "tops": round(cus * khz.value * 1e3 * MFMA_I8_OPS_PER_CLK_CU / 1e12, 1)}
 
 
-READ_PROBE_BYTES = 2 << 30  # 8x the 256 MB memory-side cache
+READ_PROBE_BYTES = 8 << 30  # 32x the 256 MB memory-side cache, so the probe's own ramp and tail are < 1 %
 
 
 def hbm_read_probe(stream, fence_free, reps=5):
     """The HBM read rate this device reaches: moe_w8a8_read_probe (the GEMMs'
-    weight-stream access pattern, nothing else) over a 2 GiB range, one
+    weight-stream access pattern, nothing else) over an 8 GiB range, one
     untimed pass, then `reps` timed passes (HIP events on the launch stream).
     Returns the median GB/s and the passes' figures."""
     buf = torch.empty(READ_PROBE_BYTES, dtype=torch.uint8, device="cuda")  # contents are never used
