@@ -591,30 +591,12 @@ hipError_t launch_w(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s,
 // Group-wise scales (a.gsteps = GS steps of 64 per group): every wave's K
 // slice must hold whole groups, so K is split over W = min(8, groups) waves
 // (groups = k_dim / (64 * GS), a power-of-two count is not required: W is the
-// largest of 8, 4, 2, 1 dividing it). One row tile (MT = 1): a slice of up
-// to 8 steps is one batch, longer slices go in batches of one group. Two row
-// tiles (32-row items): batches of one group (MOE_GRP_WIDE_BATCH).
-// Two row tiles: batches of one group (0), or of 4 steps where they fit (4).
-// Measured on the T = 512 workload with 128-element groups: one group per
-// batch 1246 us per layer (GEMM1 774 us), 4-step batches 1438 us (GEMM1 979
-// us at 184 VGPRs, two waves per SIMD).
-#ifndef MOE_GRP_WIDE_BATCH
-#define MOE_GRP_WIDE_BATCH 0
-#endif
-template <int KIND, bool PACKED, int GS, int W, int MT>
+// largest of 8, 4, 2, 1 dividing it). A slice of up to 8 steps is one batch,
+// longer slices go in batches of one group. (Chunks of two row tiles take
+// the wide kernel of gemm_wide.hip instead.)
+template <int KIND, bool PACKED, int GS, int W>
 hipError_t launch_grp_w(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const int spw = k_dim / (64 * W);
-    if constexpr (MT == 2) {
-        if (MOE_GRP_WIDE_BATCH == 4 && spw % 4 == 0) {
-            const int np = spw / 4;
-            if (np == 1) launch_one<KIND, W, 4, PACKED, 2, 1, GS>(a, grid, k_dim, 1, s, e0, e1);
-            else if (np == 2) launch_one<KIND, W, 4, PACKED, 2, 2, GS>(a, grid, k_dim, 2, s, e0, e1);
-            else launch_one<KIND, W, 4, PACKED, 2, 0, GS>(a, grid, k_dim, np, s, e0, e1);
-        } else {
-            launch_one<KIND, W, GS, PACKED, 2, 0, GS>(a, grid, k_dim, spw / GS, s, e0, e1);
-        }
-        return hipGetLastError();
-    }
     switch (spw) {
         case GS: launch_one<KIND, W, GS, PACKED, 1, 1, GS>(a, grid, k_dim, 1, s, e0, e1); break;
         case 2 * GS: launch_one<KIND, W, 2 * GS, PACKED, 1, 1, GS>(a, grid, k_dim, 1, s, e0, e1); break;
@@ -631,21 +613,21 @@ hipError_t launch_grp_w(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, 
     return hipGetLastError();
 }
 
-template <int KIND, bool PACKED, int GS, int MT>
+template <int KIND, bool PACKED, int GS>
 hipError_t launch_grp(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const int groups = k_dim / (64 * GS);
-    if (groups % 8 == 0) return launch_grp_w<KIND, PACKED, GS, 8, MT>(a, grid, k_dim, s, e0, e1);
-    if (groups % 4 == 0) return launch_grp_w<KIND, PACKED, GS, 4, MT>(a, grid, k_dim, s, e0, e1);
-    if (groups % 2 == 0) return launch_grp_w<KIND, PACKED, GS, 2, MT>(a, grid, k_dim, s, e0, e1);
-    return launch_grp_w<KIND, PACKED, GS, 1, MT>(a, grid, k_dim, s, e0, e1);
+    if (groups % 8 == 0) return launch_grp_w<KIND, PACKED, GS, 8>(a, grid, k_dim, s, e0, e1);
+    if (groups % 4 == 0) return launch_grp_w<KIND, PACKED, GS, 4>(a, grid, k_dim, s, e0, e1);
+    if (groups % 2 == 0) return launch_grp_w<KIND, PACKED, GS, 2>(a, grid, k_dim, s, e0, e1);
+    return launch_grp_w<KIND, PACKED, GS, 1>(a, grid, k_dim, s, e0, e1);
 }
 
-template <int KIND, bool PACKED, int MT>
+template <int KIND, bool PACKED>
 hipError_t launch_grp_p(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     switch (a.gsteps) {
-        case 1: return launch_grp<KIND, PACKED, 1, MT>(a, grid, k_dim, s, e0, e1);
-        case 2: return launch_grp<KIND, PACKED, 2, MT>(a, grid, k_dim, s, e0, e1);
-        case 4: return launch_grp<KIND, PACKED, 4, MT>(a, grid, k_dim, s, e0, e1);
+        case 1: return launch_grp<KIND, PACKED, 1>(a, grid, k_dim, s, e0, e1);
+        case 2: return launch_grp<KIND, PACKED, 2>(a, grid, k_dim, s, e0, e1);
+        case 4: return launch_grp<KIND, PACKED, 4>(a, grid, k_dim, s, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
@@ -653,15 +635,12 @@ hipError_t launch_grp_p(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, 
 template <int KIND>
 hipError_t launch_kind(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     if (a.gsteps > 0) {
-        if ((a.mt != 1 && a.mt != 2) || k_dim % (64 * a.gsteps)) return hipErrorInvalidValue;
+        if (a.mt != 1 || k_dim % (64 * a.gsteps)) return hipErrorInvalidValue;
         const long blocks = static_cast<long>(max_chunks) * a.n_tiles;
         if (blocks <= 0) return hipSuccess;
         const dim3 grid(static_cast<unsigned>(blocks));
-        if (a.mt == 2)
-            return a.packed ? launch_grp_p<KIND, true, 2>(a, grid, k_dim, s, e0, e1)
-                            : launch_grp_p<KIND, false, 2>(a, grid, k_dim, s, e0, e1);
-        return a.packed ? launch_grp_p<KIND, true, 1>(a, grid, k_dim, s, e0, e1)
-                        : launch_grp_p<KIND, false, 1>(a, grid, k_dim, s, e0, e1);
+        return a.packed ? launch_grp_p<KIND, true>(a, grid, k_dim, s, e0, e1)
+                        : launch_grp_p<KIND, false>(a, grid, k_dim, s, e0, e1);
     }
     constexpr int W = KIND == 1 ? MOE_GEMM1_WAVES : MOE_GEMM2_WAVES;
     constexpr int KS = KIND == 1 ? MOE_GEMM1_KSTEPS : MOE_GEMM2_KSTEPS;

@@ -9,10 +9,12 @@
 //     h = (y_g / (1 + exp(-y_g))) * y_u.
 //   GEMM2: acc over q_h and W2 likewise; z = bf16((acc * w2s[n]) * hs[r]).
 //
-// The work decomposition is gemm.hip's decode one (chunks of 16 rows, or of 32
-// rows above 16 tokens, a 16-channel tile pair per workgroup, K split over the
-// waves, partial tiles summed in LDS, linear blockIdx so every XCD streams a
-// share of every expert); only the operands change:
+// Chunks of 16 rows take gemm.hip's decode decomposition (a 16-channel tile
+// pair per workgroup, K split over the waves, partial tiles summed in LDS,
+// linear blockIdx so every XCD streams a share of every expert); chunks of 32
+// rows (batches whose local experts average 16 rows or more) take the
+// two-tile kernel at the end of this file, which walks the whole K per wave.
+// Against the INT8 kernels only the operands change:
 //   - a K step is 128 elements: the FP8 A operand of lane l (row l % 16,
 //     g = l / 16) is 32 bytes, row bytes 16g .. +16 (register bytes 0..15)
 //     and 64 + 16g .. +16 (bytes 16..31) of the step; the FP4 B operand is 16
@@ -48,7 +50,7 @@ __device__ __forceinline__ v4i ld16_stream(const uint8_t *p) {
 // KIND 1 = GEMM1 + SwiGLU, 2 = GEMM2 + bf16. KS = 128-element K steps a wave
 // loads per batch; NPASS = batches per wave (0: n_pass_rt at run time); MT =
 // 16-row tiles per chunk (each weight fragment feeds all of them, so a chunk
-// reads its weights once).
+// reads its weights once; the library instantiates MT = 1).
 // (Four-wave one-tile blocks ask for three resident blocks per CU: the
 // register budget of three waves per SIMD, which the 8-step batch fits.)
 template <int KIND, int WAVES, int KS, int NPASS, int MT>
@@ -305,34 +307,21 @@ hipError_t launch_split(const GemmArgs &a, dim3 grid, int k_dim, int spw, hipStr
     return launch_one<KIND, W, 1, 0, MT>(a, grid, k_dim, spw, s, e0, e1);
 }
 
-// One row tile per chunk (batches of at most 16 tokens) splits K over
-// MOE_MX_WAVES waves; two row tiles (32-row chunks, larger batches) over 8,
-// which keeps a wave's A and weight registers of a batch within budget.
-#ifndef MOE_MX_WIDE_KS
-#define MOE_MX_WIDE_KS 0  // two row tiles: steps per batch (0: the whole slice when it is at most 8 steps)
-#endif
-template <int KIND, int MT>
-hipError_t launch_mt(const GemmArgs &a, dim3 grid, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    constexpr int W = MT == 1 ? MOE_MX_WAVES : 8;
-    const int steps = k_dim / kStepK;
-    if constexpr (MT == 2 && MOE_MX_WIDE_KS > 0) {
-        if (steps % (W * MOE_MX_WIDE_KS) == 0)
-            return launch_one<KIND, W, MOE_MX_WIDE_KS, 0, MT>(a, grid, k_dim, steps / (W * MOE_MX_WIDE_KS), s, e0,
-                                                               e1);
-    }
-    if (steps % W == 0) return launch_split<KIND, W, MT>(a, grid, k_dim, steps / W, s, e0, e1);
-    if (steps % 4 == 0) return launch_one<KIND, 4, 1, 0, MT>(a, grid, k_dim, steps / 4, s, e0, e1);
-    return launch_one<KIND, 2, 1, 0, MT>(a, grid, k_dim, steps / 2, s, e0, e1);
-}
-
+// Chunks of one row tile (batches of at most 16 tokens, or larger batches
+// whose local experts average fewer than 16 rows) split K over MOE_MX_WAVES
+// waves; chunks of two row tiles take the two-tile kernel below.
 template <int KIND>
 hipError_t launch_kind(const GemmArgs &a, int max_chunks, int k_dim, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     static_assert(MOE_MX_WAVES == 8 || MOE_MX_WAVES == 4, "MOE_MX_WAVES is 8 or 4");
-    if ((a.mt != 1 && a.mt != 2) || k_dim % 256) return hipErrorInvalidValue;
+    constexpr int W = MOE_MX_WAVES;
+    if (a.mt != 1 || k_dim % 256) return hipErrorInvalidValue;
     const long blocks = static_cast<long>(max_chunks) * a.n_tiles;
     if (blocks <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(blocks));
-    return a.mt == 1 ? launch_mt<KIND, 1>(a, grid, k_dim, s, e0, e1) : launch_mt<KIND, 2>(a, grid, k_dim, s, e0, e1);
+    const int steps = k_dim / kStepK;
+    if (steps % W == 0) return launch_split<KIND, W, 1>(a, grid, k_dim, steps / W, s, e0, e1);
+    if (steps % 4 == 0) return launch_one<KIND, 4, 1, 0, 1>(a, grid, k_dim, steps / 4, s, e0, e1);
+    return launch_one<KIND, 2, 1, 0, 1>(a, grid, k_dim, steps / 2, s, e0, e1);
 }
 
 // ---------------------------------------------------------------------------
