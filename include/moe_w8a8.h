@@ -208,6 +208,14 @@ MOE_W8A8_API moe_status_t moe_w8a8_workspace_size(const moe_w8a8_dims_t *dims, s
  *                     need not be zeroed; contents are undefined afterwards
  *  dbg                NULL in production; else intermediates (above)
  *  stream             hipStream_t to launch on (NULL = the default stream)
+ *
+ * Values: x, the routing weights, the weight scales and the smooth scales are
+ * taken to be finite (the block the pages describe defines nothing else). A
+ * NaN or infinity in a token's inputs makes that token's rows and outputs
+ * unspecified; every row of the block is computed independently of the other
+ * tokens, so the rest of the result is unaffected. Expert ids outside
+ * [0, moe_expert_num) drop their pair (the routing diagnostics word counts
+ * them); duplicated ids in one token's top-k are kept as separate pairs.
  */
 MOE_W8A8_API moe_status_t moe_w8a8_forward(const moe_w8a8_dims_t *dims,
                               const void *x,
