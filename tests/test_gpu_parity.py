@@ -274,6 +274,20 @@ def test_duplicate_expert_in_topk():
     check(dataclasses.replace(c, expert_ids=ids))
 
 
+@pytest.mark.parametrize("T,packed", [(12, True), (40, False)], ids=["decode", "wide"])
+def test_non_finite_token_leaves_other_tokens_exact(T, packed):
+    # a NaN and an infinity in one token's x make only that token's rows
+    # unspecified: routing, and every stage of every other token, still match
+    # the oracle (which is run on those tokens only)
+    c = synth.make_case(spec(T=T, H=512, I=256, E_g=8, K=3, I_s=256, seed=118))
+    x = c.x.copy()
+    x[3, 5] = 0x7FC0   # bf16 NaN
+    x[3, 17] = 0x7F80  # bf16 +inf
+    others = [t for t in range(T) if t != 3]
+    stats, gpu, _ = check(dataclasses.replace(c, x=x), tokens=others, packed=packed)
+    assert stats["rows"] > 0
+
+
 def test_deterministic_dirty_workspace_and_side_stream():
     c = synth.make_case(spec(T=33, H=512, I=512, E_g=8, K=4, I_s=256, seed=113))
     t = moe.upload(c)
