@@ -54,6 +54,11 @@ SMALL = {
     # weight tiles, so the two chunks of a group run 8 blocks apart
     "tall_two_chunks_grouped": spec(T=512, H=256, I=1024, E_g=1, K=1, I_s=256, seed=141),
     "tall_three_chunks_ragged": spec(T=700, H=512, I=256, E_g=1, K=1, seed=142),
+    # tall items with long contractions: GEMM1 over H = 8192 (128 stages of
+    # the four-buffer copy ring), and GEMM2 over I = 4096 (its GEMM1 has 32
+    # N groups; the shared expert's I_s = 512 takes a second GEMM2 launch)
+    "tall_long_k_gemm1": spec(T=260, H=8192, I=512, E_g=1, K=1, seed=146),
+    "tall_long_k_gemm2": spec(T=270, H=512, I=4096, E_g=1, K=1, I_s=512, seed=147),
     # XCD-ordered tall items: 4 experts of one or two ragged chunks (262, 279,
     # 244, 255 rows) and a shared expert of 3 chunks with I_s != I (a split
     # GEMM2): 36 GEMM1 items, so the first 32 are renumbered over the 8 XCDs
