@@ -1,13 +1,17 @@
 """GPU parity: the HIP path, called through the C ABI, against the CPU oracle
 on the same seeded inputs, stage by stage (tolerances in gpu_util.py).
 
-Small cases run the whole oracle; they span several MFMA row tiles, several
-64-row chunks per expert, ragged tails, masks, expert-parallel shares, smooth
-scales, a shared expert whose intermediate differs from the routed one, and
-the degenerate cases (T = 0, T = 1, every token masked, ids out of range).
-The five named workloads (and the compute-bound probe) run at full size with
-every token through the oracle, whose tokens are split over the host's
-threads.
+Small cases run the whole oracle (the tiny workload among them); they span
+every work-item size (16-, 32- and 256-row chunks, several per expert, ragged
+tails, the XCD-ordered tall items), masks, expert-parallel shares, smooth
+scales, a shared expert whose intermediate differs from the routed one, the
+fused route scale, requantisation in GEMM1's epilogue, seeded random shapes,
+and the degenerate cases (T = 0, T = 1, every token masked, ids out of range,
+duplicated ids, a token with non-finite inputs). The four larger workloads and
+the compute-bound probe run at full size with every token through the oracle,
+whose tokens are split over the host's threads. Graph replay, timing events,
+dirty workspaces, shrinking batches, the cache warm and the read probe are
+checked for changing nothing they should not.
 """
 import dataclasses
 
