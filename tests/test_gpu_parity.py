@@ -58,6 +58,11 @@ SMALL = {
     # weight tiles, so the two chunks of a group run 8 blocks apart
     "tall_two_chunks_grouped": spec(T=512, H=256, I=1024, E_g=1, K=1, I_s=256, seed=141),
     "tall_three_chunks_ragged": spec(T=700, H=512, I=256, E_g=1, K=1, seed=142),
+    # the DeepSeek-V3 hidden size (H = 7168 = 28 x 256, not a power of two) on
+    # each item size: decode with I = 2048, 32-row items, tall items
+    "h7168_decode": spec(T=8, H=7168, I=2048, E_g=16, K=4, I_s=2048, seed=148),
+    "h7168_wide": spec(T=40, H=7168, I=512, E_g=8, K=2, I_s=512, seed=149),
+    "h7168_tall": spec(T=260, H=7168, I=512, E_g=1, K=1, seed=150),
     # tall items with long contractions: GEMM1 over H = 8192 (128 stages of
     # the four-buffer copy ring), and GEMM2 over I = 4096 (its GEMM1 has 32
     # N groups; the shared expert's I_s = 512 takes a second GEMM2 launch)
