@@ -69,6 +69,10 @@ CASES = {
     "wide_g128_shared_smooth": (spec(T=40, H=2048, I=1024, E_g=2, K=2, I_s=512, share_smooth=True,
                                      quant_group=128, seed=515), None),
     "wide_g256_long_k": (spec(T=36, H=4096, I=768, E_g=2, K=1, I_s=256, quant_group=256, seed=516), None),
+    # the DeepSeek-V3 hidden size H = 7168 (56 groups of 128: 8 waves of 7
+    # one-group batches) on 16-row and 32-row items
+    "h7168_g128_decode": (spec(T=8, H=7168, I=1024, E_g=8, K=3, I_s=512, quant_group=128, seed=517), None),
+    "h7168_g128_wide": (spec(T=40, H=7168, I=512, E_g=2, K=2, I_s=256, quant_group=128, seed=518), None),
     # the decode workload's shape with 128-element groups (every token)
     "decode_full_shape": (spec(T=8, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1235), None),
     # the large-batch workload's shape (two-tile items): every other token,

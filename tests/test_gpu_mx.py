@@ -58,6 +58,11 @@ CASES = {
     # steps), and I 2048 (16 steps: an 8-step ring in two turns)
     "t40_rings_2_and_4": (spec(T=40, H=768, I=512, E_g=2, K=2, I_s=256, seed=315), None),
     "t36_ring_8_two_turns": (spec(T=36, H=1024, I=2048, E_g=2, K=2, I_s=1024, active=33, seed=316), None),
+    # the DeepSeek-V3 hidden size H = 7168: 56 steps of 128, so the K-split
+    # kernel's waves take 14 steps in 7 batches of 2, and the two-tile
+    # kernel's 8-step ring turns 7 times
+    "h7168_decode": (spec(T=8, H=7168, I=1024, E_g=8, K=3, I_s=512, seed=317), None),
+    "h7168_two_tile": (spec(T=40, H=7168, I=512, E_g=2, K=2, I_s=256, seed=318), None),
     "t1": (spec(T=1, H=512, I=256, E_g=4, K=2, I_s=512, seed=308), None),
     # H 2048 (16 steps: 4 waves x 4), I 3072 (24 steps: 4 waves x 6)
     "mid_k": (spec(T=9, H=2048, I=3072, E_g=4, K=2, I_s=1024, seed=312), None),
