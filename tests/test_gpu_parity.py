@@ -63,6 +63,18 @@ SMALL = {
     "h7168_decode": spec(T=8, H=7168, I=2048, E_g=16, K=4, I_s=2048, seed=148),
     "h7168_wide": spec(T=40, H=7168, I=512, E_g=8, K=2, I_s=512, seed=149),
     "h7168_tall": spec(T=260, H=7168, I=512, E_g=1, K=1, seed=150),
+    # decode batches at the production intermediate sizes (I = 1024, 2048):
+    # masks, a shared expert, EP shares, smooth and fused route scales, T = 1
+    # with K = 16, 16 tokens over 512 local experts with top-16 (272 chunks),
+    # one expert with 16 rows, and the H = 4096 decode shape
+    "dec_i1024_mask_shared": spec(T=12, H=512, I=1024, E_g=8, K=3, I_s=1024, active=9, seed=171),
+    "dec_i2048_ep_smooth": spec(T=16, H=768, I=2048, E_g=32, K=6, ep_size=4, ep_rank=1, smooth=True, seed=172),
+    "dec_fused_share_smooth": spec(T=8, H=512, I=1024, E_g=16, K=4, I_s=1024, fuse_route_scale=True,
+                                   share_smooth=True, seed=173),
+    "dec_t1_k16": spec(T=1, H=1024, I=1024, E_g=32, K=16, I_s=1024, seed=174),
+    "dec_t16_k16_e512": spec(T=16, H=256, I=1024, E_g=512, K=16, seed=175),
+    "dec_one_expert_16_rows": spec(T=16, H=512, I=1024, E_g=1, K=1, I_s=1024, seed=176),
+    "dec_h4096": spec(T=8, H=4096, I=2048, E_g=16, K=8, I_s=2048, active=7, seed=177),
     # tall items with long contractions: GEMM1 over H = 8192 (128 stages of
     # the four-buffer copy ring), and GEMM2 over I = 4096 (its GEMM1 has 32
     # N groups; the shared expert's I_s = 512 takes a second GEMM2 launch)
@@ -130,6 +142,8 @@ FIN = {
     "fin_ignored_above_16_tokens": spec(T=40, H=512, I=256, E_g=4, K=2, I_s=512, requant_in_epilogue=True,
                                         seed=168),
     "fin_decode_h4096": spec(T=8, H=4096, I=2048, E_g=16, K=4, I_s=2048, requant_in_epilogue=True, seed=169),
+    "fin_i1024_mask": spec(T=12, H=512, I=1024, E_g=8, K=3, I_s=1024, active=9, requant_in_epilogue=True,
+                               seed=170),
 }
 
 
