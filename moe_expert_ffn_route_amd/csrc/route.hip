@@ -4,14 +4,18 @@
 // reused across calls must be reset per call, which this kernel does by
 // rebuilding every index it owns from scratch).
 //
-// One workgroup of 1024 threads (16 waves) does the whole job: the problem is
-// at most a few thousand (token, k) pairs, so the cost is a handful of LDS
-// passes. The order of rows is a stable counting sort keyed by
-// (local expert, token, k): within each round of 1024 pairs, a wave finds the
-// lanes that share its expert with ballots on the expert id's bits, ranks
-// itself with a popcount of the lower lanes, and adds the counts of the lower
-// waves and of earlier rounds. No step depends on the order of atomics, so the
-// result is deterministic.
+// Block 0 of the launch routes (the other blocks quantise x); the order of
+// rows is a stable counting sort keyed by (local expert, token, k), and no
+// step depends on the order of atomics, so the result is deterministic. Three
+// paths by the number of (token, k) pairs, all with the same outputs:
+//   - at most 64 pairs (decode): one wave, no workgroup barrier (route_wave);
+//   - up to 4096 pairs and 1024 tokens: the 16 waves take consecutive runs
+//     of pairs, keep per-wave running counts in LDS, and meet at four
+//     barriers (route_block_fast);
+//   - beyond that, rounds of 1024 pairs: within a round a wave finds the
+//     lanes that share its expert with ballots on the expert id's bits, ranks
+//     itself with a popcount of the lower lanes, and adds the counts of the
+//     lower waves and of earlier rounds (route_block).
 #include "internal.h"
 #include "rowquant.h"
 
