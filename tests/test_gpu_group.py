@@ -9,8 +9,7 @@ group path takes (8, 4, 2 and 1 waves; a batch of whole groups, or one group
 per batch over several passes), 16- and 32-row items with several chunks per
 expert, masks, smooth scales, an EP share, a shared expert with a different
 intermediate (two GEMM2 launches), T = 0 / 1, and the full shapes of the
-decode workload (every token) and of the T = 512 workload (every other
-token).
+decode workload and of the T = 512 workload (every token of both).
 """
 import numpy as np
 import pytest
@@ -75,10 +74,9 @@ CASES = {
     "h7168_g128_wide": (spec(T=40, H=7168, I=512, E_g=2, K=2, I_s=256, quant_group=128, seed=518), None),
     # the decode workload's shape with 128-element groups (every token)
     "decode_full_shape": (spec(T=8, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1235), None),
-    # the large-batch workload's shape (two-tile items): every other token,
-    # 2304 grouped rows
-    "t512_full_shape": (spec(T=512, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1238, wseed=1235),
-                        list(range(1, 512, 2))),
+    # the large-batch workload's shape (two-tile items), every token: all
+    # 4608 grouped rows
+    "t512_full_shape": (spec(T=512, H=4096, I=2048, E_g=256, K=8, I_s=2048, seed=1238, wseed=1235), None),
 }
 
 
