@@ -113,6 +113,13 @@ def moe_w8a8_workspace_size(dims: Dims) -> int:
     return int(n.value)
 
 
+def _stream(stream):
+    """The HIP stream handle to pass: torch's current stream when None."""
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else stream
+
+
 def moe_w8a8_pack_weights(src, which, dst=None, stream=None):
     """Pack an int8 weight tensor [groups, n, k] or [n, k] (device) into the
     kernels' streaming order; `which` is MOE_PACK_GMM1 for a gmm1 tensor and
@@ -120,20 +127,10 @@ def moe_w8a8_pack_weights(src, which, dst=None, stream=None):
     if dst is None:
         dst = torch.empty_like(src)
     shape = src.shape if src.dim() == 3 else (1, *src.shape)
-    if stream is None:
-        stream = torch.cuda.current_stream().cuda_stream
-    elif isinstance(stream, torch.cuda.Stream):
-        stream = stream.cuda_stream
-    rc = library().moe_w8a8_pack_weights(_ptr(src), _ptr(dst), shape[0], shape[1], shape[2], which, stream)
+    rc = library().moe_w8a8_pack_weights(_ptr(src), _ptr(dst), shape[0], shape[1], shape[2], which, _stream(stream))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_w8a8_pack_weights")
     return dst
-
-
-def _stream(stream):
-    if stream is None:
-        return torch.cuda.current_stream().cuda_stream
-    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else stream
 
 
 def moe_w8a8_warm(t, nbytes: Optional[int] = None, stream=None) -> None:
@@ -191,9 +188,9 @@ def _ptr(t) -> Optional[int]:
     if isinstance(t, int):
         return t
     if not t.is_cuda:
-        raise ValueError("tensors passed to moe_w8a8_forward must be device tensors")
+        raise ValueError("tensors passed to libmoe_w8a8 must be device tensors")
     if not t.is_contiguous():
-        raise ValueError("tensors passed to moe_w8a8_forward must be contiguous")
+        raise ValueError("tensors passed to libmoe_w8a8 must be contiguous")
     return t.data_ptr()
 
 
@@ -205,10 +202,6 @@ def moe_w8a8_forward(dims: Dims, x, expert_ids, expert_scales, gmm1_weight, gmm1
                      dbg: Optional[Debug] = None, stream=None, check: bool = True) -> int:
     """Call the C entry point with device tensors (or raw device addresses).
     Returns the status code; raises MoeError on failure when check=True."""
-    if stream is None:
-        stream = torch.cuda.current_stream().cuda_stream
-    elif isinstance(stream, torch.cuda.Stream):
-        stream = stream.cuda_stream
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [x, expert_ids, expert_scales, gmm1_weight, gmm1_weight_scale, gmm2_weight, gmm2_weight_scale,
@@ -216,7 +209,7 @@ def moe_w8a8_forward(dims: Dims, x, expert_ids, expert_scales, gmm1_weight, gmm1
             expert_smooth_scales, share_smooth_scales, x_active_mask, output, share_output, expert_token_nums,
             workspace]
     rc = library().moe_w8a8_forward(ctypes.byref(dims), *[_ptr(a) for a in args], workspace_bytes,
-                                    ctypes.byref(dbg) if dbg is not None else None, stream)
+                                    ctypes.byref(dbg) if dbg is not None else None, _stream(stream))
     if check and rc != MOE_OK:
         raise MoeError(rc, "moe_w8a8_forward")
     return rc
