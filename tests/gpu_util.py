@@ -18,6 +18,7 @@ Tolerances (checked in compare()):
 """
 from __future__ import annotations
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -33,6 +34,30 @@ F32 = synth.bf16_bits_to_f32
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def with_floor_rows(case, zero=(), tiny=(), seed=0, cols=slice(None)):
+    """x with token rows (or the columns `cols` of them) at the amax floor:
+    `zero` rows all zero, `tiny` rows N(0, 1) * 3e-9 (|x| about 1e-8 at most,
+    far below eps = 1e-6, also after smooth scales of at most 2). Every
+    quantiser of those rows (or groups) then divides by eps instead of their
+    maximum; whole floored rows give h rows of zero or about 1e-15, which take
+    the floor again in requantisation."""
+    x = case.x.copy()
+    rng = np.random.default_rng(seed)
+    for t in zero:
+        x[t, cols] = 0
+    for t in tiny:
+        x[t, cols] = synth.f32_to_bf16_bits((rng.standard_normal(x[t, cols].shape) * 3e-9).astype(np.float32))
+    return dataclasses.replace(case, x=x)
+
+
+def grouped_row_tokens(case, ref):
+    """Token of every grouped row: the routed pairs in the oracle's grouped
+    order, then one shared-expert row per active token."""
+    K, P = case.spec.K, ref["P"]
+    n = P + (ref["T_act"] if case.spec.I_s else 0)
+    return [int(ref["sorted_pair"][r]) // K if r < P else int(ref["shared_token"][r - P]) for r in range(n)]
 
 
 def run_gpu(case, tensors=None, dbg=True, stream=None, garbage_workspace=False, packed=False):

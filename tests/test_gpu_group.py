@@ -17,7 +17,7 @@ import torch
 
 from moe_expert_ffn_route_amd import synth
 import moe_expert_ffn_route_amd as moe
-from gpu_util import check_group, say
+from gpu_util import check_group, grouped_row_tokens, say, with_floor_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -91,6 +91,26 @@ def test_group_parity(name):
         stats, _, _ = check_group(c, tokens=tokens, packed=False)
         say(f"[grp] {name} row-major: {stats}")
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T,G", [(12, 128), (40, 64)], ids=["decode_g128", "wide_g64"])
+def test_group_amax_floor(T, G):
+    # one group of a row at the amax floor: token 0's first group all zero,
+    # token 2's second group far below eps; only those groups' scales are
+    # eps / 127, the row's other groups keep their own
+    c = synth.make_case(spec(T=T, H=512, I=256, E_g=4, K=2, I_s=256, quant_group=G, seed=530 + T))
+    c = with_floor_rows(c, zero=[0], seed=T, cols=slice(0, G))
+    c = with_floor_rows(c, tiny=[2], seed=T + 1, cols=slice(G, 2 * G))
+    stats, gpu, ref = check_group(c, packed=True)
+    say(f"[grp] amax floor T={T} G={G}: {stats}")
+    floor = np.float32(np.float32(c.spec.eps) * np.float32(1.0 / 127.0))
+    tok = grouped_row_tokens(c, ref)
+    for r, t in enumerate(tok):
+        if t == 0:
+            assert gpu["xs"][r, 0] == floor and not gpu["q_x"][r, :G].any() and gpu["xs"][r, 1] > floor
+        elif t == 2:
+            assert gpu["xs"][r, 1] == floor and gpu["xs"][r, 0] > floor
+    assert 0 in tok and 2 in tok
 
 
 def _random_specs(n, seed=6060):

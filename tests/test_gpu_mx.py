@@ -19,7 +19,7 @@ import torch
 
 import moe_expert_ffn_route_amd as moe
 from moe_expert_ffn_route_amd import synth
-from gpu_util import check_mx, pack_reference, say
+from gpu_util import check_mx, grouped_row_tokens, pack_reference, say, with_floor_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +86,25 @@ def test_mx_parity(name):
     stats, _, _ = check_mx(synth.make_case(sp), tokens=tokens)
     say(f"[mx] {name}: {stats}")
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [12, 40], ids=["decode", "two_tile"])
+def test_mx_amax_floor_rows(T):
+    # rows at the amax floor: the FP8 quantisers divide by eps (scale
+    # eps / 448) for x and again for h; all-zero rows give zero codes
+    c = synth.make_case(spec(T=T, H=512, I=256, E_g=4, K=2, I_s=256, smooth=True, seed=330 + T))
+    zero, tiny = [0, 7], [3, T - 1]
+    c = with_floor_rows(c, zero=zero, tiny=tiny, seed=T)
+    stats, gpu, ref = check_mx(c)
+    say(f"[mx] amax floor T={T}: {stats}")
+    floor = np.float32(np.float32(c.spec.eps) * np.float32(1.0 / 448.0))
+    tok = grouped_row_tokens(c, ref)
+    hit = [r for r in range(len(tok)) if tok[r] in zero + tiny]
+    assert len(hit) >= len(zero + tiny)
+    for r in hit:
+        assert gpu["xs"][r] == floor and gpu["hs"][r] == floor, f"row {r} (token {tok[r]})"
+        if tok[r] in zero:
+            assert not gpu["q_x"][r].any() and not gpu["q_h"][r].any()
 
 
 def _random_specs(n, seed=4242):

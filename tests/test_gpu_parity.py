@@ -7,7 +7,7 @@ tails, the XCD-ordered tall items), masks, expert-parallel shares, smooth
 scales, a shared expert whose intermediate differs from the routed one, the
 fused route scale, requantisation in GEMM1's epilogue, seeded random shapes,
 and the degenerate cases (T = 0, T = 1, every token masked, ids out of range,
-duplicated ids, a token with non-finite inputs). The four larger workloads and
+duplicated ids, a token with non-finite inputs, rows at the amax floor). The four larger workloads and
 the compute-bound probe run at full size with every token through the oracle,
 whose tokens are split over the host's threads. Graph replay, timing events,
 dirty workspaces, shrinking batches, the cache warm and the read probe are
@@ -22,7 +22,7 @@ import torch
 import moe_expert_ffn_route_amd as moe
 import oracle
 from moe_expert_ffn_route_amd import synth
-from gpu_util import check, compare, pack_reference, run_gpu, say
+from gpu_util import check, compare, grouped_row_tokens, pack_reference, run_gpu, say, with_floor_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -293,6 +293,30 @@ def test_out_of_range_ids_are_dropped_and_counted():
     c = dataclasses.replace(c, expert_ids=ids)
     stats, gpu, ref = check(c)
     assert gpu["num_rows"][2] == 3 == ref["n_bad"]
+
+
+@pytest.mark.parametrize("T,packed,smooth", [(12, True, False), (12, False, True), (40, True, True),
+                                             (40, False, False)],
+                         ids=["decode", "decode_smooth_rowmajor", "wide_smooth", "wide_rowmajor"])
+def test_amax_floor_rows(T, packed, smooth):
+    c = synth.make_case(spec(T=T, H=512, I=256, E_g=8, K=3, I_s=256, smooth=smooth, share_smooth=smooth,
+                             seed=120 + T))
+    zero, tiny = [0, 5], [2, T - 1]
+    c = with_floor_rows(c, zero=zero, tiny=tiny, seed=T)
+    stats, gpu, ref = check(c, packed=packed)
+    say(f"[parity] amax floor T={T}: {stats}")
+    # every grouped row of a floored token has the scale eps / 127 in both
+    # quantisations (its h is zero or about 1e-15) and, for an all-zero
+    # token, zero codes
+    floor = np.float32(np.float32(c.spec.eps) * np.float32(1.0 / 127.0))
+    tok = grouped_row_tokens(c, ref)
+    hit = [r for r in range(len(tok)) if tok[r] in zero + tiny]
+    assert len(hit) >= len(zero + tiny)
+    for r in hit:
+        assert gpu["xs"][r] == floor, f"row {r} (token {tok[r]}): scale {gpu['xs'][r]} is not eps / 127"
+        assert gpu["hs"][r] == floor, f"row {r} (token {tok[r]}): h scale {gpu['hs'][r]} is not eps / 127"
+        if tok[r] in zero:
+            assert not gpu["q_x"][r].any() and not gpu["q_h"][r].any()
 
 
 def test_duplicate_expert_in_topk():
