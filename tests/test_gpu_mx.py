@@ -13,6 +13,8 @@ whose intermediate differs (two GEMM2 launches), the fused route scale,
 T = 0 and T = 1, and the full shapes of the decode workload (every token) and
 of the T = 512 workload (32 tokens spread over the batch).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -105,6 +107,44 @@ def test_mx_amax_floor_rows(T):
         assert gpu["xs"][r] == floor and gpu["hs"][r] == floor, f"row {r} (token {tok[r]})"
         if tok[r] in zero:
             assert not gpu["q_x"][r].any() and not gpu["q_h"][r].any()
+
+
+def _e4m3_ties():
+    """Values v whose E4M3 encoding is an exact tie after the quantiser's
+    fp32 steps with a row maximum of 448 ((v * 448) * (1/448) == v): the
+    bf16-representable midpoints of neighbouring E4M3 values, subnormal ones
+    included, and their negatives."""
+    f = np.float32
+    inv = f(1) / f(448)
+    vals = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    mids = (vals[:-1] + vals[1:]) / 2
+    out = [f(m) for m in mids
+           if not (np.array([m], np.float32).view(np.uint32)[0] & 0xFFFF) and (f(m) * f(448)) * inv == f(m)]
+    return np.array(out + [-v for v in out], np.float32)
+
+
+@pytest.mark.parametrize("T", [12, 40], ids=["decode", "two_tile"])
+def test_mx_quant_ties_round_to_even(T):
+    # a token row whose maximum is 448: each value below lands exactly halfway
+    # between two E4M3 values, which the encoder rounds to the even code (the
+    # codes torch's float8_e4m3fn conversion gives)
+    ties = _e4m3_ties()
+    c = synth.make_case(spec(T=T, H=512, I=256, E_g=4, K=2, I_s=256, seed=340 + T))
+    t, n = 5, len(ties)
+    assert n >= 60
+    row = np.zeros(c.spec.H, np.float32)
+    row[0], row[1:1 + n] = 448.0, ties
+    x = c.x.copy()
+    x[t] = synth.f32_to_bf16_bits(row)
+    c = dataclasses.replace(c, x=x)
+    stats, gpu, ref = check_mx(c)
+    expect = torch.from_numpy(ties).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    tok = grouped_row_tokens(c, ref)
+    hit = [r for r in range(len(tok)) if tok[r] == t]
+    assert hit
+    for r in hit:
+        codes = gpu["q_x"][r].view(np.uint8)
+        assert codes[0] == 0x7E and np.array_equal(codes[1:1 + n], expect), f"row {r}"
 
 
 def _random_specs(n, seed=4242):

@@ -7,7 +7,8 @@ tails, the XCD-ordered tall items), masks, expert-parallel shares, smooth
 scales, a shared expert whose intermediate differs from the routed one, the
 fused route scale, requantisation in GEMM1's epilogue, seeded random shapes,
 and the degenerate cases (T = 0, T = 1, every token masked, ids out of range,
-duplicated ids, a token with non-finite inputs, rows at the amax floor). The four larger workloads and
+duplicated ids, a token with non-finite inputs, rows at the amax floor,
+exact rounding ties). The four larger workloads and
 the compute-bound probe run at full size with every token through the oracle,
 whose tokens are split over the host's threads. Graph replay, timing events,
 dirty workspaces, shrinking batches, the cache warm and the read probe are
@@ -317,6 +318,31 @@ def test_amax_floor_rows(T, packed, smooth):
         assert gpu["hs"][r] == floor, f"row {r} (token {tok[r]}): h scale {gpu['hs'][r]} is not eps / 127"
         if tok[r] in zero:
             assert not gpu["q_x"][r].any() and not gpu["q_h"][r].any()
+
+
+INT8_TIES = np.array([0.5, 1.5, 2.5, 3.5, 4.5, 6.5, 10.5, 62.5, 63.5, -0.5, -1.5, -2.5, -4.5, -63.5], np.float32)
+
+
+@pytest.mark.parametrize("T", [12, 40], ids=["decode", "wide"])
+def test_quant_ties_round_to_even(T):
+    # a token row whose maximum is 127: (v * 127) * (1/127) is then exactly v
+    # in fp32 for each v below, so every one of them is an exact tie, which
+    # the quantiser rounds to even (np.rint), not away from zero
+    c = synth.make_case(spec(T=T, H=512, I=256, E_g=8, K=3, I_s=256, seed=160 + T))
+    t, n = 4, len(INT8_TIES)
+    row = np.zeros(c.spec.H, np.float32)
+    row[0], row[1:1 + n] = 127.0, INT8_TIES
+    x = c.x.copy()
+    x[t] = synth.f32_to_bf16_bits(row)
+    c = dataclasses.replace(c, x=x)
+    stats, gpu, ref = check(c)
+    expect = np.rint(INT8_TIES).astype(np.int8)
+    tok = grouped_row_tokens(c, ref)
+    hit = [r for r in range(len(tok)) if tok[r] == t]
+    assert hit
+    for r in hit:
+        assert gpu["q_x"][r, 0] == 127 and np.array_equal(gpu["q_x"][r, 1:1 + n], expect), f"row {r}"
+        assert not gpu["q_x"][r, 1 + n:].any()
 
 
 def test_duplicate_expert_in_topk():
