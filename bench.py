@@ -446,16 +446,17 @@ def large_batch_record(base_case, layers, wkeys, weight_layout, steps, warmup, s
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--gpus", type=int, default=1, help="must be 1: the block runs on one GPU")
+    ap.add_argument("--steps", type=int, default=50, help="timed steps (one forward each)")
+    ap.add_argument("--warmup", type=int, default=10, help="untimed steps before the timed region")
     ap.add_argument("--config", type=int, default=1,
                     help="workload index (0-4; 1 is the headline decode step; 5 is the supplementary "
                          "compute-bound probe)")
     ap.add_argument("--layers", type=int, default=4, help="weight copies cycled through to keep the cache cold")
     ap.add_argument("--row-major", action="store_true",
                     help="stream the weights in their row-major layout instead of the packed one")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the CPU oracle (cpu_baseline and cpu_baseline_all_cores)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB 5 times (calibrates HBM byte counters)")
     ap.add_argument("--graph", action="store_true",
