@@ -154,6 +154,17 @@ def algorithmic_bytes(case, counts):
     return touched * per_expert + shared + act, gemm1, gemm2, touched, rows
 
 
+def gemm_write_bytes(case, counts):
+    """Bytes each GEMM writes (part of its algorithmic bytes): GEMM1 the fp32 h
+    rows (4 * max(I, I_s) per grouped row), GEMM2 the bf16 z rows and shared
+    output rows (2 * H per routed row and per active token)."""
+    s = case.spec
+    routed = int(counts.sum())
+    t_act = s.T if case.mask is None else int(np.count_nonzero(case.mask))
+    rows = routed + (t_act if s.I_s else 0)
+    return rows * 4 * max(s.I, s.I_s), rows * 2 * s.H
+
+
 def layer_ops(case, counts):
     """Integer multiply-adds (x2) of the two GEMMs: 2 * rows * 3 * H * I for
     the routed rows and the same with I_s for the shared rows."""
@@ -217,6 +228,32 @@ def hbm_read_probe(stream, fence_free, reps=5):
     return {"gbps": round(float(np.median(gbs)), 1), "passes_gbps": [round(g, 1) for g in gbs],
             "bytes": READ_PROBE_BYTES, "entry_point": "moe_w8a8_read_probe",
             "pattern": "1 KB contiguous per wave load, non-temporal, 8 loads in flight per wave, whole chip"}
+
+
+def hbm_read_write_probe(stream, fence_free, read_bytes, write_bytes, reps=5):
+    """The time a GEMM's byte mix takes on this device: moe_w8a8_read_write_probe
+    reads `read_bytes` (rounded down to whole 256 KB work items, the time scaled
+    back up) with the larger-batch GEMMs' weight-stream pattern and writes
+    `write_bytes` in equal shares at the items' ends, as those GEMMs write their
+    output rows. One untimed pass, then `reps` timed passes; returns the median
+    time in µs and the passes' figures."""
+    item = 256 * 1024
+    src_bytes = (read_bytes // item) * item
+    dst_bytes = min((write_bytes // 16) * 16, src_bytes)
+    src = torch.empty(src_bytes, dtype=torch.uint8, device="cuda")  # contents are never used
+    dst = torch.empty(max(16, dst_bytes), dtype=torch.uint8, device="cuda")
+    evs = [TimingEvent(fence_free) for _ in range(reps + 1)]
+    with torch.cuda.stream(stream):
+        moe.moe_w8a8_read_write_probe(src, src_bytes, dst, dst_bytes, stream=stream)
+        for i in range(reps):
+            evs[i].record(stream)
+            moe.moe_w8a8_read_write_probe(src, src_bytes, dst, dst_bytes, stream=stream)
+        evs[reps].record(stream)
+    torch.cuda.synchronize()
+    us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 * read_bytes / src_bytes for i in range(reps)]
+    del src, dst
+    return {"us": round(float(np.median(us)), 2), "passes_us": [round(u, 2) for u in us],
+            "read_bytes": read_bytes, "write_bytes": write_bytes, "entry_point": "moe_w8a8_read_write_probe"}
 
 
 def gemm_traffic(workload, kernel_prefix):
@@ -419,6 +456,7 @@ def large_batch_record(base_case, layers, wkeys, weight_layout, steps, warmup, s
     m = measure(leg, steps, warmup, stream, fence_free, gate=gate)
     counts = m["counts"]
     layer_bytes, g1_bytes, g2_bytes, touched, rows = algorithmic_bytes(case4, counts)
+    g1_write, g2_write = gemm_write_bytes(case4, counts)
     g1_ops, g2_ops = gemm_ops(case4, counts)
     us = m["us"]
     tops = layer_ops(case4, counts) / (us * 1e-6) / 1e12
@@ -429,12 +467,12 @@ def large_batch_record(base_case, layers, wkeys, weight_layout, steps, warmup, s
         "tops": round(tops, 1), "mfma_i8_frac": round(tops / MFMA_I8_PEAK_TOPS, 4),
         "hbm_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
         "hbm_frac": round(layer_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-        "gemm1": {"avg_us": round(m["g1_us"], 2), "algorithmic_bytes": g1_bytes,
+        "gemm1": {"avg_us": round(m["g1_us"], 2), "algorithmic_bytes": g1_bytes, "write_bytes": g1_write,
                   "achieved_gbps": round(g1_bytes / (m["g1_us"] * 1e-6) / 1e9, 1),
                   "hbm_frac": round(g1_bytes / (m["g1_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                   "tops": round(g1_ops / (m["g1_us"] * 1e-6) / 1e12, 1),
                   "traffic": gemm_traffic(spec4.name, gemm1_kernel_prefix(case4, False))},
-        "gemm2": {"avg_us": round(m["g2_us"], 2), "algorithmic_bytes": g2_bytes,
+        "gemm2": {"avg_us": round(m["g2_us"], 2), "algorithmic_bytes": g2_bytes, "write_bytes": g2_write,
                   "achieved_gbps": round(g2_bytes / (m["g2_us"] * 1e-6) / 1e9, 1),
                   "hbm_frac": round(g2_bytes / (m["g2_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                   "tops": round(g2_ops / (m["g2_us"] * 1e-6) / 1e12, 1)},
@@ -654,6 +692,13 @@ def main():
         for g in ("gemm1", "gemm2"):
             lb = rec["large_batch_t512"][g]
             lb["frac_of_measured_peak"] = round(lb["achieved_gbps"] / read_probe["gbps"], 4)
+            # the same byte mix (reads, and the writes among the algorithmic
+            # bytes) as a probe: the ceiling for a kernel that must write its
+            # output rows while its weights stream
+            w = lb["write_bytes"]
+            rw = hbm_read_write_probe(stream, fence_free, lb["algorithmic_bytes"] - w, w)
+            lb["read_write_probe"] = rw
+            lb["frac_of_read_write_probe"] = round(rw["us"] / lb["avg_us"], 4)
     if args.no_cpu_baseline:
         rec["cpu_baseline"] = None
     else:

@@ -359,6 +359,25 @@ MOE_W8A8_API moe_status_t moe_w8a8_warm(const void *ptr, size_t bytes, void *str
  */
 MOE_W8A8_API moe_status_t moe_w8a8_read_probe(const void *ptr, size_t bytes, void *stream);
 
+/*
+ * Read-and-write probe, for measurement only: the larger-batch GEMMs' weight
+ * stream together with their output writes. [src, src + src_bytes) is read in
+ * work items of 256 KB (one two-wave workgroup each, six resident per CU;
+ * each wave reads two 64 KB tiles in 1 KB steps through a ring of eight
+ * non-temporal loads per tile), and every item then writes its equal share
+ * of [dst, dst + dst_bytes) with 16-byte stores, as a GEMM workgroup writes
+ * its output rows after its contraction. Timing it with a GEMM's own read and
+ * write byte counts gives the rate that mix reaches on the device: writes to
+ * HBM while the read stream saturates it cost several times their bytes.
+ * src is not changed; dst receives arbitrary values. src 16-byte aligned,
+ * src_bytes a multiple of 262144 (0 is a no-op); dst_bytes a multiple of 16
+ * and at most src_bytes; dst 16-byte aligned and not overlapping src when
+ * dst_bytes > 0 (MOE_ERR_INVALID_ARG otherwise). Stream-ordered, no
+ * allocation.
+ */
+MOE_W8A8_API moe_status_t moe_w8a8_read_write_probe(const void *src, size_t src_bytes, void *dst, size_t dst_bytes,
+                                                    void *stream);
+
 /* Static description of a status code. Never NULL. */
 MOE_W8A8_API const char *moe_w8a8_status_string(moe_status_t status);
 

@@ -6,7 +6,7 @@ seeded synthetic inputs.
 """
 from .binding import (Debug, Dims, MoeError, Runner, debug_buffers, dims_of_case, library, make_dims,  # noqa: F401
                       moe_w8a8_forward, moe_w8a8_forward_noalloc, moe_w8a8_pack_weights, moe_w8a8_pack_weights_mx,
-                      moe_w8a8_packed_mx_bytes, moe_w8a8_read_probe, moe_w8a8_status_string, moe_w8a8_warm,
-                      moe_w8a8_workspace_size,
+                      moe_w8a8_packed_mx_bytes, moe_w8a8_read_probe, moe_w8a8_read_write_probe,
+                      moe_w8a8_status_string, moe_w8a8_warm, moe_w8a8_workspace_size,
                       pack_weights, upload, MOE_PACK_GMM1, MOE_PACK_GMM2, MOE_WEIGHT_INT8, MOE_WEIGHT_MXFP4,
                       MOE_WEIGHT_PACKED, MOE_WEIGHT_ROW_MAJOR)

@@ -23,7 +23,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20  # MOE_W8A8_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_forward", "moe_w8a8_forward_noalloc", "moe_w8a8_pack_weights",
            "moe_w8a8_packed_mx_bytes", "moe_w8a8_pack_weights_mx", "moe_w8a8_warm", "moe_w8a8_read_probe",
-           "moe_w8a8_status_string")
+           "moe_w8a8_read_write_probe", "moe_w8a8_status_string")
 MOE_WEIGHT_ROW_MAJOR, MOE_WEIGHT_PACKED = 0, 1
 MOE_WEIGHT_INT8, MOE_WEIGHT_MXFP4 = 0, 1
 MOE_PACK_GMM1, MOE_PACK_GMM2 = 1, 2
@@ -88,6 +88,8 @@ def library() -> ctypes.CDLL:
         L.moe_w8a8_warm.argtypes = [P, ctypes.c_size_t, P]
         L.moe_w8a8_read_probe.restype = ctypes.c_int
         L.moe_w8a8_read_probe.argtypes = [P, ctypes.c_size_t, P]
+        L.moe_w8a8_read_write_probe.restype = ctypes.c_int
+        L.moe_w8a8_read_write_probe.argtypes = [P, ctypes.c_size_t, P, ctypes.c_size_t, P]
         L.moe_w8a8_status_string.restype = ctypes.c_char_p
         L.moe_w8a8_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -148,6 +150,15 @@ def moe_w8a8_read_probe(t, nbytes: Optional[int] = None, stream=None) -> None:
     rc = library().moe_w8a8_read_probe(_ptr(t), n, _stream(stream))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_w8a8_read_probe")
+
+
+def moe_w8a8_read_write_probe(src, src_bytes: int, dst=None, dst_bytes: int = 0, stream=None) -> None:
+    """Read src_bytes of a device tensor in 256 KB work items and write dst_bytes
+    of another (arbitrary values) in equal shares at the items' ends: the
+    larger-batch GEMMs' read and write mix, for measurement."""
+    rc = library().moe_w8a8_read_write_probe(_ptr(src), src_bytes, _ptr(dst), dst_bytes, _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_w8a8_read_write_probe")
 
 
 def moe_w8a8_packed_mx_bytes(groups: int, n: int, k: int) -> int:

@@ -164,6 +164,21 @@ extern "C" moe_status_t moe_w8a8_read_probe(const void *ptr, size_t bytes, void 
     return launch_read_probe(ptr, bytes, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+extern "C" moe_status_t moe_w8a8_read_write_probe(const void *src, size_t src_bytes, void *dst, size_t dst_bytes,
+                                                  void *stream) {
+    if (src_bytes % (256 * 1024) || dst_bytes % 16 || dst_bytes > src_bytes) return MOE_ERR_INVALID_ARG;
+    if (src_bytes == 0) return MOE_OK;
+    if (!src || !aligned(src, 16) || src_bytes / (256 * 1024) > 0x7FFFFFFFu) return MOE_ERR_INVALID_ARG;
+    if (dst_bytes > 0) {
+        if (!dst || !aligned(dst, 16)) return MOE_ERR_INVALID_ARG;
+        const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+        if (s0 < d0 + dst_bytes && d0 < s0 + src_bytes) return MOE_ERR_INVALID_ARG;  // overlap
+    }
+    return launch_rw_probe(src, src_bytes, dst, dst_bytes, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
+}
+
 extern "C" const char *moe_w8a8_status_string(moe_status_t s) {
     switch (s) {
         case MOE_OK: return "ok";

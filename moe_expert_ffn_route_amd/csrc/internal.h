@@ -211,6 +211,7 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 // Reads [ptr, ptr + bytes) once and discards it (a cache warm); bytes % 16 == 0.
 hipError_t launch_warm(const void *ptr, size_t bytes, hipStream_t s);
 hipError_t launch_read_probe(const void *ptr, size_t bytes, hipStream_t s);
+hipError_t launch_rw_probe(const void *src, size_t src_bytes, void *dst, size_t dst_bytes, hipStream_t s);
 hipError_t launch_pack(const int8_t *src, int8_t *dst, int64_t groups, int n, int k, int which, hipStream_t s);
 hipError_t launch_pack_mx(const uint8_t *data, const uint8_t *bscale, uint8_t *dst, int64_t groups, int n, int k,
                           int which, hipStream_t s);

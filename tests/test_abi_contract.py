@@ -262,3 +262,22 @@ def test_noalloc_scratch_size_matches_header():
 def test_warm_and_read_probe_reject_bad_arguments(lib, entry, ptr, nbytes, code):
     # zero bytes is a no-op that launches nothing, whatever the pointer
     assert getattr(lib, entry)(ptr, nbytes, None) == code
+
+
+KB256 = 256 * 1024
+
+
+@pytest.mark.parametrize("src,src_bytes,dst,dst_bytes,code", [
+    (None, KB256, None, 0, binding.MOE_ERR_INVALID_ARG),            # NULL source
+    (FAKE + 8, KB256, None, 0, binding.MOE_ERR_INVALID_ARG),        # misaligned source
+    (FAKE, KB256 + 16, None, 0, binding.MOE_ERR_INVALID_ARG),       # not whole 256 KB items
+    (FAKE, KB256, None, 16, binding.MOE_ERR_INVALID_ARG),           # NULL destination
+    (FAKE, KB256, FAKE + 8, 16, binding.MOE_ERR_INVALID_ARG),       # misaligned destination
+    (FAKE, KB256, FAKE + 2 * KB256, 24, binding.MOE_ERR_INVALID_ARG),   # destination not whole 16 bytes
+    (FAKE, KB256, FAKE + 2 * KB256, 2 * KB256, binding.MOE_ERR_INVALID_ARG),  # writes more than it reads
+    (FAKE, KB256, FAKE + KB256 - 16, 32, binding.MOE_ERR_INVALID_ARG),  # destination overlaps the source
+    (FAKE, 0, None, 16, binding.MOE_ERR_INVALID_ARG),               # writes with nothing read
+    (None, 0, None, 0, binding.MOE_OK),                              # nothing at all: a no-op
+])
+def test_read_write_probe_rejects_bad_arguments(lib, src, src_bytes, dst, dst_bytes, code):
+    assert lib.moe_w8a8_read_write_probe(src, src_bytes, dst, dst_bytes, None) == code

@@ -62,3 +62,16 @@ def test_gemm_ops_count_two_per_multiply_add():
     rows = 4096 + 512
     assert g1 == 2 * rows * 2 * 2048 * 4096 and g2 == 2 * rows * 4096 * 2048
     assert bench.layer_ops(case, counts) == g1 + g2
+
+
+def test_gemm_write_bytes_at_t512():
+    # GEMM1 writes an fp32 h row of max(I, I_s) per grouped row, GEMM2 a bf16
+    # row of H per routed row and per active token (z and share_output)
+    s = synth.WORKLOADS[4]
+    case = _shape_only(s)
+    counts = np.full(256, 16, np.int32)  # 4096 routed rows
+    w1, w2 = bench.gemm_write_bytes(case, counts)
+    assert w1 == (4096 + 512) * 4 * 2048 == 37_748_736
+    assert w2 == (4096 + 512) * 2 * 4096
+    _, g1, g2, _, _ = bench.algorithmic_bytes(case, counts)
+    assert w1 < g1 and w2 < g2

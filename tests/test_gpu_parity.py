@@ -569,3 +569,19 @@ def test_read_probe_reads_and_changes_nothing(nbytes):
         moe.moe_w8a8_read_probe(buf, nbytes)
     torch.cuda.synchronize()
     assert torch.equal(buf, ref)
+
+
+@pytest.mark.parametrize("items,dst_bytes", [(1, 0), (1, 4096), (16, 48 * 1024 + 16 * 7), (64, 1 << 20)])
+def test_read_write_probe_writes_only_its_range(items, dst_bytes):
+    # the read-and-write probe leaves its source unchanged and writes nothing
+    # outside [dst, dst + dst_bytes): the guard band after the range keeps
+    # every byte, also when the range does not split evenly over the items
+    src_bytes = items * 256 * 1024
+    src = torch.randint(0, 256, (src_bytes,), dtype=torch.uint8, device="cuda")
+    dst = torch.randint(0, 256, (dst_bytes + 8192,), dtype=torch.uint8, device="cuda")
+    src_ref, guard = src.clone(), dst[dst_bytes:].clone()
+    for _ in range(2):
+        moe.moe_w8a8_read_write_probe(src, src_bytes, dst, dst_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(src, src_ref)
+    assert torch.equal(dst[dst_bytes:], guard)
