@@ -12,9 +12,11 @@
 //     expert (sec. 6.2: the shared expert's rows go to memory, routed rows on
 //     to combine).
 //
-// Decode (at most 16 tokens, so at most 16 rows per expert; larger batches
-// go to gemm_wide.hip) is bound by the weight stream: each touched expert's
-// bytes are read once, so the kernel is shaped around HBM, not around MFMA
+// Work items of 16 rows: decode batches (at most 16 tokens, so at most 16
+// rows per expert; larger batches go to gemm_wide.hip), and with group-wise
+// activation scales any batch whose local experts average fewer than 16
+// rows. That work is bound by the weight stream: each touched expert's bytes
+// are read once, so the kernel is shaped around HBM, not around MFMA
 // throughput:
 //   - a work item is (chunk of <= 16 rows of one expert, 16-channel N tile
 //     pair); its 2 x 16 weight rows are split over the waves along K; each
