@@ -14,8 +14,9 @@ constexpr int kRouteWaves = kRouteThreads / kWave;
 // Grouped rows per GEMM work item (INT8 weights, one scale per row): one
 // 16-row MFMA tile when T <= 16 (decode; gemm.hip), MOE_WIDE_MT tiles
 // otherwise (gemm_wide.hip, which shares each chunk's activations across the
-// waves of a workgroup), or tall items (below). Group-wise scales run 16-row
-// items at every T; FP4 weights 16- or 32-row items (gemm_mx.hip).
+// waves of a workgroup), or tall items (below). Group-wise scales and FP4
+// weights run 16-row items, or 32-row ones when the local experts can average
+// 16 rows or more (group-wise: gemm.hip / gemm_wide.hip; FP4: gemm_mx.hip).
 #ifndef MOE_WIDE_MT
 #define MOE_WIDE_MT 2
 #endif
