@@ -646,6 +646,20 @@ def main():
     if roofline["bound"] == "hbm":
         roofline["measured_peak"] = read_probe["gbps"]
         roofline["frac_of_measured_peak"] = round(g1_gbs / read_probe["gbps"], 4)
+    gemm2_rec = {"achieved": round(gemm2_bytes / (g2_us * 1e-6) / 1e9, 1), "unit": "GB/s",
+                 "algorithmic_bytes": gemm2_bytes, "avg_us": round(g2_us, 2),
+                 "tops": round(g2_ops / (g2_us * 1e-6) / 1e12, 1)}
+    if spec.T > 16 and roofline["bound"] == "hbm":
+        # batches past decode write tens of MB of output rows while their
+        # weights stream: each GEMM is also set against a probe of its own
+        # read and write bytes
+        log("[bench] read-write probes (each GEMM's byte mix)")
+        for rec_g, total, w, g_us in ((roofline, gemm1_bytes, gemm_write_bytes(case, counts)[0], g1_us),
+                                      (gemm2_rec, gemm2_bytes, gemm_write_bytes(case, counts)[1], g2_us)):
+            rw = hbm_read_write_probe(stream, fence_free, total - w, w)
+            rec_g["write_bytes"] = w
+            rec_g["read_write_probe"] = rw
+            rec_g["frac_of_read_write_probe"] = round(rw["us"] / g_us, 4)
     headline = args.config == 1 and not mx and not args.quant_group
     rec = {
         "metric": ("µs per MoE layer (T=8 decode); achieved HBM GB/s in hbm_gbps; INT8 TOP/s at T=512 in "
@@ -680,9 +694,7 @@ def main():
         "hbm_read_probe": read_probe,
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},  # separate pass, every stage bracketed
         "roofline": roofline,
-        "gemm2": {"achieved": round(gemm2_bytes / (g2_us * 1e-6) / 1e9, 1), "unit": "GB/s",
-                  "algorithmic_bytes": gemm2_bytes, "avg_us": round(g2_us, 2),
-                  "tops": round(g2_ops / (g2_us * 1e-6) / 1e12, 1)},
+        "gemm2": gemm2_rec,
     }
     if headline and not args.no_large_batch and not graphs:
         log("[bench] large-batch leg (T = 512, same resident weights)")
