@@ -14,7 +14,11 @@ its experts' weights from HBM rather than from the 256 MB last-level cache.
 Prints one JSON line: the metric (µs per MoE layer), the achieved HBM GB/s of
 the layer, the roofline of the dominant kernel (GEMM1) from HIP events bound
 to that kernel's launch (hipExtLaunchKernel) in every timed step, and the CPU
-oracle's time on this host as a baseline.
+oracle's time on this host as a baseline. Memory-bound GEMMs are also set
+against measured ceilings: a read probe with their weight-stream pattern
+(moe_w8a8_read_probe) and, for batches past decode, whose GEMMs write tens
+of MB of output rows while their weights stream, a probe of each GEMM's own
+read and write bytes (moe_w8a8_read_write_probe).
 
 `--weight-format mxfp4` times the FP4-weight / FP8-activation variant of the
 same workload instead (E2M1 weights with E8M0 block scales, 0.53 bytes per
